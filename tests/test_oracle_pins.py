@@ -1,0 +1,407 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+None of these re-types the oracle's own formula: each check is a closed
+form, an invariant, a special case that reduces to a library routine, brute
+force, or a hand-derived fixture, chosen so that a dropped term, a wrong
+sign, a wrong index or a swapped operand in the oracle fails at least one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _clustered(rng, N, d, n_comp=4, spread=0.3):
+    lab = rng.integers(0, n_comp, N)
+    mu = rng.standard_normal((n_comp, d)) * 2.0
+    return mu[lab] + spread * rng.standard_normal((N, d))
+
+
+def _sdpa(q, k, v):
+    """Dense softmax attention from torch's own routine, fp64 on the CPU."""
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v))[0, 0].numpy()
+
+
+# --- bookkeeping ------------------------------------------------------------
+
+def test_block_counts_and_topk_rounding():
+    assert O.n_blocks(245952, 128) == 1922
+    assert list(O.block_sizes(245952, 128)[-2:]) == [128, 64]
+    assert O.n_blocks(16128, 128) == 126
+    assert O.block_sizes(1025, 64)[-1] == 1
+    # the budget covers the ratio: ceil, clamped to [1, n]
+    assert O.topk_from_ratio(0.1, 1922) == 193
+    assert O.topk_from_ratio(0.1, 126) == 13
+    assert O.topk_from_ratio(0.2, 126) == 26
+    assert O.topk_from_ratio(0.3, 126) == 38
+    assert O.topk_from_ratio(1.0, 126) == 126
+    assert O.topk_from_ratio(0.25, 16) == 4
+    assert O.topk_from_ratio(0.2, 1985) == 397
+    assert O.topk_from_ratio(0.0, 10) == 1
+    assert O.topk_from_ratio(2.0, 10) == 10
+
+
+# --- moments, square root, whitening ---------------------------------------
+
+def test_second_moment_is_uncentred_and_divides_by_n():
+    u = np.array([1.0, -2.0, 3.0])
+    x = np.tile(u, (7, 1))               # every row equal: centred moment would be 0
+    np.testing.assert_allclose(O.second_moment(x), np.outer(u, u), rtol=0, atol=1e-14)
+    # two orthogonal rows: diag(1/2, 1/2, 0)
+    x = np.array([[1.0, 0, 0], [0, 1.0, 0]])
+    np.testing.assert_allclose(O.second_moment(x), np.diag([0.5, 0.5, 0.0]), atol=1e-15)
+
+
+def test_psd_sqrt_squares_back_and_is_psd():
+    rng = _rng(1)
+    A = rng.standard_normal((64, 40))
+    M = A @ A.T / 40                      # rank-deficient PSD
+    W = O.psd_sqrt(M)
+    np.testing.assert_allclose(W @ W, M, atol=1e-12 * np.abs(M).max() * 64)
+    np.testing.assert_allclose(W, W.T, atol=1e-14)
+    assert np.linalg.eigvalsh(W).min() > -1e-10
+    # diagonal case is the elementwise root
+    np.testing.assert_allclose(O.psd_sqrt(np.diag([4.0, 9.0, 0.0])), np.diag([2.0, 3.0, 0.0]), atol=1e-15)
+
+
+def test_whiten_gives_mahalanobis_cosine():
+    """x^_i . x^_j must equal the cosine under the metric M = W^2:
+    x_i^T M x_j / sqrt(x_i^T M x_i x_j^T M x_j) (the d_Q equation)."""
+    rng = _rng(2)
+    d = 16
+    A = rng.standard_normal((d, d))
+    M = A @ A.T / d + 0.1 * np.eye(d)
+    W = O.psd_sqrt(M)
+    x = rng.standard_normal((10, d))
+    xh = O.whiten(x, W)
+    G = x @ M @ x.T
+    cos = G / np.sqrt(np.outer(np.diag(G), np.diag(G)))
+    np.testing.assert_allclose(xh @ xh.T, cos, atol=1e-12)
+    # zero rows stay zero
+    x[3] = 0
+    assert np.all(O.whiten(x, W)[3] == 0)
+
+
+# --- the partitioner ---------------------------------------------------------
+
+def test_split_hand_derived_fixture():
+    g = json.load(open(os.path.join(GOLDEN, "split_hand_example.json")))
+    x = np.array(g["x"], dtype=np.float64)
+    perm = O.split_partition(x, g["block"])
+    assert perm.tolist() == g["perm"]
+    g = json.load(open(os.path.join(GOLDEN, "split_hand_example_odd.json")))
+    x = np.array(g["x"], dtype=np.float64)
+    for case in g["cases"]:
+        assert O.split_partition(x, case["block"]).tolist() == case["perm"]
+
+
+def _check_perm_structure(perm, N, b):
+    assert sorted(perm.tolist()) == list(range(N))          # bijection
+    nb = O.n_blocks(N, b)
+    for B in range(nb):
+        leaf = perm[B * b:min(N, (B + 1) * b)]
+        assert np.all(np.diff(leaf) > 0)                       # ids ascending inside a leaf
+
+
+@pytest.mark.parametrize("N,b", [(1024, 64), (1025, 64), (1000, 128), (7, 2), (1, 4), (130, 128), (512, 1)])
+def test_split_is_bijection_with_leaves_of_block_size(N, b):
+    rng = _rng(N + b)
+    x = O.whiten(rng.standard_normal((N, 8)), np.eye(8))
+    perm = O.split_partition(x, b)
+    _check_perm_structure(perm, N, b)
+
+
+def test_split_recovers_tight_clusters_matching_capacities():
+    """8 tight clusters of exactly one block each, spread along an arc of a
+    plane: the two poles land in the end clusters, the score orders whole
+    clusters along the arc, so with capacities equal to cluster sizes every
+    leaf must be one pure cluster and every subtree a contiguous arc."""
+    rng = _rng(3)
+    b, C, d = 16, 8, 8
+    ang = np.deg2rad(np.arange(C) * 20.0)
+    centers = np.zeros((C, d))
+    centers[:, 0], centers[:, 1] = np.cos(ang), np.sin(ang)
+    lab = rng.permutation(np.repeat(np.arange(C), b))
+    x = centers[lab] + 0.005 * rng.standard_normal((C * b, d))
+    perm = O.split_partition(O.whiten(x, np.eye(d)), b)
+    leaf_labels = []
+    for B in range(C):
+        ls = set(lab[perm[B * b:(B + 1) * b]].tolist())
+        assert len(ls) == 1
+        leaf_labels.append(ls.pop())
+    assert sorted(leaf_labels[:4]) in ([0, 1, 2, 3], [4, 5, 6, 7])
+    for m in range(0, C, 2):
+        assert abs(leaf_labels[m] - leaf_labels[m + 1]) == 1
+
+
+def test_queries_are_whitened_by_the_key_moment():
+    """Keys carry no energy along e_0, so M_K kills every query difference
+    along e_0: all queries become identical under d_Q and the partition is
+    the identity (all ties -> lower id).  Whitening queries by their own
+    moment would separate them."""
+    rng = _rng(4)
+    N, d, b = 256, 8, 32
+    k = rng.standard_normal((N, d))
+    k[:, 0] = 0.0
+    q = np.tile(rng.standard_normal(d), (N, 1))
+    q[:, 0] = rng.standard_normal(N) * 3.0
+    pq, pk = O.reblock_head(q, k, b)
+    assert pq.tolist() == list(range(N))
+    assert pk.tolist() != list(range(N))
+    # control: the same queries whitened by their own moment do get reordered
+    own = O.split_partition(O.whiten(q, O.psd_sqrt(O.second_moment(q))), b)
+    assert own.tolist() != list(range(N))
+
+
+def test_any_factor_of_the_moment_gives_the_same_partition():
+    """Cosines under M depend only on M = L L^T: whitening with the
+    Cholesky factor (x -> L^T x) must give the same permutation."""
+    rng = _rng(5)
+    q = _clustered(rng, 512, 16)
+    k = _clustered(rng, 512, 16)
+    b = 32
+    MK = O.second_moment(k)
+    L = np.linalg.cholesky(MK)
+    p_sqrt = O.split_partition(O.whiten(q, O.psd_sqrt(MK)), b)
+    p_chol = O.split_partition(O.whiten(q, L.T), b)
+    assert p_sqrt.tolist() == p_chol.tolist()
+
+
+def test_reblock_invariant_to_rotation_and_scale():
+    rng = _rng(6)
+    N, d, b = 768, 16, 64
+    q = _clustered(rng, N, d, 6)
+    k = _clustered(rng, N, d, 6)
+    pq, pk = O.reblock_head(q, k, b)
+    R, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    pq2, pk2 = O.reblock_head(q @ R, k @ R, b)
+    assert pq.tolist() == pq2.tolist() and pk.tolist() == pk2.tolist()
+    pq3, pk3 = O.reblock_head(3.5 * q, 0.25 * k, b)
+    assert pq.tolist() == pq3.tolist() and pk.tolist() == pk3.tolist()
+
+
+# --- pooling, scores, top-k --------------------------------------------------
+
+def test_gather_pool_means_over_real_rows():
+    x = np.repeat(np.arange(5, dtype=np.float64)[:, None], 3, axis=1)   # row i = (i, i, i)
+    perm = np.array([4, 2, 0, 1, 3])
+    xp, means = O.gather_pool(x, perm, 2)
+    assert xp[:, 0].tolist() == [4, 2, 0, 1, 3]
+    np.testing.assert_allclose(means[:, 0], [3.0, 0.5, 3.0])            # last block has one row
+
+
+def test_block_scores_closed_form():
+    d = 16
+    qbar = np.zeros((2, d)); qbar[0, 0] = 2.0; qbar[1, 1] = -1.0
+    kbar = np.zeros((3, d)); kbar[0, 0] = 3.0; kbar[1, 1] = 5.0; kbar[2, 0] = 1.0
+    S = O.block_scores(qbar, kbar)
+    np.testing.assert_allclose(S, np.array([[6.0, 0, 2.0], [0, -5.0, 0]]) / 4.0)
+
+
+def _brute_topk(row, k):
+    items = sorted(range(len(row)), key=lambda j: (1 if math.isnan(row[j]) else 0,
+                                                   0.0 if math.isnan(row[j]) else -row[j], j))
+    return sorted(items[:k])
+
+
+def test_topk_matches_brute_force_with_ties_and_nan():
+    rng = _rng(7)
+    S = rng.integers(-3, 4, size=(40, 50)).astype(np.float64)    # many ties
+    S[0, :] = 1.0
+    S[1, 5] = np.nan
+    S[2, :] = -np.inf
+    S[2, 7] = np.nan
+    for k in (1, 7, 25, 50):
+        idx = O.select_topk(S, k)
+        for A in range(S.shape[0]):
+            assert idx[A].tolist() == _brute_topk(S[A].tolist(), k)
+    assert O.select_topk(S, 3)[0].tolist() == [0, 1, 2]
+    assert 7 not in O.select_topk(S, 49)[2].tolist()            # NaN below -inf
+
+
+# --- Spark-Reweight ----------------------------------------------------------
+
+def test_anchor_is_mean_of_video_queries():
+    q = np.arange(12, dtype=np.float64).reshape(6, 2)
+    np.testing.assert_allclose(O.anchor_query(q, 4), [3.0, 4.0])
+    np.testing.assert_allclose(O.anchor_query(q, 6), [5.0, 6.0])
+
+
+def test_size_one_tail_block_summary_is_the_token():
+    rng = _rng(8)
+    N, d, b = 1025, 64, 64
+    k = rng.standard_normal((N, d))
+    v = rng.standard_normal((N, d))
+    qhat = rng.standard_normal(d)
+    ks, vs, beta = O.reweight_summaries(k, v, qhat, b)
+    assert beta[-1] == 0.0
+    assert np.array_equal(ks[-1], k[-1]) and np.array_equal(vs[-1], v[-1])
+
+
+def test_bias_restores_mean_exponential():
+    """exp(anchor logit of the summary + bias) = the block's mean exp-logit
+    under the anchor (the Jensen-gap figure of the Spark-Reweight section)."""
+    rng = _rng(9)
+    N, d, b = 700, 32, 128
+    k = rng.standard_normal((N, d)) * 1.5
+    v = rng.standard_normal((N, d))
+    qhat = rng.standard_normal(d)
+    ks, vs, beta = O.reweight_summaries(k, v, qhat, b)
+    for B in range(O.n_blocks(N, b)):
+        kB = k[B * b:min(N, (B + 1) * b)]
+        want = np.mean([math.exp(float(kj @ qhat) / math.sqrt(d)) for kj in kB])
+        got = math.exp(float(qhat @ ks[B]) / math.sqrt(d) + beta[B])
+        assert abs(got / want - 1) < 1e-12
+
+
+def test_summary_is_first_order_exact_around_the_anchor():
+    """For q = q^ + eps*u the summary logit (+ log|B|) matches the block's
+    exact log-partition to O(eps^2): the weighted key is the gradient of
+    the log-partition at the anchor.  A wrong k~ leaves an O(eps) error."""
+    rng = _rng(10)
+    d, n = 32, 128
+    kB = rng.standard_normal((n, d)) * 1.2
+    vB = rng.standard_normal((n, d))
+    qhat = rng.standard_normal(d) * 0.5
+    ks, vs, beta = O.reweight_summaries(kB, vB, qhat, n)
+    u = rng.standard_normal(d)
+    errs = []
+    for eps in (1e-2, 5e-3):
+        q = qhat + eps * u
+        exact = np.log(np.exp(kB @ q / math.sqrt(d)).sum())
+        approx = float(q @ ks[0]) / math.sqrt(d) + beta[0] + math.log(n)
+        errs.append(abs(exact - approx))
+    assert errs[0] < 1e-3 and errs[1] < errs[0] / 3.0      # quadratic decay
+
+
+def test_equal_keys_block_is_exact_for_every_query():
+    rng = _rng(11)
+    N, d, b = 256, 16, 64
+    k = rng.standard_normal((N, d))
+    k[64:128] = k[64]                       # block 1: all keys equal
+    v = rng.standard_normal((N, d))
+    qhat = rng.standard_normal(d)
+    ks, vs, beta = O.reweight_summaries(k, v, qhat, b)
+    np.testing.assert_allclose(ks[1], k[64], atol=1e-13)
+    assert abs(beta[1]) < 1e-12
+    for _ in range(5):
+        q = rng.standard_normal(d) * 2
+        exact_mass = np.exp(k[64:128] @ q / 4.0).sum()
+        exact_num = np.exp(k[64:128] @ q / 4.0) @ v[64:128]
+        lam = float(q @ ks[1]) / 4.0 + beta[1]
+        np.testing.assert_allclose(64 * math.exp(lam), exact_mass, rtol=1e-12)
+        np.testing.assert_allclose(64 * math.exp(lam) * vs[1], exact_num, rtol=1e-10, atol=1e-12)
+
+
+def test_mean_pooling_underestimates_mass_jensen():
+    rng = _rng(12)
+    N, d, b = 512, 32, 64
+    k = rng.standard_normal((N, d)) * 2
+    v = rng.standard_normal((N, d))
+    ks, vs, beta = O.mean_summaries(k, v, b)
+    assert np.all(beta == 0)
+    for _ in range(10):
+        q = rng.standard_normal(d)
+        for B in range(N // b):
+            kB = k[B * b:(B + 1) * b]
+            assert b * math.exp(float(q @ ks[B]) / math.sqrt(d)) <= np.exp(kB @ q / math.sqrt(d)).sum()
+
+
+# --- the two-branch attention ------------------------------------------------
+
+@pytest.mark.parametrize("layout", ["reblock", "identity"])
+def test_full_density_equals_dense_attention(layout):
+    rng = _rng(13)
+    N, d, b = 1000, 32, 64
+    q, k, v = (rng.standard_normal((N, d)) * s for s in (1.0, 1.5, 1.0))
+    nb = O.n_blocks(N, b)
+    r = O.forward_head(q, k, v, b, nb, layout=layout)
+    np.testing.assert_allclose(r.out, _sdpa(q, k, v), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("topk", [1, 3, 40])
+def test_block_size_one_equals_dense_at_any_density(topk):
+    rng = _rng(14)
+    N, d = 80, 16
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    r = O.forward_head(q, k, v, 1, topk)
+    np.testing.assert_allclose(r.out, _sdpa(q, k, v), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("summary", ["reweight", "mean"])
+def test_anchor_query_gets_dense_output_only_with_reweight(summary):
+    """Set q_0 to the mean of the other video queries, so the anchor (mean of
+    all video queries) equals q_0.  Under Spark-Reweight that query's output
+    equals dense attention at any density (every compressed block contributes
+    exactly its dense mass and value); mean pooling does not."""
+    rng = _rng(15)
+    N, d, b, n_anchor = 640, 32, 64, 600
+    q = _clustered(rng, N, d, 5, 0.5)
+    k = _clustered(rng, N, d, 5, 0.5)
+    v = rng.standard_normal((N, d))
+    q[0] = q[1:n_anchor].mean(axis=0)
+    r = O.forward_head(q, k, v, b, 2, n_anchor=n_anchor, summary=summary)
+    np.testing.assert_allclose(r.anchor, q[0], atol=1e-12)
+    dense0 = _sdpa(q[:1], k, v)[0]
+    err = np.abs(r.out[0] - dense0).max()
+    if summary == "reweight":
+        assert err < 1e-10
+    else:
+        assert err > 1e-4
+
+
+def test_relabelling_tokens_permutes_outputs():
+    rng = _rng(16)
+    N, d, b = 512, 16, 32
+    q = _clustered(rng, N, d, 5, 0.4)
+    k = _clustered(rng, N, d, 5, 0.4)
+    v = rng.standard_normal((N, d))
+    sigma = rng.permutation(N)
+    r1 = O.forward_head(q, k, v, b, 3)
+    r2 = O.forward_head(q[sigma], k[sigma], v[sigma], b, 3)
+    np.testing.assert_allclose(r2.out, r1.out[sigma], atol=1e-10)
+    # the same block memberships, only relabelled
+    for B in range(N // b):
+        assert set(sigma[r2.perm_q[B * b:(B + 1) * b]].tolist()) == set(r1.perm_q[B * b:(B + 1) * b].tolist())
+
+
+def test_recall_and_log_mass_closed_forms():
+    rng = _rng(17)
+    N, d, b = 256, 8, 32
+    k = rng.standard_normal((N, d))
+    v = rng.standard_normal((N, d))
+    q = np.zeros((N, d))                     # uniform dense attention
+    r = O.forward_head(q, k, v, b, 3, layout="identity")
+    assert abs(O.attention_mass_recall(r, b) - 3 * b / N) < 1e-12
+    r = O.forward_head(rng.standard_normal((N, d)), k, v, b, 8)
+    assert abs(O.attention_mass_recall(r, b) - 1.0) < 1e-12
+    r = O.forward_head(rng.standard_normal((N, d)), k, v, 1, 5)
+    assert O.log_mass_error(r, 1) < 1e-12
+
+
+def test_direction_of_the_pages_ablations_on_clustered_data():
+    """Direction only (the pages' numbers come from model activations and
+    are not reproducible here): reblocking raises attention-mass recall over
+    consecutive blocks, and reweighting lowers the log-mass error of mean
+    pooling, at 10% density on the clustered generator."""
+    from block_sparse_attention_mahalanobis_amd.workload import WORKLOADS, make_head
+    w = WORKLOADS["draft"]
+    q, k, v = make_head(w, 0)
+    b, kk = w.block, O.topk_from_ratio(w.ratio, O.n_blocks(w.N, w.block))
+    re = O.forward_head(q, k, v, b, kk)
+    fx = O.forward_head(q, k, v, b, kk, layout="identity")
+    mn = O.forward_head(q, k, v, b, kk, layout="identity", summary="mean")
+    assert O.attention_mass_recall(re, b) > O.attention_mass_recall(fx, b)
+    assert O.log_mass_error(fx, b) < O.log_mass_error(mn, b)
