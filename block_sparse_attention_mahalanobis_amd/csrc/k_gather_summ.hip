@@ -1,0 +1,256 @@
+// Permutation gather + block pooling ("Spark-H3" blog, 01 / Method:
+// Spark-Reblock: token IDs track membership through the tree, and blocks are
+// scored from block-level means, Discussion section) and the compressed-branch
+// summaries (02 / Method: Spark-Reweight: each block is scored once with the
+// mean video query; the scores give weighted key/value summaries and a
+// log-mass bias).  Both are HBM-streaming kernels: one workgroup per
+// (head, block), 16-byte row loads, fp32 accumulation in a fixed order.
+#include "common.hpp"
+
+namespace spark {
+
+// ---------------------------------------------------------------------------
+// gather: x_p[h][p] = x[h][perm[h][p]] (rows >= N zero), x_pt the
+// block-transposed layout [H, nb, D, BK], xbar the fp32 block means.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ x,
+                                                     const int32_t* __restrict__ perm,
+                                                     T* __restrict__ xp, T* __restrict__ xpt,
+                                                     float* __restrict__ xbar, int N, int BK,
+                                                     int nb, int identity) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  T* tile = reinterpret_cast<T*>(smem);  // [BK][D + pad]
+  constexpr int PAD = 16 / sizeof(T);
+  constexpr int RS = D + PAD;
+  const int h = blockIdx.x / nb, B = blockIdx.x % nb;
+  const int tid = threadIdx.x;
+  const int n_real = min(BK, N - B * BK);
+  const long Np = (long)nb * BK;
+  constexpr int CPR = D / 8;  // 8-element chunks per row
+  for (int ch = tid; ch < BK * CPR; ch += blockDim.x) {
+    const int j = ch / CPR, c = (ch % CPR) * 8;
+    float v[8];
+    if (j < n_real) {
+      const long p = (long)B * BK + j;
+      const long src = identity ? p : (long)perm[(long)h * N + p];
+      load8(x + ((long)h * N + src) * D + c, v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    }
+    if (xp) store8(xp + ((long)h * Np + (long)B * BK + j) * D + c, v);
+    if (sizeof(T) == 2) {
+      uint16_t* t16 = reinterpret_cast<uint16_t*>(tile + j * RS + c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t16[e] = f2bf(v[e]);  // exact: v came from bf16
+    } else {
+      float* t32 = reinterpret_cast<float*>(tile + j * RS + c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t32[e] = v[e];
+    }
+  }
+  __syncthreads();
+  if (xpt) {
+    // [D][BK]: thread handles (c, j-run); consecutive threads take consecutive j
+    for (int e = tid; e < D * BK; e += blockDim.x) {
+      const int c = e / BK, j = e % BK;
+      xpt[(((long)h * nb + B) * D + c) * BK + j] = tile[j * RS + c];
+    }
+  }
+  if (xbar) {
+    for (int c = tid; c < D; c += blockDim.x) {
+      float s = 0.f;
+      for (int j = 0; j < n_real; ++j) s += Elem<T>::load(tile + j * RS + c);
+      xbar[((long)h * nb + B) * D + c] = s / (float)n_real;
+    }
+  }
+}
+
+template <typename T, int D>
+static int gather_t(int H, int N, int BK, const void* x, const int32_t* perm, void* xp, void* xpt,
+                    float* xbar, hipStream_t st) {
+  const int nb = cdiv(N, BK);
+  constexpr int PAD = 16 / sizeof(T);
+  const size_t lds = (size_t)BK * (D + PAD) * sizeof(T);
+  static bool attr = false;
+  if (!attr) {
+    hipFuncSetAttribute((const void*)gather_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+    attr = true;
+  }
+  hipLaunchKernelGGL((gather_kernel<T, D>), dim3(H * nb), dim3(256), lds, st, (const T*)x, perm,
+                     (T*)xp, (T*)xpt, xbar, N, BK, nb, perm == nullptr ? 1 : 0);
+  return spark_check_launch("gather");
+}
+
+int gather_launch(int H, int N, int D, int BK, int dtype, const void* x, const int32_t* perm,
+                  void* xp, void* xpt, float* xbar, hipStream_t st) {
+  if (dtype == SPARK_F32)
+    return D == 128 ? gather_t<float, 128>(H, N, BK, x, perm, xp, xpt, xbar, st)
+                    : gather_t<float, 64>(H, N, BK, x, perm, xp, xpt, xbar, st);
+  return D == 128 ? gather_t<uint16_t, 128>(H, N, BK, x, perm, xp, xpt, xbar, st)
+                  : gather_t<uint16_t, 64>(H, N, BK, x, perm, xp, xpt, xbar, st);
+}
+
+// ---------------------------------------------------------------------------
+// summaries.  REWEIGHT:  t_j = anchor.k_j / sqrt(d);  w = softmax_B(t);
+//   ksum = sum w_j k_j;  vsum = sum w_j v_j;
+//   bias = max t + log sum exp(t - max t) - log n_B - anchor.ksum / sqrt(d)
+// MEAN: w_j = 1 / n_B, bias = 0.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void summarize_kernel(const T* __restrict__ kp,
+                                                        const T* __restrict__ vpt,
+                                                        const float* __restrict__ anchor,
+                                                        float* __restrict__ ksum,
+                                                        float* __restrict__ vsum,
+                                                        float* __restrict__ bias, int N, int BK,
+                                                        int nb, int mean_mode, float rsd) {
+  __shared__ float s_anchor[D];
+  __shared__ float s_w[128];
+  __shared__ float s_t[128];
+  __shared__ float s_part[16][D];
+  __shared__ float s_red[2];
+  const int h = blockIdx.x / nb, B = blockIdx.x % nb;
+  const int tid = threadIdx.x;
+  const int n_real = min(BK, N - B * BK);
+  const long Np = (long)nb * BK;
+  const T* kblk = kp + ((long)h * Np + (long)B * BK) * D;
+  const T* vblk = vpt + ((long)h * nb + B) * (long)D * BK;
+  constexpr int CPR = D / 8;           // chunks per row
+  constexpr int RPP = 256 / CPR;       // rows per pass
+
+  if (!mean_mode) {
+    for (int c = tid; c < D; c += 256) s_anchor[c] = anchor[(long)h * D + c];
+    __syncthreads();
+    // t_j: CPR lanes per row, reduced with shuffles (CPR is 8 or 16)
+    for (int j0 = 0; j0 < n_real; j0 += RPP) {
+      const int j = j0 + tid / CPR, c = (tid % CPR) * 8;
+      float acc = 0.f;
+      if (j < n_real) {
+        float v[8];
+        load8(kblk + (long)j * D + c, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf(v[e], s_anchor[c + e], acc);
+      }
+#pragma unroll
+      for (int o = CPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+      if (j < n_real && (tid % CPR) == 0) s_w[j] = acc * rsd;
+    }
+    __syncthreads();
+    if (tid < 64) {
+      float m = -INFINITY;
+      for (int j = tid; j < n_real; j += 64) m = fmaxf(m, s_w[j]);
+      m = wave_max(m);
+      float z = 0.f;
+      for (int j = tid; j < n_real; j += 64) z += expf(s_w[j] - m);
+      z = wave_sum(z);
+      if (tid == 0) { s_red[0] = m; s_red[1] = z; }
+    }
+    __syncthreads();
+    const float m = s_red[0], z = s_red[1];
+    for (int j = tid; j < n_real; j += 256) {
+      s_t[j] = s_w[j];
+      s_w[j] = expf(s_w[j] - m) / z;
+    }
+    __syncthreads();
+  } else {
+    for (int j = tid; j < n_real; j += 256) s_w[j] = 1.f / (float)n_real;
+    __syncthreads();
+  }
+
+  // ksum: row-chunk partials over RPP row groups, then a fixed-order reduce
+  {
+    const int rg = tid / CPR, c = (tid % CPR) * 8;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = rg; j < n_real; j += RPP) {
+      float v[8];
+      load8(kblk + (long)j * D + c, v);
+      const float w = s_w[j];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, v[e], acc[e]);
+    }
+    if (rg < 16) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_part[rg][c + e] = acc[e];
+    }
+    // RPP is 16 (D=128) or 32 (D=64): fold rows 16..31 in a second step
+    __syncthreads();
+    if (RPP > 16 && rg >= 16) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_part[rg - 16][c + e] += acc[e];
+    }
+    __syncthreads();
+  }
+  float kval = 0.f;
+  if (tid < D) {
+    for (int r = 0; r < 16; ++r) kval += s_part[r][tid];
+    ksum[((long)h * nb + B) * D + tid] = kval;
+  }
+  // vsum from the transposed block: row c of vpt holds the block's values of column c
+  for (int c = tid; c < D; c += 256) {
+    const T* row = vblk + (long)c * BK;
+    float acc = 0.f;
+    for (int j = 0; j < n_real; ++j) acc = fmaf(s_w[j], Elem<T>::load(row + j), acc);
+    vsum[((long)h * nb + B) * D + c] = acc;
+  }
+  if (mean_mode) {
+    if (tid == 0) bias[(long)h * nb + B] = 0.f;
+    return;
+  }
+  // bias = m + log z - log n_B - anchor . ksum / sqrt(d).  Since
+  // anchor . ksum / sqrt(d) = sum_j w_j t_j, this equals
+  // log z - log n_B + sum_j w_j (m - t_j), which is exactly 0 for a
+  // one-token block.  s_t holds the logits t_j (saved before w overwrote them).
+  if (tid < 64) {
+    const float m = s_red[0], z = s_red[1];
+    float a = 0.f;
+    for (int j = tid; j < n_real; j += 64) a = fmaf(s_w[j], m - s_t[j], a);
+    a = wave_sum(a);
+    if (tid == 0) bias[(long)h * nb + B] = logf(z) - logf((float)n_real) + a;
+  }
+}
+
+template <typename T, int D>
+static int summarize_t(int H, int N, int BK, const void* kp, const void* vpt, const float* anchor,
+                       float* ksum, float* vsum, float* bias, int mean_mode, hipStream_t st) {
+  const int nb = cdiv(N, BK);
+  hipLaunchKernelGGL((summarize_kernel<T, D>), dim3(H * nb), dim3(256), 0, st, (const T*)kp,
+                     (const T*)vpt, anchor, ksum, vsum, bias, N, BK, nb, mean_mode,
+                     1.f / sqrtf((float)D));
+  return spark_check_launch("summarize");
+}
+
+int summarize_launch(int H, int N, int D, int BK, int dtype, const void* kp, const void* vpt,
+                     const float* anchor, float* ksum, float* vsum, float* bias, int mean_mode,
+                     hipStream_t st) {
+  if (dtype == SPARK_F32)
+    return D == 128 ? summarize_t<float, 128>(H, N, BK, kp, vpt, anchor, ksum, vsum, bias, mean_mode, st)
+                    : summarize_t<float, 64>(H, N, BK, kp, vpt, anchor, ksum, vsum, bias, mean_mode, st);
+  return D == 128 ? summarize_t<uint16_t, 128>(H, N, BK, kp, vpt, anchor, ksum, vsum, bias, mean_mode, st)
+                  : summarize_t<uint16_t, 64>(H, N, BK, kp, vpt, anchor, ksum, vsum, bias, mean_mode, st);
+}
+
+// anchor[h] = mean of query rows [0, n_anchor) (column sums in row order)
+template <typename T>
+__global__ __launch_bounds__(256) void anchor_kernel(const T* __restrict__ q,
+                                                     float* __restrict__ anchor, int N, int D,
+                                                     int n_anchor) {
+  const int h = blockIdx.x;
+  for (int c = threadIdx.x; c < D; c += blockDim.x) {
+    float s = 0.f;
+    for (int i = 0; i < n_anchor; ++i) s += Elem<T>::load(q + ((long)h * N + i) * D + c);
+    anchor[(long)h * D + c] = s / (float)n_anchor;
+  }
+}
+
+int anchor_launch(int H, int N, int D, int dtype, const void* q, float* anchor, int n_anchor,
+                  hipStream_t st) {
+  if (dtype == SPARK_F32)
+    hipLaunchKernelGGL(anchor_kernel<float>, dim3(H), dim3(128), 0, st, (const float*)q, anchor, N, D, n_anchor);
+  else
+    hipLaunchKernelGGL(anchor_kernel<uint16_t>, dim3(H), dim3(128), 0, st, (const uint16_t*)q, anchor, N, D, n_anchor);
+  return spark_check_launch("anchor");
+}
+
+}  // namespace spark

@@ -1,0 +1,722 @@
+// Spark-Reblock's iterative hierarchical partitioner ("Spark-H3" blog,
+// 01 / Method: Spark-Reblock: starting from the full token set, every group
+// is split level by level according to the distance while enforcing the
+// assigned child capacities, until every leaf holds one block; token IDs
+// track membership through the tree).
+//
+// Rule implemented (two-pole capacity bisection), per group g with nb_g >= 2
+// blocks:  left capacity c_L = ceil(nb_g / 2) * block;  centroid c = sum x^_i;
+// pole A = argmin (x^_i . c, id);  pole B = argmin (x^_i . x^_A, id);
+// s_i = x^_i . (x^_A - x^_B);  left child = the c_L members first in
+// (s descending, id ascending) order (NaN last), right child = the rest, both
+// keeping ascending ids.  Leaves end up in depth-first left-first order.
+//
+// Every tree (head x side) has the same shape, which depends only on
+// (N, block), so a group is found from a block index (or a slot number = its
+// left/right path) by walking down from the root; no tables are needed.
+//
+// Large groups (global levels) use level-synchronous passes over all trees:
+//   cent_partial  -> per-block partial centroid sums (rows gathered by id)
+//   cent_reduce   -> per-group centroid (fixed chunk order: deterministic)
+//   argmin_partial/argmin_reduce (twice: pole A, pole B; 64-bit (key, id) mins)
+//   score         -> s_i for every position
+//   select_partition (one workgroup per group): exact radix select of the
+//                 c_L-th key, then a stable partition of the ids.
+// Once every group fits in LDS (<= FIN_MAX tokens) one workgroup per group
+// loads its rows once and finishes all remaining levels in LDS.
+#include "common.hpp"
+
+namespace spark {
+
+constexpr int SPL_T = 256;
+constexpr int FIN_MAX = 1024;         // tokens per finisher group
+constexpr int FIN_LDS = 140 * 1024;   // bytes of rows in the finisher
+
+// ---- tree navigation --------------------------------------------------------
+// Group containing block cb at `level`; false if that block is already in a
+// leaf (a group of one block) at an earlier level.  slot = path bits.
+__device__ __forceinline__ bool group_of_block(int cb, int level, int nb, int& start, int& nbg,
+                                               int& slot) {
+  start = 0;
+  nbg = nb;
+  slot = 0;
+  for (int l = 0; l < level; ++l) {
+    if (nbg <= 1) return false;
+    const int nl = (nbg + 1) >> 1;
+    if (cb < start + nl) {
+      nbg = nl;
+      slot = slot << 1;
+    } else {
+      start += nl;
+      nbg -= nl;
+      slot = (slot << 1) | 1;
+    }
+  }
+  return nbg >= 2;
+}
+
+__device__ __forceinline__ bool group_of_slot(int slot, int level, int nb, int& start, int& nbg) {
+  start = 0;
+  nbg = nb;
+  for (int l = level - 1; l >= 0; --l) {
+    if (nbg <= 1) return false;
+    const int nl = (nbg + 1) >> 1;
+    if ((slot >> l) & 1) {
+      start += nl;
+      nbg -= nl;
+    } else {
+      nbg = nl;
+    }
+  }
+  return true;
+}
+
+__device__ __forceinline__ uint32_t pref_key_desc(float s) {
+  if (s != s) return 0xffffffffu;
+  return ~float_key_asc(s);
+}
+
+__device__ __forceinline__ uint64_t argmin_key(float v, int id) {
+  return ((uint64_t)float_key_asc(v) << 32) | (uint32_t)id;
+}
+
+// 16-byte chunk of a row as floats
+template <typename T> struct Chunk;
+template <> struct Chunk<uint16_t> {
+  static constexpr int VE = 8;
+  __device__ __forceinline__ static void load(const uint16_t* p, float* v) { load8(p, v); }
+};
+template <> struct Chunk<float> {
+  static constexpr int VE = 4;
+  __device__ __forceinline__ static void load(const float* p, float* v) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  }
+};
+
+// ---- global-level passes ----------------------------------------------------
+// ids[t][i] = i; trees t >= split_at go to hi (offset by split_at trees).
+__global__ void iota_kernel(int32_t* __restrict__ lo, int32_t* __restrict__ hi, int split_at,
+                            int N, long total) {
+  for (long e = blockIdx.x * (long)blockDim.x + threadIdx.x; e < total;
+       e += (long)gridDim.x * blockDim.x) {
+    const long t = e / N;
+    int32_t* dst = (t < split_at) ? lo + e : hi + (e - (long)split_at * N);
+    *dst = (int32_t)(e % N);
+  }
+}
+
+// Per block (chunk) of the current order: partial centroid sum.
+template <typename T, int D>
+__global__ __launch_bounds__(SPL_T) void cent_partial(const T* __restrict__ xh,
+                                                      const int32_t* __restrict__ ids,
+                                                      float* __restrict__ cpart, int N, int BK,
+                                                      int nb, int level) {
+  constexpr int VE = Chunk<T>::VE, CPR = D / VE, RPP = SPL_T / CPR;
+  __shared__ float s_p[RPP][D];
+  const int cb = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+  int start, nbg, slot;
+  if (!group_of_block(cb, level, nb, start, nbg, slot)) return;
+  const int n_real = min(BK, N - cb * BK);
+  const int rg = tid / CPR, c = (tid % CPR) * VE;
+  float acc[VE];
+#pragma unroll
+  for (int e = 0; e < VE; ++e) acc[e] = 0.f;
+  const int32_t* idr = ids + (long)t * N + (long)cb * BK;
+  const T* xt = xh + (long)t * N * D;
+  for (int j = rg; j < n_real; j += RPP) {
+    float v[VE];
+    Chunk<T>::load(xt + (long)idr[j] * D + c, v);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) acc[e] += v[e];
+  }
+#pragma unroll
+  for (int e = 0; e < VE; ++e) s_p[rg][c + e] = acc[e];
+  __syncthreads();
+  for (int cc = tid; cc < D; cc += SPL_T) {
+    float s = 0.f;
+    for (int r = 0; r < RPP; ++r) s += s_p[r][cc];
+    cpart[((long)t * nb + cb) * D + cc] = s;
+  }
+}
+
+// Per group: centroid = sum of its blocks' partials, in block order.
+template <int D>
+__global__ __launch_bounds__(D) void cent_reduce(const float* __restrict__ cpart,
+                                                 float* __restrict__ cen, int nb, int level,
+                                                 int S) {
+  const int slot = blockIdx.x, t = blockIdx.y, c = threadIdx.x;
+  int start, nbg;
+  if (!group_of_slot(slot, level, nb, start, nbg) || nbg < 2) return;
+  float s = 0.f;
+  for (int b = start; b < start + nbg; ++b) s += cpart[((long)t * nb + b) * D + c];
+  cen[((long)t * S + slot) * D + c] = s;
+}
+
+// Per chunk: min over rows of (x^_i . vec_g, id), vec_g = cen[slot] (mode 0)
+// or x^[poleA[slot]] (mode 1).
+template <typename T, int D>
+__global__ __launch_bounds__(SPL_T) void argmin_partial(const T* __restrict__ xh,
+                                                        const int32_t* __restrict__ ids,
+                                                        const float* __restrict__ cen,
+                                                        const int32_t* __restrict__ poleA,
+                                                        uint64_t* __restrict__ mpart, int N,
+                                                        int BK, int nb, int level, int S,
+                                                        int mode) {
+  constexpr int VE = Chunk<T>::VE, CPR = D / VE, RPP = SPL_T / CPR;
+  __shared__ uint64_t s_min[SPL_T / 64];
+  const int cb = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+  int start, nbg, slot;
+  if (!group_of_block(cb, level, nb, start, nbg, slot)) return;
+  const int n_real = min(BK, N - cb * BK);
+  const int rg = tid / CPR, c = (tid % CPR) * VE;
+  const T* xt = xh + (long)t * N * D;
+  float vec[VE];
+  if (mode == 0) {
+#pragma unroll
+    for (int e = 0; e < VE; ++e) vec[e] = cen[((long)t * S + slot) * D + c + e];
+  } else {
+    Chunk<T>::load(xt + (long)poleA[(long)t * S + slot] * D + c, vec);
+  }
+  const int32_t* idr = ids + (long)t * N + (long)cb * BK;
+  uint64_t best = ~0ull;
+  for (int j0 = 0; j0 < n_real; j0 += RPP) {
+    const int j = j0 + rg;
+    float acc = 0.f;
+    int id = 0;
+    if (j < n_real) {
+      id = idr[j];
+      float v[VE];
+      Chunk<T>::load(xt + (long)id * D + c, v);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc = fmaf(v[e], vec[e], acc);
+    }
+#pragma unroll
+    for (int o = CPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (j < n_real) {
+      const uint64_t k = argmin_key(acc, id);
+      best = k < best ? k : best;
+    }
+  }
+  // wave min, then across waves
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t other = __shfl_xor(best, o, 64);
+    best = other < best ? other : best;
+  }
+  if ((tid & 63) == 0) s_min[tid >> 6] = best;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t b = s_min[0];
+    for (int w = 1; w < SPL_T / 64; ++w) b = s_min[w] < b ? s_min[w] : b;
+    mpart[(long)t * nb + cb] = b;
+  }
+}
+
+// Per group: min over its chunks' partials -> pole id.  mode 1 also writes
+// diff = x^_A - x^_B.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void argmin_reduce(const uint64_t* __restrict__ mpart,
+                                                    const T* __restrict__ xh,
+                                                    int32_t* __restrict__ poleA,
+                                                    int32_t* __restrict__ poleB,
+                                                    float* __restrict__ diff, int N, int nb,
+                                                    int level, int S, int mode) {
+  const int slot = blockIdx.x, t = blockIdx.y, lane = threadIdx.x;
+  int start, nbg;
+  if (!group_of_slot(slot, level, nb, start, nbg) || nbg < 2) return;
+  uint64_t best = ~0ull;
+  for (int b = start + lane; b < start + nbg; b += 64) {
+    const uint64_t k = mpart[(long)t * nb + b];
+    best = k < best ? k : best;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t other = __shfl_xor(best, o, 64);
+    best = other < best ? other : best;
+  }
+  const int id = (int)(uint32_t)(best & 0xffffffffu);
+  if (mode == 0) {
+    if (lane == 0) poleA[(long)t * S + slot] = id;
+    return;
+  }
+  if (lane == 0) poleB[(long)t * S + slot] = id;
+  const T* xt = xh + (long)t * N * D;
+  const int ia = poleA[(long)t * S + slot];
+  for (int c = lane; c < D; c += 64)
+    diff[((long)t * S + slot) * D + c] =
+        Elem<T>::load(xt + (long)ia * D + c) - Elem<T>::load(xt + (long)id * D + c);
+}
+
+// s at every position of groups with >= 2 blocks: x^_i . diff_g
+template <typename T, int D>
+__global__ __launch_bounds__(SPL_T) void score_kernel(const T* __restrict__ xh,
+                                                      const int32_t* __restrict__ ids,
+                                                      const float* __restrict__ diff,
+                                                      float* __restrict__ s, int N, int BK,
+                                                      int nb, int level, int S) {
+  constexpr int VE = Chunk<T>::VE, CPR = D / VE, RPP = SPL_T / CPR;
+  const int cb = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+  int start, nbg, slot;
+  if (!group_of_block(cb, level, nb, start, nbg, slot)) return;
+  const int n_real = min(BK, N - cb * BK);
+  const int rg = tid / CPR, c = (tid % CPR) * VE;
+  const T* xt = xh + (long)t * N * D;
+  float vec[VE];
+#pragma unroll
+  for (int e = 0; e < VE; ++e) vec[e] = diff[((long)t * S + slot) * D + c + e];
+  const long pos0 = (long)t * N + (long)cb * BK;
+  for (int j0 = 0; j0 < n_real; j0 += RPP) {
+    const int j = j0 + rg;
+    float acc = 0.f;
+    if (j < n_real) {
+      float v[VE];
+      Chunk<T>::load(xt + (long)ids[pos0 + j] * D + c, v);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc = fmaf(v[e], vec[e], acc);
+    }
+#pragma unroll
+    for (int o = CPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (j < n_real && (tid % CPR) == 0) s[pos0 + j] = acc;
+  }
+}
+
+// ---- workgroup helpers (radix select + stable partition) ---------------------
+// Exclusive scan of one int per thread over SPL_T threads; returns the total.
+__device__ __forceinline__ int wg_exscan(int v, int* s_tmp, int& total) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) s_tmp[w] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < SPL_T / 64; ++i) {
+    if (i < w) base += s_tmp[i];
+    tot += s_tmp[i];
+  }
+  __syncthreads();
+  total = tot;
+  return base + incl - v;
+}
+
+// After a histogram round: find the digit where the running count reaches
+// *need (wave 0 only), updating *prefix and *need.
+__device__ __forceinline__ void radix_pick(const int* s_hist, uint32_t* s_prefix, int* s_need,
+                                           int shift) {
+  const int lane = threadIdx.x & 63;
+  int c[4], run = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    run += s_hist[4 * lane + i];
+    c[i] = run;
+  }
+  int incl = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  const int base = incl - run;
+  const int need = *s_need;
+  const uint32_t pre = *s_prefix;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int before = base + (i ? c[i - 1] : 0);
+    const int after = base + c[i];
+    if (before < need && after >= need) {
+      *s_prefix = pre | ((uint32_t)(4 * lane + i) << shift);
+      *s_need = need - before;
+    }
+  }
+}
+
+// One workgroup per group: radix-select the c_L-th key of the group's scores
+// (streamed from global), then stable-partition the ids.
+__global__ __launch_bounds__(SPL_T) void select_partition(const float* __restrict__ s,
+                                                          const int32_t* __restrict__ ids_in,
+                                                          int32_t* __restrict__ ids_out, int N,
+                                                          int BK, int nb, int level) {
+  __shared__ int s_hist[256];
+  __shared__ int s_tmp[SPL_T / 64];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_need;
+  const int slot = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+  int start, nbg;
+  if (!group_of_slot(slot, level, nb, start, nbg)) return;
+  const long g0 = (long)start * BK;
+  const int n = (int)(min((long)N, (long)(start + nbg) * BK) - g0);
+  const long base = (long)t * N + g0;
+  if (nbg < 2) {  // a leaf carried through this level: copy
+    for (int i = tid; i < n; i += SPL_T) ids_out[base + i] = ids_in[base + i];
+    return;
+  }
+  const int cL = ((nbg + 1) >> 1) * BK;
+  if (tid == 0) {
+    s_prefix = 0;
+    s_need = cL;
+  }
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += SPL_T) s_hist[i] = 0;
+    __syncthreads();
+    const uint32_t pre = s_prefix;
+    const uint32_t hmask = (shift == 24) ? 0u : (0xffffffffu << (shift + 8));
+    for (int i = tid; i < n; i += SPL_T) {
+      const uint32_t k = pref_key_desc(s[base + i]);
+      if ((k & hmask) == pre) atomicAdd(&s_hist[(k >> shift) & 255], 1);
+    }
+    __syncthreads();
+    if (tid < 64) radix_pick(s_hist, &s_prefix, &s_need, shift);
+    __syncthreads();
+  }
+  const uint32_t thr = s_prefix;
+  const int ties_needed = s_need;
+  // stable partition in tiles of SPL_T * E positions, E consecutive per thread
+  constexpr int E = 8;
+  int run_left = 0, run_eq = 0;  // lefts / ties before this tile
+  for (int p0 = 0; p0 < n; p0 += SPL_T * E) {
+    uint32_t k[E];
+    int nl = 0, ne = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int p = p0 + tid * E + e;
+      k[e] = (p < n) ? pref_key_desc(s[base + p]) : 0xffffffffu;
+      const bool valid = p < n;
+      ne += (valid && k[e] == thr);
+    }
+    // a tie goes left iff its rank among ties < ties_needed
+    int tot_eq;
+    const int eq_before = run_eq + wg_exscan(ne, s_tmp, tot_eq);
+    int ce = eq_before;
+    bool left[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int p = p0 + tid * E + e;
+      const bool valid = p < n;
+      bool l = false;
+      if (valid) {
+        if (k[e] < thr) l = true;
+        else if (k[e] == thr) { l = ce < ties_needed; ++ce; }
+      }
+      left[e] = l;
+      nl += l;
+    }
+    int tot_l;
+    const int l_before = run_left + wg_exscan(nl, s_tmp, tot_l);
+    int cl = l_before;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int p = p0 + tid * E + e;
+      if (p >= n) continue;
+      const int r_before = p - cl;  // rights before p
+      const int dst = left[e] ? cl : cL + r_before;
+      if (dst < n) ids_out[base + dst] = ids_in[base + p];
+      cl += left[e];
+    }
+    run_left += tot_l;
+    run_eq += tot_eq;
+  }
+}
+
+// ---- LDS finisher -----------------------------------------------------------
+// One workgroup per group of <= FIN_MAX tokens at level L: rows in LDS, all
+// remaining splits done in place, final perm written.
+template <typename T, int D>
+__global__ __launch_bounds__(SPL_T) void finisher(const T* __restrict__ xh,
+                                                  const int32_t* __restrict__ ids_in,
+                                                  int32_t* __restrict__ perm_lo,
+                                                  int32_t* __restrict__ perm_hi, int split_at,
+                                                  int N, int BK, int nb, int level) {
+  constexpr int RS = D + 16 / (int)sizeof(T);  // padded row stride (elements)
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  T* sX = reinterpret_cast<T*>(smem);                          // [n][RS]
+  __shared__ int32_t s_oid[FIN_MAX];    // original id of local row r
+  __shared__ int16_t s_lid[FIN_MAX];    // current local order (row indices)
+  __shared__ int16_t s_tmp_lid[FIN_MAX];
+  __shared__ float s_val[FIN_MAX];
+  __shared__ float s_vec[D];
+  __shared__ float s_part[SPL_T / D > 0 ? SPL_T / D : 1][D];
+  __shared__ uint64_t s_min[SPL_T / 64];
+  __shared__ int s_hist[256];
+  __shared__ int s_tmp[SPL_T / 64];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_need;
+  __shared__ int s_pole[2];
+
+  const int slot = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+  int start, nbg;
+  if (!group_of_slot(slot, level, nb, start, nbg)) return;
+  const long g0 = (long)start * BK;
+  const int n = (int)(min((long)N, (long)(start + nbg) * BK) - g0);
+  const long base = (long)t * N + g0;
+  const T* xt = xh + (long)t * N * D;
+
+  // load rows in the current order
+  constexpr int VE = 16 / sizeof(T), CPR = D / VE;
+  for (int i = tid; i < n; i += SPL_T) {
+    s_oid[i] = ids_in ? ids_in[base + i] : (int32_t)(g0 + i);
+    s_lid[i] = (int16_t)i;
+  }
+  __syncthreads();
+  for (int ch = tid; ch < n * CPR; ch += SPL_T) {
+    const int r = ch / CPR, c = (ch % CPR) * VE;
+    *reinterpret_cast<uint4*>(sX + r * RS + c) =
+        *reinterpret_cast<const uint4*>(xt + (long)s_oid[r] * D + c);
+  }
+  __syncthreads();
+
+  // dot of local row r with s_vec
+  auto rowdot = [&](int r) -> float {
+    float acc = 0.f;
+    const T* row = sX + r * RS;
+#pragma unroll 8
+    for (int c = 0; c < D; c += 8) {
+      float v[8];
+      load8(row + c, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf(v[e], s_vec[c + e], acc);
+    }
+    return acc;
+  };
+  // argmin over local positions [a, a+len) of (rowdot, oid)
+  auto argmin_range = [&](int a, int len) -> int {
+    uint64_t best = ~0ull;
+    for (int i = tid; i < len; i += SPL_T) {
+      const int r = s_lid[a + i];
+      const uint64_t k = argmin_key(rowdot(r), s_oid[r]);
+      best = k < best ? k : best;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const uint64_t other = __shfl_xor(best, o, 64);
+      best = other < best ? other : best;
+    }
+    if ((tid & 63) == 0) s_min[tid >> 6] = best;
+    __syncthreads();
+    uint64_t b = s_min[0];
+#pragma unroll
+    for (int w = 1; w < SPL_T / 64; ++w) b = s_min[w] < b ? s_min[w] : b;
+    __syncthreads();
+    // map the winning original id back to its local row
+    const int id = (int)(uint32_t)(b & 0xffffffffu);
+    for (int i = tid; i < len; i += SPL_T) {
+      const int r = s_lid[a + i];
+      if (s_oid[r] == id) s_pole[0] = r;
+    }
+    __syncthreads();
+    return s_pole[0];
+  };
+
+  // walk the subtree level by level; subgroups are contiguous local ranges
+  for (int sub = 0;; ++sub) {
+    // subgroups at depth `sub` below this group: enumerate by path
+    bool any = false;
+    for (int path = 0; path < (1 << sub); ++path) {
+      // locate subgroup (block range relative to the group)
+      int sstart = 0, snb = nbg;
+      bool exists = true;
+      for (int l = sub - 1; l >= 0; --l) {
+        if (snb <= 1) { exists = false; break; }
+        const int nl = (snb + 1) >> 1;
+        if ((path >> l) & 1) { sstart += nl; snb -= nl; } else snb = nl;
+      }
+      if (!exists || snb < 2) continue;
+      any = true;
+      const int a = sstart * BK;
+      const int len = min(n, (sstart + snb) * BK) - a;
+      const int cL = ((snb + 1) >> 1) * BK;
+      // centroid (fixed order): column c summed over the range by one thread group
+      {
+        constexpr int G = SPL_T / D > 0 ? SPL_T / D : 1;  // row groups
+        const int c = tid % D, g = tid / D;
+        if (g < G) {
+          float acc = 0.f;
+          for (int i = g; i < len; i += G) acc += Elem<T>::load(sX + s_lid[a + i] * RS + c);
+          s_part[g][c] = acc;
+        }
+        __syncthreads();
+        if (tid < D) {
+          float acc = 0.f;
+          for (int gg = 0; gg < G; ++gg) acc += s_part[gg][tid];
+          s_vec[tid] = acc;
+        }
+        __syncthreads();
+      }
+      const int rA = argmin_range(a, len);
+      for (int c = tid; c < D; c += SPL_T) s_vec[c] = Elem<T>::load(sX + rA * RS + c);
+      __syncthreads();
+      const int rB = argmin_range(a, len);
+      for (int c = tid; c < D; c += SPL_T)
+        s_vec[c] = Elem<T>::load(sX + rA * RS + c) - Elem<T>::load(sX + rB * RS + c);
+      __syncthreads();
+      for (int i = tid; i < len; i += SPL_T) s_val[i] = rowdot(s_lid[a + i]);
+      // radix select of the cL-th key
+      if (tid == 0) { s_prefix = 0; s_need = cL; }
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = tid; i < 256; i += SPL_T) s_hist[i] = 0;
+        __syncthreads();
+        const uint32_t pre = s_prefix;
+        const uint32_t hmask = (shift == 24) ? 0u : (0xffffffffu << (shift + 8));
+        for (int i = tid; i < len; i += SPL_T) {
+          const uint32_t k = pref_key_desc(s_val[i]);
+          if ((k & hmask) == pre) atomicAdd(&s_hist[(k >> shift) & 255], 1);
+        }
+        __syncthreads();
+        if (tid < 64) radix_pick(s_hist, &s_prefix, &s_need, shift);
+        __syncthreads();
+      }
+      const uint32_t thr = s_prefix;
+      const int ties_needed = s_need;
+      // stable partition: E = ceil(len / SPL_T) consecutive positions per thread
+      const int E = (len + SPL_T - 1) / SPL_T;  // <= FIN_MAX / SPL_T = 4
+      int ne = 0;
+      for (int e = 0; e < E; ++e) {
+        const int p = tid * E + e;
+        if (p < len && pref_key_desc(s_val[p]) == thr) ++ne;
+      }
+      int tot;
+      int ce = wg_exscan(ne, s_tmp, tot);
+      int nl = 0;
+      bool left[FIN_MAX / SPL_T];
+      for (int e = 0; e < E; ++e) {
+        const int p = tid * E + e;
+        bool l = false;
+        if (p < len) {
+          const uint32_t k = pref_key_desc(s_val[p]);
+          if (k < thr) l = true;
+          else if (k == thr) { l = ce < ties_needed; ++ce; }
+        }
+        left[e] = l;
+        nl += l;
+      }
+      int cl = wg_exscan(nl, s_tmp, tot);
+      for (int e = 0; e < E; ++e) {
+        const int p = tid * E + e;
+        if (p >= len) continue;
+        const int dst = left[e] ? cl : cL + (p - cl);
+        if (dst < len) s_tmp_lid[a + dst] = s_lid[a + p];
+        cl += left[e];
+      }
+      __syncthreads();
+      for (int i = tid; i < len; i += SPL_T) s_lid[a + i] = s_tmp_lid[a + i];
+      __syncthreads();
+    }
+    if (!any) break;
+  }
+  int32_t* perm = (t < split_at) ? perm_lo + (long)t * N : perm_hi + (long)(t - split_at) * N;
+  for (int i = tid; i < n; i += SPL_T) perm[g0 + i] = s_oid[s_lid[i]];
+}
+
+// ---- host side ---------------------------------------------------------------
+struct SplitPlan {
+  int nb, F, Lf, S;
+};
+
+static SplitPlan split_plan(int N, int D, int BK, int esz) {
+  SplitPlan p;
+  p.nb = cdiv(N, BK);
+  int fb = FIN_LDS / (BK * (D * esz + 16));
+  fb = std::min(fb, FIN_MAX / BK);
+  int F = 1;
+  while (F * 2 <= fb) F *= 2;
+  p.F = std::max(F, 1);
+  // first level whose largest group has <= F blocks
+  int L = 0, mx = p.nb;
+  while (mx > p.F) {
+    mx = (mx + 1) / 2;
+    ++L;
+  }
+  p.Lf = L;
+  p.S = L > 0 ? (1 << (L - 1)) : 1;  // slots at the deepest global level
+  return p;
+}
+
+static size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t split_ws_bytes(int count, int N, int D, int BK, int dtype) {
+  const int esz = dtype == SPARK_BF16 ? 2 : 4;
+  const SplitPlan p = split_plan(N, D, BK, esz);
+  size_t b = 0;
+  b += 2 * up256((size_t)count * N * 4);            // ids ping-pong
+  b += up256((size_t)count * N * 4);                // s
+  b += up256((size_t)count * p.nb * D * 4);         // cpart
+  b += up256((size_t)count * p.nb * 8);             // mpart
+  b += 2 * up256((size_t)count * p.S * D * 4);      // cen, diff
+  b += 2 * up256((size_t)count * p.S * 4);          // poleA, poleB
+  return b;
+}
+
+template <typename T, int D>
+static int split_t(int count, int N, int BK, const void* xhv, int32_t* perm_lo,
+                   int32_t* perm_hi, int split_at, void* ws, hipStream_t st) {
+  const T* xh = (const T*)xhv;
+  const SplitPlan p = split_plan(N, D, BK, sizeof(T));
+  char* w = (char*)ws;
+  int32_t* ids_a = (int32_t*)w; w += up256((size_t)count * N * 4);
+  int32_t* ids_b = (int32_t*)w; w += up256((size_t)count * N * 4);
+  float* s = (float*)w; w += up256((size_t)count * N * 4);
+  float* cpart = (float*)w; w += up256((size_t)count * p.nb * D * 4);
+  uint64_t* mpart = (uint64_t*)w; w += up256((size_t)count * p.nb * 8);
+  float* cen = (float*)w; w += up256((size_t)count * p.S * D * 4);
+  float* diff = (float*)w; w += up256((size_t)count * p.S * D * 4);
+  int32_t* poleA = (int32_t*)w; w += up256((size_t)count * p.S * 4);
+  int32_t* poleB = (int32_t*)w;
+  const long total = (long)count * N;
+  if (p.nb <= 1) {
+    hipLaunchKernelGGL(iota_kernel, dim3((int)std::min<long>((total + 255) / 256, 8192)), dim3(256), 0, st, perm_lo, perm_hi, split_at, N, total);
+    return spark_check_launch("split iota");
+  }
+  int32_t* cur = nullptr;
+  if (p.Lf > 0) {
+    hipLaunchKernelGGL(iota_kernel, dim3((int)std::min<long>((total + 255) / 256, 8192)), dim3(256), 0, st, ids_a, ids_a, count, N, total);
+    cur = ids_a;
+    int32_t* nxt = ids_b;
+    for (int lev = 0; lev < p.Lf; ++lev) {
+      const int S = 1 << lev;
+      dim3 gc(p.nb, count), gs(S, count);
+      hipLaunchKernelGGL((cent_partial<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, cpart, N, BK, p.nb, lev);
+      hipLaunchKernelGGL((cent_reduce<D>), gs, dim3(D), 0, st, cpart, cen, p.nb, lev, p.S);
+      hipLaunchKernelGGL((argmin_partial<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, cen, poleA, mpart, N, BK, p.nb, lev, p.S, 0);
+      hipLaunchKernelGGL((argmin_reduce<T, D>), gs, dim3(64), 0, st, mpart, xh, poleA, poleB, diff, N, p.nb, lev, p.S, 0);
+      hipLaunchKernelGGL((argmin_partial<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, cen, poleA, mpart, N, BK, p.nb, lev, p.S, 1);
+      hipLaunchKernelGGL((argmin_reduce<T, D>), gs, dim3(64), 0, st, mpart, xh, poleA, poleB, diff, N, p.nb, lev, p.S, 1);
+      hipLaunchKernelGGL((score_kernel<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, diff, s, N, BK, p.nb, lev, p.S);
+      hipLaunchKernelGGL(select_partition, gs, dim3(SPL_T), 0, st, s, cur, nxt, N, BK, p.nb, lev);
+      int rc = spark_check_launch("split level");
+      if (rc) return rc;
+      std::swap(cur, nxt);
+    }
+  }
+  const int SF = 1 << p.Lf;
+  constexpr int RS = D + 16 / (int)sizeof(T);
+  const size_t lds = (size_t)std::min(N, p.F * BK) * RS * sizeof(T);
+  static bool attr = false;
+  if (!attr) {
+    hipFuncSetAttribute((const void*)finisher<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize, FIN_LDS);
+    attr = true;
+  }
+  hipLaunchKernelGGL((finisher<T, D>), dim3(SF, count), dim3(SPL_T), lds, st, xh, cur, perm_lo, perm_hi, split_at, N, BK, p.nb, p.Lf);
+  return spark_check_launch("split finisher");
+}
+
+int iota_launch(int count, int N, int32_t* lo, int32_t* hi, int split_at, hipStream_t st) {
+  const long total = (long)count * N;
+  hipLaunchKernelGGL(iota_kernel, dim3((int)std::min<long>((total + 255) / 256, 8192)), dim3(256), 0, st, lo, hi, split_at, N, total);
+  return spark_check_launch("iota");
+}
+
+// Trees [0, split_at) write to perm_lo, trees [split_at, count) to perm_hi.
+int split_launch(int count, int N, int D, int BK, int dtype, const void* xh, int32_t* perm_lo,
+                 int32_t* perm_hi, int split_at, void* ws, hipStream_t st) {
+  if (dtype == SPARK_BF16)
+    return D == 128 ? split_t<uint16_t, 128>(count, N, BK, xh, perm_lo, perm_hi, split_at, ws, st)
+                    : split_t<uint16_t, 64>(count, N, BK, xh, perm_lo, perm_hi, split_at, ws, st);
+  return D == 128 ? split_t<float, 128>(count, N, BK, xh, perm_lo, perm_hi, split_at, ws, st)
+                  : split_t<float, 64>(count, N, BK, xh, perm_lo, perm_hi, split_at, ws, st);
+}
+
+}  // namespace spark

@@ -1,0 +1,461 @@
+// Spark-Reblock's metric ("Spark-H3" blog, 01 / Method: Spark-Reblock, the
+// d_Q equation): second moments M = E[x x^T] of each side, their symmetric
+// square roots, and the whitened, unit-normalised rows x^ = W x / ||W x||,
+// whose dot products are the Mahalanobis cosines 1 - d_Q.
+//
+//  * moments: bf16 rows go through v_mfma_f32_32x32x16_bf16 (X^T X with the
+//    chunk staged transposed in LDS), fp32 rows through VALU; per-chunk
+//    partials are summed in a fixed order (deterministic).  The anchor query
+//    (mean of the video queries, 02 / Method: Spark-Reweight) is fused into
+//    the query pass.
+//  * msqrt: coupled Newton-Schulz iteration in fp32, one workgroup per matrix.
+//  * whiten: X W on MFMA (bf16, W rounded to bf16) or VALU (fp32), row norms
+//    in the epilogue.
+#include "common.hpp"
+
+namespace spark {
+
+constexpr int MOM_ROWS = 8192;   // rows per moment partial
+constexpr int MOM_TOK = 64;      // rows staged per LDS round
+
+// partial[t][c][D*D] (+ colsum partial[t][c][D] for anchors)
+template <int D>
+__global__ __launch_bounds__(256) void moments_mfma(const uint16_t* __restrict__ x,
+                                                    float* __restrict__ part,
+                                                    float* __restrict__ cpart, int N,
+                                                    int n_anchor, int nchunk, int q_trees) {
+  constexpr int RS = MOM_TOK + 8;  // LDS row stride (bf16) of X^T
+  __shared__ __attribute__((aligned(16))) uint16_t sXT[D * RS];
+  const int t = blockIdx.y, chunk = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const long r0 = (long)chunk * MOM_ROWS;
+  const long r1 = min((long)N, r0 + MOM_ROWS);
+  const uint16_t* xt = x + (long)t * N * D;
+  constexpr int MT = D / 32;                 // output tiles per side
+  constexpr int TPW = MT * MT / 4;           // output tiles per wave (4 or 1)
+  f32x16 acc[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+  const bool want_cs = cpart != nullptr && t < q_trees;
+  float cs[8] = {0, 0, 0, 0, 0, 0, 0, 0};   // column sums of rows < n_anchor
+
+  // staging: thread -> (4-row group, 8-col chunk)
+  constexpr int CPR = D / 8;                 // 16 or 8
+  constexpr int RG = 256 / CPR;              // 4-row groups per round: 16 or 32
+  static_assert(RG * 4 >= MOM_TOK, "staging covers the round");
+  const int g = tid / CPR, cc = (tid % CPR) * 8;
+
+  for (long rb = r0; rb < r1; rb += MOM_TOK) {
+    __syncthreads();
+    if (g * 4 < MOM_TOK) {
+      uint16_t vals[4][8];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const long row = rb + g * 4 + rr;
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (row < r1) u = *reinterpret_cast<const uint4*>(xt + row * D + cc);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vals[rr][2 * e] = (uint16_t)(w[e] & 0xffff);
+          vals[rr][2 * e + 1] = (uint16_t)(w[e] >> 16);
+        }
+        if (want_cs && row < r1 && row < n_anchor) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) cs[e] += bf2f(vals[rr][e]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint2 p;
+        p.x = (uint32_t)vals[0][e] | ((uint32_t)vals[1][e] << 16);
+        p.y = (uint32_t)vals[2][e] | ((uint32_t)vals[3][e] << 16);
+        *reinterpret_cast<uint2*>(sXT + (cc + e) * RS + g * 4) = p;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < MOM_TOK / 16; ++ks) {
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        const int tile = wave * TPW + i;
+        const int mt = tile / MT, nt = tile % MT;
+        if (tile >= MT * MT) continue;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sXT + (32 * mt + l32) * RS + 16 * ks + 8 * hf);
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(sXT + (32 * nt + l32) * RS + 16 * ks + 8 * hf);
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
+      }
+    }
+  }
+  float* pout = part + ((long)t * nchunk + chunk) * D * D;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int tile = wave * TPW + i;
+    if (tile >= MT * MT) continue;
+    const int mt = tile / MT, nt = tile % MT;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = 32 * mt + 8 * (v / 4) + 4 * hf + (v % 4);
+      const int col = 32 * nt + l32;
+      pout[row * D + col] = acc[i][v];
+    }
+  }
+  if (want_cs) {
+    // reduce the RG row groups' column sums through LDS (reuse sXT as floats)
+    __syncthreads();
+    float* sf = reinterpret_cast<float*>(sXT);
+    if (g * 4 < MOM_TOK)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sf[g * D + cc + e] = cs[e];
+    __syncthreads();
+    const int ng = MOM_TOK / 4;
+    for (int c = tid; c < D; c += 256) {
+      float s = 0.f;
+      for (int gg = 0; gg < ng; ++gg) s += sf[gg * D + c];
+      cpart[((long)t * nchunk + chunk) * D + c] = s;
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void moments_f32(const float* __restrict__ x,
+                                                   float* __restrict__ part,
+                                                   float* __restrict__ cpart, int N, int n_anchor,
+                                                   int nchunk, int q_trees) {
+  constexpr int RPT = D * D / 256;  // outputs per thread: 64 (D=128) or 16 (D=64)
+  constexpr int SUB = (D == 128) ? 8 : 4;  // output sub-block side
+  __shared__ float sX[MOM_TOK][D];
+  const int t = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
+  const long r0 = (long)chunk * MOM_ROWS;
+  const long r1 = min((long)N, r0 + MOM_ROWS);
+  const float* xt = x + (long)t * N * D;
+  const int bi = (tid / (D / SUB)) * SUB, bj = (tid % (D / SUB)) * SUB;
+  float acc[SUB][SUB];
+#pragma unroll
+  for (int i = 0; i < SUB; ++i)
+#pragma unroll
+    for (int j = 0; j < SUB; ++j) acc[i][j] = 0.f;
+  const bool want_cs = cpart != nullptr && t < q_trees;
+  float cs = 0.f;
+  static_assert(RPT == SUB * SUB, "tiling");
+  for (long rb = r0; rb < r1; rb += MOM_TOK) {
+    __syncthreads();
+    for (int e = tid; e < MOM_TOK * D; e += 256) {
+      const long row = rb + e / D;
+      sX[e / D][e % D] = (row < r1) ? xt[row * D + e % D] : 0.f;
+    }
+    __syncthreads();
+    for (int r = 0; r < MOM_TOK; ++r) {
+      float a[SUB], b[SUB];
+#pragma unroll
+      for (int i = 0; i < SUB; ++i) { a[i] = sX[r][bi + i]; b[i] = sX[r][bj + i]; }
+#pragma unroll
+      for (int i = 0; i < SUB; ++i)
+#pragma unroll
+        for (int j = 0; j < SUB; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    if (want_cs && tid < D)
+      for (int r = 0; r < MOM_TOK; ++r)
+        if (rb + r < r1 && rb + r < n_anchor) cs += sX[r][tid];
+  }
+  float* pout = part + ((long)t * nchunk + chunk) * D * D;
+#pragma unroll
+  for (int i = 0; i < SUB; ++i)
+#pragma unroll
+    for (int j = 0; j < SUB; ++j) pout[(bi + i) * D + bj + j] = acc[i][j];
+  if (want_cs && tid < D) cpart[((long)t * nchunk + chunk) * D + tid] = cs;
+}
+
+// M[t] = (sum over chunks in order) / N; anchor[t] = colsum / n_anchor
+__global__ void moments_reduce(const float* __restrict__ part, const float* __restrict__ cpart,
+                               float* __restrict__ MQ, float* __restrict__ MK,
+                               float* __restrict__ anchor, int H, int D, int N, int n_anchor,
+                               int nchunk) {
+  const int t = blockIdx.y;  // 0..2H-1: q trees then k trees
+  const long DD = (long)D * D;
+  for (long e = blockIdx.x * (long)blockDim.x + threadIdx.x; e < DD; e += (long)gridDim.x * blockDim.x) {
+    float s = 0.f;
+    for (int c = 0; c < nchunk; ++c) s += part[((long)t * nchunk + c) * DD + e];
+    float* dst = (t < H) ? (MQ + (long)t * DD) : (MK + (long)(t - H) * DD);
+    dst[e] = s / (float)N;
+  }
+  if (anchor != nullptr && t < H && blockIdx.x == 0) {
+    for (int c = threadIdx.x; c < D; c += blockDim.x) {
+      float s = 0.f;
+      for (int ch = 0; ch < nchunk; ++ch) s += cpart[((long)t * nchunk + ch) * D + c];
+      anchor[(long)t * D + c] = s / (float)n_anchor;
+    }
+  }
+}
+
+size_t moments_ws_bytes(int H, int N, int D) {
+  const int nchunk = cdiv(N, MOM_ROWS);
+  return (size_t)2 * H * nchunk * D * D * 4 + (size_t)2 * H * nchunk * D * 4 + 512;
+}
+
+// q and k are read as two consecutive launches over the same partial buffer.
+int moments_launch(int H, int N, int D, int dtype, const void* q, const void* k, float* MQ,
+                   float* MK, float* anchor, int n_anchor, void* ws, hipStream_t st) {
+  const int nchunk = cdiv(N, MOM_ROWS);
+  float* part = (float*)ws;
+  float* cpart = part + (size_t)2 * H * nchunk * D * D;
+  const size_t esz = dtype == SPARK_BF16 ? 2 : 4;
+  for (int side = 0; side < 2; ++side) {
+    const void* x = side == 0 ? q : k;
+    float* pp = part + (size_t)side * H * nchunk * D * D;
+    float* cp = side == 0 ? cpart : nullptr;
+    (void)esz;
+    dim3 grid(nchunk, H);
+    if (dtype == SPARK_BF16) {
+      if (D == 128)
+        hipLaunchKernelGGL(moments_mfma<128>, grid, dim3(256), 0, st, (const uint16_t*)x, pp, cp, N, n_anchor, nchunk, H);
+      else
+        hipLaunchKernelGGL(moments_mfma<64>, grid, dim3(256), 0, st, (const uint16_t*)x, pp, cp, N, n_anchor, nchunk, H);
+    } else {
+      if (D == 128)
+        hipLaunchKernelGGL(moments_f32<128>, grid, dim3(256), 0, st, (const float*)x, pp, cp, N, n_anchor, nchunk, H);
+      else
+        hipLaunchKernelGGL(moments_f32<64>, grid, dim3(256), 0, st, (const float*)x, pp, cp, N, n_anchor, nchunk, H);
+    }
+    int rc = spark_check_launch("moments");
+    if (rc) return rc;
+  }
+  hipLaunchKernelGGL(moments_reduce, dim3(16, 2 * H), dim3(256), 0, st, part, cpart, MQ, MK,
+                     anchor, H, D, N, n_anchor, nchunk);
+  return spark_check_launch("moments_reduce");
+}
+
+// ---------------------------------------------------------------------------
+// msqrt: Y0 = M / s + delta I with s = ||M||_F, Z0 = I;  T = (3I - Z Y) / 2;
+// Y <- Y T;  Z <- T Z.  Y -> (M/s + delta I)^{1/2}, so W = sqrt(s) Y.  The
+// ridge delta = 1e-6 bounds the smallest eigenvalue the iteration has to
+// reach (and keeps rank-deficient moments from amplifying round-off in their
+// null space); it moves W by at most sqrt(delta * s) in directions of zero
+// energy.  Y and Z live in LDS; T goes through a per-matrix global scratch
+// (L2-resident).  Stops when max|ZY - I| < 3e-5, after at most 40 iterations.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void msqrt_kernel(const float* __restrict__ M,
+                                                    float* __restrict__ W,
+                                                    float* __restrict__ Tscr) {
+  constexpr int SUB = (D == 128) ? 8 : 4;
+  __shared__ float sY[D * D];
+  __shared__ float sZ[D * D];
+  __shared__ float s_red[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const long off = (long)blockIdx.x * D * D;
+  const float* m = M + off;
+  float* tg = Tscr + off;
+  const int bi = (tid / (D / SUB)) * SUB, bj = (tid % (D / SUB)) * SUB;
+
+  // Frobenius norm (symmetrised input)
+  float ss = 0.f;
+  for (int e = tid; e < D * D; e += 256) {
+    const int r = e / D, c = e % D;
+    const float v = 0.5f * (m[r * D + c] + m[c * D + r]);
+    sY[e] = v;
+    ss += v * v;
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) s_red[wave] = ss;
+  __syncthreads();
+  const float fro = sqrtf(s_red[0] + s_red[1] + s_red[2] + s_red[3]);
+  if (!(fro > 0.f) || !isfinite(fro)) {
+    for (int e = tid; e < D * D; e += 256) W[off + e] = (fro == 0.f) ? 0.f : NAN;
+    return;
+  }
+  const float inv = 1.f / fro;
+  constexpr float kRidge = 1e-6f;
+  for (int e = tid; e < D * D; e += 256) {
+    const bool diag = (e / D == e % D);
+    sY[e] = sY[e] * inv + (diag ? kRidge : 0.f);
+    sZ[e] = diag ? 1.f : 0.f;
+  }
+  __syncthreads();
+
+  for (int it = 0; it < 40; ++it) {
+    // P = Z Y (this thread's SUB x SUB block), T = (3I - P)/2 to global
+    float acc[SUB][SUB];
+#pragma unroll
+    for (int i = 0; i < SUB; ++i)
+#pragma unroll
+      for (int j = 0; j < SUB; ++j) acc[i][j] = 0.f;
+    for (int kx = 0; kx < D; ++kx) {
+      float a[SUB], b[SUB];
+#pragma unroll
+      for (int i = 0; i < SUB; ++i) { a[i] = sZ[(bi + i) * D + kx]; b[i] = sY[kx * D + bj + i]; }
+#pragma unroll
+      for (int i = 0; i < SUB; ++i)
+#pragma unroll
+        for (int j = 0; j < SUB; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    float dev = 0.f;
+#pragma unroll
+    for (int i = 0; i < SUB; ++i)
+#pragma unroll
+      for (int j = 0; j < SUB; ++j) {
+        const float id = (bi + i == bj + j) ? 1.f : 0.f;
+        dev = fmaxf(dev, fabsf(acc[i][j] - id));
+        tg[(bi + i) * D + bj + j] = 0.5f * (3.f * id - acc[i][j]);
+      }
+    dev = wave_max(dev);
+    if (lane == 0) s_red[wave] = dev;
+    __syncthreads();  // T visible to the workgroup; s_red ready
+    const float gdev = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    if (gdev < 3e-5f) break;
+    // Ynew = Y T, Znew = T Z
+    float ay[SUB][SUB], az[SUB][SUB];
+#pragma unroll
+    for (int i = 0; i < SUB; ++i)
+#pragma unroll
+      for (int j = 0; j < SUB; ++j) { ay[i][j] = 0.f; az[i][j] = 0.f; }
+    for (int kx = 0; kx < D; ++kx) {
+      float ya[SUB], tb[SUB], ta[SUB], zb[SUB];
+#pragma unroll
+      for (int i = 0; i < SUB; ++i) {
+        ya[i] = sY[(bi + i) * D + kx];
+        tb[i] = tg[kx * D + bj + i];
+        ta[i] = tg[(bi + i) * D + kx];
+        zb[i] = sZ[kx * D + bj + i];
+      }
+#pragma unroll
+      for (int i = 0; i < SUB; ++i)
+#pragma unroll
+        for (int j = 0; j < SUB; ++j) {
+          ay[i][j] = fmaf(ya[i], tb[j], ay[i][j]);
+          az[i][j] = fmaf(ta[i], zb[j], az[i][j]);
+        }
+    }
+    __syncthreads();  // everyone done reading old Y, Z and T
+#pragma unroll
+    for (int i = 0; i < SUB; ++i)
+#pragma unroll
+      for (int j = 0; j < SUB; ++j) {
+        sY[(bi + i) * D + bj + j] = ay[i][j];
+        sZ[(bi + i) * D + bj + j] = az[i][j];
+      }
+    __syncthreads();
+  }
+  const float sc = sqrtf(fro);
+  for (int e = tid; e < D * D; e += 256) {
+    const int r = e / D, c = e % D;
+    W[off + e] = 0.5f * (sY[r * D + c] + sY[c * D + r]) * sc;
+  }
+}
+
+size_t msqrt_ws_bytes(int count, int D) { return (size_t)count * D * D * 4; }
+
+int msqrt_launch(int count, int D, const float* M, float* W, float* Tscr, hipStream_t st) {
+  if (D == 128)
+    hipLaunchKernelGGL(msqrt_kernel<128>, dim3(count), dim3(256), 0, st, M, W, Tscr);
+  else
+    hipLaunchKernelGGL(msqrt_kernel<64>, dim3(count), dim3(256), 0, st, M, W, Tscr);
+  return spark_check_launch("msqrt");
+}
+
+// ---------------------------------------------------------------------------
+// whiten: xhat = normalize(W x) row by row.  bf16: x^T-side MFMA with W (bf16)
+// as the A operand: O^T[c][i] = sum_k W[c][k] x_i[k]; lane l32 owns row i.
+// ---------------------------------------------------------------------------
+constexpr int WH_ROWS = 128;  // rows per workgroup (4 waves x 32)
+
+template <int D>
+__global__ __launch_bounds__(256) void whiten_mfma(const uint16_t* __restrict__ x,
+                                                   const float* __restrict__ W,
+                                                   uint16_t* __restrict__ xh, int N) {
+  constexpr int RS = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t sW[D * RS];
+  const int t = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const float* w = W + (long)t * D * D;
+  for (int e = tid; e < D * D; e += 256) sW[(e / D) * RS + e % D] = f2bf(w[e]);
+  __syncthreads();
+  const long row = (long)blockIdx.x * WH_ROWS + wave * 32 + l32;
+  const bool ok = row < N;
+  const uint16_t* xr = x + ((long)t * N + (ok ? row : 0)) * D;
+  bf16x8 xb[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) xb[s] = *reinterpret_cast<const bf16x8*>(xr + 16 * s + 8 * hf);
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int ct = 0; ct < D / 32; ++ct) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[ct][v] = 0.f;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sW + (32 * ct + l32) * RS + 16 * s + 8 * hf);
+      acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xb[s], acc[ct], 0, 0, 0);
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int ct = 0; ct < D / 32; ++ct)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) ss = fmaf(acc[ct][v], acc[ct][v], ss);
+  ss += __shfl_xor(ss, 32, 64);
+  const float inv = (ss > 0.f) ? 1.f / sqrtf(ss) : 0.f;
+  if (!ok) return;
+  uint16_t* dst = xh + ((long)t * N + row) * D;
+#pragma unroll
+  for (int ct = 0; ct < D / 32; ++ct)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      uint2 p;
+      p.x = pack_bf2(acc[ct][4 * a] * inv, acc[ct][4 * a + 1] * inv);
+      p.y = pack_bf2(acc[ct][4 * a + 2] * inv, acc[ct][4 * a + 3] * inv);
+      *reinterpret_cast<uint2*>(dst + 32 * ct + 8 * a + 4 * hf) = p;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void whiten_f32(const float* __restrict__ x,
+                                                  const float* __restrict__ W,
+                                                  float* __restrict__ xh, int N) {
+  __shared__ float sW[D * (D + 1)];
+  const int t = blockIdx.y, tid = threadIdx.x;
+  const float* w = W + (long)t * D * D;
+  for (int e = tid; e < D * D; e += 256) sW[(e / D) * (D + 1) + e % D] = w[e];
+  __syncthreads();
+  // one thread per row
+  const long row = (long)blockIdx.x * 256 + tid;
+  if (row >= N) return;
+  const float* xr = x + ((long)t * N + row) * D;
+  float xv[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) xv[c] = xr[c];
+  float ss = 0.f;
+  float* dst = xh + ((long)t * N + row) * D;
+  for (int c = 0; c < D; ++c) {
+    float acc = 0.f;
+#pragma unroll
+    for (int k2 = 0; k2 < D; ++k2) acc = fmaf(sW[c * (D + 1) + k2], xv[k2], acc);
+    dst[c] = acc;
+    ss = fmaf(acc, acc, ss);
+  }
+  const float inv = (ss > 0.f) ? 1.f / sqrtf(ss) : 0.f;
+  for (int c = 0; c < D; ++c) dst[c] *= inv;
+}
+
+int whiten_launch(int count, int N, int D, int dtype, const void* x, const float* W, void* xh,
+                  hipStream_t st) {
+  if (dtype == SPARK_BF16) {
+    dim3 grid(cdiv(N, WH_ROWS), count);
+    if (D == 128)
+      hipLaunchKernelGGL(whiten_mfma<128>, grid, dim3(256), 0, st, (const uint16_t*)x, W, (uint16_t*)xh, N);
+    else
+      hipLaunchKernelGGL(whiten_mfma<64>, grid, dim3(256), 0, st, (const uint16_t*)x, W, (uint16_t*)xh, N);
+  } else {
+    dim3 grid(cdiv(N, 256), count);
+    if (D == 128)
+      hipLaunchKernelGGL(whiten_f32<128>, grid, dim3(256), 0, st, (const float*)x, W, (float*)xh, N);
+    else
+      hipLaunchKernelGGL(whiten_f32<64>, grid, dim3(256), 0, st, (const float*)x, W, (float*)xh, N);
+  }
+  return spark_check_launch("whiten");
+}
+
+}  // namespace spark

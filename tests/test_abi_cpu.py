@@ -1,0 +1,121 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol that
+include/spark.h declares, and its host-side logic (argument validation,
+workspace sizing, top-k rounding) behaves as documented.  No call here
+reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle as O
+from block_sparse_attention_mahalanobis_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spark.h")
+
+FAKE = ctypes.c_void_p(0x10000)       # aligned, never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(spark_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libspark.so is not built (run __graft_entry__.build())")
+    return L.lib()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    declared = _declared()
+    assert len(declared) >= 16
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(L.EXPORTED) == declared
+
+
+def test_version_and_status_strings(lib):
+    assert lib.spark_version() == 10000
+    assert lib.spark_status_string(0) == b"SPARK_OK"
+    assert lib.spark_status_string(-5) == b"SPARK_E_WORKSPACE"
+    assert lib.spark_status_string(42) == b"SPARK_E_UNKNOWN"
+
+
+@pytest.mark.parametrize("nb", [1, 7, 16, 126, 1922, 1985])
+@pytest.mark.parametrize("ratio", [0.0, 0.1, 0.2, 0.25, 0.3, 1.0, 1.5])
+def test_topk_from_ratio_matches_oracle(lib, nb, ratio):
+    assert lib.spark_topk_from_ratio(ratio, nb) == O.topk_from_ratio(ratio, nb)
+
+
+def test_block_count(lib):
+    assert lib.spark_block_count(245952, 128) == 1922
+    assert lib.spark_block_count(1025, 64) == 17
+    assert lib.spark_block_count(0, 64) < 0
+
+
+def _args(**kw):
+    base = dict(H=2, N=1000, d=64, block=64, dtype=0, n_anchor=None)
+    base.update(kw)
+    return L.make_args(base["H"], base["N"], base["d"], base["block"], base["dtype"], base["n_anchor"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), -4), (dict(d=32), -4), (dict(dtype=7), -3), (dict(H=0), -2), (dict(N=0), -2),
+    (dict(block=0), -2), (dict(block=129), -2), (dict(n_anchor=1001), -2), (dict(n_anchor=0), -2),
+])
+def test_bad_shapes_rejected_before_launch(lib, kw, status):
+    a = _args(**kw)
+    rc = lib.spark_attn(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                        1 << 40, None)
+    assert rc == status, L.last_error()
+    assert L.last_error().startswith("spark_attn")
+
+
+def test_null_misaligned_topk_and_workspace_errors(lib):
+    a = _args(dtype=1)
+    nb = O.n_blocks(1000, 64)
+    rc = lib.spark_attn(ctypes.byref(a), None, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 40, None)
+    assert rc == -1 and "q_p is NULL" in L.last_error()
+    rc = lib.spark_attn(ctypes.byref(a), MISALIGNED, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 40, None)
+    assert rc == -1 and "aligned" in L.last_error()
+    for k in (0, nb + 1):
+        rc = lib.spark_attn(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, k, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 40, None)
+        assert rc == -2
+    need = L.workspace_bytes(a, L.OP_ATTN)
+    assert need > 0
+    rc = lib.spark_attn(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None, FAKE, FAKE, need - 1, None)
+    assert rc == -5
+    rc = lib.spark_select(ctypes.byref(a), None, FAKE, None, 4, FAKE, None, None)
+    assert rc == -1 and "qbar" in L.last_error()
+    bad_flags = _args()
+    bad_flags.flags = 0x3
+    rc = lib.spark_reblock(ctypes.byref(bad_flags), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                           FAKE, None, FAKE, 1 << 40, None)
+    assert rc == -1
+    reserved = _args()
+    reserved.reserved = 1
+    assert lib.spark_summarize(ctypes.byref(reserved), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert lib.spark_msqrt(0, 64, FAKE, FAKE, FAKE, 1 << 30, None) == -2
+    assert lib.spark_msqrt(2, 64, FAKE, FAKE, FAKE, 100, None) == -5
+    a2 = _args()
+    a2.flags = L.LAYOUT_GIVEN
+    assert lib.spark_layer(ctypes.byref(a2), FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1 << 40, None) == -1
+
+
+def test_workspace_sizes_are_consistent(lib):
+    a = L.make_args(40, 245952, 128, 128, 1)
+    reb = L.workspace_bytes(a, L.OP_REBLOCK)
+    # at least the whitened rows of both sides
+    assert reb >= 2 * 40 * 245952 * 128 * 2
+    lay = L.workspace_bytes(a, L.OP_LAYER, 193)
+    assert lay > reb
+    assert L.workspace_bytes(a, L.OP_SELECT) == 0
+    ident = L.make_args(40, 245952, 128, 128, 1, layout="identity")
+    assert L.workspace_bytes(ident, L.OP_REBLOCK) == 0
+    assert lib.spark_workspace_bytes(ctypes.byref(a), 99, 0) == ctypes.c_size_t(-1).value
+    assert lib.spark_workspace_bytes(ctypes.byref(a), L.OP_LAYER, 0) == ctypes.c_size_t(-1).value
