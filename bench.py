@@ -1,0 +1,277 @@
+"""Benchmark of one Spark-Attn layer on one MI355X.
+
+A step is one pass of the whole layer -- spark_reblock (moments, square
+roots, whitening, hierarchical split, gather + pooling), spark_select,
+spark_summarize, spark_attn (fused exact + compressed attention with the
+scatter) -- over the 768p workload: a 61x48x84 latent (245,952 tokens),
+H=40, d=128, block 128, density 0.1 (top 193 of 1922 key blocks), bf16,
+seeded synthetic clustered q/k (see block_sparse_attention_mahalanobis_amd/
+workload.py).  Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` is the layer latency in ms (lower is better);
+the exact-branch MFMA fraction of the bf16 dense peak, per-stage times, the
+attention kernel's roofline and the fp64 CPU oracle baseline ride along.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", default="full768", choices=["full768", "draft", "ref2va", "tiny"])
+    p.add_argument("--ratio", type=float, default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-blocks", type=int, default=768,
+                   help="query blocks of head 0 the oracle attends in the CPU baseline sample")
+    return p.parse_args()
+
+
+def load_inputs(w, torch, dtype, threads):
+    """q, k, v [H, N, d] on cuda:0, generated head by head on the host."""
+    from block_sparse_attention_mahalanobis_amd.workload import make_head
+    H, N, d = w.H, w.N, w.d
+    out = [torch.empty((H, N, d), dtype=dtype, device="cuda:0") for _ in range(3)]
+    with ThreadPoolExecutor(threads) as ex:
+        for h, arrs in enumerate(ex.map(lambda hh: make_head(w, hh), range(H))):
+            for t, a in zip(out, arrs):
+                t[h].copy_(torch.from_numpy(a).to(dtype))
+    torch.cuda.synchronize()
+    return out
+
+
+def attn_flops(idx, N, b, d):
+    """Algorithmic flops of the fused attention: 4 d per (query row, exact
+    key) plus 4 d per (query row, unselected block summary)."""
+    H, nb, k = idx.shape
+    sizes = np.full(nb, b, dtype=np.int64)
+    sizes[-1] = N - (nb - 1) * b
+    keys_per_qblock = sizes[idx].sum(axis=2)                  # [H, nb]
+    exact = 4 * d * int((keys_per_qblock * sizes[None, :]).sum())
+    comp = 4 * d * int(H * N * (nb - k))
+    return exact, comp
+
+
+def reblock_bytes(H, N, d, b, es, levels_global, nb):
+    """Algorithmic HBM bytes of reblock + summaries (per layer)."""
+    vol = H * N * d * es                      # one [H, N, d] tensor
+    moments = 2 * vol
+    whiten = 4 * vol
+    split = 2 * levels_global * 4 * vol + 2 * vol       # 4 row passes per global level + finisher
+    gather = 6 * vol
+    summ = 2 * vol
+    return moments + whiten + split + gather + summ
+
+
+def cpu_baseline(w, topk, sample_blocks):
+    """The fp64 oracle as it stands, timed on this host: head 0 end to end
+    (reblock of both sides, pooling, scores, top-k, summaries) plus the
+    two-branch attention of `sample_blocks` query blocks, scaled to the whole
+    layer (H heads, all query blocks)."""
+    import oracle as O
+    from block_sparse_attention_mahalanobis_amd.workload import make_head
+    cores = len(os.sched_getaffinity(0))
+    q, k, v = make_head(w, 0)
+    b = w.block
+    nb = O.n_blocks(w.N, b)
+    t0 = time.perf_counter()
+    pq, pk = O.reblock_head(q, k, b)
+    qp, qbar = O.gather_pool(q, pq, b)
+    kp, kbar = O.gather_pool(k, pk, b)
+    vp = np.asarray(v, np.float64)[pk]
+    S = O.block_scores(qbar, kbar)
+    idx = O.select_topk(S, topk)
+    ks, vs, beta = O.reweight_summaries(kp, vp, O.anchor_query(q, w.n_anchor), b)
+    t1 = time.perf_counter()
+    nsamp = min(sample_blocks, nb)
+    O.sparse_attention(qp, kp, vp, idx, ks, vs, beta, b, qblocks=range(nsamp))
+    t2 = time.perf_counter()
+    per_head = (t1 - t0) + (t2 - t1) * (nb / nsamp)
+    layer_ms = per_head * w.H * 1e3
+    return {"value": round(layer_ms, 1), "unit": "ms", "cores": cores, "kind": "oracle",
+            "sample": (f"head 0 of {w.H}: full reblock/select/summaries ({t1 - t0:.1f} s) + attention "
+                       f"of {nsamp}/{nb} query blocks ({t2 - t1:.1f} s), scaled x{nb / nsamp:.1f} blocks "
+                       f"and x{w.H} heads; numpy fp64, BLAS threads = {cores}")}
+
+
+def load_traffic(kernel_src):
+    """HBM traffic per attention launch from the committed rocprofv3 --pmc
+    summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "attn_full768_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except Exception:
+        return None
+    h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
+    if rec.get("kernel_sha") != h:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this layer runs on one GPU; multi-GPU runs are not part of "
+                                   "this build (heads would shard with zero communication)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import block_sparse_attention_mahalanobis_amd as S
+    from block_sparse_attention_mahalanobis_amd import _lib as L
+    from block_sparse_attention_mahalanobis_amd.workload import WORKLOADS
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    L.lib()
+    w = WORKLOADS[args.config]
+    if args.ratio is not None:
+        w = w.with_(ratio=args.ratio)
+    dtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    es = 2 if w.dtype == "bf16" else 4
+    H, N, d, b = w.H, w.N, w.d, w.block
+    nb = L.n_blocks(N, b)
+    topk = L.topk_from_ratio(w.ratio, nb)
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    log(f"workload {w.name}: H={H} N={N} d={d} block={b} n_b={nb} topk={topk} dtype={w.dtype}")
+    t = time.perf_counter()
+    q, k, v = load_inputs(w, torch, dtype, threads)
+    log(f"inputs resident ({time.perf_counter() - t:.1f} s)")
+
+    # buffers and workspaces, allocated once
+    Np = nb * b
+    dev = "cuda:0"
+    perm_q = torch.empty((H, N), dtype=torch.int32, device=dev)
+    perm_k = torch.empty((H, N), dtype=torch.int32, device=dev)
+    q_p = torch.empty((H, Np, d), dtype=dtype, device=dev)
+    k_p = torch.empty((H, Np, d), dtype=dtype, device=dev)
+    v_pt = torch.empty((H, nb, d, b), dtype=dtype, device=dev)
+    qbar = torch.empty((H, nb, d), dtype=torch.float32, device=dev)
+    kbar = torch.empty((H, nb, d), dtype=torch.float32, device=dev)
+    anchor = torch.empty((H, d), dtype=torch.float32, device=dev)
+    idx = torch.empty((H, nb, topk), dtype=torch.int32, device=dev)
+    ksum = torch.empty((H, nb, d), dtype=torch.float32, device=dev)
+    vsum = torch.empty((H, nb, d), dtype=torch.float32, device=dev)
+    bias = torch.empty((H, nb), dtype=torch.float32, device=dev)
+    out = torch.empty_like(q)
+    a = L.make_args(H, N, d, b, dtype, w.n_anchor)
+    ws_r = L.workspace_bytes(a, L.OP_REBLOCK)
+    ws_a = L.workspace_bytes(a, L.OP_ATTN)
+    ws = torch.empty(max(ws_r, ws_a, 256), dtype=torch.uint8, device=dev)
+    lib = L.lib()
+    import ctypes
+    P = L._ptr
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    ab = ctypes.byref(a)
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        L._check(lib.spark_reblock(ab, P(q), P(k), P(v), P(perm_q), P(perm_k), P(q_p), P(k_p), P(v_pt),
+                                   P(qbar), P(kbar), P(anchor), P(ws), ws.numel(), sp), "spark_reblock")
+        if ev: ev[1].record(stream)
+        L._check(lib.spark_select(ab, P(qbar), P(kbar), None, topk, P(idx), None, sp), "spark_select")
+        if ev: ev[2].record(stream)
+        L._check(lib.spark_summarize(ab, P(k_p), P(v_pt), P(anchor), P(ksum), P(vsum), P(bias), sp),
+                 "spark_summarize")
+        if ev: ev[3].record(stream)
+        L._check(lib.spark_attn(ab, P(q_p), P(k_p), P(v_pt), P(idx), topk, P(ksum), P(vsum), P(bias),
+                                P(perm_q), P(out), P(ws), ws.numel(), sp), "spark_attn")
+        if ev: ev[4].record(stream)
+
+    for i in range(args.warmup):
+        step()
+        log(f"warmup {i + 1}/{args.warmup}")
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stages = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs])  # ms
+    layer_ms = wall * 1e3 / args.steps
+    st_mean = stages.mean(axis=0)
+    log(f"layer {layer_ms:.2f} ms; reblock {st_mean[0]:.2f} select {st_mean[1]:.2f} "
+        f"summarize {st_mean[2]:.2f} attn {st_mean[3]:.2f} ms")
+
+    exact, comp = attn_flops(idx.cpu().numpy(), N, b, d)
+    attn_s = st_mean[3] * 1e-3
+    exact_tf = exact / attn_s / 1e12
+    alg_tf = (exact + comp) / attn_s / 1e12
+    # deepest global split level: groups must fit the LDS finisher
+    fb = (140 * 1024) // (b * (d * es + 16))
+    fb = min(fb, 1024 // b)
+    F = 1
+    while F * 2 <= fb:
+        F *= 2
+    lev, mx = 0, nb
+    while mx > F:
+        mx = (mx + 1) // 2
+        lev += 1
+    rb_bytes = reblock_bytes(H, N, d, b, es, lev, nb)
+    rb_ms = st_mean[0] + st_mean[2]
+    traffic = load_traffic(os.path.join(ROOT, "block_sparse_attention_mahalanobis_amd", "csrc", "k_attn.hip"))
+
+    base = None
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on a sample (cpu_baseline)")
+        base = cpu_baseline(w, topk, args.cpu_sample_blocks)
+        log(f"cpu baseline {base['value']:.0f} ms projected ({base['sample']})")
+
+    rec = {
+        "metric": "Spark-Attn layer latency (ms) + exact-branch MFMA % peak, 245,952 tok @10% density",
+        "value": round(layer_ms, 3),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(layer_ms, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded clustered Gaussian-mixture q/k on the latent grid, v ~ N(0,1))",
+        "config": {"workload": w.name, "H": H, "N": N, "d": d, "block": b, "n_blocks": nb,
+                   "topk": topk, "density": w.ratio, "layout": "reblock", "summary": "reweight"},
+        "exact_mfma_pct_peak": round(100.0 * exact_tf / PEAK_BF16_TFLOPS, 2),
+        "stages_ms": {"reblock": round(st_mean[0], 3), "select": round(st_mean[1], 3),
+                      "summarize": round(st_mean[2], 3), "attn": round(st_mean[3], 3)},
+        "attn_tflops": {"exact": round(exact_tf, 1), "exact_plus_compressed": round(alg_tf, 1),
+                        "exact_tflop": round(exact / 1e12, 2), "compressed_tflop": round(comp / 1e12, 2)},
+        "reblock_summaries_hbm": {"algorithmic_gb": round(rb_bytes / 1e9, 1),
+                                  "achieved_gbs": round(rb_bytes / (rb_ms * 1e-3) / 1e9, 1),
+                                  "frac_of_8tbs": round(rb_bytes / (rb_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)},
+        "roofline": {"kernel": "attn_mfma<128,128> (spark_attn)", "bound": "mfma",
+                     "achieved": round(alg_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(alg_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+        "cpu_baseline": base,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -288,14 +288,15 @@ def mean_summaries(kp: np.ndarray, vp: np.ndarray, b: int):
 # Two-branch attention ([blog] Spark-Reblock section, BSA(Q_A) equations)
 # ----------------------------------------------------------------------------
 
-def sparse_attention(qp, kp, vp, idx, ksum, vsum, bias, b: int) -> np.ndarray:
+def sparse_attention(qp, kp, vp, idx, ksum, vsum, bias, b: int, qblocks=None) -> np.ndarray:
     """BSA(Q_A) = Softmax(Q_A K~_A^T / sqrt(d)) V~_A with one row-wise softmax
     over the concatenation, per key block B, of
         B in S_A : the exact rows K_B, V_B;
         B not in S_A : the summary k~_B, v~_B repeated |B| times (the
                        all-ones vector), its logit shifted by beta_B.
     The |B| identical summary rows are carried as one row of weight |B|.
-    Returns the output in permuted order [N, d]."""
+    Returns the output in permuted order [N, d].  ``qblocks`` (optional)
+    restricts the work to those query blocks; other rows stay 0."""
     qp = np.asarray(qp, np.float64)
     kp = np.asarray(kp, np.float64)
     vp = np.asarray(vp, np.float64)
@@ -304,7 +305,7 @@ def sparse_attention(qp, kp, vp, idx, ksum, vsum, bias, b: int) -> np.ndarray:
     sizes = block_sizes(N, b).astype(np.float64)
     rs = 1.0 / math.sqrt(d)
     out = np.zeros((N, d))
-    for A in range(nb):
+    for A in (range(nb) if qblocks is None else qblocks):
         rows = slice(A * b, min(N, (A + 1) * b))
         QA = qp[rows]
         sel = np.zeros(nb, dtype=bool)
