@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--config", default="full768", choices=["full768", "draft", "ref2va", "tiny"])
     p.add_argument("--ratio", type=float, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="run one plain device copy of this size before timing (counter calibration)")
     p.add_argument("--cpu-sample-blocks", type=int, default=768,
                    help="query blocks of head 0 the oracle attends in the CPU baseline sample")
     return p.parse_args()
@@ -118,7 +120,7 @@ def cpu_baseline(w, topk, sample_blocks):
 def load_traffic(kernel_src):
     """HBM traffic per attention launch from the committed rocprofv3 --pmc
     summary, if it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", "attn_full768_traffic.json")
+    path = os.path.join(ROOT, "profiles", "attn_full768_traffic.txt")
     if not os.path.exists(path):
         return None
     try:
@@ -201,6 +203,14 @@ def main():
                                 P(perm_q), P(out), P(ws), ws.numel(), sp), "spark_attn")
         if ev: ev[4].record(stream)
 
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {n} bytes read + {n} bytes written")
+        del src, dst
     for i in range(args.warmup):
         step()
         log(f"warmup {i + 1}/{args.warmup}")
@@ -265,7 +275,7 @@ def main():
         "reblock_summaries_hbm": {"algorithmic_gb": round(rb_bytes / 1e9, 1),
                                   "achieved_gbs": round(rb_bytes / (rb_ms * 1e-3) / 1e9, 1),
                                   "frac_of_8tbs": round(rb_bytes / (rb_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)},
-        "roofline": {"kernel": "attn_mfma<128,128> (spark_attn)", "bound": "mfma",
+        "roofline": {"kernel": "attn_mfma_d128 (spark_attn)", "bound": "mfma",
                      "achieved": round(alg_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(alg_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "cpu_baseline": base,

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <utility>
 
 #include "../../include/spark.h"

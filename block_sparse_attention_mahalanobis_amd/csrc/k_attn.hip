@@ -5,14 +5,16 @@
 // summary repeated |B| times; the summaries and log-mass bias come from
 // 02 / Method: Spark-Reweight).
 //
-// Two kernels:
+// Three kernels:
+//  * attn_mfma_d128: bf16, d = 128, block 128 (the 768p layer shape); see its
+//    own comment below.
 //  * attn_mfma: bf16, block size 32/64/128, d 64/128.  One workgroup per
 //    (head, query block), one wave per 32 query rows.  S^T = K Q^T and
 //    O^T = V^T P^T on v_mfma_f32_32x32x16_bf16 with fp32 accumulation, an
-//    online softmax in the log2 domain, K / V^T tiles staged through LDS with
-//    a register prefetch of the next tile.  The compressed branch runs the
-//    same loop over tiles of bf16 summaries, with the per-block bias
-//    (+ log |B|) added to the logits and the selected blocks masked to -inf.
+//    online softmax in the log2 domain, K / V^T tiles staged through LDS.
+//    The compressed branch runs the same loop over tiles of bf16 summaries,
+//    with the per-block bias (+ log |B|) added to the logits and the selected
+//    blocks masked to -inf.
 //  * attn_generic: fp32 or bf16, any block size 1..128; one thread per query
 //    row, fp32 VALU arithmetic.  Small and slow; it exists for the fp32
 //    workloads and odd block sizes.
@@ -267,26 +269,12 @@ __global__ __launch_bounds__(2 * BK) void attn_mfma(
 }
 
 // ---------------------------------------------------------------------------
-// attn_mfma_d128: the d = 128, block = 128 kernel.
-//
-// 8 waves per workgroup: wave w owns query rows 32*(w&3).. and keys
-// 64*(w>>2).. of every tile, i.e. the two waves of a row group split each key
-// tile and keep independent online-softmax states that are merged at the end.
-// Two waves per SIMD let one wave's softmax (VALU, exp) run while the other
-// issues MFMAs.  K and V^T tiles are double-buffered in LDS and filled by
-// direct global->LDS loads (global_load_lds_dwordx4) issued one tile ahead,
-// so no registers hold the prefetch.  Tiles are stored with 256-byte rows and
-// the 16-byte chunk index XOR-swizzled by (row & 15), which keeps the
-// MFMA-operand reads (16 rows x 16 B per quarter-wave) free of bank conflicts
-// without padding (direct loads fill 1 KB contiguous per instruction).
-// The running max is only raised when a tile's max exceeds it by more than
-// 8 (log2 units); otherwise the stale max is kept and the O rescale skipped
-// (exact: numerator and denominator use the same reference).
+// Helpers of the d = 128 kernel.  Tiles sit in LDS as 128 rows of 256 bytes
+// with the 16-byte chunk index XOR-swizzled by (row & 15): the MFMA operand
+// reads (16 consecutive rows, one chunk each, per quarter-wave) then hit 16
+// different bank groups, and the direct global->LDS loads, which write 1 KB
+// contiguous per instruction, need no padding.
 // ---------------------------------------------------------------------------
-constexpr int V2_NT = 512;                 // 8 waves
-constexpr int V2_TILE_BYTES = 2 * 128 * 256;   // K + V^T of one tile
-constexpr int V2_LDS_TILES = 2 * V2_TILE_BYTES;  // double buffer: 128 KB
-
 __device__ __forceinline__ int sw_off(int row, int lc) {  // byte offset in a 128x256 B tile
   return row * 256 + ((lc ^ (row & 15)) << 4);
 }
@@ -295,7 +283,7 @@ __device__ __forceinline__ int sw_off(int row, int lc) {  // byte offset in a 12
 // ranges, one per XCD: every XCD works on the same head at the same time
 // (that head's K/V stays in the shared last-level cache), and each XCD walks
 // tree-adjacent query blocks (similar selections, L2 reuse).
-__device__ __forceinline__ bool v2_map(int bid, int nb, int& h, int& A) {
+__device__ __forceinline__ bool d128_map(int bid, int nb, int& h, int& A) {
   const int nb8 = (nb + 7) & ~7;
   h = bid / nb8;
   const int r = bid - h * nb8;
@@ -303,7 +291,19 @@ __device__ __forceinline__ bool v2_map(int bid, int nb, int& h, int& A) {
   return A < nb;
 }
 
-__global__ __launch_bounds__(V2_NT) void attn_mfma_d128(
+// ---------------------------------------------------------------------------
+// attn_mfma_d128: d = 128, block = 128, 4 waves x 32 query rows, full 128-key
+// tiles per wave, and TWO workgroups per CU (72 KB of LDS each): while one
+// workgroup waits on a barrier or a tile load the other one's waves issue
+// MFMAs and softmax, so the two interleave on every SIMD.  K and V^T use one
+// LDS buffer each, refilled by direct global->LDS loads in split phases:
+// K(t+1) streams in during softmax(t) + PV(t), V(t+1) during QK(t+1) +
+// softmax(t+1).
+// ---------------------------------------------------------------------------
+constexpr int D128_NT = 256;
+constexpr int D128_LDS_TILES = 2 * 128 * 256;   // K + V^T, 64 KB
+
+__global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
     const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vpt, const int32_t* __restrict__ idx, int topk,
     const uint16_t* __restrict__ ks16, const uint16_t* __restrict__ vs16t,
@@ -311,64 +311,62 @@ __global__ __launch_bounds__(V2_NT) void attn_mfma_d128(
     uint16_t* __restrict__ out, int H, int N, int nb, int nbp, float scale_log2) {
   constexpr int D = 128, BK = 128;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  float* sBias = reinterpret_cast<float*>(smem + V2_LDS_TILES);
+  unsigned char* sK = smem;
+  unsigned char* sV = smem + 128 * 256;
+  float* sBias = reinterpret_cast<float*>(smem + D128_LDS_TILES);
 
   int h, A;
-  if (!v2_map(blockIdx.x, nb, h, A)) return;
+  if (!d128_map(blockIdx.x, nb, h, A)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
-  const int rg = wave & 3, kh = wave >> 2;
   const long Np = (long)nb * BK;
   const int nct = (topk < nb) ? nbp / BK : 0;
   const int ntiles = topk + nct;
   const int32_t* myidx = idx + ((long)h * nb + A) * topk;
 
   if (nct > 0) {
-    for (int i = tid; i < nbp; i += V2_NT) sBias[i] = bias2[(long)h * nbp + i];
+    for (int i = tid; i < nbp; i += D128_NT) sBias[i] = bias2[(long)h * nbp + i];
     __syncthreads();
-    for (int t = tid; t < topk; t += V2_NT) sBias[myidx[t]] = -INFINITY;
-    // made visible by the first barrier of the tile loop
+    for (int t = tid; t < topk; t += D128_NT) sBias[myidx[t]] = -INFINITY;
   }
 
-  // direct-load plan of this wave: 8 x 1 KB per tile; instructions g = 8w..8w+7
-  // (g < 32: K slots 4g..4g+3; g >= 32: V^T rows 4(g-32)..)
-  const int p_row = lane >> 4, p_pc = lane & 15;
-  auto issue_tile = [&](int t, int buf) {
-    const uint16_t* ksrc;
-    const uint16_t* vsrc;
+  // per-lane byte offsets (loop invariant) of this wave's 8 direct loads per
+  // tensor: instruction i fills LDS rows 4*(8*wave+i) .. +3
+  uint32_t koff[8], voff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int srow = 4 * (8 * wave + i) + (lane >> 4);
+    const int lc = (lane & 15) ^ (srow & 15);
+    const int grow = (srow & ~31) + ((((srow & 31) >> 3) >> 1) << 4) + (((srow >> 2) & 1) << 3) +
+                     ((((srow & 31) >> 3) & 1) << 2) + (srow & 3);
+    koff[i] = (uint32_t)(grow * D + lc * 8) * 2u;
+    voff[i] = (uint32_t)(srow * BK + lc * 8) * 2u;
+  }
+  auto tile_base = [&](int t, const char*& kb, const char*& vb) {
     if (t < topk) {
       const int B = myidx[t];
-      ksrc = kp + ((long)h * Np + (long)B * BK) * D;
-      vsrc = vpt + ((long)h * nb + B) * (long)D * BK;
+      kb = reinterpret_cast<const char*>(kp + ((long)h * Np + (long)B * BK) * D);
+      vb = reinterpret_cast<const char*>(vpt + ((long)h * nb + B) * (long)D * BK);
     } else {
       const int c = t - topk;
-      ksrc = ks16 + ((long)h * nbp + (long)c * BK) * D;
-      vsrc = vs16t + ((long)h * (nbp / BK) + c) * (long)D * BK;
-    }
-    unsigned char* base = smem + buf * V2_TILE_BYTES;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int g = wave * 8 + i;
-      const int part = g >> 5, gg = g & 31;
-      const int srow = 4 * gg + p_row;
-      const int lc = p_pc ^ (srow & 15);
-      const uint16_t* src;
-      if (part == 0) {
-        const int grow = (srow & ~31) + ((((srow & 31) >> 3) >> 1) << 4) + (((srow >> 2) & 1) << 3) +
-                         ((((srow & 31) >> 3) & 1) << 2) + (srow & 3);
-        src = ksrc + (long)grow * D + lc * 8;
-      } else {
-        src = vsrc + (long)srow * BK + lc * 8;
-      }
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)src,
-          (void __attribute__((address_space(3)))*)(base + part * (128 * 256) + gg * 1024), 16, 0, 0);
+      kb = reinterpret_cast<const char*>(ks16 + ((long)h * nbp + (long)c * BK) * D);
+      vb = reinterpret_cast<const char*>(vs16t + ((long)h * (nbp / BK) + c) * (long)D * BK);
     }
   };
+  // one 32 KB tile through a buffer resource (scalar base, 32-bit lane
+  // offsets; bytes past the tile would read as 0)
+  auto issue = [&](const char* base, const uint32_t* off, unsigned char* dst) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 128 * 256, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (void __attribute__((address_space(3)))*)(dst + (8 * wave + i) * 1024), 16, off[i], 0,
+          0, 0);
+  };
 
-  // Q operand: rows 32rg + l32, d = 16s + 8hf ..
-  const long qrow = (long)h * Np + (long)A * BK + rg * 32 + l32;
+  const long qrow = (long)h * Np + (long)A * BK + wave * 32 + l32;
   bf16x8 qop[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s)
@@ -381,50 +379,81 @@ __global__ __launch_bounds__(V2_NT) void attn_mfma_d128(
     for (int v = 0; v < 16; ++v) oacc[t][v] = 0.f;
   float m_ref = -1e30f, l_run = 0.f;
 
-  if (ntiles > 0) issue_tile(0, 0);
+  // per-lane LDS read offsets (loop invariant): row 32*jt + l32, logical
+  // chunk 2s + hf; the 32-row tile index only adds the constant jt * 8 KB.
+  int ro[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) ro[s] = sw_off(l32, 2 * s + hf);
+
+  {
+    const char *kb, *vb;
+    tile_base(0, kb, vb);
+    issue(kb, koff, sK);
+    issue(vb, voff, sV);
+  }
 
   for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // tile t landed (all waves); buffer buf^1 free
-    if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
-    const unsigned char* tK = smem + buf * V2_TILE_BYTES;
-    const unsigned char* tV = tK + 128 * 256;
-
-    // S^T for keys 64kh .. 64kh+63 (two 32-key tiles)
-    f32x16 sacc[2];
+    const bool exact = t < topk;
+    // K(t) landed (V(t) may still be in flight)
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    __syncthreads();
+    f32x16 sacc[4];
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt) {
+    for (int jt = 0; jt < 4; ++jt) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[jt][v] = 0.f;
-      const int row = 32 * (2 * kh + jt) + l32;
+    }
+    __builtin_amdgcn_s_setprio(2);  // favour the wave that feeds the matrix core
+    {
+      // operands of step s+1 are read while the 4 MFMAs of step s run
+      bf16x8 kop[2][4];
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+        kop[0][jt] = *reinterpret_cast<const bf16x8*>(sK + ro[0] + jt * 8192);
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(tK + sw_off(row, 2 * s + hf));
-        sacc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[s], sacc[jt], 0, 0, 0);
+        if (s + 1 < D / 16) {
+#pragma unroll
+          for (int jt = 0; jt < 4; ++jt)
+            kop[(s + 1) & 1][jt] = *reinterpret_cast<const bf16x8*>(sK + ro[s + 1] + jt * 8192);
+        }
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt)
+          sacc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[s & 1][jt], qop[s], sacc[jt], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
+    __syncthreads();  // every wave is done reading sK
+    const char *kb1 = nullptr, *vb1 = nullptr;
+    if (t + 1 < ntiles) {
+      tile_base(t + 1, kb1, vb1);
+      issue(kb1, koff, sK);
+    }
 
-    float mx = -INFINITY;
-    if (t < topk) {
+    float mx;
+    if (exact) {
       const int B = myidx[t];
       const int valid = (B == nb - 1) ? (N - (nb - 1) * BK) : BK;
+      if (valid < BK) {
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
+        for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float s2 = sacc[jt][v] * scale_log2;
-          if (valid < BK) {
-            const int j = 64 * kh + 32 * jt + ((v < 8) ? 8 * hf + v : 16 + 8 * hf + v - 8);
-            if (j >= valid) s2 = -INFINITY;
+          for (int v = 0; v < 16; ++v) {
+            const int j = 32 * jt + ((v < 8) ? 8 * hf + v : 16 + 8 * hf + v - 8);
+            if (j >= valid) sacc[jt][v] = -INFINITY;
           }
-          sacc[jt][v] = s2;
-          mx = fmaxf(mx, s2);
-        }
-    } else {
-      const float* bb = sBias + (t - topk) * BK + 64 * kh;
+      }
+      float mr = sacc[0][0];
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mr = fmaxf(mr, sacc[jt][v]);
+      mx = mr * scale_log2;
+    } else {
+      const float* bb = sBias + (t - topk) * BK;
+      mx = -INFINITY;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int j = 32 * jt + ((v < 8) ? 8 * hf + v : 16 + 8 * hf + v - 8);
@@ -434,7 +463,6 @@ __global__ __launch_bounds__(V2_NT) void attn_mfma_d128(
         }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // raise the reference max only when this tile exceeds it by > 8
     const bool need = mx > m_ref + 8.f;
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
       const float m_new = fmaxf(m_ref, mx);
@@ -446,50 +474,62 @@ __global__ __launch_bounds__(V2_NT) void attn_mfma_d128(
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
     }
-    bf16x8 pop[4];
+    bf16x8 pop[8];
+    if (exact) {
+      const float nm = -m_ref;
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
+      for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(sacc[jt][8 * hh + e] - m_ref);
-          l_run += p;
-          pop[2 * jt + hh][e] = (__bf16)p;
+          for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[jt][8 * hh + e], scale_log2, nm));
+            l_run += p;
+            pop[2 * jt + hh][e] = (__bf16)p;
+          }
+    } else {
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(sacc[jt][8 * hh + e] - m_ref);
+            l_run += p;
+            pop[2 * jt + hh][e] = (__bf16)p;
+          }
+    }
+
+    // V(t) landed: only this wave's 8 K(t+1) loads may be outstanding
+    if (t + 1 < ntiles) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    __builtin_amdgcn_s_setprio(2);
+    {
+      bf16x8 vop[2][4];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        vop[0][dt] = *reinterpret_cast<const bf16x8*>(sV + ro[0] + dt * 8192);
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        if (ks + 1 < BK / 16) {
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+            vop[(ks + 1) & 1][dt] = *reinterpret_cast<const bf16x8*>(sV + ro[ks + 1] + dt * 8192);
         }
-
-    // O^T += V^T P^T over this wave's 64 keys
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int ks = 4 * kh + kk;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(tV + sw_off(32 * dt + l32, 2 * ks + hf));
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[kk], oacc[dt], 0, 0, 0);
+        for (int dt = 0; dt < D / 32; ++dt)
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[ks & 1][dt], pop[ks], oacc[dt], 0, 0, 0);
       }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    __syncthreads();  // every wave is done reading sV
+    if (t + 1 < ntiles) issue(vb1, voff, sV);
   }
 
-  // --- merge the two key halves of each row group, then scatter ---------------
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  __syncthreads();  // all waves done with the tile buffers
-  float* sm = reinterpret_cast<float*>(smem);
-  // per row group: [64 lanes][16 v][4 dt] O^T values + m, l per lane
-  float* mo = sm + rg * (64 * 16 * 4 + 128);
-  if (kh == 1) {
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mo[(dt * 16 + v) * 64 + lane] = oacc[dt][v];
-    mo[64 * 64 + lane] = m_ref;
-    mo[64 * 64 + 64 + lane] = l_tot;
-  }
-  __syncthreads();
-  if (kh == 1) return;
-  const float m2 = mo[64 * 64 + lane], l2 = mo[64 * 64 + 64 + lane];
-  const float mm = fmaxf(m_ref, m2);
-  const float f1 = __builtin_amdgcn_exp2f(m_ref - mm), f2 = __builtin_amdgcn_exp2f(m2 - mm);
-  const float inv = 1.f / (l_tot * f1 + l2 * f2);
-  const long prow = (long)A * BK + rg * 32 + l32;
+  const float inv = 1.f / l_tot;
+  const long prow = (long)A * BK + wave * 32 + l32;
   uint16_t* dst;
   if (perm_q != nullptr) {
     if (prow >= N) return;
@@ -504,11 +544,7 @@ __global__ __launch_bounds__(V2_NT) void attn_mfma_d128(
     for (int a = 0; a < 4; ++a) {
       float o[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int v = 4 * a + c;
-        const float val = (oacc[dt][v] * f1 + mo[(dt * 16 + v) * 64 + lane] * f2) * inv;
-        o[c] = pad ? 0.f : val;
-      }
+      for (int c = 0; c < 4; ++c) o[c] = pad ? 0.f : oacc[dt][4 * a + c] * inv;
       uint2 w;
       w.x = pack_bf2(o[0], o[1]);
       w.y = pack_bf2(o[2], o[3]);
@@ -677,23 +713,20 @@ static int launch_mfma(const void* qp, const void* kp, const void* vpt, const in
   return spark_check_launch("attn_mfma");
 }
 
-static int launch_v2(const void* qp, const void* kp, const void* vpt, const int32_t* idx, int topk,
+static int launch_d128(const void* qp, const void* kp, const void* vpt, const int32_t* idx, int topk,
                      const uint16_t* ks16, const uint16_t* vs16t, const float* bias2,
                      const int32_t* perm_q, void* out, int H, int N, int nb, int nbp,
                      hipStream_t st) {
-  const size_t lds = V2_LDS_TILES + (size_t)nbp * 4;
-  if (lds > 160 * 1024)
-    return spark_set_error(SPARK_E_SHAPE, "spark_attn: %d blocks need %zu B of LDS (max 163840)",
-                           nb, lds);
+  const size_t lds = D128_LDS_TILES + (size_t)nbp * 4;
   static bool attr_set = false;
   if (!attr_set) {
     hipFuncSetAttribute((const void*)attn_mfma_d128, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        160 * 1024);
+                        80 * 1024);
     attr_set = true;
   }
   const float scale_log2 = kLog2e / sqrtf(128.f);
   const int nb8 = (nb + 7) & ~7;
-  hipLaunchKernelGGL(attn_mfma_d128, dim3(H * nb8), dim3(V2_NT), lds, st, (const uint16_t*)qp,
+  hipLaunchKernelGGL(attn_mfma_d128, dim3(H * nb8), dim3(D128_NT), lds, st, (const uint16_t*)qp,
                      (const uint16_t*)kp, (const uint16_t*)vpt, idx, topk, ks16, vs16t, bias2,
                      perm_q, (uint16_t*)out, H, N, nb, nbp, scale_log2);
   return spark_check_launch("attn_mfma_d128");
@@ -731,8 +764,8 @@ int attn_launch(int H, int N, int D, int BK, int dtype, const void* qp, const vo
     int rc = spark_check_launch("attn_prep_summaries");
     if (rc) return rc;
     if (D == 128) {
-      if (BK == 128 && (size_t)V2_LDS_TILES + (size_t)nbp * 4 <= 160 * 1024)
-        return launch_v2(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, nb, nbp, st);
+      if (BK == 128 && (size_t)D128_LDS_TILES + (size_t)nbp * 4 <= 80 * 1024)
+        return launch_d128(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, nb, nbp, st);
       if (BK == 128) return launch_mfma<128, 128>(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, nb, nbp, st);
       if (BK == 64) return launch_mfma<128, 64>(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, nb, nbp, st);
       return launch_mfma<128, 32>(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, nb, nbp, st);
