@@ -83,17 +83,146 @@ __device__ __forceinline__ uint32_t float_key_asc(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Wave64 reductions through cross-lane shuffles.
-__device__ __forceinline__ float wave_sum(float v) {
+// k-th smallest (1-based) of n <= 64 * KPL uint32 keys, found by ONE wave:
+// every lane copies its keys (i = lane + 64 j) into registers, then a
+// bisection over the key space runs 32 rounds of count(key <= mid) -- register
+// compares plus a wave reduction; no atomics, no barriers, no LDS traffic.
+// Returns the key; *ties_needed = k - count(key < result).  Padding slots
+// hold 0xffffffff and never count below a real threshold (k <= n).
+template <int KPL>
+__device__ __forceinline__ uint32_t wave_kth_key(const uint32_t* keys, int n, int k,
+                                                 int* ties_needed) {
+  const int lane = threadIdx.x & 63;
+  uint32_t r[KPL];
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
+  for (int j = 0; j < KPL; ++j) {
+    const int i = lane + 64 * j;
+    r[j] = (i < n) ? keys[i] : 0xffffffffu;
+  }
+  uint32_t lo = 0u, hi = 0xffffffffu;
+  while (lo < hi) {
+    const uint32_t mid = lo + ((hi - lo) >> 1);
+    // wave-wide count as a sum of ballot popcounts (scalar unit, no shuffles);
+    // padding keys (0xffffffff) never count: mid < 0xffffffff inside the loop
+    int c = 0;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+    for (int j = 0; j < KPL; ++j) c += __builtin_popcountll(__builtin_amdgcn_ballot_w64(r[j] <= mid));
+    if (c >= k) hi = mid; else lo = mid + 1;
+  }
+  int less = 0;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) less += __builtin_popcountll(__builtin_amdgcn_ballot_w64(r[j] < lo));
+  *ties_needed = k - less;
+  return lo;
 }
+
+// Same result for any n, reading the keys from LDS every round (slower).
+__device__ __forceinline__ uint32_t wave_kth_key_lds(const uint32_t* keys, int n, int k,
+                                                     int* ties_needed) {
+  const int lane = threadIdx.x & 63;
+  uint32_t lo = 0u, hi = 0xffffffffu;
+  while (lo < hi) {
+    const uint32_t mid = lo + ((hi - lo) >> 1);
+    int c = 0;
+    for (int i0 = 0; i0 < n; i0 += 64) {
+      const int i = i0 + lane;
+      c += __builtin_popcountll(__builtin_amdgcn_ballot_w64(i < n && keys[i] <= mid));
+    }
+    if (c >= k) hi = mid; else lo = mid + 1;
+  }
+  int less = 0;
+  for (int i0 = 0; i0 < n; i0 += 64) {
+    const int i = i0 + lane;
+    less += __builtin_popcountll(__builtin_amdgcn_ballot_w64(i < n && keys[i] < lo));
+  }
+  *ties_needed = k - less;
+  return lo;
+}
+
+// Butterfly reductions over aligned groups of G lanes (G a power of two,
+// 2..64); every lane of a group ends with the group's result, bit-identical
+// across the group.  Step S combines each lane with its xor-S partner.  Within
+// a 16-lane row the partner comes from DPP moves; across rows,
+// v_permlane16_swap / v_permlane32_swap exchange whole rows in one VALU op.
+// No LDS crossbar (ds_bpermute) traffic.
+//
+// A reduction that starts at step 1 may use a half-row / row mirror for steps
+// 4 and 8 (after the earlier steps every S-subgroup is uniform, so lane 7-i
+// holds what lane i^4 holds); one that starts at S0 > 1 (folding lanes that
+// own the same column chunk of different rows) needs the exact xor, built
+// from two bank-masked row shifts.
+template <int CTRL, int BANKS = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, 0xf, BANKS, false);
+}
+template <int S, bool UNIFORM>
+__device__ __forceinline__ uint32_t dpp_partner(uint32_t v) {
+  static_assert(S == 1 || S == 2 || S == 4 || S == 8, "DPP step");
+  if constexpr (S == 1) return dpp_u32<0xB1>(0, v);       // quad_perm [1,0,3,2]
+  else if constexpr (S == 2) return dpp_u32<0x4E>(0, v);  // quad_perm [2,3,0,1]
+  else if constexpr (UNIFORM && S == 4) return dpp_u32<0x141>(0, v);  // row_half_mirror
+  else if constexpr (UNIFORM && S == 8) return dpp_u32<0x140>(0, v);  // row_mirror
+  else if constexpr (S == 4)
+    // banks (4-lane groups of a row) 0 and 2 read lane+4, banks 1 and 3 lane-4
+    return dpp_u32<0x104, 0x5>(dpp_u32<0x114, 0xA>(0, v), v);
+  else
+    // banks 0-1 read lane+8, banks 2-3 lane-8
+    return dpp_u32<0x108, 0x3>(dpp_u32<0x118, 0xC>(0, v), v);
+}
+// (a, b) = this lane's value and its xor-S partner's (in either order).
+template <int S, bool UNIFORM>
+__device__ __forceinline__ void bfly_pair(uint32_t v, uint32_t& a, uint32_t& b) {
+  if constexpr (S <= 8) {
+    a = v;
+    b = dpp_partner<S, UNIFORM>(v);
+  } else if constexpr (S == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    a = r[0];
+    b = r[1];
+  } else {
+    static_assert(S == 32, "step");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    a = r[0];
+    b = r[1];
+  }
+}
+
+// Sum over aligned groups of G lanes; with S0 > 1, lanes S0 apart hold
+// partial sums of the same quantity and lanes within an S0-group are unrelated.
+template <int G, int S0 = 1, int S = S0>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (S < G) {
+    uint32_t a, b;
+    bfly_pair<S, S0 == 1>(__float_as_uint(v), a, b);
+    return group_sum<G, S0, 2 * S>(__uint_as_float(a) + __uint_as_float(b));
+  } else {
+    return v;
+  }
+}
+template <int G, int S = 1>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (S < G) {
+    uint32_t a, b;
+    bfly_pair<S, true>(__float_as_uint(v), a, b);
+    return group_max<G, 2 * S>(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  } else {
+    return v;
+  }
+}
+template <int G, int S = 1>
+__device__ __forceinline__ uint64_t group_min_u64(uint64_t v) {
+  if constexpr (S < G) {
+    uint32_t ah, bh, al, bl;
+    bfly_pair<S, true>((uint32_t)(v >> 32), ah, bh);
+    bfly_pair<S, true>((uint32_t)v, al, bl);
+    const uint64_t a = ((uint64_t)ah << 32) | al, b = ((uint64_t)bh << 32) | bl;
+    return group_min_u64<G, 2 * S>(a < b ? a : b);
+  } else {
+    return v;
+  }
+}
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
+__device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
 
 inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 

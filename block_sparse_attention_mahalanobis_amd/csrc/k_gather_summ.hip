@@ -52,10 +52,33 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ x,
   }
   __syncthreads();
   if (xpt) {
-    // [D][BK]: thread handles (c, j-run); consecutive threads take consecutive j
-    for (int e = tid; e < D * BK; e += blockDim.x) {
-      const int c = e / BK, j = e % BK;
-      xpt[(((long)h * nb + B) * D + c) * BK + j] = tile[j * RS + c];
+    // [D][BK]: a thread packs VE consecutive j of one column c into 16 bytes
+    constexpr int VE = 16 / sizeof(T);
+    if (BK % VE == 0) {
+      const int runs = BK / VE;
+      for (int e = tid; e < D * runs; e += blockDim.x) {
+        const int c = e / runs, j0 = (e % runs) * VE;
+        uint4 u;
+        if constexpr (sizeof(T) == 2) {
+          const uint16_t* tt = reinterpret_cast<const uint16_t*>(tile) + j0 * RS + c;
+          u.x = (uint32_t)tt[0] | ((uint32_t)tt[RS] << 16);
+          u.y = (uint32_t)tt[2 * RS] | ((uint32_t)tt[3 * RS] << 16);
+          u.z = (uint32_t)tt[4 * RS] | ((uint32_t)tt[5 * RS] << 16);
+          u.w = (uint32_t)tt[6 * RS] | ((uint32_t)tt[7 * RS] << 16);
+        } else {
+          const float* tt = reinterpret_cast<const float*>(tile) + j0 * RS + c;
+          u.x = __float_as_uint(tt[0]);
+          u.y = __float_as_uint(tt[RS]);
+          u.z = __float_as_uint(tt[2 * RS]);
+          u.w = __float_as_uint(tt[3 * RS]);
+        }
+        *reinterpret_cast<uint4*>(xpt + (((long)h * nb + B) * D + c) * BK + j0) = u;
+      }
+    } else {
+      for (int e = tid; e < D * BK; e += blockDim.x) {
+        const int c = e / BK, j = e % BK;
+        xpt[(((long)h * nb + B) * D + c) * BK + j] = tile[j * RS + c];
+      }
     }
   }
   if (xbar) {
@@ -133,8 +156,7 @@ __global__ __launch_bounds__(256) void summarize_kernel(const T* __restrict__ kp
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc = fmaf(v[e], s_anchor[c + e], acc);
       }
-#pragma unroll
-      for (int o = CPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+      acc = group_sum<CPR>(acc);
       if (j < n_real && (tid % CPR) == 0) s_w[j] = acc * rsd;
     }
     __syncthreads();

@@ -2,11 +2,11 @@
 // are scored from block-level means and the Top-K selected blocks get exact
 // attention; 01 / Method: Spark-Reblock: a fixed Top-K budget per query block).
 //
-// One workgroup per (head, query block A): the row S[A, :] = qbar_A . kbar_B /
-// sqrt(d) is computed into LDS (or read from scores_in), then an exact radix
-// select over 32-bit order keys finds the k-th best (score desc, block asc);
-// the selected blocks are written in ascending block order through a
-// workgroup prefix sum.  Integer decisions only; bit-exact for given scores.
+// One workgroup per (head, 8 consecutive query blocks): the rows S[A, :] =
+// qbar_A . kbar_B / sqrt(d) are computed into LDS (each k_bar chunk read once
+// for all 8 rows; or read from scores_in); then one wave per row finds the
+// k-th best order key (score desc, block asc) by bisection and writes the
+// selected blocks in ascending order with ballot prefix sums.  Integer decisions only; bit-exact for given scores.
 #include "common.hpp"
 
 namespace spark {
@@ -19,26 +19,7 @@ __device__ __forceinline__ uint32_t pref_key(float s) {
   return ~float_key_asc(s);
 }
 
-// Exclusive prefix sum over the workgroup of one int per thread.
-__device__ __forceinline__ int block_exscan(int v, int* s_tmp, int& total) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
-  }
-  if (lane == 63) s_tmp[w] = incl;
-  __syncthreads();
-  int base = 0, tot = 0;
-  for (int i = 0; i < SEL_T / 64; ++i) {
-    if (i < w) base += s_tmp[i];
-    tot += s_tmp[i];
-  }
-  __syncthreads();
-  total = tot;
-  return base + incl - v;
-}
+constexpr int SEL_QB = 8;   // query blocks per workgroup (they share each k_bar read)
 
 template <int D>
 __global__ __launch_bounds__(SEL_T) void select_kernel(const float* __restrict__ qbar,
@@ -46,121 +27,86 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(const float* __restrict__
                                                        const float* __restrict__ scores_in,
                                                        int topk, int32_t* __restrict__ idx,
                                                        float* __restrict__ scores_out, int nb,
-                                                       float rsd) {
+                                                       int qb, float rsd) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint32_t* s_key = reinterpret_cast<uint32_t*>(smem);  // [nb]
-  __shared__ int s_hist[256];
-  __shared__ int s_tmp[SEL_T / 64];
-  __shared__ uint32_t s_prefix;
-  __shared__ int s_need;
+  uint32_t* s_keys = reinterpret_cast<uint32_t*>(smem);  // [qb][nb]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = blockIdx.x / nb, A = blockIdx.x % nb;
-  const long rowoff = ((long)h * nb + A) * nb;
+  const int nqb = (nb + qb - 1) / qb;
+  const int h = blockIdx.x / nqb, A0 = (blockIdx.x % nqb) * qb;
+  const int nq = min(qb, nb - A0);
 
-  // --- scores -------------------------------------------------------------
+  // --- scores of rows A0 .. A0+nq-1 ----------------------------------------
   if (scores_in) {
-    for (int B = tid; B < nb; B += SEL_T) {
-      const float s = scores_in[rowoff + B];
-      if (scores_out) scores_out[rowoff + B] = s;
-      s_key[B] = pref_key(s);
+    for (int q = 0; q < nq; ++q) {
+      const long rowoff = ((long)h * nb + A0 + q) * nb;
+      for (int B = tid; B < nb; B += SEL_T) {
+        const float sc = scores_in[rowoff + B];
+        if (scores_out) scores_out[rowoff + B] = sc;
+        s_keys[q * nb + B] = pref_key(sc);
+      }
     }
   } else {
-    // half-wave per key block, 4 consecutive dims per lane (D/4 lanes used)
-    constexpr int LPB = D / 4;  // lanes per block row: 32 or 16
-    constexpr int BPW = 64 / LPB;
-    const int sub = lane / LPB, l = lane % LPB;
-    const float4 qa = *reinterpret_cast<const float4*>(qbar + ((long)h * nb + A) * D + 4 * l);
-    for (int B0 = wave * BPW; B0 < nb; B0 += (SEL_T / 64) * BPW) {
-      const int B = B0 + sub;
-      float acc = 0.f;
-      if (B < nb) {
-        const float4 kb = *reinterpret_cast<const float4*>(kbar + ((long)h * nb + B) * D + 4 * l);
-        acc = qa.x * kb.x;
-        acc = fmaf(qa.y, kb.y, acc);
-        acc = fmaf(qa.z, kb.z, acc);
-        acc = fmaf(qa.w, kb.w, acc);
-      }
-#pragma unroll
-      for (int o = LPB / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-      if (B < nb && l == 0) {
-        const float s = acc * rsd;
-        if (scores_out) scores_out[rowoff + B] = s;
-        s_key[B] = pref_key(s);
-      }
-    }
-  }
-  if (tid == 0) {
-    s_prefix = 0;
-    s_need = topk;  // rank (1-based) of the threshold among keys matching the prefix
-  }
-  __syncthreads();
-
-  // --- radix select of the topk-th smallest key, 8 bits per round ----------
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += SEL_T) s_hist[i] = 0;
+    // one key block per lane: the nq query means sit in LDS (broadcast
+    // reads), the lane streams its k_bar row; no cross-lane reductions
+    float* s_q = reinterpret_cast<float*>(smem + (size_t)qb * nb * 4);   // [qb][D]
+    for (int e = tid; e < nq * D; e += SEL_T) s_q[e] = qbar[((long)h * nb + A0) * D + e];
     __syncthreads();
-    const uint32_t pre = s_prefix;
-    const uint32_t hmask = (shift == 24) ? 0u : (0xffffffffu << (shift + 8));
     for (int B = tid; B < nb; B += SEL_T) {
-      const uint32_t k = s_key[B];
-      if ((k & hmask) == pre) atomicAdd(&s_hist[(k >> shift) & 255], 1);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // inclusive scan of 256 bins, 4 per lane
-      int c[4], run = 0;
+      const float* kr = kbar + ((long)h * nb + B) * D;
+      float acc[SEL_QB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { run += s_hist[4 * lane + i]; c[i] = run; }
-      int incl = run;
+      for (int q = 0; q < SEL_QB; ++q) acc[q] = 0.f;
+#pragma unroll 4
+      for (int c = 0; c < D; c += 4) {
+        const float4 kv = *reinterpret_cast<const float4*>(kr + c);
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += t;
+        for (int q = 0; q < SEL_QB; ++q) {
+          if (q < nq) {
+            const float4 qv = *reinterpret_cast<const float4*>(s_q + q * D + c);
+            acc[q] = fmaf(qv.x, kv.x, acc[q]);
+            acc[q] = fmaf(qv.y, kv.y, acc[q]);
+            acc[q] = fmaf(qv.z, kv.z, acc[q]);
+            acc[q] = fmaf(qv.w, kv.w, acc[q]);
+          }
+        }
       }
-      const int base = incl - run;
-      const int need = s_need;
-      // the digit whose cumulative count first reaches `need`
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int before = base + (i ? c[i - 1] : 0);
-        const int after = base + c[i];
-        if (before < need && after >= need) {
-          s_prefix = pre | ((uint32_t)(4 * lane + i) << shift);
-          s_need = need - before;
+      for (int q = 0; q < SEL_QB; ++q) {
+        if (q < nq) {
+          const float sc = acc[q] * rsd;
+          if (scores_out) scores_out[((long)h * nb + A0 + q) * nb + B] = sc;
+          s_keys[q * nb + B] = pref_key(sc);
         }
       }
     }
-    __syncthreads();
   }
-  const uint32_t thr = s_prefix;
-  const int ties_needed = s_need;  // how many keys == thr to take, lowest B first
+  __syncthreads();
 
-  // --- emit in ascending B: thread owns a contiguous range -------------------
-  const int per = (nb + SEL_T - 1) / SEL_T;
-  const int b0 = tid * per, b1 = min(nb, b0 + per);
-  int n_less = 0, n_eq = 0;
-  for (int B = b0; B < b1; ++B) {
-    const uint32_t k = s_key[B];
-    n_less += (k < thr);
-    n_eq += (k == thr);
-  }
-  int tot_less, tot_eq;
-  const int off_less = block_exscan(n_less, s_tmp, tot_less);
-  const int off_eq = block_exscan(n_eq, s_tmp, tot_eq);
-  (void)tot_less;
-  (void)tot_eq;
-  // output position of B = (#less before B) + min(#eq before B, ties_needed)
-  int cl = off_less, ce = off_eq;
-  int32_t* out = idx + ((long)h * nb + A) * topk;
-  for (int B = b0; B < b1; ++B) {
-    const uint32_t k = s_key[B];
-    if (k < thr) {
-      const int pos = cl + min(ce, ties_needed);
-      if (pos < topk) out[pos] = B;
-      ++cl;
-    } else if (k == thr) {
-      if (ce < ties_needed && cl + ce < topk) out[cl + ce] = B;
-      ++ce;
+  // one wave per row: bisection for the threshold key, then ballot prefix
+  // sums emit the selected blocks in ascending order (no barriers)
+  for (int q = wave; q < nq; q += SEL_T / 64) {
+    const uint32_t* s_key = s_keys + q * nb;
+    int ties_needed;
+    uint32_t thr;
+    if (nb <= 1024) thr = wave_kth_key<16>(s_key, nb, topk, &ties_needed);
+    else if (nb <= 2048) thr = wave_kth_key<32>(s_key, nb, topk, &ties_needed);
+    else if (nb <= 4096) thr = wave_kth_key<64>(s_key, nb, topk, &ties_needed);
+    else thr = wave_kth_key_lds(s_key, nb, topk, &ties_needed);
+    int32_t* out = idx + ((long)h * nb + A0 + q) * topk;
+    int taken = 0, ties_seen = 0;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int B0 = 0; B0 < nb; B0 += 64) {
+      const int B = B0 + lane;
+      const uint32_t k = (B < nb) ? s_key[B] : 0xffffffffu;
+      const bool tie = (B < nb) && (k == thr);
+      const uint64_t tmask = __builtin_amdgcn_ballot_w64(tie);
+      const int tie_rank = ties_seen + __builtin_popcountll(tmask & below);
+      const bool sel = (B < nb) && (k < thr || (tie && tie_rank < ties_needed));
+      const uint64_t smask = __builtin_amdgcn_ballot_w64(sel);
+      const int pos = taken + __builtin_popcountll(smask & below);
+      if (sel && pos < topk) out[pos] = B;
+      taken += __builtin_popcountll(smask);
+      ties_seen += __builtin_popcountll(tmask);
     }
   }
 }
@@ -169,9 +115,11 @@ int select_launch(int H, int N, int D, int BK, const float* qbar, const float* k
                   const float* scores_in, int topk, int32_t* idx, float* scores_out,
                   hipStream_t st) {
   const int nb = cdiv(N, BK);
-  const size_t lds = (size_t)nb * 4;
-  if (lds > 128 * 1024)
+  if ((size_t)nb * 4 + 128 * 4 > 128 * 1024)
     return spark_set_error(SPARK_E_SHAPE, "spark_select: %d blocks exceed the LDS row buffer", nb);
+  int qb = (int)std::min<size_t>(SEL_QB, (size_t)(128 * 1024) / ((size_t)nb * 4 + (size_t)D * 4));
+  qb = std::max(qb, 1);
+  const size_t lds = (size_t)qb * nb * 4 + (size_t)qb * D * 4;
   const float rsd = 1.f / sqrtf((float)D);
   static bool attr = false;
   if (!attr) {
@@ -179,12 +127,13 @@ int select_launch(int H, int N, int D, int BK, const float* qbar, const float* k
     hipFuncSetAttribute((const void*)select_kernel<64>, hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
     attr = true;
   }
+  const int grid = H * ((nb + qb - 1) / qb);
   if (D == 128)
-    hipLaunchKernelGGL(select_kernel<128>, dim3(H * nb), dim3(SEL_T), lds, st, qbar, kbar,
-                       scores_in, topk, idx, scores_out, nb, rsd);
+    hipLaunchKernelGGL(select_kernel<128>, dim3(grid), dim3(SEL_T), lds, st, qbar, kbar,
+                       scores_in, topk, idx, scores_out, nb, qb, rsd);
   else
-    hipLaunchKernelGGL(select_kernel<64>, dim3(H * nb), dim3(SEL_T), lds, st, qbar, kbar,
-                       scores_in, topk, idx, scores_out, nb, rsd);
+    hipLaunchKernelGGL(select_kernel<64>, dim3(grid), dim3(SEL_T), lds, st, qbar, kbar,
+                       scores_in, topk, idx, scores_out, nb, qb, rsd);
   return spark_check_launch("select");
 }
 

@@ -30,7 +30,7 @@ namespace spark {
 
 constexpr int SPL_T = 256;
 constexpr int FIN_MAX = 1024;         // tokens per finisher group
-constexpr int FIN_LDS = 140 * 1024;   // bytes of rows in the finisher
+constexpr int FIN_LDS = 136 * 1024;   // bytes of rows in the finisher
 
 // ---- tree navigation --------------------------------------------------------
 // Group containing block cb at `level`; false if that block is already in a
@@ -106,37 +106,71 @@ __global__ void iota_kernel(int32_t* __restrict__ lo, int32_t* __restrict__ hi, 
   }
 }
 
+// Rows of one block (chunk) of the current order, gathered by id: every lane
+// loads its NIT row chunks up front (ids staged in LDS first), so all the
+// row reads of the block are in flight together.
+template <typename T, int D>
+struct ChunkRows {
+  static constexpr int VE = Chunk<T>::VE, CPR = D / VE, RPP = SPL_T / CPR, NIT = 128 / RPP;
+  float v[NIT][VE];
+  __device__ __forceinline__ void load(const T* __restrict__ xt, const int32_t* s_ids, int n_real,
+                                       int rg, int c) {
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int j = it * RPP + rg;
+      if (j < n_real) {
+        Chunk<T>::load(xt + (long)s_ids[j] * D + c, v[it]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) v[it][e] = 0.f;
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ void stage_ids(int32_t* s_ids, const int32_t* __restrict__ idr,
+                                          int n_real) {
+  for (int i = threadIdx.x; i < n_real; i += SPL_T) s_ids[i] = idr[i];
+  __syncthreads();
+}
+
 // Per block (chunk) of the current order: partial centroid sum.
 template <typename T, int D>
 __global__ __launch_bounds__(SPL_T) void cent_partial(const T* __restrict__ xh,
                                                       const int32_t* __restrict__ ids,
                                                       float* __restrict__ cpart, int N, int BK,
                                                       int nb, int level) {
-  constexpr int VE = Chunk<T>::VE, CPR = D / VE, RPP = SPL_T / CPR;
-  __shared__ float s_p[RPP][D];
+  using CR = ChunkRows<T, D>;
+  constexpr int VE = CR::VE, CPR = CR::CPR, RPP = CR::RPP;
+  __shared__ float s_p[SPL_T / 64][D];
+  __shared__ int32_t s_ids[128];
   const int cb = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
   int start, nbg, slot;
   if (!group_of_block(cb, level, nb, start, nbg, slot)) return;
   const int n_real = min(BK, N - cb * BK);
   const int rg = tid / CPR, c = (tid % CPR) * VE;
+  stage_ids(s_ids, ids + (long)t * N + (long)cb * BK, n_real);
+  CR rows;
+  rows.load(xh + (long)t * N * D, s_ids, n_real, rg, c);
   float acc[VE];
 #pragma unroll
   for (int e = 0; e < VE; ++e) acc[e] = 0.f;
-  const int32_t* idr = ids + (long)t * N + (long)cb * BK;
-  const T* xt = xh + (long)t * N * D;
-  for (int j = rg; j < n_real; j += RPP) {
-    float v[VE];
-    Chunk<T>::load(xt + (long)idr[j] * D + c, v);
 #pragma unroll
-    for (int e = 0; e < VE; ++e) acc[e] += v[e];
-  }
+  for (int it = 0; it < CR::NIT; ++it)
 #pragma unroll
-  for (int e = 0; e < VE; ++e) s_p[rg][c + e] = acc[e];
+    for (int e = 0; e < VE; ++e) acc[e] += rows.v[it][e];
+  // lanes holding the same chunk: fold within the wave, then across waves
+#pragma unroll
+  for (int e = 0; e < VE; ++e) acc[e] = group_sum<64, CPR>(acc[e]);
+  if ((tid & 63) < CPR)
+#pragma unroll
+    for (int e = 0; e < VE; ++e) s_p[tid >> 6][c + e] = acc[e];
   __syncthreads();
   for (int cc = tid; cc < D; cc += SPL_T) {
-    float s = 0.f;
-    for (int r = 0; r < RPP; ++r) s += s_p[r][cc];
-    cpart[((long)t * nb + cb) * D + cc] = s;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < SPL_T / 64; ++w) sum += s_p[w][cc];
+    cpart[((long)t * nb + cb) * D + cc] = sum;
   }
 }
 
@@ -163,8 +197,10 @@ __global__ __launch_bounds__(SPL_T) void argmin_partial(const T* __restrict__ xh
                                                         uint64_t* __restrict__ mpart, int N,
                                                         int BK, int nb, int level, int S,
                                                         int mode) {
-  constexpr int VE = Chunk<T>::VE, CPR = D / VE, RPP = SPL_T / CPR;
+  using CR = ChunkRows<T, D>;
+  constexpr int VE = CR::VE, CPR = CR::CPR, RPP = CR::RPP;
   __shared__ uint64_t s_min[SPL_T / 64];
+  __shared__ int32_t s_ids[128];
   const int cb = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
   int start, nbg, slot;
   if (!group_of_block(cb, level, nb, start, nbg, slot)) return;
@@ -178,32 +214,23 @@ __global__ __launch_bounds__(SPL_T) void argmin_partial(const T* __restrict__ xh
   } else {
     Chunk<T>::load(xt + (long)poleA[(long)t * S + slot] * D + c, vec);
   }
-  const int32_t* idr = ids + (long)t * N + (long)cb * BK;
+  stage_ids(s_ids, ids + (long)t * N + (long)cb * BK, n_real);
+  CR rows;
+  rows.load(xt, s_ids, n_real, rg, c);
   uint64_t best = ~0ull;
-  for (int j0 = 0; j0 < n_real; j0 += RPP) {
-    const int j = j0 + rg;
+#pragma unroll
+  for (int it = 0; it < CR::NIT; ++it) {
+    const int j = it * RPP + rg;
     float acc = 0.f;
-    int id = 0;
-    if (j < n_real) {
-      id = idr[j];
-      float v[VE];
-      Chunk<T>::load(xt + (long)id * D + c, v);
 #pragma unroll
-      for (int e = 0; e < VE; ++e) acc = fmaf(v[e], vec[e], acc);
-    }
-#pragma unroll
-    for (int o = CPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    for (int e = 0; e < VE; ++e) acc = fmaf(rows.v[it][e], vec[e], acc);
+    acc = group_sum<CPR>(acc);
     if (j < n_real) {
-      const uint64_t k = argmin_key(acc, id);
+      const uint64_t k = argmin_key(acc, s_ids[j]);
       best = k < best ? k : best;
     }
   }
-  // wave min, then across waves
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint64_t other = __shfl_xor(best, o, 64);
-    best = other < best ? other : best;
-  }
+  best = group_min_u64<64>(best);
   if ((tid & 63) == 0) s_min[tid >> 6] = best;
   __syncthreads();
   if (tid == 0) {
@@ -230,11 +257,7 @@ __global__ __launch_bounds__(64) void argmin_reduce(const uint64_t* __restrict__
     const uint64_t k = mpart[(long)t * nb + b];
     best = k < best ? k : best;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint64_t other = __shfl_xor(best, o, 64);
-    best = other < best ? other : best;
-  }
+  best = group_min_u64<64>(best);
   const int id = (int)(uint32_t)(best & 0xffffffffu);
   if (mode == 0) {
     if (lane == 0) poleA[(long)t * S + slot] = id;
@@ -255,28 +278,28 @@ __global__ __launch_bounds__(SPL_T) void score_kernel(const T* __restrict__ xh,
                                                       const float* __restrict__ diff,
                                                       float* __restrict__ s, int N, int BK,
                                                       int nb, int level, int S) {
-  constexpr int VE = Chunk<T>::VE, CPR = D / VE, RPP = SPL_T / CPR;
+  using CR = ChunkRows<T, D>;
+  constexpr int VE = CR::VE, CPR = CR::CPR, RPP = CR::RPP;
+  __shared__ int32_t s_ids[128];
   const int cb = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
   int start, nbg, slot;
   if (!group_of_block(cb, level, nb, start, nbg, slot)) return;
   const int n_real = min(BK, N - cb * BK);
   const int rg = tid / CPR, c = (tid % CPR) * VE;
-  const T* xt = xh + (long)t * N * D;
   float vec[VE];
 #pragma unroll
   for (int e = 0; e < VE; ++e) vec[e] = diff[((long)t * S + slot) * D + c + e];
   const long pos0 = (long)t * N + (long)cb * BK;
-  for (int j0 = 0; j0 < n_real; j0 += RPP) {
-    const int j = j0 + rg;
+  stage_ids(s_ids, ids + pos0, n_real);
+  CR rows;
+  rows.load(xh + (long)t * N * D, s_ids, n_real, rg, c);
+#pragma unroll
+  for (int it = 0; it < CR::NIT; ++it) {
+    const int j = it * RPP + rg;
     float acc = 0.f;
-    if (j < n_real) {
-      float v[VE];
-      Chunk<T>::load(xt + (long)ids[pos0 + j] * D + c, v);
 #pragma unroll
-      for (int e = 0; e < VE; ++e) acc = fmaf(v[e], vec[e], acc);
-    }
-#pragma unroll
-    for (int o = CPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    for (int e = 0; e < VE; ++e) acc = fmaf(rows.v[it][e], vec[e], acc);
+    acc = group_sum<CPR>(acc);
     if (j < n_real && (tid % CPR) == 0) s[pos0 + j] = acc;
   }
 }
@@ -296,6 +319,28 @@ __device__ __forceinline__ int wg_exscan(int v, int* s_tmp, int& total) {
   int base = 0, tot = 0;
 #pragma unroll
   for (int i = 0; i < SPL_T / 64; ++i) {
+    if (i < w) base += s_tmp[i];
+    tot += s_tmp[i];
+  }
+  __syncthreads();
+  total = tot;
+  return base + incl - v;
+}
+
+// Exclusive scan of one int per thread over FIN_T (512) threads.
+__device__ __forceinline__ int fin_exscan(int v, int* s_tmp, int& total) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) s_tmp[w] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
     if (i < w) base += s_tmp[i];
     tot += s_tmp[i];
   }
@@ -423,14 +468,20 @@ __global__ __launch_bounds__(SPL_T) void select_partition(const float* __restric
 }
 
 // ---- LDS finisher -----------------------------------------------------------
-// One workgroup per group of <= FIN_MAX tokens at level L: rows in LDS, all
-// remaining splits done in place, final perm written.
+// One workgroup (FIN_T threads) per group of <= FIN_MAX tokens at level L:
+// the rows are loaded into LDS once, every remaining split of the subtree runs
+// in place, and the final permutation is written.  Row dots use CPR lanes per
+// row (one 16-byte chunk each) reduced with shuffles; the centroid sums
+// independent rows per lane; all reductions run in a fixed order.
+constexpr int FIN_T = 512;
+
 template <typename T, int D>
-__global__ __launch_bounds__(SPL_T) void finisher(const T* __restrict__ xh,
+__global__ __launch_bounds__(FIN_T) void finisher(const T* __restrict__ xh,
                                                   const int32_t* __restrict__ ids_in,
                                                   int32_t* __restrict__ perm_lo,
                                                   int32_t* __restrict__ perm_hi, int split_at,
                                                   int N, int BK, int nb, int level) {
+  constexpr int VE = Chunk<T>::VE, CPR = D / VE, RPP = FIN_T / CPR, NW = FIN_T / 64;
   constexpr int RS = D + 16 / (int)sizeof(T);  // padded row stride (elements)
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   T* sX = reinterpret_cast<T*>(smem);                          // [n][RS]
@@ -438,16 +489,17 @@ __global__ __launch_bounds__(SPL_T) void finisher(const T* __restrict__ xh,
   __shared__ int16_t s_lid[FIN_MAX];    // current local order (row indices)
   __shared__ int16_t s_tmp_lid[FIN_MAX];
   __shared__ float s_val[FIN_MAX];
+  __shared__ uint32_t s_keys[FIN_MAX];
   __shared__ float s_vec[D];
-  __shared__ float s_part[SPL_T / D > 0 ? SPL_T / D : 1][D];
-  __shared__ uint64_t s_min[SPL_T / 64];
-  __shared__ int s_hist[256];
-  __shared__ int s_tmp[SPL_T / 64];
+  __shared__ float s_part[NW][D];
+  __shared__ uint64_t s_min[NW];
+  __shared__ int s_tmp[NW];
   __shared__ uint32_t s_prefix;
   __shared__ int s_need;
-  __shared__ int s_pole[2];
+  __shared__ int s_pole;
 
   const int slot = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   int start, nbg;
   if (!group_of_slot(slot, level, nb, start, nbg)) return;
   const long g0 = (long)start * BK;
@@ -455,68 +507,67 @@ __global__ __launch_bounds__(SPL_T) void finisher(const T* __restrict__ xh,
   const long base = (long)t * N + g0;
   const T* xt = xh + (long)t * N * D;
 
-  // load rows in the current order
-  constexpr int VE = 16 / sizeof(T), CPR = D / VE;
-  for (int i = tid; i < n; i += SPL_T) {
+  for (int i = tid; i < n; i += FIN_T) {
     s_oid[i] = ids_in ? ids_in[base + i] : (int32_t)(g0 + i);
     s_lid[i] = (int16_t)i;
   }
   __syncthreads();
-  for (int ch = tid; ch < n * CPR; ch += SPL_T) {
+  for (int ch = tid; ch < n * CPR; ch += FIN_T) {
     const int r = ch / CPR, c = (ch % CPR) * VE;
     *reinterpret_cast<uint4*>(sX + r * RS + c) =
         *reinterpret_cast<const uint4*>(xt + (long)s_oid[r] * D + c);
   }
   __syncthreads();
 
-  // dot of local row r with s_vec
-  auto rowdot = [&](int r) -> float {
-    float acc = 0.f;
-    const T* row = sX + r * RS;
-#pragma unroll 8
-    for (int c = 0; c < D; c += 8) {
-      float v[8];
-      load8(row + c, v);
+  const int rslot = tid / CPR, cc = (tid % CPR) * VE;
+  // dot of every row of [a, a+len) with s_vec; calls f(i, r, dot) on the
+  // lane that owns the row's first chunk
+  auto rows_dot = [&](int a, int len, auto&& f) {
+    float vec[VE];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc = fmaf(v[e], s_vec[c + e], acc);
+    for (int e = 0; e < VE; ++e) vec[e] = s_vec[cc + e];
+    for (int i0 = 0; i0 < len; i0 += RPP) {
+      const int i = i0 + rslot;
+      float acc = 0.f;
+      int r = 0;
+      if (i < len) {
+        r = s_lid[a + i];
+        float v[VE];
+        Chunk<T>::load(sX + r * RS + cc, v);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc = fmaf(v[e], vec[e], acc);
+      }
+      acc = group_sum<CPR>(acc);
+      if (i < len && (tid % CPR) == 0) f(i, r, acc);
     }
-    return acc;
   };
-  // argmin over local positions [a, a+len) of (rowdot, oid)
+  // argmin over [a, a+len) of (row . s_vec, original id) -> local row
   auto argmin_range = [&](int a, int len) -> int {
     uint64_t best = ~0ull;
-    for (int i = tid; i < len; i += SPL_T) {
-      const int r = s_lid[a + i];
-      const uint64_t k = argmin_key(rowdot(r), s_oid[r]);
+    rows_dot(a, len, [&](int, int r, float dv) {
+      const uint64_t k = argmin_key(dv, s_oid[r]);
       best = k < best ? k : best;
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const uint64_t other = __shfl_xor(best, o, 64);
-      best = other < best ? other : best;
-    }
-    if ((tid & 63) == 0) s_min[tid >> 6] = best;
+    });
+    best = group_min_u64<64>(best);
+    if (lane == 0) s_min[wave] = best;
     __syncthreads();
     uint64_t b = s_min[0];
 #pragma unroll
-    for (int w = 1; w < SPL_T / 64; ++w) b = s_min[w] < b ? s_min[w] : b;
-    __syncthreads();
-    // map the winning original id back to its local row
+    for (int w = 1; w < NW; ++w) b = s_min[w] < b ? s_min[w] : b;
     const int id = (int)(uint32_t)(b & 0xffffffffu);
-    for (int i = tid; i < len; i += SPL_T) {
+    for (int i = tid; i < len; i += FIN_T) {
       const int r = s_lid[a + i];
-      if (s_oid[r] == id) s_pole[0] = r;
+      if (s_oid[r] == id) s_pole = r;
     }
     __syncthreads();
-    return s_pole[0];
+    const int rp = s_pole;
+    __syncthreads();
+    return rp;
   };
 
-  // walk the subtree level by level; subgroups are contiguous local ranges
   for (int sub = 0;; ++sub) {
-    // subgroups at depth `sub` below this group: enumerate by path
     bool any = false;
     for (int path = 0; path < (1 << sub); ++path) {
-      // locate subgroup (block range relative to the group)
       int sstart = 0, snb = nbg;
       bool exists = true;
       for (int l = sub - 1; l >= 0; --l) {
@@ -529,63 +580,67 @@ __global__ __launch_bounds__(SPL_T) void finisher(const T* __restrict__ xh,
       const int a = sstart * BK;
       const int len = min(n, (sstart + snb) * BK) - a;
       const int cL = ((snb + 1) >> 1) * BK;
-      // centroid (fixed order): column c summed over the range by one thread group
+      // centroid: per-lane partial sums over independent rows, then lanes with
+      // the same chunk (shuffles), then waves (LDS), all in a fixed order
       {
-        constexpr int G = SPL_T / D > 0 ? SPL_T / D : 1;  // row groups
-        const int c = tid % D, g = tid / D;
-        if (g < G) {
-          float acc = 0.f;
-          for (int i = g; i < len; i += G) acc += Elem<T>::load(sX + s_lid[a + i] * RS + c);
-          s_part[g][c] = acc;
+        float acc[VE];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[e] = 0.f;
+        for (int i = rslot; i < len; i += RPP) {
+          float v[VE];
+          Chunk<T>::load(sX + s_lid[a + i] * RS + cc, v);
+#pragma unroll
+          for (int e = 0; e < VE; ++e) acc[e] += v[e];
         }
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[e] = group_sum<64, CPR>(acc[e]);
+        if (lane < CPR)
+#pragma unroll
+          for (int e = 0; e < VE; ++e) s_part[wave][cc + e] = acc[e];
         __syncthreads();
-        if (tid < D) {
-          float acc = 0.f;
-          for (int gg = 0; gg < G; ++gg) acc += s_part[gg][tid];
-          s_vec[tid] = acc;
+        for (int c = tid; c < D; c += FIN_T) {
+          float sum = 0.f;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) sum += s_part[w][c];
+          s_vec[c] = sum;
         }
         __syncthreads();
       }
       const int rA = argmin_range(a, len);
-      for (int c = tid; c < D; c += SPL_T) s_vec[c] = Elem<T>::load(sX + rA * RS + c);
+      for (int c = tid; c < D; c += FIN_T) s_vec[c] = Elem<T>::load(sX + rA * RS + c);
       __syncthreads();
       const int rB = argmin_range(a, len);
-      for (int c = tid; c < D; c += SPL_T)
+      for (int c = tid; c < D; c += FIN_T)
         s_vec[c] = Elem<T>::load(sX + rA * RS + c) - Elem<T>::load(sX + rB * RS + c);
       __syncthreads();
-      for (int i = tid; i < len; i += SPL_T) s_val[i] = rowdot(s_lid[a + i]);
-      // radix select of the cL-th key
-      if (tid == 0) { s_prefix = 0; s_need = cL; }
-      for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = tid; i < 256; i += SPL_T) s_hist[i] = 0;
-        __syncthreads();
-        const uint32_t pre = s_prefix;
-        const uint32_t hmask = (shift == 24) ? 0u : (0xffffffffu << (shift + 8));
-        for (int i = tid; i < len; i += SPL_T) {
-          const uint32_t k = pref_key_desc(s_val[i]);
-          if ((k & hmask) == pre) atomicAdd(&s_hist[(k >> shift) & 255], 1);
-        }
-        __syncthreads();
-        if (tid < 64) radix_pick(s_hist, &s_prefix, &s_need, shift);
-        __syncthreads();
+      rows_dot(a, len, [&](int i, int, float dv) { s_val[i] = dv; });
+      __syncthreads();
+      // the cL-th key: wave 0 bisects over the keys in LDS
+      if (wave == 0) {
+        for (int i = lane; i < len; i += 64) s_keys[i] = pref_key_desc(s_val[i]);
+        int tn;
+        const uint32_t th = wave_kth_key<FIN_MAX / 64>(s_keys, len, cL, &tn);
+        if (lane == 0) { s_prefix = th; s_need = tn; }
       }
+      __syncthreads();
       const uint32_t thr = s_prefix;
       const int ties_needed = s_need;
-      // stable partition: E = ceil(len / SPL_T) consecutive positions per thread
-      const int E = (len + SPL_T - 1) / SPL_T;  // <= FIN_MAX / SPL_T = 4
+      // stable partition: E consecutive positions per thread (E <= 2)
+      const int E = (len + FIN_T - 1) / FIN_T;
       int ne = 0;
       for (int e = 0; e < E; ++e) {
         const int p = tid * E + e;
         if (p < len && pref_key_desc(s_val[p]) == thr) ++ne;
       }
       int tot;
-      int ce = wg_exscan(ne, s_tmp, tot);
+      int ce = fin_exscan(ne, s_tmp, tot);
       int nl = 0;
-      bool left[FIN_MAX / SPL_T];
-      for (int e = 0; e < E; ++e) {
+      bool left[FIN_MAX / FIN_T];
+#pragma unroll
+      for (int e = 0; e < FIN_MAX / FIN_T; ++e) {
         const int p = tid * E + e;
         bool l = false;
-        if (p < len) {
+        if (e < E && p < len) {
           const uint32_t k = pref_key_desc(s_val[p]);
           if (k < thr) l = true;
           else if (k == thr) { l = ce < ties_needed; ++ce; }
@@ -593,22 +648,23 @@ __global__ __launch_bounds__(SPL_T) void finisher(const T* __restrict__ xh,
         left[e] = l;
         nl += l;
       }
-      int cl = wg_exscan(nl, s_tmp, tot);
-      for (int e = 0; e < E; ++e) {
+      int cl = fin_exscan(nl, s_tmp, tot);
+#pragma unroll
+      for (int e = 0; e < FIN_MAX / FIN_T; ++e) {
         const int p = tid * E + e;
-        if (p >= len) continue;
+        if (e >= E || p >= len) continue;
         const int dst = left[e] ? cl : cL + (p - cl);
         if (dst < len) s_tmp_lid[a + dst] = s_lid[a + p];
         cl += left[e];
       }
       __syncthreads();
-      for (int i = tid; i < len; i += SPL_T) s_lid[a + i] = s_tmp_lid[a + i];
+      for (int i = tid; i < len; i += FIN_T) s_lid[a + i] = s_tmp_lid[a + i];
       __syncthreads();
     }
     if (!any) break;
   }
   int32_t* perm = (t < split_at) ? perm_lo + (long)t * N : perm_hi + (long)(t - split_at) * N;
-  for (int i = tid; i < n; i += SPL_T) perm[g0 + i] = s_oid[s_lid[i]];
+  for (int i = tid; i < n; i += FIN_T) perm[g0 + i] = s_oid[s_lid[i]];
 }
 
 // ---- host side ---------------------------------------------------------------
@@ -699,7 +755,7 @@ static int split_t(int count, int N, int BK, const void* xhv, int32_t* perm_lo,
     hipFuncSetAttribute((const void*)finisher<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize, FIN_LDS);
     attr = true;
   }
-  hipLaunchKernelGGL((finisher<T, D>), dim3(SF, count), dim3(SPL_T), lds, st, xh, cur, perm_lo, perm_hi, split_at, N, BK, p.nb, p.Lf);
+  hipLaunchKernelGGL((finisher<T, D>), dim3(SF, count), dim3(FIN_T), lds, st, xh, cur, perm_lo, perm_hi, split_at, N, BK, p.nb, p.Lf);
   return spark_check_launch("split finisher");
 }
 

@@ -360,7 +360,7 @@ int msqrt_launch(int count, int D, const float* M, float* W, float* Tscr, hipStr
 // whiten: xhat = normalize(W x) row by row.  bf16: x^T-side MFMA with W (bf16)
 // as the A operand: O^T[c][i] = sum_k W[c][k] x_i[k]; lane l32 owns row i.
 // ---------------------------------------------------------------------------
-constexpr int WH_ROWS = 128;  // rows per workgroup (4 waves x 32)
+constexpr int WH_ROWS = 1024;  // rows per workgroup: 8 rounds of 4 waves x 32
 
 template <int D>
 __global__ __launch_bounds__(256) void whiten_mfma(const uint16_t* __restrict__ x,
@@ -374,41 +374,45 @@ __global__ __launch_bounds__(256) void whiten_mfma(const uint16_t* __restrict__ 
   const float* w = W + (long)t * D * D;
   for (int e = tid; e < D * D; e += 256) sW[(e / D) * RS + e % D] = f2bf(w[e]);
   __syncthreads();
-  const long row = (long)blockIdx.x * WH_ROWS + wave * 32 + l32;
-  const bool ok = row < N;
-  const uint16_t* xr = x + ((long)t * N + (ok ? row : 0)) * D;
-  bf16x8 xb[D / 16];
+  for (int r0 = 0; r0 < WH_ROWS; r0 += 128) {
+    const long row = (long)blockIdx.x * WH_ROWS + r0 + wave * 32 + l32;
+    if ((long)blockIdx.x * WH_ROWS + r0 >= N) break;  // uniform across the workgroup
+    const bool ok = row < N;
+    const uint16_t* xr = x + ((long)t * N + (ok ? row : 0)) * D;
+    bf16x8 xb[D / 16];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) xb[s] = *reinterpret_cast<const bf16x8*>(xr + 16 * s + 8 * hf);
-  f32x16 acc[D / 32];
+    for (int s2 = 0; s2 < D / 16; ++s2) xb[s2] = *reinterpret_cast<const bf16x8*>(xr + 16 * s2 + 8 * hf);
+    f32x16 acc[D / 32];
 #pragma unroll
-  for (int ct = 0; ct < D / 32; ++ct) {
+    for (int ct = 0; ct < D / 32; ++ct) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[ct][v] = 0.f;
+      for (int v = 0; v < 16; ++v) acc[ct][v] = 0.f;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sW + (32 * ct + l32) * RS + 16 * s + 8 * hf);
-      acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xb[s], acc[ct], 0, 0, 0);
+      for (int s2 = 0; s2 < D / 16; ++s2) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sW + (32 * ct + l32) * RS + 16 * s2 + 8 * hf);
+        acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xb[s2], acc[ct], 0, 0, 0);
+      }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int ct = 0; ct < D / 32; ++ct)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) ss = fmaf(acc[ct][v], acc[ct][v], ss);
+    ss = group_sum<64, 32>(ss);
+    const float inv = (ss > 0.f) ? 1.f / sqrtf(ss) : 0.f;
+    if (ok) {
+      uint16_t* dst = xh + ((long)t * N + row) * D;
+#pragma unroll
+      for (int ct = 0; ct < D / 32; ++ct)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          uint2 p;
+          p.x = pack_bf2(acc[ct][4 * a] * inv, acc[ct][4 * a + 1] * inv);
+          p.y = pack_bf2(acc[ct][4 * a + 2] * inv, acc[ct][4 * a + 3] * inv);
+          *reinterpret_cast<uint2*>(dst + 32 * ct + 8 * a + 4 * hf) = p;
+        }
     }
   }
-  float ss = 0.f;
-#pragma unroll
-  for (int ct = 0; ct < D / 32; ++ct)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) ss = fmaf(acc[ct][v], acc[ct][v], ss);
-  ss += __shfl_xor(ss, 32, 64);
-  const float inv = (ss > 0.f) ? 1.f / sqrtf(ss) : 0.f;
-  if (!ok) return;
-  uint16_t* dst = xh + ((long)t * N + row) * D;
-#pragma unroll
-  for (int ct = 0; ct < D / 32; ++ct)
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      uint2 p;
-      p.x = pack_bf2(acc[ct][4 * a] * inv, acc[ct][4 * a + 1] * inv);
-      p.y = pack_bf2(acc[ct][4 * a + 2] * inv, acc[ct][4 * a + 3] * inv);
-      *reinterpret_cast<uint2*>(dst + 32 * ct + 8 * a + 4 * hf) = p;
-    }
 }
 
 template <int D>
