@@ -301,6 +301,22 @@ __device__ __forceinline__ bool d128_map(int bid, int nb, int& h, int& A) {
 // softmax(t+1).
 // ---------------------------------------------------------------------------
 constexpr int D128_NT = 256;
+constexpr int D128_PF = 2;   // operand prefetch distance, in 16-deep k steps
+
+// Issue order of one 4-MFMA-per-step block (mask 0x100: LDS reads, 0x008:
+// MFMAs): the operand reads of the first D128_PF steps, then for every step
+// its 4 MFMAs, each followed by one read D128_PF steps ahead.
+template <int STEPS>
+__device__ __forceinline__ void d128_pipeline() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 4 * D128_PF, 0);
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (s + D128_PF < STEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+}
 constexpr int D128_LDS_TILES = 2 * 128 * 256;   // K + V^T, 64 KB
 
 __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
@@ -332,10 +348,13 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
   }
 
   // per-lane byte offsets (loop invariant) of this wave's 8 direct loads per
-  // tensor: instruction i fills LDS rows 4*(8*wave+i) .. +3
-  uint32_t koff[8], voff[8];
+  // tensor: instruction i fills LDS rows 4*(8*wave+i) .. +3.  Loads i and i+4
+  // fill rows 16 apart, which sit 16 rows (4096 bytes) apart in the source
+  // tile for K and V^T alike, so only i = 0..3 need lane offsets; the 4096
+  // goes into the scalar offset.
+  uint32_t koff[4], voff[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {
     const int srow = 4 * (8 * wave + i) + (lane >> 4);
     const int lc = (lane & 15) ^ (srow & 15);
     const int grow = (srow & ~31) + ((((srow & 31) >> 3) >> 1) << 4) + (((srow >> 2) & 1) << 3) +
@@ -362,8 +381,8 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (void __attribute__((address_space(3)))*)(dst + (8 * wave + i) * 1024), 16, off[i], 0,
-          0, 0);
+          rs, (void __attribute__((address_space(3)))*)(dst + (8 * wave + i) * 1024), 16, off[i & 3],
+          (i >> 2) * 4096, 0, 0);
   };
 
   const long qrow = (long)h * Np + (long)A * BK + wave * 32 + l32;
@@ -405,22 +424,22 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
     }
     __builtin_amdgcn_s_setprio(2);  // favour the wave that feeds the matrix core
     {
-      // operands of step s+1 are read while the 4 MFMAs of step s run
-      bf16x8 kop[2][4];
+      // all 32 K operand reads and MFMAs are written out; the group barriers
+      // below fix the issue order: the reads of steps 0..D128_PF-1 first,
+      // then each MFMA of step s followed by one read of step s+D128_PF, so
+      // every read has D128_PF steps of MFMAs to land in
+      bf16x8 kop[D / 16][4];
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt)
-        kop[0][jt] = *reinterpret_cast<const bf16x8*>(sK + ro[0] + jt * 8192);
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        if (s + 1 < D / 16) {
-#pragma unroll
-          for (int jt = 0; jt < 4; ++jt)
-            kop[(s + 1) & 1][jt] = *reinterpret_cast<const bf16x8*>(sK + ro[s + 1] + jt * 8192);
-        }
+      for (int s = 0; s < D / 16; ++s)
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt)
-          sacc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[s & 1][jt], qop[s], sacc[jt], 0, 0, 0);
-      }
+          kop[s][jt] = *reinterpret_cast<const bf16x8*>(sK + ro[s] + jt * 8192);
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt)
+          sacc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[s][jt], qop[s], sacc[jt], 0, 0, 0);
+      d128_pipeline<D / 16>();
     }
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();  // every wave is done reading sK
@@ -506,21 +525,18 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
     __syncthreads();
     __builtin_amdgcn_s_setprio(2);
     {
-      bf16x8 vop[2][4];
+      bf16x8 vop[BK / 16][4];
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        vop[0][dt] = *reinterpret_cast<const bf16x8*>(sV + ro[0] + dt * 8192);
+      for (int ks = 0; ks < BK / 16; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        if (ks + 1 < BK / 16) {
+        for (int dt = 0; dt < 4; ++dt)
+          vop[ks][dt] = *reinterpret_cast<const bf16x8*>(sV + ro[ks] + dt * 8192);
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt)
-            vop[(ks + 1) & 1][dt] = *reinterpret_cast<const bf16x8*>(sV + ro[ks + 1] + dt * 8192);
-        }
+      for (int ks = 0; ks < BK / 16; ++ks)
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[ks & 1][dt], pop[ks], oacc[dt], 0, 0, 0);
-      }
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[ks][dt], pop[ks], oacc[dt], 0, 0, 0);
+      d128_pipeline<BK / 16>();
     }
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();  // every wave is done reading sV
