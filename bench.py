@@ -117,27 +117,29 @@ def cpu_baseline(w, topk, sample_blocks):
                        f"and x{w.H} heads; numpy fp64, BLAS threads = {cores}")}
 
 
-def load_traffic(kernel_src):
-    """HBM traffic per attention launch from the committed rocprofv3 --pmc
-    summary, if it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", "attn_full768_traffic.txt")
+def load_traffic(name, sources, key):
+    """Measured HBM bytes from a committed rocprofv3 --pmc summary under
+    profiles/, if it was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path))
     except Exception:
         return None
-    h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
-    if rec.get("kernel_sha") != h:
+    h = hashlib.sha256()
+    for src in sources:
+        h.update(open(src, "rb").read())
+    if rec.get("kernel_sha") != h.hexdigest()[:16]:
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get(key)
 
 
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this layer runs on one GPU; multi-GPU runs are not part of "
-                                   "this build (heads would shard with zero communication)",
+                                   "this implementation (heads would shard with zero communication)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
@@ -244,7 +246,12 @@ def main():
         lev += 1
     rb_bytes = reblock_bytes(H, N, d, b, es, lev, nb)
     rb_ms = st_mean[0] + st_mean[2]
-    traffic = load_traffic(os.path.join(ROOT, "block_sparse_attention_mahalanobis_amd", "csrc", "k_attn.hip"))
+    csrc = os.path.join(ROOT, "block_sparse_attention_mahalanobis_amd", "csrc")
+    traffic = load_traffic("attn_full768_traffic.txt", [os.path.join(csrc, "k_attn.hip")],
+                           "bytes_per_launch") if args.config == "full768" else None
+    rb_traffic = load_traffic("reblock_full768_traffic.txt",
+                              [os.path.join(csrc, f) for f in ("k_whiten.hip", "k_split.hip", "k_gather_summ.hip")],
+                              "bytes_per_layer") if args.config == "full768" else None
 
     base = None
     if not args.no_cpu_baseline:
@@ -274,7 +281,8 @@ def main():
                         "exact_tflop": round(exact / 1e12, 2), "compressed_tflop": round(comp / 1e12, 2)},
         "reblock_summaries_hbm": {"algorithmic_gb": round(rb_bytes / 1e9, 1),
                                   "achieved_gbs": round(rb_bytes / (rb_ms * 1e-3) / 1e9, 1),
-                                  "frac_of_8tbs": round(rb_bytes / (rb_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)},
+                                  "frac_of_8tbs": round(rb_bytes / (rb_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
+                                  "traffic_gb": None if rb_traffic is None else round(rb_traffic / 1e9, 1)},
         "roofline": {"kernel": "attn_mfma_d128 (spark_attn)", "bound": "mfma",
                      "achieved": round(alg_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(alg_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic},

@@ -507,15 +507,52 @@ __global__ __launch_bounds__(FIN_T) void finisher(const T* __restrict__ xh,
   const long base = (long)t * N + g0;
   const T* xt = xh + (long)t * N * D;
 
-  for (int i = tid; i < n; i += FIN_T) {
-    s_oid[i] = ids_in ? ids_in[base + i] : (int32_t)(g0 + i);
-    s_lid[i] = (int16_t)i;
+  // ids, then rows: every load of a batch is issued before the first store,
+  // so a batch costs one memory latency, not one per load
+  {
+    constexpr int IB = FIN_MAX / FIN_T;
+    int32_t idv[IB];
+#pragma unroll
+    for (int j = 0; j < IB; ++j) {
+      const int i = min(tid + j * FIN_T, n - 1);
+      idv[j] = ids_in ? ids_in[base + i] : (int32_t)(g0 + i);
+    }
+#pragma unroll
+    for (int j = 0; j < IB; ++j) {
+      const int i = tid + j * FIN_T;
+      if (i < n) {
+        s_oid[i] = idv[j];
+        s_lid[i] = (int16_t)i;
+      }
+    }
   }
   __syncthreads();
-  for (int ch = tid; ch < n * CPR; ch += FIN_T) {
-    const int r = ch / CPR, c = (ch % CPR) * VE;
-    *reinterpret_cast<uint4*>(sX + r * RS + c) =
-        *reinterpret_cast<const uint4*>(xt + (long)s_oid[r] * D + c);
+  // rows -> LDS with direct 4-byte-per-lane loads: one instruction moves
+  // 256 bytes of one row to LDS (lane i -> row start + 4 i), so the padded
+  // row stride is kept and a wave's loads all issue back to back; the row's
+  // global offset is a scalar (readlane of its id).
+  {
+    constexpr int RB = D * (int)sizeof(T);  // row bytes
+    constexpr int IPR = (RB + 255) / 256;   // instructions per row
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)xt, (short)0, 0x7fffffff, 0x00020000);
+    for (int r0 = __builtin_amdgcn_readfirstlane(wave) * 64; r0 < n; r0 += NW * 64) {
+      const int myid = (r0 + lane < n) ? s_oid[r0 + lane] : 0;
+      const int cnt = min(64, n - r0);
+      for (int j = 0; j < cnt; ++j) {
+        const int id = __builtin_amdgcn_readlane(myid, j);
+#pragma unroll
+        for (int qq = 0; qq < IPR; ++qq) {
+          if (qq * 256 + lane * 4 < RB)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs,
+                (void __attribute__((address_space(3)))*)(reinterpret_cast<unsigned char*>(sX + (r0 + j) * RS) +
+                                                          qq * 256),
+                4, (uint32_t)(lane * 4), id * RB + qq * 256, 0, 0);
+        }
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   __syncthreads();
 
