@@ -28,7 +28,7 @@ EXPORTED = [
     "spark_version", "spark_status_string", "spark_last_error", "spark_block_count",
     "spark_topk_from_ratio", "spark_workspace_bytes", "spark_reblock", "spark_select",
     "spark_summarize", "spark_attn", "spark_layer", "spark_moments", "spark_msqrt",
-    "spark_whiten", "spark_split", "spark_gather",
+    "spark_whiten", "spark_split", "spark_gather", "spark_diagnostics",
 ]
 
 
@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
         "spark_whiten": ([_A, _I, _P, _P, _P, _P], ctypes.c_int),
         "spark_split": ([_A, _I, _P, _P, _P, _Z, _P], ctypes.c_int),
         "spark_gather": ([_A, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+        "spark_diagnostics": ([_A, _P, _P, _P, _I, _P, _P, _P, _P, _P], ctypes.c_int),
     }
     for name, (argt, rest) in sig.items():
         f = getattr(L, name)
@@ -228,6 +229,20 @@ def spark_attn(q_p, k_p, v_pt, idx, ksum, vsum, bias, N: int, block: int, perm_q
                             _ptr(vsum), _ptr(bias), _ptr(perm_q), _ptr(out), _ptr(ws), nws, _stream()),
            "spark_attn")
     return out
+
+
+def spark_diagnostics(q_p, k_p, idx, ksum, bias, N: int, block: int):
+    """Per-query attention-mass recall and log-mass error, [H, N] fp32 each,
+    in the permuted order of q_p."""
+    H, Np, d = q_p.shape
+    topk = idx.shape[2]
+    a = make_args(H, N, d, block, q_p.dtype)
+    recall = torch.empty((H, N), dtype=torch.float32, device=q_p.device)
+    logmass = torch.empty((H, N), dtype=torch.float32, device=q_p.device)
+    _check(lib().spark_diagnostics(ctypes.byref(a), _ptr(q_p), _ptr(k_p), _ptr(idx), topk, _ptr(ksum),
+                                   _ptr(bias), _ptr(recall), _ptr(logmass), _stream()),
+           "spark_diagnostics")
+    return recall, logmass
 
 
 def spark_layer(q, k, v, block: int, topk: int, layout: str = "reblock", summary: str = "reweight",

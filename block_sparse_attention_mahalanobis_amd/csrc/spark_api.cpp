@@ -39,6 +39,9 @@ size_t split_ws_bytes(int count, int N, int D, int BK, int dtype);
 int split_launch(int count, int N, int D, int BK, int dtype, const void* xh, int32_t* perm_lo,
                  int32_t* perm_hi, int split_at, void* ws, hipStream_t st);
 int iota_launch(int count, int N, int32_t* lo, int32_t* hi, int split_at, hipStream_t st);
+int diag_launch(int H, int N, int D, int BK, int dtype, const void* qp, const void* kp,
+                const int32_t* idx, int topk, const float* ksum, const float* bias, float* recall,
+                float* logmass, hipStream_t st);
 }  // namespace spark
 
 using namespace spark;
@@ -417,3 +420,22 @@ int spark_layer(const spark_args* a, const void* q, const void* k, const void* v
 }
 
 }  // extern "C"
+
+int spark_diagnostics(const spark_args* a, const void* q_p, const void* k_p, const int32_t* idx,
+                      int32_t topk, const float* ksum, const float* bias, float* recall,
+                      float* logmass, spark_stream_t stream) {
+  const char* fn = "spark_diagnostics";
+  CHECK(check_args(a, fn));
+  const int nb = nblocks(a);
+  if (topk < 1 || topk > nb) return spark_set_error(SPARK_E_SHAPE, "%s: topk=%d not in [1, %d]", fn, topk, nb);
+  CHECK(check_ptr(q_p, fn, "q_p"));
+  CHECK(check_ptr(k_p, fn, "k_p"));
+  CHECK(check_ptr(idx, fn, "idx"));
+  CHECK(check_ptr(ksum, fn, "ksum"));
+  CHECK(check_ptr(bias, fn, "bias"));
+  CHECK(check_ptr(recall, fn, "recall", true));
+  CHECK(check_ptr(logmass, fn, "logmass", true));
+  if (recall == nullptr && logmass == nullptr)
+    return spark_set_error(SPARK_E_ARG, "%s: recall and logmass are both NULL", fn);
+  return diag_launch(a->H, a->N, a->d, a->block, a->dtype, q_p, k_p, idx, topk, ksum, bias, recall, logmass, (hipStream_t)stream);
+}

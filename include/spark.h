@@ -237,6 +237,25 @@ int spark_split(const spark_args* args, int32_t count, const void* xhat, int32_t
 int spark_gather(const spark_args* args, const void* x, const int32_t* perm, void* x_p,
                  void* x_pt, float* xbar, spark_stream_t stream);
 
+/* ---- routing diagnostics (outside the layer; dense cost) ---------------- */
+
+/* Per query row p of the permuted order (q_p, k_p as written by
+ * spark_reblock; idx, ksum, bias as for spark_attn):
+ *   recall[h][p]  = dense softmax mass of row p on the exact keys of its
+ *                   query block's selected blocks (the attention-mass recall
+ *                   compared between reblocked and fixed blocks in [blog]
+ *                   01 / Method: Spark-Reblock);
+ *   logmass[h][p] = | log sum over unselected blocks' keys of e^{q.k/sqrt d}
+ *                   - log sum over unselected blocks of
+ *                     n_B e^{q.ksum_B/sqrt d + bias_B} |
+ *                   (the log-mass error of [blog] 02 / Method: Spark-Reweight;
+ *                   0 when every block is selected).
+ * recall, logmass: [H, N] fp32, either may be NULL (not both).  Reads every
+ * key for every query: O(H N^2 d) work, fp32 accumulation. */
+int spark_diagnostics(const spark_args* args, const void* q_p, const void* k_p, const int32_t* idx,
+                      int32_t topk, const float* ksum, const float* bias, float* recall,
+                      float* logmass, spark_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

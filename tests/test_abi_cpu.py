@@ -119,3 +119,17 @@ def test_workspace_sizes_are_consistent(lib):
     assert L.workspace_bytes(ident, L.OP_REBLOCK) == 0
     assert lib.spark_workspace_bytes(ctypes.byref(a), 99, 0) == ctypes.c_size_t(-1).value
     assert lib.spark_workspace_bytes(ctypes.byref(a), L.OP_LAYER, 0) == ctypes.c_size_t(-1).value
+
+
+def test_diagnostics_validation(lib):
+    a = _args(dtype=1)
+    nb = O.n_blocks(1000, 64)
+    f = lib.spark_diagnostics
+    for k in (0, nb + 1):
+        assert f(ctypes.byref(a), FAKE, FAKE, FAKE, k, FAKE, FAKE, FAKE, FAKE, None) == -2
+    assert f(ctypes.byref(a), FAKE, FAKE, FAKE, 4, FAKE, FAKE, None, None, None) == -1
+    assert "both NULL" in L.last_error()
+    assert f(ctypes.byref(a), FAKE, None, FAKE, 4, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert "k_p is NULL" in L.last_error()
+    assert f(ctypes.byref(a), FAKE, FAKE, FAKE, 4, FAKE, FAKE, MISALIGNED, FAKE, None) == -1
+    assert f(ctypes.byref(_args(d=96)), FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, None) == -4
