@@ -47,6 +47,8 @@ def parse():
                    help="run one plain device copy of this size before timing (counter calibration)")
     p.add_argument("--cpu-sample-blocks", type=int, default=768,
                    help="query blocks of head 0 the oracle attends in the CPU baseline sample")
+    p.add_argument("--sweep", action="store_true",
+                   help="the density / noise sweep at the draft shape instead of the layer line")
     return p.parse_args()
 
 
@@ -135,6 +137,68 @@ def load_traffic(name, sources, key):
     return rec.get(key)
 
 
+def sweep(args):
+    """Density and noise sweep at the 16x24x42 draft shape (H=24, N=16,128):
+    clustered and i.i.d. N(0,1) q/k, top-k ratio 0.1/0.2/0.3/1.0, Reblock
+    vs fixed consecutive blocks.  Per row: layer latency (HIP events around
+    spark_layer, inputs resident) and, outside the timing, the mean
+    attention-mass recall and log-mass error from spark_diagnostics.  One JSON
+    line; not the headline measurement."""
+    import torch
+
+    from block_sparse_attention_mahalanobis_amd import _lib as L
+    from block_sparse_attention_mahalanobis_amd.workload import WORKLOADS
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    w0 = WORKLOADS["sweep"]
+    H, N, d, b = w0.H, w0.N, w0.d, w0.block
+    nb = L.n_blocks(N, b)
+    rows = []
+    for iid in (False, True):
+        w = w0.with_(iid=iid)
+        q, k, v = load_inputs(w, torch, torch.bfloat16, threads)
+        out = torch.empty_like(q)
+        for ratio in (0.1, 0.2, 0.3, 1.0):
+            topk = L.topk_from_ratio(ratio, nb)
+            for layout in ("reblock", "identity"):
+                a = L.make_args(H, N, d, b, torch.bfloat16, None, layout)
+                ws = torch.empty(max(L.workspace_bytes(a, L.OP_LAYER, topk), 256), dtype=torch.uint8,
+                                 device="cuda:0")
+                for _ in range(args.warmup):
+                    L.spark_layer(q, k, v, b, topk, layout=layout, out=out, ws=ws)
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(args.steps):
+                    L.spark_layer(q, k, v, b, topk, layout=layout, out=out, ws=ws)
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / args.steps
+                del ws
+                g = L.spark_reblock(q, k, v, b, layout=layout)
+                idx = L.spark_select(g["qbar"], g["kbar"], topk, N, b)
+                ks, vs, bias = L.spark_summarize(g["k_p"], g["v_pt"], g["anchor"], N, b)
+                rec, lme = L.spark_diagnostics(g["q_p"], g["k_p"], idx, ks, bias, N, b)
+                torch.cuda.synchronize()
+                row = {"data": "iid" if iid else "clustered", "ratio": ratio, "topk": topk, "layout": layout,
+                       "ms": round(ms, 3), "recall": round(float(rec.mean()), 4),
+                       "log_mass_error": round(float(lme.mean()), 4)}
+                log(json.dumps(row))
+                rows.append(row)
+                del g, idx, ks, vs, bias, rec, lme
+        del q, k, v, out
+    print(json.dumps({"metric": "density/noise sweep: layer latency (ms) and attention-mass recall, "
+                                "Reblock vs fixed blocks",
+                      "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "data": "synthetic (seeded; clustered Gaussian mixture on the latent grid, or "
+                              "i.i.d. N(0,1) q/k; v ~ N(0,1))",
+                      "config": {"workload": "sweep", "H": H, "N": N, "d": d, "block": b, "n_blocks": nb,
+                                 "summary": "reweight"},
+                      "rows": rows}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -142,6 +206,9 @@ def main():
                                    "this implementation (heads would shard with zero communication)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.sweep:
+        sweep(args)
+        return
     import torch
 
     import block_sparse_attention_mahalanobis_amd as S

@@ -224,6 +224,20 @@ __device__ __forceinline__ uint64_t group_min_u64(uint64_t v) {
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 __device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
 
+// 16-byte chunk of a row as floats
+template <typename T> struct Chunk;
+template <> struct Chunk<uint16_t> {
+  static constexpr int VE = 8;
+  __device__ __forceinline__ static void load(const uint16_t* p, float* v) { load8(p, v); }
+};
+template <> struct Chunk<float> {
+  static constexpr int VE = 4;
+  __device__ __forceinline__ static void load(const float* p, float* v) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  }
+};
+
 inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
 }  // namespace spark

@@ -254,24 +254,86 @@ int summarize_launch(int H, int N, int D, int BK, int dtype, const void* kp, con
 }
 
 // anchor[h] = mean of query rows [0, n_anchor) (column sums in row order)
-template <typename T>
-__global__ __launch_bounds__(256) void anchor_kernel(const T* __restrict__ q,
-                                                     float* __restrict__ anchor, int N, int D,
-                                                     int n_anchor) {
-  const int h = blockIdx.x;
-  for (int c = threadIdx.x; c < D; c += blockDim.x) {
+// Anchor without the moments pass (IDENTITY / GIVEN layouts): per head, the
+// mean of the first n_anchor query rows.  Pass 1: chunk c of every head sums
+// its rows (16 row lanes x 8-column chunks per workgroup, batched loads),
+// pass 2 adds the chunk sums in chunk order (deterministic).
+constexpr int ANC_T = 256;
+
+template <typename T, int D>
+__global__ __launch_bounds__(ANC_T) void anchor_partial(const T* __restrict__ q, float* __restrict__ part,
+                                                        int N, int n_anchor, int rows_per_chunk,
+                                                        long part_head_stride) {
+  constexpr int VE = 16 / (int)sizeof(T), CPR = D / VE, RL = ANC_T / CPR;
+  __shared__ float sp[RL][D];
+  const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int rl = tid / CPR, cc = (tid % CPR) * VE;
+  const long r0 = (long)c * rows_per_chunk;
+  const long r1 = min((long)n_anchor, r0 + rows_per_chunk);
+  const T* qh = q + (long)h * N * D;
+  float acc[VE];
+#pragma unroll
+  for (int e = 0; e < VE; ++e) acc[e] = 0.f;
+  for (long r = r0 + rl; r < r1; r += 4 * RL) {
+    float v[4][VE];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const long rr = r + (long)u * RL;
+      if (rr < r1) {
+        Chunk<T>::load(qh + rr * D + cc, v[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) v[u][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc[e] += v[u][e];
+  }
+#pragma unroll
+  for (int e = 0; e < VE; ++e) sp[rl][cc + e] = acc[e];
+  __syncthreads();
+  for (int col = tid; col < D; col += ANC_T) {
     float s = 0.f;
-    for (int i = 0; i < n_anchor; ++i) s += Elem<T>::load(q + ((long)h * N + i) * D + c);
-    anchor[(long)h * D + c] = s / (float)n_anchor;
+    for (int l = 0; l < RL; ++l) s += sp[l][col];
+    part[(long)h * part_head_stride + (long)c * D + col] = s;
   }
 }
 
-int anchor_launch(int H, int N, int D, int dtype, const void* q, float* anchor, int n_anchor,
-                  hipStream_t st) {
-  if (dtype == SPARK_F32)
-    hipLaunchKernelGGL(anchor_kernel<float>, dim3(H), dim3(128), 0, st, (const float*)q, anchor, N, D, n_anchor);
-  else
-    hipLaunchKernelGGL(anchor_kernel<uint16_t>, dim3(H), dim3(128), 0, st, (const uint16_t*)q, anchor, N, D, n_anchor);
+__global__ void anchor_reduce(const float* __restrict__ part, float* __restrict__ anchor, int D,
+                              int nchunk, long part_head_stride, int n_anchor) {
+  const int h = blockIdx.x;
+  for (int col = threadIdx.x; col < D; col += blockDim.x) {
+    float s = 0.f;
+    for (int c = 0; c < nchunk; ++c) s += part[(long)h * part_head_stride + (long)c * D + col];
+    anchor[(long)h * D + col] = s / (float)n_anchor;
+  }
+}
+
+template <typename T, int D>
+static void anchor_t(int H, int N, const void* q, float* anchor, int n_anchor, float* scratch,
+                     int nb, hipStream_t st) {
+  // up to nb chunks, so the partials fit in a [H, nb, D] fp32 scratch
+  const int nchunk = std::max(1, std::min(nb, cdiv(n_anchor, 512)));
+  const int rpc = cdiv(n_anchor, nchunk);
+  const long stride = (long)nb * D;
+  hipLaunchKernelGGL((anchor_partial<T, D>), dim3(nchunk, H), dim3(ANC_T), 0, st, (const T*)q, scratch, N,
+                     n_anchor, rpc, stride);
+  hipLaunchKernelGGL(anchor_reduce, dim3(H), dim3(D), 0, st, scratch, anchor, D, nchunk, stride, n_anchor);
+}
+
+// scratch: [H, ceil(N / BK), D] fp32 (e.g. the qbar output, written later)
+int anchor_launch(int H, int N, int D, int BK, int dtype, const void* q, float* anchor, int n_anchor,
+                  float* scratch, hipStream_t st) {
+  const int nb = cdiv(N, BK);
+  if (dtype == SPARK_F32) {
+    if (D == 128) anchor_t<float, 128>(H, N, q, anchor, n_anchor, scratch, nb, st);
+    else anchor_t<float, 64>(H, N, q, anchor, n_anchor, scratch, nb, st);
+  } else {
+    if (D == 128) anchor_t<uint16_t, 128>(H, N, q, anchor, n_anchor, scratch, nb, st);
+    else anchor_t<uint16_t, 64>(H, N, q, anchor, n_anchor, scratch, nb, st);
+  }
   return spark_check_launch("anchor");
 }
 

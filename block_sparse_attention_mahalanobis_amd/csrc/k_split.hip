@@ -80,20 +80,6 @@ __device__ __forceinline__ uint64_t argmin_key(float v, int id) {
   return ((uint64_t)float_key_asc(v) << 32) | (uint32_t)id;
 }
 
-// 16-byte chunk of a row as floats
-template <typename T> struct Chunk;
-template <> struct Chunk<uint16_t> {
-  static constexpr int VE = 8;
-  __device__ __forceinline__ static void load(const uint16_t* p, float* v) { load8(p, v); }
-};
-template <> struct Chunk<float> {
-  static constexpr int VE = 4;
-  __device__ __forceinline__ static void load(const float* p, float* v) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  }
-};
-
 // ---- global-level passes ----------------------------------------------------
 // ids[t][i] = i; trees t >= split_at go to hi (offset by split_at trees).
 __global__ void iota_kernel(int32_t* __restrict__ lo, int32_t* __restrict__ hi, int split_at,

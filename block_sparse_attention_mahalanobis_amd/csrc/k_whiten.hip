@@ -15,23 +15,38 @@
 
 namespace spark {
 
-constexpr int MOM_ROWS = 8192;   // rows per moment partial
 constexpr int MOM_TOK = 64;      // rows staged per LDS round
 
-// partial[t][c][D*D] (+ colsum partial[t][c][D] for anchors)
+// Rows per moment partial: enough chunks that both sides of all heads give
+// about 2048 workgroups (the chip holds 256 CUs x several), a multiple of
+// MOM_TOK, at least 256 rows.
+struct MomPlan {
+  int nchunk, rpc;
+};
+static MomPlan mom_plan(int H, int N) {
+  const int want = std::max(1, cdiv(2048, 2 * H));
+  int rpc = std::max(256, cdiv(N, want));
+  rpc = cdiv(rpc, MOM_TOK) * MOM_TOK;
+  return {cdiv(N, rpc), rpc};
+}
+
+// partial[t][c][D*D] (+ colsum partial[t][c][D] for anchors); trees t < H
+// are the query side (xq), the others the key side (xk).  The next round's
+// rows are loaded into registers while the current round's MFMAs run.
 template <int D>
-__global__ __launch_bounds__(256) void moments_mfma(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(256) void moments_mfma(const uint16_t* __restrict__ xq,
+                                                    const uint16_t* __restrict__ xk,
                                                     float* __restrict__ part,
-                                                    float* __restrict__ cpart, int N,
-                                                    int n_anchor, int nchunk, int q_trees) {
+                                                    float* __restrict__ cpart, int H, int N,
+                                                    int n_anchor, int nchunk, int rpc) {
   constexpr int RS = MOM_TOK + 8;  // LDS row stride (bf16) of X^T
   __shared__ __attribute__((aligned(16))) uint16_t sXT[D * RS];
   const int t = blockIdx.y, chunk = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
-  const long r0 = (long)chunk * MOM_ROWS;
-  const long r1 = min((long)N, r0 + MOM_ROWS);
-  const uint16_t* xt = x + (long)t * N * D;
+  const long r0 = (long)chunk * rpc;
+  const long r1 = min((long)N, r0 + rpc);
+  const uint16_t* xt = (t < H) ? xq + (long)t * N * D : xk + (long)(t - H) * N * D;
   constexpr int MT = D / 32;                 // output tiles per side
   constexpr int TPW = MT * MT / 4;           // output tiles per wave (4 or 1)
   f32x16 acc[TPW];
@@ -39,7 +54,7 @@ __global__ __launch_bounds__(256) void moments_mfma(const uint16_t* __restrict__
   for (int i = 0; i < TPW; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
-  const bool want_cs = cpart != nullptr && t < q_trees;
+  const bool want_cs = cpart != nullptr && t < H;
   float cs[8] = {0, 0, 0, 0, 0, 0, 0, 0};   // column sums of rows < n_anchor
 
   // staging: thread -> (4-row group, 8-col chunk)
@@ -47,17 +62,26 @@ __global__ __launch_bounds__(256) void moments_mfma(const uint16_t* __restrict__
   constexpr int RG = 256 / CPR;              // 4-row groups per round: 16 or 32
   static_assert(RG * 4 >= MOM_TOK, "staging covers the round");
   const int g = tid / CPR, cc = (tid % CPR) * 8;
+  const bool stager = g * 4 < MOM_TOK;
 
+  uint4 pf[4];
+  auto fetch = [&](long rb) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const long row = rb + g * 4 + rr;
+      pf[rr] = (stager && row < r1) ? *reinterpret_cast<const uint4*>(xt + row * D + cc)
+                                    : make_uint4(0, 0, 0, 0);
+    }
+  };
+  fetch(r0);
   for (long rb = r0; rb < r1; rb += MOM_TOK) {
-    __syncthreads();
-    if (g * 4 < MOM_TOK) {
+    __syncthreads();  // the previous round's MFMAs are done with sXT
+    if (stager) {
       uint16_t vals[4][8];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const long row = rb + g * 4 + rr;
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (row < r1) u = *reinterpret_cast<const uint4*>(xt + row * D + cc);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+        const uint32_t w[4] = {pf[rr].x, pf[rr].y, pf[rr].z, pf[rr].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           vals[rr][2 * e] = (uint16_t)(w[e] & 0xffff);
@@ -77,6 +101,7 @@ __global__ __launch_bounds__(256) void moments_mfma(const uint16_t* __restrict__
       }
     }
     __syncthreads();
+    if (rb + MOM_TOK < r1) fetch(rb + MOM_TOK);
 #pragma unroll
     for (int ks = 0; ks < MOM_TOK / 16; ++ks) {
 #pragma unroll
@@ -107,7 +132,7 @@ __global__ __launch_bounds__(256) void moments_mfma(const uint16_t* __restrict__
     // reduce the RG row groups' column sums through LDS (reuse sXT as floats)
     __syncthreads();
     float* sf = reinterpret_cast<float*>(sXT);
-    if (g * 4 < MOM_TOK)
+    if (stager)
 #pragma unroll
       for (int e = 0; e < 8; ++e) sf[g * D + cc + e] = cs[e];
     __syncthreads();
@@ -121,24 +146,25 @@ __global__ __launch_bounds__(256) void moments_mfma(const uint16_t* __restrict__
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void moments_f32(const float* __restrict__ x,
+__global__ __launch_bounds__(256) void moments_f32(const float* __restrict__ xq,
+                                                   const float* __restrict__ xk,
                                                    float* __restrict__ part,
-                                                   float* __restrict__ cpart, int N, int n_anchor,
-                                                   int nchunk, int q_trees) {
+                                                   float* __restrict__ cpart, int H, int N,
+                                                   int n_anchor, int nchunk, int rpc) {
   constexpr int RPT = D * D / 256;  // outputs per thread: 64 (D=128) or 16 (D=64)
   constexpr int SUB = (D == 128) ? 8 : 4;  // output sub-block side
   __shared__ float sX[MOM_TOK][D];
   const int t = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
-  const long r0 = (long)chunk * MOM_ROWS;
-  const long r1 = min((long)N, r0 + MOM_ROWS);
-  const float* xt = x + (long)t * N * D;
+  const long r0 = (long)chunk * rpc;
+  const long r1 = min((long)N, r0 + rpc);
+  const float* xt = (t < H) ? xq + (long)t * N * D : xk + (long)(t - H) * N * D;
   const int bi = (tid / (D / SUB)) * SUB, bj = (tid % (D / SUB)) * SUB;
   float acc[SUB][SUB];
 #pragma unroll
   for (int i = 0; i < SUB; ++i)
 #pragma unroll
     for (int j = 0; j < SUB; ++j) acc[i][j] = 0.f;
-  const bool want_cs = cpart != nullptr && t < q_trees;
+  const bool want_cs = cpart != nullptr && t < H;
   float cs = 0.f;
   static_assert(RPT == SUB * SUB, "tiling");
   for (long rb = r0; rb < r1; rb += MOM_TOK) {
@@ -192,37 +218,31 @@ __global__ void moments_reduce(const float* __restrict__ part, const float* __re
 }
 
 size_t moments_ws_bytes(int H, int N, int D) {
-  const int nchunk = cdiv(N, MOM_ROWS);
+  const int nchunk = mom_plan(H, N).nchunk;
   return (size_t)2 * H * nchunk * D * D * 4 + (size_t)2 * H * nchunk * D * 4 + 512;
 }
 
-// q and k are read as two consecutive launches over the same partial buffer.
+// One launch over both sides: trees 0..H-1 are q, H..2H-1 are k.
 int moments_launch(int H, int N, int D, int dtype, const void* q, const void* k, float* MQ,
                    float* MK, float* anchor, int n_anchor, void* ws, hipStream_t st) {
-  const int nchunk = cdiv(N, MOM_ROWS);
+  const MomPlan mp = mom_plan(H, N);
+  const int nchunk = mp.nchunk;
   float* part = (float*)ws;
   float* cpart = part + (size_t)2 * H * nchunk * D * D;
-  const size_t esz = dtype == SPARK_BF16 ? 2 : 4;
-  for (int side = 0; side < 2; ++side) {
-    const void* x = side == 0 ? q : k;
-    float* pp = part + (size_t)side * H * nchunk * D * D;
-    float* cp = side == 0 ? cpart : nullptr;
-    (void)esz;
-    dim3 grid(nchunk, H);
-    if (dtype == SPARK_BF16) {
-      if (D == 128)
-        hipLaunchKernelGGL(moments_mfma<128>, grid, dim3(256), 0, st, (const uint16_t*)x, pp, cp, N, n_anchor, nchunk, H);
-      else
-        hipLaunchKernelGGL(moments_mfma<64>, grid, dim3(256), 0, st, (const uint16_t*)x, pp, cp, N, n_anchor, nchunk, H);
-    } else {
-      if (D == 128)
-        hipLaunchKernelGGL(moments_f32<128>, grid, dim3(256), 0, st, (const float*)x, pp, cp, N, n_anchor, nchunk, H);
-      else
-        hipLaunchKernelGGL(moments_f32<64>, grid, dim3(256), 0, st, (const float*)x, pp, cp, N, n_anchor, nchunk, H);
-    }
-    int rc = spark_check_launch("moments");
-    if (rc) return rc;
+  dim3 grid(nchunk, 2 * H);
+  if (dtype == SPARK_BF16) {
+    if (D == 128)
+      hipLaunchKernelGGL(moments_mfma<128>, grid, dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k, part, cpart, H, N, n_anchor, nchunk, mp.rpc);
+    else
+      hipLaunchKernelGGL(moments_mfma<64>, grid, dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k, part, cpart, H, N, n_anchor, nchunk, mp.rpc);
+  } else {
+    if (D == 128)
+      hipLaunchKernelGGL(moments_f32<128>, grid, dim3(256), 0, st, (const float*)q, (const float*)k, part, cpart, H, N, n_anchor, nchunk, mp.rpc);
+    else
+      hipLaunchKernelGGL(moments_f32<64>, grid, dim3(256), 0, st, (const float*)q, (const float*)k, part, cpart, H, N, n_anchor, nchunk, mp.rpc);
   }
+  int rc = spark_check_launch("moments");
+  if (rc) return rc;
   hipLaunchKernelGGL(moments_reduce, dim3(16, 2 * H), dim3(256), 0, st, part, cpart, MQ, MK,
                      anchor, H, D, N, n_anchor, nchunk);
   return spark_check_launch("moments_reduce");
@@ -363,7 +383,7 @@ int msqrt_launch(int count, int D, const float* M, float* W, float* Tscr, hipStr
 constexpr int WH_ROWS = 1024;  // rows per workgroup: 8 rounds of 4 waves x 32
 
 template <int D>
-__global__ __launch_bounds__(256) void whiten_mfma(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(256, 4) void whiten_mfma(const uint16_t* __restrict__ x,
                                                    const float* __restrict__ W,
                                                    uint16_t* __restrict__ xh, int N) {
   constexpr int RS = D + 8;

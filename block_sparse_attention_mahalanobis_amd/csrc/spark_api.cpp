@@ -23,7 +23,8 @@ int gather_launch(int H, int N, int D, int BK, int dtype, const void* x, const i
 int summarize_launch(int H, int N, int D, int BK, int dtype, const void* kp, const void* vpt,
                      const float* anchor, float* ksum, float* vsum, float* bias, int mean_mode,
                      hipStream_t st);
-int anchor_launch(int H, int N, int D, int dtype, const void* q, float* anchor, int n_anchor,
+int anchor_launch(int H, int N, int D, int BK, int dtype, const void* q, float* anchor, int n_anchor,
+                  float* scratch,
                   hipStream_t st);
 int select_launch(int H, int N, int D, int BK, const float* qbar, const float* kbar,
                   const float* scores_in, int topk, int32_t* idx, float* scores_out,
@@ -329,7 +330,8 @@ int spark_reblock(const spark_args* a, const void* q, const void* k, const void*
       pq = nullptr;  // gather treats NULL as the identity
       pk = nullptr;
     }
-    if (anchor) CHECK(anchor_launch(H, N, D, a->dtype, q, anchor, a->n_anchor, st));
+    // qbar (written by the gather below) holds the anchor's chunk sums
+    if (anchor) CHECK(anchor_launch(H, N, D, BK, a->dtype, q, anchor, a->n_anchor, qbar, st));
   }
   CHECK(gather_launch(H, N, D, BK, a->dtype, q, pq, q_p, nullptr, qbar, st));
   CHECK(gather_launch(H, N, D, BK, a->dtype, k, pk, k_p, nullptr, kbar, st));
