@@ -52,7 +52,7 @@ import numpy as np
 
 __all__ = [
     "n_blocks", "block_sizes", "topk_from_ratio", "second_moment", "psd_sqrt",
-    "whiten", "split_group", "split_partition", "reblock_head", "gather_pool",
+    "whiten", "split_group", "split_partition", "reblock_head", "reblock_keys", "gather_pool",
     "block_scores", "select_topk", "anchor_query", "reweight_summaries",
     "mean_summaries", "sparse_attention", "dense_attention", "forward_head",
     "forward", "attention_mass_recall", "log_mass_error", "HeadResult",
@@ -189,6 +189,14 @@ def reblock_head(q: np.ndarray, k: np.ndarray, b: int):
     perm_q = split_partition(whiten(q, WQ), b)
     perm_k = split_partition(whiten(k, WK), b)
     return perm_q, perm_k
+
+
+def reblock_keys(q: np.ndarray, k: np.ndarray, b: int):
+    """The key permutation alone (keys whitened by M_Q^{1/2}, split as in
+    reblock_head).  The q_reuse_k layout ([news] Workflows: every example
+    workflow of the release sets reblock_layout=q_reuse_k) groups the queries
+    with this same key partition instead of splitting them separately."""
+    return split_partition(whiten(k, psd_sqrt(second_moment(q))), b)
 
 
 def gather_pool(x: np.ndarray, perm: np.ndarray, b: int):
@@ -359,7 +367,8 @@ def forward_head(q, k, v, b: int, topk: int, n_anchor: Optional[int] = None,
                  layout: str = "reblock", perm_q=None, perm_k=None,
                  summary: str = "reweight", scores_in=None) -> HeadResult:
     """Reblock -> select -> summarise -> attend -> scatter, one head.
-    layout: "reblock" (Spark-Reblock), "identity" (consecutive blocks, the
+    layout: "reblock" (Spark-Reblock), "q_reuse_k" (the key partition reused
+    for the queries), "identity" (consecutive blocks, the
     fixed-partition BSA baseline) or "given" (perm_q / perm_k supplied).
     summary: "reweight" (Spark-Reweight) or "mean" (BSA mean pooling).
     scores_in: optional block scores to select from instead of q_bar.k_bar."""
@@ -370,6 +379,9 @@ def forward_head(q, k, v, b: int, topk: int, n_anchor: Optional[int] = None,
     n_anchor = N if n_anchor is None else n_anchor
     if layout == "reblock":
         perm_q, perm_k = reblock_head(q, k, b)
+    elif layout == "q_reuse_k":
+        perm_k = reblock_keys(q, k, b)
+        perm_q = perm_k.copy()
     elif layout == "identity":
         perm_q = np.arange(N)
         perm_k = np.arange(N)

@@ -405,3 +405,24 @@ def test_direction_of_the_pages_ablations_on_clustered_data():
     mn = O.forward_head(q, k, v, b, kk, layout="identity", summary="mean")
     assert O.attention_mass_recall(re, b) > O.attention_mass_recall(fx, b)
     assert O.log_mass_error(fx, b) < O.log_mass_error(mn, b)
+
+
+def test_q_reuse_k_layout():
+    """q_reuse_k: the queries take the key partition.  The key side must be
+    the key side of the full Spark-Reblock (keys whitened by M_Q^{1/2}: a
+    key path whitened by M_K instead, or splitting the queries, differs on
+    generic data), and with q = k the two sides of the full reblock coincide,
+    so the two layouts agree on both sides."""
+    rng = _rng(23)
+    N, d, b = 600, 16, 32
+    q = _clustered(rng, N, d)
+    k = _clustered(rng, N, d) @ np.diag(rng.uniform(0.3, 3.0, d))
+    pq, pk = O.reblock_head(q, k, b)
+    assert np.array_equal(O.reblock_keys(q, k, b), pk)
+    wrong = O.split_partition(O.whiten(k, O.psd_sqrt(O.second_moment(k))), b)
+    assert not np.array_equal(wrong, pk)
+    r = O.forward_head(q, k, rng.standard_normal((N, d)), b, 4, layout="q_reuse_k")
+    assert np.array_equal(r.perm_q, pk) and np.array_equal(r.perm_k, pk)
+    pq2, pk2 = O.reblock_head(k, k, b)
+    assert np.array_equal(pq2, pk2)
+    assert np.array_equal(O.reblock_keys(k, k, b), pq2)
