@@ -47,6 +47,8 @@ def parse():
                    help="run one plain device copy of this size before timing (counter calibration)")
     p.add_argument("--cpu-sample-blocks", type=int, default=768,
                    help="query blocks of head 0 the oracle attends in the CPU baseline sample")
+    p.add_argument("--layout", default="reblock", choices=["reblock", "q_reuse_k"],
+                   help="token partition: separate query/key Spark-Reblock, or the key partition reused")
     p.add_argument("--sweep", action="store_true",
                    help="the density / noise sweep at the draft shape instead of the layer line")
     return p.parse_args()
@@ -77,12 +79,13 @@ def attn_flops(idx, N, b, d):
     return exact, comp
 
 
-def reblock_bytes(H, N, d, b, es, levels_global, nb):
-    """Algorithmic HBM bytes of reblock + summaries (per layer)."""
+def reblock_bytes(H, N, d, b, es, levels_global, nb, sides=2):
+    """Algorithmic HBM bytes of reblock + summaries (per layer); sides = 1
+    for q_reuse_k (moments of q only, keys whitened and split)."""
     vol = H * N * d * es                      # one [H, N, d] tensor
-    moments = 2 * vol
-    whiten = 4 * vol
-    split = 2 * levels_global * 4 * vol + 2 * vol       # 4 row passes per global level + finisher
+    moments = sides * vol
+    whiten = 2 * sides * vol
+    split = sides * (levels_global * 4 * vol + vol)     # 4 row passes per global level + finisher
     gather = 6 * vol
     summ = 2 * vol
     return moments + whiten + split + gather + summ
@@ -139,8 +142,9 @@ def load_traffic(name, sources, key):
 
 def sweep(args):
     """Density and noise sweep at the 16x24x42 draft shape (H=24, N=16,128):
-    clustered and i.i.d. N(0,1) q/k, top-k ratio 0.1/0.2/0.3/1.0, Reblock
-    vs fixed consecutive blocks.  Per row: layer latency (HIP events around
+    clustered and i.i.d. N(0,1) q/k, top-k ratio 0.1/0.2/0.3/1.0, Reblock,
+    q_reuse_k (the key partition reused for the queries) and fixed
+    consecutive blocks.  Per row: layer latency (HIP events around
     spark_layer, inputs resident) and, outside the timing, the mean
     attention-mass recall and log-mass error from spark_diagnostics.  One JSON
     line; not the headline measurement."""
@@ -161,7 +165,7 @@ def sweep(args):
         out = torch.empty_like(q)
         for ratio in (0.1, 0.2, 0.3, 1.0):
             topk = L.topk_from_ratio(ratio, nb)
-            for layout in ("reblock", "identity"):
+            for layout in ("reblock", "q_reuse_k", "identity"):
                 a = L.make_args(H, N, d, b, torch.bfloat16, None, layout)
                 ws = torch.empty(max(L.workspace_bytes(a, L.OP_LAYER, topk), 256), dtype=torch.uint8,
                                  device="cuda:0")
@@ -190,7 +194,7 @@ def sweep(args):
                 del g, idx, ks, vs, bias, rec, lme
         del q, k, v, out
     print(json.dumps({"metric": "density/noise sweep: layer latency (ms) and attention-mass recall, "
-                                "Reblock vs fixed blocks",
+                                "Reblock vs q_reuse_k vs fixed blocks",
                       "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                       "data": "synthetic (seeded; clustered Gaussian mixture on the latent grid, or "
                               "i.i.d. N(0,1) q/k; v ~ N(0,1))",
@@ -247,7 +251,7 @@ def main():
     vsum = torch.empty((H, nb, d), dtype=torch.float32, device=dev)
     bias = torch.empty((H, nb), dtype=torch.float32, device=dev)
     out = torch.empty_like(q)
-    a = L.make_args(H, N, d, b, dtype, w.n_anchor)
+    a = L.make_args(H, N, d, b, dtype, w.n_anchor, args.layout)
     ws_r = L.workspace_bytes(a, L.OP_REBLOCK)
     ws_a = L.workspace_bytes(a, L.OP_ATTN)
     ws = torch.empty(max(ws_r, ws_a, 256), dtype=torch.uint8, device=dev)
@@ -311,14 +315,14 @@ def main():
     while mx > F:
         mx = (mx + 1) // 2
         lev += 1
-    rb_bytes = reblock_bytes(H, N, d, b, es, lev, nb)
+    rb_bytes = reblock_bytes(H, N, d, b, es, lev, nb, 1 if args.layout == "q_reuse_k" else 2)
     rb_ms = st_mean[0] + st_mean[2]
     csrc = os.path.join(ROOT, "block_sparse_attention_mahalanobis_amd", "csrc")
     traffic = load_traffic("attn_full768_traffic.txt", [os.path.join(csrc, "k_attn.hip")],
                            "bytes_per_launch") if args.config == "full768" else None
     rb_traffic = load_traffic("reblock_full768_traffic.txt",
                               [os.path.join(csrc, f) for f in ("k_whiten.hip", "k_split.hip", "k_gather_summ.hip")],
-                              "bytes_per_layer") if args.config == "full768" else None
+                              "bytes_per_layer") if args.config == "full768" and args.layout == "reblock" else None
 
     base = None
     if not args.no_cpu_baseline:
@@ -340,7 +344,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded clustered Gaussian-mixture q/k on the latent grid, v ~ N(0,1))",
         "config": {"workload": w.name, "H": H, "N": N, "d": d, "block": b, "n_blocks": nb,
-                   "topk": topk, "density": w.ratio, "layout": "reblock", "summary": "reweight"},
+                   "topk": topk, "density": w.ratio, "layout": args.layout, "summary": "reweight"},
         "exact_mfma_pct_peak": round(100.0 * exact_tf / PEAK_BF16_TFLOPS, 2),
         "stages_ms": {"reblock": round(st_mean[0], 3), "select": round(st_mean[1], 3),
                       "summarize": round(st_mean[2], 3), "attn": round(st_mean[3], 3)},

@@ -18,10 +18,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libspark.so")
 
 SPARK_F32, SPARK_BF16 = 0, 1
-LAYOUT_REBLOCK, LAYOUT_IDENTITY, LAYOUT_GIVEN = 0x0, 0x1, 0x2
+LAYOUT_REBLOCK, LAYOUT_IDENTITY, LAYOUT_GIVEN, LAYOUT_Q_REUSE_K = 0x0, 0x1, 0x2, 0x3
 SUMMARY_REWEIGHT, SUMMARY_MEAN = 0x0, 0x4
 OP_REBLOCK, OP_SELECT, OP_SUMMARIZE, OP_ATTN, OP_SPLIT, OP_LAYER = range(6)
-_LAYOUTS = {"reblock": LAYOUT_REBLOCK, "identity": LAYOUT_IDENTITY, "given": LAYOUT_GIVEN}
+_LAYOUTS = {"reblock": LAYOUT_REBLOCK, "identity": LAYOUT_IDENTITY, "given": LAYOUT_GIVEN,
+            "q_reuse_k": LAYOUT_Q_REUSE_K}
 _SUMMARIES = {"reweight": SUMMARY_REWEIGHT, "mean": SUMMARY_MEAN}
 
 EXPORTED = [

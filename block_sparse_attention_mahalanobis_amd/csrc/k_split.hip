@@ -782,6 +782,17 @@ static int split_t(int count, int N, int BK, const void* xhv, int32_t* perm_lo,
   return spark_check_launch("split finisher");
 }
 
+__global__ void copy_perm_kernel(const int32_t* __restrict__ src, int32_t* __restrict__ dst, long n) {
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
+int copy_perm_launch(long count, const int32_t* src, int32_t* dst, hipStream_t st) {
+  hipLaunchKernelGGL(copy_perm_kernel, dim3((int)std::min<long>((count + 255) / 256, 8192)), dim3(256), 0, st,
+                     src, dst, count);
+  return spark_check_launch("copy_perm");
+}
+
 int iota_launch(int count, int N, int32_t* lo, int32_t* hi, int split_at, hipStream_t st) {
   const long total = (long)count * N;
   hipLaunchKernelGGL(iota_kernel, dim3((int)std::min<long>((total + 255) / 256, 8192)), dim3(256), 0, st, lo, hi, split_at, N, total);

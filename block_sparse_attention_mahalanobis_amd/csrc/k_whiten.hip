@@ -222,14 +222,16 @@ size_t moments_ws_bytes(int H, int N, int D) {
   return (size_t)2 * H * nchunk * D * D * 4 + (size_t)2 * H * nchunk * D * 4 + 512;
 }
 
-// One launch over both sides: trees 0..H-1 are q, H..2H-1 are k.
+// One launch over both sides: trees 0..H-1 are q, H..2H-1 are k (k, MK may
+// be NULL: then only the query side, M_Q and the anchor).
 int moments_launch(int H, int N, int D, int dtype, const void* q, const void* k, float* MQ,
                    float* MK, float* anchor, int n_anchor, void* ws, hipStream_t st) {
   const MomPlan mp = mom_plan(H, N);
   const int nchunk = mp.nchunk;
   float* part = (float*)ws;
   float* cpart = part + (size_t)2 * H * nchunk * D * D;
-  dim3 grid(nchunk, 2 * H);
+  const int trees = (k != nullptr) ? 2 * H : H;  // k == NULL: the query side only
+  dim3 grid(nchunk, trees);
   if (dtype == SPARK_BF16) {
     if (D == 128)
       hipLaunchKernelGGL(moments_mfma<128>, grid, dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k, part, cpart, H, N, n_anchor, nchunk, mp.rpc);
@@ -243,7 +245,7 @@ int moments_launch(int H, int N, int D, int dtype, const void* q, const void* k,
   }
   int rc = spark_check_launch("moments");
   if (rc) return rc;
-  hipLaunchKernelGGL(moments_reduce, dim3(16, 2 * H), dim3(256), 0, st, part, cpart, MQ, MK,
+  hipLaunchKernelGGL(moments_reduce, dim3(16, trees), dim3(256), 0, st, part, cpart, MQ, MK,
                      anchor, H, D, N, n_anchor, nchunk);
   return spark_check_launch("moments_reduce");
 }

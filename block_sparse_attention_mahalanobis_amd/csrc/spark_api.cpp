@@ -32,6 +32,7 @@ int select_launch(int H, int N, int D, int BK, const float* qbar, const float* k
 size_t moments_ws_bytes(int H, int N, int D);
 int moments_launch(int H, int N, int D, int dtype, const void* q, const void* k, float* MQ,
                    float* MK, float* anchor, int n_anchor, void* ws, hipStream_t st);
+int copy_perm_launch(long count, const int32_t* src, int32_t* dst, hipStream_t st);
 size_t msqrt_ws_bytes(int count, int D);
 int msqrt_launch(int count, int D, const float* M, float* W, float* Tscr, hipStream_t st);
 int whiten_launch(int count, int N, int D, int dtype, const void* x, const float* W, void* xh,
@@ -102,7 +103,7 @@ int check_args(const spark_args* a, const char* fn) {
   if (a->n_anchor < 1 || a->n_anchor > a->N)
     return spark_set_error(SPARK_E_SHAPE, "%s: n_anchor=%d not in [1, N=%d]", fn, a->n_anchor, a->N);
   const uint32_t layout = a->flags & SPARK_LAYOUT_MASK;
-  if (layout > SPARK_LAYOUT_GIVEN || (a->flags & ~(SPARK_LAYOUT_MASK | SPARK_SUMMARY_MEAN)))
+  if (layout > SPARK_LAYOUT_Q_REUSE_K || (a->flags & ~(SPARK_LAYOUT_MASK | SPARK_SUMMARY_MEAN)))
     return spark_set_error(SPARK_E_ARG, "%s: bad flags 0x%x", fn, a->flags);
   const long nb = (a->N + (long)a->block - 1) / a->block;
   if ((long)a->H * nb > 0x7fffffffL || (long)a->N * a->d > 0x7fffffffL)
@@ -113,7 +114,8 @@ int check_args(const spark_args* a, const char* fn) {
 int nblocks(const spark_args* a) { return (a->N + a->block - 1) / a->block; }
 
 size_t reblock_ws(const spark_args* a) {
-  if ((a->flags & SPARK_LAYOUT_MASK) != SPARK_LAYOUT_REBLOCK) return 0;
+  const uint32_t layout = a->flags & SPARK_LAYOUT_MASK;
+  if (layout != SPARK_LAYOUT_REBLOCK && layout != SPARK_LAYOUT_Q_REUSE_K) return 0;
   const int H = a->H, N = a->N, D = a->d;
   size_t b = 0;
   b += up((size_t)2 * H * D * D * 4);                     // moments [MK | MQ]
@@ -325,6 +327,22 @@ int spark_reblock(const spark_args* a, const void* q, const void* k, const void*
     CHECK(whiten_launch(H, N, D, a->dtype, k, Ws + (size_t)H * D * D,
                         (char*)xh + (size_t)H * N * D * esize(a->dtype), st));
     CHECK(split_launch(2 * H, N, D, BK, a->dtype, xh, perm_q, perm_k, H, sws, st));
+  } else if (layout == SPARK_LAYOUT_Q_REUSE_K) {
+    // the same key side as REBLOCK (keys whitened by M_Q^{1/2}); the query
+    // moments are still needed for M_Q and the anchor, the key moments not
+    char* w = (char*)ws;
+    float* Ms = (float*)w;  w += up((size_t)2 * H * D * D * 4);
+    float* Ws = (float*)w;  w += up((size_t)2 * H * D * D * 4);
+    void* scr = w;          w += up(std::max(moments_ws_bytes(H, N, D), msqrt_ws_bytes(2 * H, D)));
+    void* xh = w;           w += up((size_t)2 * H * N * D * esize(a->dtype));
+    void* sws = w;
+    float* MQ = Ms;
+    CHECK(moments_launch(H, N, D, a->dtype, q, nullptr, MQ, nullptr, anchor, a->n_anchor, scr, st));
+    CHECK(msqrt_launch(H, D, MQ, Ws, (float*)scr, st));
+    CHECK(whiten_launch(H, N, D, a->dtype, k, Ws, xh, st));
+    CHECK(split_launch(H, N, D, BK, a->dtype, xh, perm_k, perm_k, H, sws, st));
+    CHECK(copy_perm_launch((long)H * N, perm_k, perm_q, st));
+    pq = perm_k;
   } else {
     if (layout == SPARK_LAYOUT_IDENTITY) {
       pq = nullptr;  // gather treats NULL as the identity

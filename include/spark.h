@@ -71,6 +71,7 @@ typedef enum spark_dtype { SPARK_F32 = 0, SPARK_BF16 = 1 } spark_dtype;
 #define SPARK_LAYOUT_REBLOCK 0x0u   /* Spark-Reblock partition ([blog] 01 / Method: Spark-Reblock) */
 #define SPARK_LAYOUT_IDENTITY 0x1u  /* consecutive tokens: the fixed-partition BSA baseline          */
 #define SPARK_LAYOUT_GIVEN 0x2u     /* perm_q / perm_k are inputs                                   */
+#define SPARK_LAYOUT_Q_REUSE_K 0x3u /* the key partition also groups the queries ([news] Workflows) */
 #define SPARK_LAYOUT_MASK 0x3u
 /* flags: compressed-branch estimator */
 #define SPARK_SUMMARY_REWEIGHT 0x0u /* Spark-Reweight ([blog] 02 / Method: Spark-Reweight)          */
@@ -141,8 +142,11 @@ size_t spark_workspace_bytes(const spark_args* args, int op, int32_t topk);
  *   representative query of [blog] 02 / Method: Spark-Reweight, one per head
  *   as in [news]).
  * flags & SPARK_LAYOUT_MASK: REBLOCK computes perm_q/perm_k (outputs);
- * IDENTITY writes perm = 0..N-1; GIVEN reads perm_q/perm_k (inputs, each a
- * permutation of 0..N-1 per head; not checked).
+ * Q_REUSE_K splits the keys only (whitened by M_Q^{1/2} as above; the
+ * reblock_layout=q_reuse_k setting of the [news] page's Workflows section)
+ * and writes that permutation to both perm_k and perm_q; IDENTITY writes
+ * perm = 0..N-1; GIVEN reads perm_q/perm_k (inputs, each a permutation of
+ * 0..N-1 per head; not checked).
  * q_p and anchor may be NULL (not written).  ws: spark_workspace_bytes(args,
  * SPARK_OP_REBLOCK, 0) bytes (0 for IDENTITY and GIVEN). */
 int spark_reblock(const spark_args* args, const void* q, const void* k, const void* v,

@@ -93,7 +93,7 @@ def test_null_misaligned_topk_and_workspace_errors(lib):
     rc = lib.spark_select(ctypes.byref(a), None, FAKE, None, 4, FAKE, None, None)
     assert rc == -1 and "qbar" in L.last_error()
     bad_flags = _args()
-    bad_flags.flags = 0x3
+    bad_flags.flags = 0x8
     rc = lib.spark_reblock(ctypes.byref(bad_flags), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
                            FAKE, None, FAKE, 1 << 40, None)
     assert rc == -1

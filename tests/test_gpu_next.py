@@ -12,6 +12,10 @@ those comparisons report.
 * Diagnostics, oracle intermediates injected: the per-query means of the
   GPU recall and log-mass error equal the oracle's attention_mass_recall and
   log_mass_error (relative 1e-4; the GPU accumulates in fp32).
+* q_reuse_k layout (the key partition groups the queries too): perm_q and
+  perm_k both equal, bit for bit, the key permutation of the full Reblock on
+  the same inputs, and the layer equals the layer run on that permutation
+  given explicitly.
 * The pages' two ablation directions, measured with the GPU path on the
   clustered draft workload (the model activations behind the pages' numbers
   are not available, so only the direction is checked): Reblock's recall is
@@ -182,3 +186,27 @@ def test_ablation_directions_on_clustered_draft():
         f"log-mass error: reweight {l_rw:.4f} vs mean {l_mean:.4f}")
     assert r_re >= r_id
     assert l_rw < l_mean
+
+
+@pytest.mark.parametrize("name", ["tiny_f32_ragged", "draft_bf16"])
+def test_q_reuse_k_layout(name):
+    q, k, v, dt, b, topk = _case(name)
+    H, N, d = q.shape
+    qd, kd, vd = dev(q, dt), dev(k, dt), dev(v, dt)
+    full = L.spark_reblock(qd, kd, vd, b)
+    rq = L.spark_reblock(qd, kd, vd, b, layout="q_reuse_k")
+    torch.cuda.synchronize()
+    pk = host(full["perm_k"])
+    assert np.array_equal(host(rq["perm_k"]), pk)
+    assert np.array_equal(host(rq["perm_q"]), pk)
+    np.testing.assert_array_equal(host(rq["anchor"]), host(full["anchor"]))
+    out = L.spark_layer(qd, kd, vd, b, topk, layout="q_reuse_k")
+    g = L.spark_reblock(qd, kd, vd, b, layout="given", perm_q=full["perm_k"], perm_k=full["perm_k"])
+    idx = L.spark_select(g["qbar"], g["kbar"], topk, N, b)
+    # the anchor of the moments pass (the GIVEN path sums it in another order)
+    ks, vs, bias = L.spark_summarize(g["k_p"], g["v_pt"], full["anchor"], N, b)
+    want = L.spark_attn(g["q_p"], g["k_p"], g["v_pt"], idx, ks, vs, bias, N, b, perm_q=g["perm_q"])
+    torch.cuda.synchronize()
+    say(f"[q_reuse_k] {name}: perms equal the full reblock's key side; layer max diff "
+        f"{float((out.float() - want.float()).abs().max()):.2e}")
+    assert torch.equal(out, want)
