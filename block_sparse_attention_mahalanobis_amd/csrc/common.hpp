@@ -116,6 +116,66 @@ __device__ __forceinline__ uint32_t wave_kth_key(const uint32_t* keys, int n, in
   return lo;
 }
 
+// k-th smallest (1-based) of n uint32 keys in LDS, found by ONE wave with a
+// private 256-int LDS histogram: 4 radix rounds of 8 bits (count the keys
+// that match the prefix so far, then pick the digit holding rank k).
+// Returns the key; *ties_needed = k - count(key < result).
+//
+// The hardware runs one wave's LDS instructions in issue order, but to the
+// compiler the other lanes' atomics race with the plain reads: without an
+// ordering point it may forward a lane's own zero store to its read of the
+// same bin (seen: lanes past n read empty bins).  wave_lds_sync() waits for
+// the wave's LDS operations and is a compiler memory barrier.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t wave_radix_kth(const uint32_t* keys, int n, int k, int* hist,
+                                                   int* ties_needed) {
+  const int lane = threadIdx.x & 63;
+  uint32_t prefix = 0;
+  int need = k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hist[4 * lane + j] = 0;
+    wave_lds_sync();
+    const uint32_t hmask = (shift == 24) ? 0u : (0xffffffffu << (shift + 8));
+    for (int i = lane; i < n; i += 64) {
+      const uint32_t key = keys[i];
+      if ((key & hmask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+    }
+    wave_lds_sync();
+    int c[4], run = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      run += hist[4 * lane + j];
+      c[j] = run;
+    }
+    wave_lds_sync();  // every lane has read its bins before the next round clears them
+    int incl = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    const int base = incl - run;
+    int found = -1, fb = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int before = base + (j ? c[j - 1] : 0);
+      if (before < need && base + c[j] >= need) {
+        found = 4 * lane + j;
+        fb = before;
+      }
+    }
+    const uint64_t m = __builtin_amdgcn_ballot_w64(found >= 0);
+    const int src = __builtin_ctzll(m);
+    const int digit = __builtin_amdgcn_readlane(found, src);
+    need -= __builtin_amdgcn_readlane(fb, src);
+    prefix |= (uint32_t)digit << shift;
+  }
+  *ties_needed = need;
+  return prefix;
+}
+
 // Same result for any n, reading the keys from LDS every round (slower).
 __device__ __forceinline__ uint32_t wave_kth_key_lds(const uint32_t* keys, int n, int k,
                                                      int* ties_needed) {

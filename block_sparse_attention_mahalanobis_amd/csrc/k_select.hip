@@ -30,6 +30,7 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(const float* __restrict__
                                                        int qb, float rsd) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint32_t* s_keys = reinterpret_cast<uint32_t*>(smem);  // [qb][nb]
+  __shared__ int s_whist[SEL_T / 64][256];                 // one radix histogram per wave
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nqb = (nb + qb - 1) / qb;
   const int h = blockIdx.x / nqb, A0 = (blockIdx.x % nqb) * qb;
@@ -82,16 +83,12 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(const float* __restrict__
   }
   __syncthreads();
 
-  // one wave per row: bisection for the threshold key, then ballot prefix
+  // one wave per row: radix select of the threshold key, then ballot prefix
   // sums emit the selected blocks in ascending order (no barriers)
   for (int q = wave; q < nq; q += SEL_T / 64) {
     const uint32_t* s_key = s_keys + q * nb;
     int ties_needed;
-    uint32_t thr;
-    if (nb <= 1024) thr = wave_kth_key<16>(s_key, nb, topk, &ties_needed);
-    else if (nb <= 2048) thr = wave_kth_key<32>(s_key, nb, topk, &ties_needed);
-    else if (nb <= 4096) thr = wave_kth_key<64>(s_key, nb, topk, &ties_needed);
-    else thr = wave_kth_key_lds(s_key, nb, topk, &ties_needed);
+    const uint32_t thr = wave_radix_kth(s_key, nb, topk, s_whist[wave], &ties_needed);
     int32_t* out = idx + ((long)h * nb + A0 + q) * topk;
     int taken = 0, ties_seen = 0;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));

@@ -373,10 +373,12 @@ __global__ __launch_bounds__(SPL_T) void select_partition(const float* __restric
                                                           int32_t* __restrict__ ids_out, int N,
                                                           int BK, int nb, int level) {
   __shared__ int s_hist[256];
+  __shared__ int s_whist[SPL_T / 64][256];  // one histogram per wave (less atomic contention)
   __shared__ int s_tmp[SPL_T / 64];
   __shared__ uint32_t s_prefix;
   __shared__ int s_need;
   const int slot = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+  const int wave = tid >> 6;
   int start, nbg;
   if (!group_of_slot(slot, level, nb, start, nbg)) return;
   const long g0 = (long)start * BK;
@@ -392,13 +394,31 @@ __global__ __launch_bounds__(SPL_T) void select_partition(const float* __restric
     s_need = cL;
   }
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += SPL_T) s_hist[i] = 0;
+    for (int i = tid; i < (SPL_T / 64) * 256; i += SPL_T) (&s_whist[0][0])[i] = 0;
     __syncthreads();
     const uint32_t pre = s_prefix;
     const uint32_t hmask = (shift == 24) ? 0u : (0xffffffffu << (shift + 8));
-    for (int i = tid; i < n; i += SPL_T) {
-      const uint32_t k = pref_key_desc(s[base + i]);
-      if ((k & hmask) == pre) atomicAdd(&s_hist[(k >> shift) & 255], 1);
+    constexpr int U = 8;  // independent loads in flight per thread
+    for (int i0 = 0; i0 < n; i0 += U * SPL_T) {
+      float v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * SPL_T + tid;
+        v[u] = (i < n) ? s[base + i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * SPL_T + tid;
+        const uint32_t k = pref_key_desc(v[u]);
+        if (i < n && (k & hmask) == pre) atomicAdd(&s_whist[wave][(k >> shift) & 255], 1);
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < 256; i += SPL_T) {
+      int c = 0;
+#pragma unroll
+      for (int w = 0; w < SPL_T / 64; ++w) c += s_whist[w][i];
+      s_hist[i] = c;
     }
     __syncthreads();
     if (tid < 64) radix_pick(s_hist, &s_prefix, &s_need, shift);
@@ -475,7 +495,7 @@ __global__ __launch_bounds__(FIN_T) void finisher(const T* __restrict__ xh,
   __shared__ int16_t s_lid[FIN_MAX];    // current local order (row indices)
   __shared__ int16_t s_tmp_lid[FIN_MAX];
   __shared__ float s_val[FIN_MAX];
-  __shared__ uint32_t s_keys[FIN_MAX];
+  __shared__ int s_hist[256];
   __shared__ float s_vec[D];
   __shared__ float s_part[NW][D];
   __shared__ uint64_t s_min[NW];
@@ -549,19 +569,32 @@ __global__ __launch_bounds__(FIN_T) void finisher(const T* __restrict__ xh,
     float vec[VE];
 #pragma unroll
     for (int e = 0; e < VE; ++e) vec[e] = s_vec[cc + e];
-    for (int i0 = 0; i0 < len; i0 += RPP) {
-      const int i = i0 + rslot;
-      float acc = 0.f;
-      int r = 0;
-      if (i < len) {
-        r = s_lid[a + i];
-        float v[VE];
-        Chunk<T>::load(sX + r * RS + cc, v);
+    // 4 row steps per iteration: index reads, then chunk reads, then math,
+    // so the LDS latencies overlap
+    constexpr int UR = 4;
+    for (int i0 = 0; i0 < len; i0 += UR * RPP) {
+      int rr[UR];
 #pragma unroll
-        for (int e = 0; e < VE; ++e) acc = fmaf(v[e], vec[e], acc);
+      for (int u = 0; u < UR; ++u) {
+        const int i = i0 + u * RPP + rslot;
+        rr[u] = (i < len) ? s_lid[a + i] : 0;
       }
-      acc = group_sum<CPR>(acc);
-      if (i < len && (tid % CPR) == 0) f(i, r, acc);
+      float v[UR][VE];
+#pragma unroll
+      for (int u = 0; u < UR; ++u) Chunk<T>::load(sX + rr[u] * RS + cc, v[u]);
+      float acc[UR];
+#pragma unroll
+      for (int u = 0; u < UR; ++u) {
+        acc[u] = 0.f;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[u] = fmaf(v[u][e], vec[e], acc[u]);
+        acc[u] = group_sum<CPR>(acc[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < UR; ++u) {
+        const int i = i0 + u * RPP + rslot;
+        if (i < len && (tid % CPR) == 0) f(i, rr[u], acc[u]);
+      }
     }
   };
   // argmin over [a, a+len) of (row . s_vec, original id) -> local row
@@ -609,11 +642,18 @@ __global__ __launch_bounds__(FIN_T) void finisher(const T* __restrict__ xh,
         float acc[VE];
 #pragma unroll
         for (int e = 0; e < VE; ++e) acc[e] = 0.f;
-        for (int i = rslot; i < len; i += RPP) {
-          float v[VE];
-          Chunk<T>::load(sX + s_lid[a + i] * RS + cc, v);
+        for (int i0 = rslot; i0 < len; i0 += 4 * RPP) {
+          int rr[4];
 #pragma unroll
-          for (int e = 0; e < VE; ++e) acc[e] += v[e];
+          for (int u = 0; u < 4; ++u) rr[u] = (i0 + u * RPP < len) ? s_lid[a + i0 + u * RPP] : -1;
+          float v[4][VE];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) Chunk<T>::load(sX + (rr[u] < 0 ? 0 : rr[u]) * RS + cc, v[u]);
+          // rows in a fixed order (u ascending), absent rows add nothing
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int e = 0; e < VE; ++e) acc[e] += (rr[u] < 0) ? 0.f : v[u][e];
         }
 #pragma unroll
         for (int e = 0; e < VE; ++e) acc[e] = group_sum<64, CPR>(acc[e]);
@@ -638,14 +678,25 @@ __global__ __launch_bounds__(FIN_T) void finisher(const T* __restrict__ xh,
       __syncthreads();
       rows_dot(a, len, [&](int i, int, float dv) { s_val[i] = dv; });
       __syncthreads();
-      // the cL-th key: wave 0 bisects over the keys in LDS
-      if (wave == 0) {
-        for (int i = lane; i < len; i += 64) s_keys[i] = pref_key_desc(s_val[i]);
-        int tn;
-        const uint32_t th = wave_kth_key<FIN_MAX / 64>(s_keys, len, cL, &tn);
-        if (lane == 0) { s_prefix = th; s_need = tn; }
+      // the cL-th key: radix select, 8 bits per round, all threads counting
+      // into an LDS histogram, wave 0 picking the digit
+      if (tid == 0) {
+        s_prefix = 0;
+        s_need = cL;
       }
-      __syncthreads();
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = tid; i < 256; i += FIN_T) s_hist[i] = 0;
+        __syncthreads();
+        const uint32_t pre = s_prefix;
+        const uint32_t hmask = (shift == 24) ? 0u : (0xffffffffu << (shift + 8));
+        for (int i = tid; i < len; i += FIN_T) {
+          const uint32_t k = pref_key_desc(s_val[i]);
+          if ((k & hmask) == pre) atomicAdd(&s_hist[(k >> shift) & 255], 1);
+        }
+        __syncthreads();
+        if (tid < 64) radix_pick(s_hist, &s_prefix, &s_need, shift);
+        __syncthreads();
+      }
       const uint32_t thr = s_prefix;
       const int ties_needed = s_need;
       // stable partition: E consecutive positions per thread (E <= 2)
