@@ -318,10 +318,12 @@ def main():
     rb_bytes = reblock_bytes(H, N, d, b, es, lev, nb, 1 if args.layout == "q_reuse_k" else 2)
     rb_ms = st_mean[0] + st_mean[2]
     csrc = os.path.join(ROOT, "block_sparse_attention_mahalanobis_amd", "csrc")
-    traffic = load_traffic("attn_full768_traffic.txt", [os.path.join(csrc, "k_attn.hip")],
+    traffic = load_traffic("attn_full768_traffic.txt",
+                           [os.path.join(csrc, f) for f in ("common.hpp", "k_attn.hip")],
                            "bytes_per_launch") if args.config == "full768" else None
     rb_traffic = load_traffic("reblock_full768_traffic.txt",
-                              [os.path.join(csrc, f) for f in ("k_whiten.hip", "k_split.hip", "k_gather_summ.hip")],
+                              [os.path.join(csrc, f) for f in ("common.hpp", "k_whiten.hip", "k_split.hip",
+                                                               "k_gather_summ.hip")],
                               "bytes_per_layer") if args.config == "full768" and args.layout == "reblock" else None
 
     base = None
