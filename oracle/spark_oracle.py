@@ -22,7 +22,8 @@ Sources ("the pages"):
   [readme] comfy.icu Spark-H3 package README, "Spark-Attn" section
           (reweighting gives different weights to tokens of each tail block).
   [news]  comfyui-wiki.com Spark-H3 news item, "What Spark-Attn changes"
-          (the mean video query serves as one anchor per head).
+          (the mean video query serves as one anchor per head),
+          "Workflows" (the example workflows' reblock_layout=q_reuse_k).
 
 Readings taken where the pages are silent:
   * split rule: two-pole capacity bisection (``split_group``);
@@ -36,7 +37,13 @@ Readings taken where the pages are silent:
   * bias anchors the mean exponential of the block and the summary keeps
     the BSA multiplicity |B| (the all-ones vector in K~_A);
   * anchor = mean of the first ``n_anchor`` raw queries (video tokens);
-  * moments are uncentred and use all N tokens.
+  * moments are uncentred and use all N tokens;
+  * context mode ([blog] Spark-Reblock: context/sink tokens stay exact and
+    lie outside the video-block Top-K budget): tokens [n_anchor, N) are
+    context tokens.  Only the video tokens are partitioned, pooled, scored,
+    selected and summarised; every video query also attends exactly to all
+    context keys; a context query's row is exact dense attention over all
+    N keys.
 
 Parity status: every function here is pinned by a ``-m "not gpu"`` test in
 tests/test_oracle_pins.py (closed forms, invariants, brute force, a
@@ -178,25 +185,29 @@ def split_partition(xhat: np.ndarray, b: int) -> np.ndarray:
     return np.concatenate(level)
 
 
-def reblock_head(q: np.ndarray, k: np.ndarray, b: int):
+def reblock_head(q: np.ndarray, k: np.ndarray, b: int, n_split: Optional[int] = None):
     """Query and key permutations of one head.  Queries are whitened by
     M_K^{1/2} (keys' second moment), keys by M_Q^{1/2}: the opposite side's
-    moment, as in the d_Q equation and its symmetric counterpart."""
+    moment, as in the d_Q equation and its symmetric counterpart.  The
+    moments use every row; only rows [0, n_split) (default: all) are
+    partitioned -- the video tokens, when the rest are context tokens."""
+    n = q.shape[0] if n_split is None else n_split
     MQ = second_moment(q)
     MK = second_moment(k)
     WQ = psd_sqrt(MK)
     WK = psd_sqrt(MQ)
-    perm_q = split_partition(whiten(q, WQ), b)
-    perm_k = split_partition(whiten(k, WK), b)
+    perm_q = split_partition(whiten(q[:n], WQ), b)
+    perm_k = split_partition(whiten(k[:n], WK), b)
     return perm_q, perm_k
 
 
-def reblock_keys(q: np.ndarray, k: np.ndarray, b: int):
+def reblock_keys(q: np.ndarray, k: np.ndarray, b: int, n_split: Optional[int] = None):
     """The key permutation alone (keys whitened by M_Q^{1/2}, split as in
     reblock_head).  The q_reuse_k layout ([news] Workflows: every example
     workflow of the release sets reblock_layout=q_reuse_k) groups the queries
     with this same key partition instead of splitting them separately."""
-    return split_partition(whiten(k, psd_sqrt(second_moment(q))), b)
+    n = k.shape[0] if n_split is None else n_split
+    return split_partition(whiten(k[:n], psd_sqrt(second_moment(q))), b)
 
 
 def gather_pool(x: np.ndarray, perm: np.ndarray, b: int):
@@ -296,12 +307,15 @@ def mean_summaries(kp: np.ndarray, vp: np.ndarray, b: int):
 # Two-branch attention ([blog] Spark-Reblock section, BSA(Q_A) equations)
 # ----------------------------------------------------------------------------
 
-def sparse_attention(qp, kp, vp, idx, ksum, vsum, bias, b: int, qblocks=None) -> np.ndarray:
+def sparse_attention(qp, kp, vp, idx, ksum, vsum, bias, b: int, qblocks=None,
+                     extra_k=None, extra_v=None) -> np.ndarray:
     """BSA(Q_A) = Softmax(Q_A K~_A^T / sqrt(d)) V~_A with one row-wise softmax
     over the concatenation, per key block B, of
         B in S_A : the exact rows K_B, V_B;
         B not in S_A : the summary k~_B, v~_B repeated |B| times (the
-                       all-ones vector), its logit shifted by beta_B.
+                       all-ones vector), its logit shifted by beta_B;
+    plus, when given, the rows of ``extra_k`` / ``extra_v`` exactly for
+    every query block (context/sink tokens: exact, outside the Top-K budget).
     The |B| identical summary rows are carried as one row of weight |B|.
     Returns the output in permuted order [N, d].  ``qblocks`` (optional)
     restricts the work to those query blocks; other rows stay 0."""
@@ -312,6 +326,12 @@ def sparse_attention(qp, kp, vp, idx, ksum, vsum, bias, b: int, qblocks=None) ->
     nb = n_blocks(N, b)
     sizes = block_sizes(N, b).astype(np.float64)
     rs = 1.0 / math.sqrt(d)
+    if extra_k is None:
+        xk = np.zeros((0, d))
+        xv = np.zeros((0, vp.shape[1]))
+    else:
+        xk = np.asarray(extra_k, np.float64)
+        xv = np.asarray(extra_v, np.float64)
     out = np.zeros((N, d))
     for A in (range(nb) if qblocks is None else qblocks):
         rows = slice(A * b, min(N, (A + 1) * b))
@@ -320,10 +340,10 @@ def sparse_attention(qp, kp, vp, idx, ksum, vsum, bias, b: int, qblocks=None) ->
         sel[np.asarray(idx[A], dtype=np.int64)] = True
         ex = np.concatenate([np.arange(B * b, min(N, (B + 1) * b)) for B in np.nonzero(sel)[0]])
         un = np.nonzero(~sel)[0]
-        logits = np.concatenate([QA @ kp[ex].T * rs,
+        logits = np.concatenate([QA @ kp[ex].T * rs, QA @ xk.T * rs,
                                  QA @ ksum[un].T * rs + bias[un][None, :]], axis=1)
-        weight = np.concatenate([np.ones(ex.shape[0]), sizes[un]])
-        vals = np.concatenate([vp[ex], vsum[un]], axis=0)
+        weight = np.concatenate([np.ones(ex.shape[0] + xk.shape[0]), sizes[un]])
+        vals = np.concatenate([vp[ex], xv, vsum[un]], axis=0)
         m = logits.max(axis=1, keepdims=True)
         p = np.exp(logits - m) * weight[None, :]
         out[rows] = (p @ vals) / p.sum(axis=1, keepdims=True)
@@ -361,38 +381,49 @@ class HeadResult:
     vsum: np.ndarray
     bias: np.ndarray
     out: np.ndarray       # original token order
+    n_video: int = -1     # context mode: rows [n_video, N) are context tokens
 
 
 def forward_head(q, k, v, b: int, topk: int, n_anchor: Optional[int] = None,
                  layout: str = "reblock", perm_q=None, perm_k=None,
-                 summary: str = "reweight", scores_in=None) -> HeadResult:
+                 summary: str = "reweight", scores_in=None,
+                 context: bool = False) -> HeadResult:
     """Reblock -> select -> summarise -> attend -> scatter, one head.
     layout: "reblock" (Spark-Reblock), "q_reuse_k" (the key partition reused
     for the queries), "identity" (consecutive blocks, the
     fixed-partition BSA baseline) or "given" (perm_q / perm_k supplied).
     summary: "reweight" (Spark-Reweight) or "mean" (BSA mean pooling).
-    scores_in: optional block scores to select from instead of q_bar.k_bar."""
+    scores_in: optional block scores to select from instead of q_bar.k_bar.
+    context: tokens [n_anchor, N) are context/sink tokens ([blog]
+    Spark-Reblock: they stay exact, outside the video-block Top-K budget):
+    blocks, scores, Top-K and summaries cover the video tokens only (topk
+    counts video blocks), every video query attends exactly to all context
+    keys, and each context query's row is dense attention over all N keys.
+    The permutations then fix the context tokens (perm[p] = p, p >= n_anchor);
+    qp / kp / vp and the block arrays hold the video tokens only."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     N = q.shape[0]
     n_anchor = N if n_anchor is None else n_anchor
+    nv = n_anchor if context else N
     if layout == "reblock":
-        perm_q, perm_k = reblock_head(q, k, b)
+        perm_q, perm_k = reblock_head(q, k, b, n_split=nv)
     elif layout == "q_reuse_k":
-        perm_k = reblock_keys(q, k, b)
+        perm_k = reblock_keys(q, k, b, n_split=nv)
         perm_q = perm_k.copy()
     elif layout == "identity":
-        perm_q = np.arange(N)
-        perm_k = np.arange(N)
+        perm_q = np.arange(nv)
+        perm_k = np.arange(nv)
     elif layout == "given":
-        perm_q = np.asarray(perm_q, np.int64)
-        perm_k = np.asarray(perm_k, np.int64)
+        perm_q = np.asarray(perm_q, np.int64)[:nv]
+        perm_k = np.asarray(perm_k, np.int64)[:nv]
     else:
         raise ValueError(layout)
-    qp, qbar = gather_pool(q, perm_q, b)
-    kp, kbar = gather_pool(k, perm_k, b)
-    vp = v[perm_k]
+    qv, kv, vv = q[:nv], k[:nv], v[:nv]
+    qp, qbar = gather_pool(qv, perm_q, b)
+    kp, kbar = gather_pool(kv, perm_k, b)
+    vp = vv[perm_k]
     S = block_scores(qbar, kbar) if scores_in is None else np.asarray(scores_in, np.float64)
     idx = select_topk(S, topk)
     qhat = anchor_query(q, n_anchor)
@@ -402,10 +433,17 @@ def forward_head(q, k, v, b: int, topk: int, n_anchor: Optional[int] = None,
         ks, vs, beta = mean_summaries(kp, vp, b)
     else:
         raise ValueError(summary)
-    op = sparse_attention(qp, kp, vp, idx, ks, vs, beta, b)
-    out = np.zeros_like(op)
+    op = sparse_attention(qp, kp, vp, idx, ks, vs, beta, b,
+                          extra_k=k[nv:] if nv < N else None, extra_v=v[nv:] if nv < N else None)
+    out = np.zeros((N, q.shape[1]))
     out[perm_q] = op
-    return HeadResult(perm_q, perm_k, qp, kp, vp, qbar, kbar, S, idx, qhat, ks, vs, beta, out)
+    if nv < N:
+        out[nv:] = dense_attention(q[nv:], k, v)
+        tail = np.arange(nv, N)
+        perm_q = np.concatenate([perm_q, tail])
+        perm_k = np.concatenate([perm_k, tail])
+    return HeadResult(perm_q, perm_k, qp, kp, vp, qbar, kbar, S, idx, qhat, ks, vs, beta, out,
+                      nv if context else -1)
 
 
 def forward(q, k, v, b: int, topk: int, n_anchor: Optional[int] = None, **kw):
@@ -420,7 +458,9 @@ def forward(q, k, v, b: int, topk: int, n_anchor: Optional[int] = None, **kw):
 
 def attention_mass_recall(res: HeadResult, b: int) -> float:
     """Mean over queries of the dense attention probability that falls in
-    the query block's selected key blocks."""
+    the query block's selected key blocks (plain layers only)."""
+    if res.n_video >= 0:
+        raise ValueError("diagnostics are defined for layers without context tokens")
     N, d = res.qp.shape
     nb = n_blocks(N, b)
     tot = 0.0
@@ -437,7 +477,10 @@ def attention_mass_recall(res: HeadResult, b: int) -> float:
 
 def log_mass_error(res: HeadResult, b: int) -> float:
     """Mean over queries of |log(sum over unselected tokens of exp(logit))
-    - log(sum over unselected blocks of |B| exp(compressed logit))|."""
+    - log(sum over unselected blocks of |B| exp(compressed logit))|
+    (plain layers only)."""
+    if res.n_video >= 0:
+        raise ValueError("diagnostics are defined for layers without context tokens")
     N, d = res.qp.shape
     nb = n_blocks(N, b)
     sizes = block_sizes(N, b).astype(np.float64)

@@ -426,3 +426,101 @@ def test_q_reuse_k_layout():
     pq2, pk2 = O.reblock_head(k, k, b)
     assert np.array_equal(pq2, pk2)
     assert np.array_equal(O.reblock_keys(k, k, b), pq2)
+
+
+# --- context / sink tokens ([blog] Spark-Reblock: context/sink tokens stay
+# --- exact and lie outside the video-block Top-K budget) ---------------------
+
+def _ctx_problem(seed, Nv, Nc, d):
+    rng = _rng(seed)
+    q = np.concatenate([_clustered(rng, Nv, d, 4, 0.4), 1.5 * rng.standard_normal((Nc, d))])
+    k = np.concatenate([_clustered(rng, Nv, d, 4, 0.4), 1.5 * rng.standard_normal((Nc, d))])
+    v = rng.standard_normal((Nv + Nc, d))
+    return rng, q, k, v
+
+
+@pytest.mark.parametrize("layout", ["reblock", "identity", "q_reuse_k"])
+def test_context_full_density_equals_dense_attention(layout):
+    """All video blocks selected: every row (video rows with the context keys
+    exact, context rows dense) is dense attention over all N tokens."""
+    Nv, Nc, d, b = 600, 70, 16, 64
+    _, q, k, v = _ctx_problem(30, Nv, Nc, d)
+    nb = O.n_blocks(Nv, b)
+    r = O.forward_head(q, k, v, b, nb, n_anchor=Nv, layout=layout, context=True)
+    np.testing.assert_allclose(r.out, _sdpa(q, k, v), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("summary", ["reweight", "mean"])
+@pytest.mark.parametrize("topk", [1, 3])
+def test_context_keys_exact_with_constant_key_blocks(summary, topk):
+    """Fixed blocks whose video keys are constant within each block make every
+    compressed term exact (block mass and value), so at any density every row
+    equals dense attention over all N tokens -- but only if every video row
+    also takes every context key exactly, once, in the same softmax, and the
+    context rows are dense.  The short last video block (44 rows) is included."""
+    Nv, Nc, d, b = 300, 50, 16, 64
+    rng, q, k, v = _ctx_problem(31, Nv, Nc, d)
+    for B in range(O.n_blocks(Nv, b)):
+        k[B * b:min(Nv, (B + 1) * b)] = k[B * b]
+    r = O.forward_head(q, k, v, b, topk, n_anchor=Nv, layout="identity", summary=summary,
+                       context=True)
+    np.testing.assert_allclose(r.out, _sdpa(q, k, v), rtol=0, atol=1e-12)
+    # the same problem without the context mode is not dense: the context
+    # tokens' own blocks are then compressed with non-constant keys
+    r0 = O.forward_head(q, k, v, b, topk, n_anchor=Nv, layout="identity", summary=summary)
+    assert np.abs(r0.out - _sdpa(q, k, v)).max() > 1e-3
+
+
+def test_context_layout_and_budget():
+    """Context tokens keep their positions (perm[p] = p for p >= n_anchor),
+    the video part is a bijection of the video ids with leaves of the block
+    size (the last one short), the Top-K budget counts video blocks only, the
+    context rows are dense, and with no context tokens the mode changes
+    nothing."""
+    Nv, Nc, d, b, topk = 600, 70, 16, 32, 3
+    _, q, k, v = _ctx_problem(32, Nv, Nc, d)
+    N = Nv + Nc
+    r = O.forward_head(q, k, v, b, topk, n_anchor=Nv, context=True)
+    for perm in (r.perm_q, r.perm_k):
+        assert np.array_equal(np.sort(perm[:Nv]), np.arange(Nv))
+        assert np.array_equal(perm[Nv:], np.arange(Nv, N))
+    nbv = O.n_blocks(Nv, b)
+    assert r.idx.shape == (nbv, topk) and r.idx.max() < nbv
+    assert r.qp.shape[0] == Nv and r.ksum.shape[0] == nbv
+    np.testing.assert_allclose(r.out[Nv:], _sdpa(q[Nv:], k, v), rtol=0, atol=1e-12)
+    a = O.forward_head(q, k, v, b, topk, n_anchor=N, context=True)
+    c = O.forward_head(q, k, v, b, topk, n_anchor=N)
+    np.testing.assert_array_equal(a.out, c.out)
+    np.testing.assert_array_equal(a.perm_q, c.perm_q)
+
+
+def test_context_moments_use_every_token():
+    """Video keys on the e1 axis and as many context keys on the e2 axis: the
+    key moment over all tokens is isotropic, so the video queries (unit
+    vectors at distinct angles in (-1.2, 1.2) rad, ids shuffled against the
+    angles) keep their angles, and the two-pole bisection of an arc cuts it
+    into runs of consecutive angles.  A moment over the video keys alone has
+    rank one and whitens every query to e1; the ties then break by id and
+    the leaves follow the ids instead."""
+    rng = _rng(33)
+    Nv = Nc = 16
+    b = 4
+    order = rng.permutation(Nv)                     # angle rank of video id i
+    theta = np.linspace(-1.2, 1.2, Nv)[order]
+    qv = np.stack([np.cos(theta), np.sin(theta)], axis=1)
+    sgn = np.where(np.arange(Nv) % 2 == 0, 1.0, -1.0)
+    kv = np.stack([sgn, np.zeros(Nv)], axis=1)
+    kc = np.stack([np.zeros(Nc), sgn], axis=1)
+    q = np.concatenate([qv, rng.standard_normal((Nc, 2))])
+    k = np.concatenate([kv, kc])
+    v = rng.standard_normal((Nv + Nc, 2))
+    np.testing.assert_allclose(O.second_moment(k), 0.5 * np.eye(2), atol=1e-15)
+
+    def runs_of_angles(perm):
+        return all(np.ptp(order[perm[B * b:(B + 1) * b]]) == b - 1 for B in range(Nv // b))
+
+    r = O.forward_head(q, k, v, b, 1, n_anchor=Nv, context=True)
+    assert runs_of_angles(r.perm_q[:Nv])
+    video_only = O.split_partition(O.whiten(qv, O.psd_sqrt(O.second_moment(kv))), b)
+    assert np.array_equal(video_only, np.arange(Nv))    # all ties: id order
+    assert not runs_of_angles(video_only)
