@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(HERE, "libspark.so")
 SPARK_F32, SPARK_BF16 = 0, 1
 LAYOUT_REBLOCK, LAYOUT_IDENTITY, LAYOUT_GIVEN, LAYOUT_Q_REUSE_K = 0x0, 0x1, 0x2, 0x3
 SUMMARY_REWEIGHT, SUMMARY_MEAN = 0x0, 0x4
+CONTEXT_EXACT = 0x8
 OP_REBLOCK, OP_SELECT, OP_SUMMARIZE, OP_ATTN, OP_SPLIT, OP_LAYER = range(6)
 _LAYOUTS = {"reblock": LAYOUT_REBLOCK, "identity": LAYOUT_IDENTITY, "given": LAYOUT_GIVEN,
             "q_reuse_k": LAYOUT_Q_REUSE_K}
@@ -119,14 +120,23 @@ def _dtype_code(dt: torch.dtype) -> int:
 
 
 def make_args(H: int, N: int, d: int, block: int, dtype, n_anchor: Optional[int] = None,
-              layout: str = "reblock", summary: str = "reweight") -> SparkArgs:
+              layout: str = "reblock", summary: str = "reweight", context: bool = False) -> SparkArgs:
     code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
     return SparkArgs(H, N, d, block, code, N if n_anchor is None else n_anchor,
-                     _LAYOUTS[layout] | _SUMMARIES[summary], 0)
+                     _LAYOUTS[layout] | _SUMMARIES[summary] | (CONTEXT_EXACT if context else 0), 0)
 
 
 def n_blocks(N: int, block: int) -> int:
     return -(-N // block)
+
+
+def geometry(N: int, block: int, n_anchor: Optional[int] = None, context: bool = False):
+    """(video tokens, video blocks, blocks of q_p / k_p / v_pt): with the
+    context mode the tokens from n_anchor on form extra blocks after the
+    video blocks; otherwise every token is a video token."""
+    nv = n_anchor if (context and n_anchor is not None) else N
+    nb = n_blocks(nv, block)
+    return nv, nb, nb + n_blocks(N - nv, block)
 
 
 def topk_from_ratio(ratio: float, nb: int) -> int:
@@ -151,15 +161,16 @@ def _ws(nbytes: int, device) -> torch.Tensor:
 # ---------------------------------------------------------------------------
 
 def spark_reblock(q, k, v, block: int, layout: str = "reblock", perm_q=None, perm_k=None,
-                  n_anchor: Optional[int] = None, want_q_p: bool = True):
+                  n_anchor: Optional[int] = None, want_q_p: bool = True, context: bool = False):
     """Reblock + gather + pool.  Returns a dict of device tensors: perm_q,
-    perm_k [H,N] int32, q_p, k_p [H,Np,d], v_pt [H,nb,d,block], qbar, kbar
-    [H,nb,d] fp32, anchor [H,d] fp32."""
+    perm_k [H,N] int32, q_p, k_p [H,Np,d], v_pt [H,nbt,d,block], qbar, kbar
+    [H,nb,d] fp32, anchor [H,d] fp32 (nb video blocks, nbt = nb + context
+    blocks, Np = nbt * block)."""
     H, N, d = q.shape
     dev = q.device
-    nb = n_blocks(N, block)
-    Np = nb * block
-    a = make_args(H, N, d, block, q.dtype, n_anchor, layout)
+    _, nb, nbt = geometry(N, block, n_anchor, context)
+    Np = nbt * block
+    a = make_args(H, N, d, block, q.dtype, n_anchor, layout, context=context)
     if layout == "given":
         perm_q = perm_q.to(device=dev, dtype=torch.int32).contiguous()
         perm_k = perm_k.to(device=dev, dtype=torch.int32).contiguous()
@@ -170,7 +181,7 @@ def spark_reblock(q, k, v, block: int, layout: str = "reblock", perm_q=None, per
         perm_q=perm_q, perm_k=perm_k,
         q_p=torch.empty((H, Np, d), dtype=q.dtype, device=dev) if want_q_p else None,
         k_p=torch.empty((H, Np, d), dtype=q.dtype, device=dev),
-        v_pt=torch.empty((H, nb, d, block), dtype=q.dtype, device=dev),
+        v_pt=torch.empty((H, nbt, d, block), dtype=q.dtype, device=dev),
         qbar=torch.empty((H, nb, d), dtype=torch.float32, device=dev),
         kbar=torch.empty((H, nb, d), dtype=torch.float32, device=dev),
         anchor=torch.empty((H, d), dtype=torch.float32, device=dev),
@@ -185,13 +196,13 @@ def spark_reblock(q, k, v, block: int, layout: str = "reblock", perm_q=None, per
 
 
 def spark_select(qbar, kbar, topk: int, N: int, block: int, scores_in=None, want_scores=False,
-                 dtype=torch.bfloat16):
+                 dtype=torch.bfloat16, n_anchor: Optional[int] = None, context: bool = False):
     """idx [H, nb, topk] int32 (ascending) and, if asked, the scores used."""
     ref = qbar if qbar is not None else scores_in
     H = ref.shape[0]
     d = qbar.shape[2] if qbar is not None else 128
-    nb = n_blocks(N, block)
-    a = make_args(H, N, d, block, dtype)
+    _, nb, _ = geometry(N, block, n_anchor, context)
+    a = make_args(H, N, d, block, dtype, n_anchor, context=context)
     idx = torch.empty((H, nb, topk), dtype=torch.int32, device=ref.device)
     sc = torch.empty((H, nb, nb), dtype=torch.float32, device=ref.device) if want_scores else None
     _check(lib().spark_select(ctypes.byref(a), _ptr(qbar), _ptr(kbar), _ptr(scores_in), topk, _ptr(idx),
@@ -199,11 +210,12 @@ def spark_select(qbar, kbar, topk: int, N: int, block: int, scores_in=None, want
     return (idx, sc) if want_scores else idx
 
 
-def spark_summarize(k_p, v_pt, anchor, N: int, block: int, summary: str = "reweight"):
+def spark_summarize(k_p, v_pt, anchor, N: int, block: int, summary: str = "reweight",
+                    n_anchor: Optional[int] = None, context: bool = False):
     """ksum, vsum [H, nb, d] fp32 and bias [H, nb] fp32."""
     H, _, d = k_p.shape
-    nb = n_blocks(N, block)
-    a = make_args(H, N, d, block, k_p.dtype, summary=summary)
+    _, nb, _ = geometry(N, block, n_anchor, context)
+    a = make_args(H, N, d, block, k_p.dtype, n_anchor, summary=summary, context=context)
     dev = k_p.device
     ksum = torch.empty((H, nb, d), dtype=torch.float32, device=dev)
     vsum = torch.empty((H, nb, d), dtype=torch.float32, device=dev)
@@ -214,12 +226,12 @@ def spark_summarize(k_p, v_pt, anchor, N: int, block: int, summary: str = "rewei
 
 
 def spark_attn(q_p, k_p, v_pt, idx, ksum, vsum, bias, N: int, block: int, perm_q=None, out=None,
-               ws=None):
+               ws=None, n_anchor: Optional[int] = None, context: bool = False):
     """Fused two-branch attention; [H, N, d] in original order if perm_q is
     given, else [H, Np, d] in permuted order."""
     H, Np, d = q_p.shape
     topk = idx.shape[2]
-    a = make_args(H, N, d, block, q_p.dtype)
+    a = make_args(H, N, d, block, q_p.dtype, n_anchor, context=context)
     dev = q_p.device
     if out is None:
         out = torch.empty((H, N if perm_q is not None else Np, d), dtype=q_p.dtype, device=dev)
@@ -247,10 +259,10 @@ def spark_diagnostics(q_p, k_p, idx, ksum, bias, N: int, block: int):
 
 
 def spark_layer(q, k, v, block: int, topk: int, layout: str = "reblock", summary: str = "reweight",
-                n_anchor: Optional[int] = None, out=None, ws=None):
+                n_anchor: Optional[int] = None, out=None, ws=None, context: bool = False):
     """The whole layer in one call; intermediates live in the workspace."""
     H, N, d = q.shape
-    a = make_args(H, N, d, block, q.dtype, n_anchor, layout, summary)
+    a = make_args(H, N, d, block, q.dtype, n_anchor, layout, summary, context)
     nws = workspace_bytes(a, OP_LAYER, topk)
     if ws is None:
         ws = _ws(nws, q.device)

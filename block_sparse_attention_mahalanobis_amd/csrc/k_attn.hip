@@ -18,9 +18,55 @@
 //  * attn_generic: fp32 or bf16, any block size 1..128; one thread per query
 //    row, fp32 VALU arithmetic.  Small and slow; it exists for the fp32
 //    workloads and odd block sizes.
+//
+// Context/sink tokens (01 / Method: Spark-Reblock: they stay exact, outside
+// the video-block Top-K budget): with Nv < N video tokens, q_p / k_p / v_pt
+// hold nb video blocks followed by nbc context blocks (nbt = nb + nbc).  A
+// video query block's exact tiles are its topk selected blocks and then the
+// nbc context blocks, followed by the compressed tiles; a context query block
+// attends exactly to all nbt blocks and has no compressed branch.  With
+// nbc = 0 this is the plain layer.
 #include "common.hpp"
 
 namespace spark {
+
+// Tiles of one (head, query block A) workgroup: exact tiles [0, nex) --
+// tile t < nidx is key block idx[t], tile t >= nidx is block t + bofs --
+// then nct compressed tiles.
+struct TilePlan {
+  int nidx, nex, bofs, nct;
+};
+__device__ __forceinline__ TilePlan tile_plan(int A, int nb, int nbc, int topk, int nct_all) {
+  TilePlan p;
+  if (A < nb) {
+    p.nidx = topk;
+    p.nex = topk + nbc;
+    p.bofs = nb - topk;
+    p.nct = (topk < nb) ? nct_all : 0;
+  } else {
+    p.nidx = 0;
+    p.nex = nb + nbc;
+    p.bofs = 0;
+    p.nct = 0;
+  }
+  return p;
+}
+
+// Real rows of key block B (the last video block and the last context block
+// may be short).
+__device__ __forceinline__ int block_rows(int B, int nb, int nbt, int N, int Nv, int BK) {
+  if (B == nb - 1) return Nv - (nb - 1) * BK;
+  if (B == nbt - 1) return N - Nv - (nbt - nb - 1) * BK;
+  return BK;
+}
+
+// Output row of query row r of block A: its position in the unpadded
+// permuted order (video rows [0, Nv), then the context rows), or -1 for a
+// padding row.  Context rows keep their original position.
+__device__ __forceinline__ long out_pos(int A, int r, int nb, int N, int Nv, int BK) {
+  const long p = (A < nb) ? (long)A * BK + r : (long)Nv + (long)(A - nb) * BK + r;
+  return p < ((A < nb) ? Nv : N) ? p : -1;
+}
 
 // ---------------------------------------------------------------------------
 // Compressed-branch operands in the layout the MFMA kernel streams:
@@ -94,7 +140,7 @@ __global__ __launch_bounds__(2 * BK) void attn_mfma(
     const uint16_t* __restrict__ vpt, const int32_t* __restrict__ idx, int topk,
     const uint16_t* __restrict__ ks16, const uint16_t* __restrict__ vs16t,
     const float* __restrict__ bias2, const int32_t* __restrict__ perm_q,
-    uint16_t* __restrict__ out, int H, int N, int nb, int nbp, float scale_log2) {
+    uint16_t* __restrict__ out, int H, int N, int Nv, int nb, int nbc, int nbp, float scale_log2) {
   using C = MfmaCfg<D, BK>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* sK = reinterpret_cast<uint16_t*>(smem);
@@ -105,17 +151,20 @@ __global__ __launch_bounds__(2 * BK) void attn_mfma(
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = logical / nb, A = logical % nb;
-  const long Np = (long)nb * BK;
-  const int nct = (topk < nb) ? nbp / BK : 0;   // compressed tiles
-  const int ntiles = topk + nct;
-  const int32_t* myidx = idx + ((long)h * nb + A) * topk;
+  const int nbt = nb + nbc;
+  const int h = logical / nbt, Ar = logical % nbt;
+  const int A = (Ar < nbc) ? nb + Ar : Ar - nbc;   // context query blocks first
+  const long Np = (long)nbt * BK;
+  const TilePlan tp = tile_plan(A, nb, nbc, topk, nbp / BK);
+  const int nct = tp.nct;
+  const int ntiles = tp.nex + nct;
+  const int32_t* myidx = (A < nb) ? idx + ((long)h * nb + A) * topk : idx;
 
   // --- summaries' bias in LDS, selected blocks masked --------------------
   if (nct > 0) {
     for (int i = tid; i < nbp; i += C::NT) sBias[i] = bias2[(long)h * nbp + i];
     __syncthreads();
-    for (int t = tid; t < topk; t += C::NT) sBias[myidx[t]] = -INFINITY;
+    for (int t = tid; t < tp.nidx; t += C::NT) sBias[myidx[t]] = -INFINITY;
   }
 
   // --- Q operand (B of S^T = K Q^T): row l32 of this wave, d = 16s+8hf.. --
@@ -133,14 +182,15 @@ __global__ __launch_bounds__(2 * BK) void attn_mfma(
   float m_run = -1e30f, l_run = 0.f;
 
   // --- tile source addresses ----------------------------------------------
-  // exact tile t < topk: key block idx[t]; compressed tile: summaries t - topk
+  // exact tile t < tp.nex: key block B (see TilePlan); compressed tile:
+  // summaries t - tp.nex
 #define SPARK_TILE_SRC(t, ksrc, vsrc)                                        \
-  if ((t) < topk) {                                                          \
-    const int B_ = myidx[(t)];                                               \
+  if ((t) < tp.nex) {                                                        \
+    const int B_ = ((t) < tp.nidx) ? myidx[(t)] : (t) + tp.bofs;             \
     ksrc = kp + ((long)h * Np + (long)B_ * BK) * D;                          \
-    vsrc = vpt + ((long)h * nb + B_) * (long)D * BK;                         \
+    vsrc = vpt + ((long)h * nbt + B_) * (long)D * BK;                        \
   } else {                                                                   \
-    const int c_ = (t) - topk;                                               \
+    const int c_ = (t) - tp.nex;                                             \
     ksrc = ks16 + ((long)h * nbp + (long)c_ * BK) * D;                       \
     vsrc = vs16t + ((long)h * (nbp / BK) + c_) * (long)D * BK;               \
   }
@@ -181,9 +231,9 @@ __global__ __launch_bounds__(2 * BK) void attn_mfma(
 
     // logits in the log2 domain; key of (jt, v) is 32jt + (v<8 ? 8hf+v : 16+8hf+v-8)
     float mx = -INFINITY;
-    if (t < topk) {
-      const int B = myidx[t];
-      const int valid = (B == nb - 1) ? (N - (nb - 1) * BK) : BK;
+    if (t < tp.nex) {
+      const int B = (t < tp.nidx) ? myidx[t] : t + tp.bofs;
+      const int valid = block_rows(B, nb, nbt, N, Nv, BK);
 #pragma unroll
       for (int jt = 0; jt < BK / 32; ++jt)
 #pragma unroll
@@ -197,7 +247,7 @@ __global__ __launch_bounds__(2 * BK) void attn_mfma(
           mx = fmaxf(mx, s2);
         }
     } else {
-      const float* bb = sBias + (t - topk) * BK;
+      const float* bb = sBias + (t - tp.nex) * BK;
 #pragma unroll
       for (int jt = 0; jt < BK / 32; ++jt)
 #pragma unroll
@@ -245,15 +295,15 @@ __global__ __launch_bounds__(2 * BK) void attn_mfma(
   // --- epilogue: normalise and scatter back to the original token order ----
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.f / l_tot;
-  const long prow = (long)A * BK + wave * 32 + l32;  // permuted row
+  const long pos = out_pos(A, wave * 32 + l32, nb, N, Nv, BK);
   uint16_t* dst;
   if (perm_q != nullptr) {
-    if (prow >= N) return;
-    dst = out + ((long)h * N + perm_q[(long)h * N + prow]) * D;
+    if (pos < 0) return;
+    dst = out + ((long)h * N + ((A < nb) ? perm_q[(long)h * N + pos] : pos)) * D;
   } else {
-    dst = out + ((long)h * Np + prow) * D;
+    dst = out + ((long)h * Np + (long)A * BK + wave * 32 + l32) * D;
   }
-  const bool pad = prow >= N;
+  const bool pad = pos < 0;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -279,15 +329,29 @@ __device__ __forceinline__ int sw_off(int row, int lc) {  // byte offset in a 12
   return row * 256 + ((lc ^ (row & 15)) << 4);
 }
 
-// Head-major order with each head's query blocks split into 8 contiguous
-// ranges, one per XCD: every XCD works on the same head at the same time
-// (that head's K/V stays in the shared last-level cache), and each XCD walks
-// tree-adjacent query blocks (similar selections, L2 reuse).
-__device__ __forceinline__ bool d128_map(int bid, int nb, int& h, int& A) {
-  const int nb8 = (nb + 7) & ~7;
-  h = bid / nb8;
-  const int r = bid - h * nb8;
-  A = (r & 7) * (nb8 >> 3) + (r >> 3);
+// Head-major order with each head's video query blocks split into 8
+// contiguous ranges, one per XCD (workgroup bid runs on XCD bid % 8): every
+// XCD works on the same head at the same time (that head's K/V stays in the
+// shared last-level cache), and each XCD walks tree-adjacent query blocks
+// (similar selections, L2 reuse).  Context query blocks, which attend to
+// every block and so run ~nbt/(topk+nbc) times longer, are dealt round-robin
+// over the XCDs and placed first in each XCD's share of the head, so they
+// start early and the short blocks fill in behind them.
+__device__ __forceinline__ int d128_slots(int nb, int nbc) {  // workgroups per head
+  return 8 * (((nbc + 7) >> 3) + ((nb + 7) >> 3));
+}
+__device__ __forceinline__ bool d128_map(int bid, int nb, int nbc, int& h, int& A) {
+  const int cpx = (nbc + 7) >> 3, vpx = (nb + 7) >> 3;
+  const int R = 8 * (cpx + vpx);
+  h = bid / R;
+  const int r = bid - h * R;
+  const int x = r & 7, j = r >> 3;
+  if (j < cpx) {
+    const int c = j * 8 + x;
+    A = nb + c;
+    return c < nbc;
+  }
+  A = x * vpx + (j - cpx);
   return A < nb;
 }
 
@@ -324,7 +388,7 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
     const uint16_t* __restrict__ vpt, const int32_t* __restrict__ idx, int topk,
     const uint16_t* __restrict__ ks16, const uint16_t* __restrict__ vs16t,
     const float* __restrict__ bias2, const int32_t* __restrict__ perm_q,
-    uint16_t* __restrict__ out, int H, int N, int nb, int nbp, float scale_log2) {
+    uint16_t* __restrict__ out, int H, int N, int Nv, int nb, int nbc, int nbp, float scale_log2) {
   constexpr int D = 128, BK = 128;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   unsigned char* sK = smem;
@@ -332,19 +396,21 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
   float* sBias = reinterpret_cast<float*>(smem + D128_LDS_TILES);
 
   int h, A;
-  if (!d128_map(blockIdx.x, nb, h, A)) return;
+  if (!d128_map(blockIdx.x, nb, nbc, h, A)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
-  const long Np = (long)nb * BK;
-  const int nct = (topk < nb) ? nbp / BK : 0;
-  const int ntiles = topk + nct;
-  const int32_t* myidx = idx + ((long)h * nb + A) * topk;
+  const int nbt = nb + nbc;
+  const long Np = (long)nbt * BK;
+  const TilePlan tp = tile_plan(A, nb, nbc, topk, nbp / BK);
+  const int nct = tp.nct;
+  const int ntiles = tp.nex + nct;
+  const int32_t* myidx = (A < nb) ? idx + ((long)h * nb + A) * topk : idx;
 
   if (nct > 0) {
     for (int i = tid; i < nbp; i += D128_NT) sBias[i] = bias2[(long)h * nbp + i];
     __syncthreads();
-    for (int t = tid; t < topk; t += D128_NT) sBias[myidx[t]] = -INFINITY;
+    for (int t = tid; t < tp.nidx; t += D128_NT) sBias[myidx[t]] = -INFINITY;
   }
 
   // per-lane byte offsets (loop invariant) of this wave's 8 direct loads per
@@ -363,12 +429,12 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
     voff[i] = (uint32_t)(srow * BK + lc * 8) * 2u;
   }
   auto tile_base = [&](int t, const char*& kb, const char*& vb) {
-    if (t < topk) {
-      const int B = myidx[t];
+    if (t < tp.nex) {
+      const int B = (t < tp.nidx) ? myidx[t] : t + tp.bofs;
       kb = reinterpret_cast<const char*>(kp + ((long)h * Np + (long)B * BK) * D);
-      vb = reinterpret_cast<const char*>(vpt + ((long)h * nb + B) * (long)D * BK);
+      vb = reinterpret_cast<const char*>(vpt + ((long)h * nbt + B) * (long)D * BK);
     } else {
-      const int c = t - topk;
+      const int c = t - tp.nex;
       kb = reinterpret_cast<const char*>(ks16 + ((long)h * nbp + (long)c * BK) * D);
       vb = reinterpret_cast<const char*>(vs16t + ((long)h * (nbp / BK) + c) * (long)D * BK);
     }
@@ -412,7 +478,7 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
   }
 
   for (int t = 0; t < ntiles; ++t) {
-    const bool exact = t < topk;
+    const bool exact = t < tp.nex;
     // K(t) landed (V(t) may still be in flight)
     asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     __syncthreads();
@@ -451,8 +517,8 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
 
     float mx;
     if (exact) {
-      const int B = myidx[t];
-      const int valid = (B == nb - 1) ? (N - (nb - 1) * BK) : BK;
+      const int B = (t < tp.nidx) ? myidx[t] : t + tp.bofs;
+      const int valid = block_rows(B, nb, nbt, N, Nv, BK);
       if (valid < BK) {
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt)
@@ -469,7 +535,7 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
         for (int v = 0; v < 16; ++v) mr = fmaxf(mr, sacc[jt][v]);
       mx = mr * scale_log2;
     } else {
-      const float* bb = sBias + (t - topk) * BK;
+      const float* bb = sBias + (t - tp.nex) * BK;
       mx = -INFINITY;
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt)
@@ -545,15 +611,15 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.f / l_tot;
-  const long prow = (long)A * BK + wave * 32 + l32;
+  const long pos = out_pos(A, wave * 32 + l32, nb, N, Nv, BK);
   uint16_t* dst;
   if (perm_q != nullptr) {
-    if (prow >= N) return;
-    dst = out + ((long)h * N + perm_q[(long)h * N + prow]) * D;
+    if (pos < 0) return;
+    dst = out + ((long)h * N + ((A < nb) ? perm_q[(long)h * N + pos] : pos)) * D;
   } else {
-    dst = out + ((long)h * Np + prow) * D;
+    dst = out + ((long)h * Np + (long)A * BK + wave * 32 + l32) * D;
   }
-  const bool pad = prow >= N;
+  const bool pad = pos < 0;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -578,28 +644,31 @@ __global__ __launch_bounds__(128) void attn_generic(
     const T* __restrict__ qp, const T* __restrict__ kp, const T* __restrict__ vpt,
     const int32_t* __restrict__ idx, int topk, const float* __restrict__ ksum,
     const float* __restrict__ vsum, const float* __restrict__ bias,
-    const int32_t* __restrict__ perm_q, T* __restrict__ out, int H, int N, int BK, int nb,
-    float scale) {
+    const int32_t* __restrict__ perm_q, T* __restrict__ out, int H, int N, int Nv, int BK, int nb,
+    int nbc, float scale) {
   __shared__ float sK[GEN_CH][D];
   __shared__ float sV[GEN_CH][D];
   __shared__ float sB[GEN_CH];
   extern __shared__ unsigned char smask[];  // nb bytes: 1 = selected
 
   const int tid = threadIdx.x;
-  const int h = blockIdx.x / nb, A = blockIdx.x % nb;
-  const long Np = (long)nb * BK;
-  const int32_t* myidx = idx + ((long)h * nb + A) * topk;
+  const int nbt = nb + nbc;
+  const int h = blockIdx.x / nbt, Ar = blockIdx.x % nbt;
+  const int A = (Ar < nbc) ? nb + Ar : Ar - nbc;   // context query blocks first
+  const long Np = (long)nbt * BK;
+  const TilePlan tp = tile_plan(A, nb, nbc, topk, 1);
+  const int32_t* myidx = (A < nb) ? idx + ((long)h * nb + A) * topk : idx;
   for (int i = tid; i < nb; i += blockDim.x) smask[i] = 0;
   __syncthreads();
-  for (int t = tid; t < topk; t += blockDim.x) smask[myidx[t]] = 1;
+  for (int t = tid; t < tp.nidx; t += blockDim.x) smask[myidx[t]] = 1;
   __syncthreads();
 
-  const long prow = (long)A * BK + tid;
+  const long qrow = (long)A * BK + tid;   // row in the padded layout of q_p
   const bool active = tid < BK;
   float q[D], o[D];
 #pragma unroll
   for (int c = 0; c < D; ++c) {
-    q[c] = active ? Elem<T>::load(qp + ((long)h * Np + prow) * D + c) : 0.f;
+    q[c] = active ? Elem<T>::load(qp + ((long)h * Np + qrow) * D + c) : 0.f;
     o[c] = 0.f;
   }
   float m_run = -1e30f, l_run = 0.f;
@@ -630,10 +699,11 @@ __global__ __launch_bounds__(128) void attn_generic(
     }
   };
 
-  // exact branch
-  for (int t = 0; t < topk; ++t) {
-    const int B = myidx[t];
-    const int valid = (B == nb - 1) ? (N - (nb - 1) * BK) : BK;
+  // exact branch: selected blocks, then the context blocks (video query
+  // blocks); every block (context query blocks)
+  for (int t = 0; t < tp.nex; ++t) {
+    const int B = (t < tp.nidx) ? myidx[t] : t + tp.bofs;
+    const int valid = block_rows(B, nb, nbt, N, Nv, BK);
     for (int j0 = 0; j0 < valid; j0 += GEN_CH) {
       const int cnt = min(GEN_CH, valid - j0);
       __syncthreads();
@@ -642,7 +712,7 @@ __global__ __launch_bounds__(128) void attn_generic(
         float kv = 0.f, vv = 0.f;
         if (j < cnt) {
           kv = Elem<T>::load(kp + ((long)h * Np + (long)B * BK + j0 + j) * D + c);
-          vv = Elem<T>::load(vpt + (((long)h * nb + B) * D + c) * BK + j0 + j);
+          vv = Elem<T>::load(vpt + (((long)h * nbt + B) * D + c) * BK + j0 + j);
         }
         sK[j][c] = kv;
         sV[j][c] = vv;
@@ -652,8 +722,9 @@ __global__ __launch_bounds__(128) void attn_generic(
       consume(cnt);
     }
   }
-  // compressed branch: every unselected block, weight |B| through log|B|
-  for (int B0 = 0; B0 < nb; B0 += GEN_CH) {
+  // compressed branch: every unselected video block, weight |B| through
+  // log|B| (none for a context query block)
+  for (int B0 = 0; B0 < (A < nb ? nb : 0); B0 += GEN_CH) {
     const int cnt = min(GEN_CH, nb - B0);
     __syncthreads();
     for (int e = tid; e < GEN_CH * D; e += blockDim.x) {
@@ -665,7 +736,7 @@ __global__ __launch_bounds__(128) void attn_generic(
       const int B = B0 + j;
       float bb = -INFINITY;
       if (j < cnt && !smask[B]) {
-        const int nB = (B == nb - 1) ? (N - (nb - 1) * BK) : BK;
+        const int nB = (B == nb - 1) ? (Nv - (nb - 1) * BK) : BK;
         bb = bias[(long)h * nb + B] + logf((float)nB);
       }
       sB[j] = bb;
@@ -676,14 +747,15 @@ __global__ __launch_bounds__(128) void attn_generic(
 
   if (!active) return;
   const float inv = 1.f / l_run;
+  const long pos = out_pos(A, tid, nb, N, Nv, BK);
   T* dst;
   if (perm_q != nullptr) {
-    if (prow >= N) return;
-    dst = out + ((long)h * N + perm_q[(long)h * N + prow]) * D;
+    if (pos < 0) return;
+    dst = out + ((long)h * N + ((A < nb) ? perm_q[(long)h * N + pos] : pos)) * D;
   } else {
-    dst = out + ((long)h * Np + prow) * D;
+    dst = out + ((long)h * Np + qrow) * D;
   }
-  const bool pad = prow >= N;
+  const bool pad = pos < 0;
 #pragma unroll
   for (int c = 0; c < D; ++c) Elem<T>::store(dst + c, pad ? 0.f : o[c] * inv);
 }
@@ -691,6 +763,7 @@ __global__ __launch_bounds__(128) void attn_generic(
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
+// N here is the number of video tokens (all tokens without context).
 size_t attn_ws_bytes(int H, int N, int D, int BK, int dtype) {
   if (dtype != SPARK_BF16 || (BK != 32 && BK != 64 && BK != 128)) return 0;
   const int nb = cdiv(N, BK);
@@ -709,8 +782,8 @@ bool attn_uses_mfma(int dtype, int BK) {
 template <int D, int BK>
 static int launch_mfma(const void* qp, const void* kp, const void* vpt, const int32_t* idx,
                        int topk, const uint16_t* ks16, const uint16_t* vs16t, const float* bias2,
-                       const int32_t* perm_q, void* out, int H, int N, int nb, int nbp,
-                       hipStream_t st) {
+                       const int32_t* perm_q, void* out, int H, int N, int Nv, int nb, int nbc,
+                       int nbp, hipStream_t st) {
   using C = MfmaCfg<D, BK>;
   const size_t lds = C::LDS_TILES + (size_t)nbp * 4;
   if (lds > 160 * 1024)
@@ -723,16 +796,16 @@ static int launch_mfma(const void* qp, const void* kp, const void* vpt, const in
     attr_set = true;
   }
   const float scale_log2 = kLog2e / sqrtf((float)D);
-  hipLaunchKernelGGL((attn_mfma<D, BK>), dim3(H * nb), dim3(C::NT), lds, st,
+  hipLaunchKernelGGL((attn_mfma<D, BK>), dim3(H * (nb + nbc)), dim3(C::NT), lds, st,
                      (const uint16_t*)qp, (const uint16_t*)kp, (const uint16_t*)vpt, idx, topk,
-                     ks16, vs16t, bias2, perm_q, (uint16_t*)out, H, N, nb, nbp, scale_log2);
+                     ks16, vs16t, bias2, perm_q, (uint16_t*)out, H, N, Nv, nb, nbc, nbp, scale_log2);
   return spark_check_launch("attn_mfma");
 }
 
 static int launch_d128(const void* qp, const void* kp, const void* vpt, const int32_t* idx, int topk,
                      const uint16_t* ks16, const uint16_t* vs16t, const float* bias2,
-                     const int32_t* perm_q, void* out, int H, int N, int nb, int nbp,
-                     hipStream_t st) {
+                     const int32_t* perm_q, void* out, int H, int N, int Nv, int nb, int nbc,
+                     int nbp, hipStream_t st) {
   const size_t lds = D128_LDS_TILES + (size_t)nbp * 4;
   static bool attr_set = false;
   if (!attr_set) {
@@ -741,32 +814,34 @@ static int launch_d128(const void* qp, const void* kp, const void* vpt, const in
     attr_set = true;
   }
   const float scale_log2 = kLog2e / sqrtf(128.f);
-  const int nb8 = (nb + 7) & ~7;
-  hipLaunchKernelGGL(attn_mfma_d128, dim3(H * nb8), dim3(D128_NT), lds, st, (const uint16_t*)qp,
+  const long slots = 8L * (((nbc + 7) >> 3) + ((nb + 7) >> 3));   // d128_slots
+  if ((long)H * slots > 0x7fffffffL) return spark_set_error(SPARK_E_SHAPE, "spark_attn: grid too large");
+  hipLaunchKernelGGL(attn_mfma_d128, dim3((unsigned)(H * slots)), dim3(D128_NT), lds, st, (const uint16_t*)qp,
                      (const uint16_t*)kp, (const uint16_t*)vpt, idx, topk, ks16, vs16t, bias2,
-                     perm_q, (uint16_t*)out, H, N, nb, nbp, scale_log2);
+                     perm_q, (uint16_t*)out, H, N, Nv, nb, nbc, nbp, scale_log2);
   return spark_check_launch("attn_mfma_d128");
 }
 
 template <typename T, int D>
 static int launch_generic(const void* qp, const void* kp, const void* vpt, const int32_t* idx,
                           int topk, const float* ksum, const float* vsum, const float* bias,
-                          const int32_t* perm_q, void* out, int H, int N, int BK, int nb,
-                          hipStream_t st) {
+                          const int32_t* perm_q, void* out, int H, int N, int Nv, int BK, int nb,
+                          int nbc, hipStream_t st) {
   if (nb > 64 * 1024)
     return spark_set_error(SPARK_E_SHAPE, "spark_attn: too many blocks (%d) for the generic kernel", nb);
   const float scale = 1.f / sqrtf((float)D);
-  hipLaunchKernelGGL((attn_generic<T, D>), dim3(H * nb), dim3(128), (size_t)nb, st,
+  hipLaunchKernelGGL((attn_generic<T, D>), dim3(H * (nb + nbc)), dim3(128), (size_t)nb, st,
                      (const T*)qp, (const T*)kp, (const T*)vpt, idx, topk, ksum, vsum, bias,
-                     perm_q, (T*)out, H, N, BK, nb, scale);
+                     perm_q, (T*)out, H, N, Nv, BK, nb, nbc, scale);
   return spark_check_launch("attn_generic");
 }
 
-int attn_launch(int H, int N, int D, int BK, int dtype, const void* qp, const void* kp,
+// Nv = N: the plain layer; Nv < N: tokens [Nv, N) are context tokens.
+int attn_launch(int H, int N, int Nv, int D, int BK, int dtype, const void* qp, const void* kp,
                 const void* vpt, const int32_t* idx, int topk, const float* ksum,
                 const float* vsum, const float* bias, const int32_t* perm_q, void* out, void* ws,
                 hipStream_t st) {
-  const int nb = cdiv(N, BK);
+  const int nb = cdiv(Nv, BK), nbc = cdiv(N - Nv, BK);
   if (attn_uses_mfma(dtype, BK)) {
     const int nbp = cdiv(nb, BK) * BK;
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -776,27 +851,27 @@ int attn_launch(int H, int N, int D, int BK, int dtype, const void* qp, const vo
     const long total = (long)H * nbp * D;
     const int grid = (int)std::min<long>((total + 255) / 256, 4096);
     hipLaunchKernelGGL(attn_prep_summaries, dim3(grid), dim3(256), 0, st, ksum, vsum, bias, ks16,
-                       vs16t, bias2, H, N, D, BK, nb, nbp);
+                       vs16t, bias2, H, Nv, D, BK, nb, nbp);
     int rc = spark_check_launch("attn_prep_summaries");
     if (rc) return rc;
     if (D == 128) {
       if (BK == 128 && (size_t)D128_LDS_TILES + (size_t)nbp * 4 <= 80 * 1024)
-        return launch_d128(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, nb, nbp, st);
-      if (BK == 128) return launch_mfma<128, 128>(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, nb, nbp, st);
-      if (BK == 64) return launch_mfma<128, 64>(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, nb, nbp, st);
-      return launch_mfma<128, 32>(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, nb, nbp, st);
+        return launch_d128(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, Nv, nb, nbc, nbp, st);
+      if (BK == 128) return launch_mfma<128, 128>(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, Nv, nb, nbc, nbp, st);
+      if (BK == 64) return launch_mfma<128, 64>(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, Nv, nb, nbc, nbp, st);
+      return launch_mfma<128, 32>(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, Nv, nb, nbc, nbp, st);
     } else {
-      if (BK == 128) return launch_mfma<64, 128>(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, nb, nbp, st);
-      if (BK == 64) return launch_mfma<64, 64>(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, nb, nbp, st);
-      return launch_mfma<64, 32>(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, nb, nbp, st);
+      if (BK == 128) return launch_mfma<64, 128>(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, Nv, nb, nbc, nbp, st);
+      if (BK == 64) return launch_mfma<64, 64>(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, Nv, nb, nbc, nbp, st);
+      return launch_mfma<64, 32>(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, Nv, nb, nbc, nbp, st);
     }
   }
   if (dtype == SPARK_F32) {
-    if (D == 128) return launch_generic<float, 128>(qp, kp, vpt, idx, topk, ksum, vsum, bias, perm_q, out, H, N, BK, nb, st);
-    return launch_generic<float, 64>(qp, kp, vpt, idx, topk, ksum, vsum, bias, perm_q, out, H, N, BK, nb, st);
+    if (D == 128) return launch_generic<float, 128>(qp, kp, vpt, idx, topk, ksum, vsum, bias, perm_q, out, H, N, Nv, BK, nb, nbc, st);
+    return launch_generic<float, 64>(qp, kp, vpt, idx, topk, ksum, vsum, bias, perm_q, out, H, N, Nv, BK, nb, nbc, st);
   }
-  if (D == 128) return launch_generic<uint16_t, 128>(qp, kp, vpt, idx, topk, ksum, vsum, bias, perm_q, out, H, N, BK, nb, st);
-  return launch_generic<uint16_t, 64>(qp, kp, vpt, idx, topk, ksum, vsum, bias, perm_q, out, H, N, BK, nb, st);
+  if (D == 128) return launch_generic<uint16_t, 128>(qp, kp, vpt, idx, topk, ksum, vsum, bias, perm_q, out, H, N, Nv, BK, nb, nbc, st);
+  return launch_generic<uint16_t, 64>(qp, kp, vpt, idx, topk, ksum, vsum, bias, perm_q, out, H, N, Nv, BK, nb, nbc, st);
 }
 
 }  // namespace spark

@@ -10,30 +10,35 @@
 namespace spark {
 
 // ---------------------------------------------------------------------------
-// gather: x_p[h][p] = x[h][perm[h][p]] (rows >= N zero), x_pt the
-// block-transposed layout [H, nb, D, BK], xbar the fp32 block means.
+// gather: x_p[h][p] = x[h][perm[h][p]] (rows past a block's real rows zero),
+// x_pt the block-transposed layout [H, nbt, D, BK], xbar the fp32 block means.
+// Blocks [0, nb) hold the Nv video tokens in permuted order, blocks
+// [nb, nbt) the context tokens Nv..N-1 in original order (none unless the
+// context mode is on: then Nv < N); xbar covers the video blocks only.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ x,
                                                      const int32_t* __restrict__ perm,
                                                      T* __restrict__ xp, T* __restrict__ xpt,
-                                                     float* __restrict__ xbar, int N, int BK,
-                                                     int nb, int identity) {
+                                                     float* __restrict__ xbar, int N, int Nv,
+                                                     int BK, int nb, int nbt, int identity) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   T* tile = reinterpret_cast<T*>(smem);  // [BK][D + pad]
   constexpr int PAD = 16 / sizeof(T);
   constexpr int RS = D + PAD;
-  const int h = blockIdx.x / nb, B = blockIdx.x % nb;
+  const int h = blockIdx.x / nbt, B = blockIdx.x % nbt;
   const int tid = threadIdx.x;
-  const int n_real = min(BK, N - B * BK);
-  const long Np = (long)nb * BK;
+  const bool ctx = B >= nb;
+  const long p0 = ctx ? (long)Nv + (long)(B - nb) * BK : (long)B * BK;  // first source position
+  const int n_real = (int)min((long)BK, (ctx ? (long)N : (long)Nv) - p0);
+  const long Np = (long)nbt * BK;
   constexpr int CPR = D / 8;  // 8-element chunks per row
   for (int ch = tid; ch < BK * CPR; ch += blockDim.x) {
     const int j = ch / CPR, c = (ch % CPR) * 8;
     float v[8];
     if (j < n_real) {
-      const long p = (long)B * BK + j;
-      const long src = identity ? p : (long)perm[(long)h * N + p];
+      const long p = p0 + j;
+      const long src = (identity || ctx) ? p : (long)perm[(long)h * N + p];
       load8(x + ((long)h * N + src) * D + c, v);
     } else {
 #pragma unroll
@@ -72,16 +77,16 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ x,
           u.z = __float_as_uint(tt[2 * RS]);
           u.w = __float_as_uint(tt[3 * RS]);
         }
-        *reinterpret_cast<uint4*>(xpt + (((long)h * nb + B) * D + c) * BK + j0) = u;
+        *reinterpret_cast<uint4*>(xpt + (((long)h * nbt + B) * D + c) * BK + j0) = u;
       }
     } else {
       for (int e = tid; e < D * BK; e += blockDim.x) {
         const int c = e / BK, j = e % BK;
-        xpt[(((long)h * nb + B) * D + c) * BK + j] = tile[j * RS + c];
+        xpt[(((long)h * nbt + B) * D + c) * BK + j] = tile[j * RS + c];
       }
     }
   }
-  if (xbar) {
+  if (xbar && !ctx) {
     for (int c = tid; c < D; c += blockDim.x) {
       float s = 0.f;
       for (int j = 0; j < n_real; ++j) s += Elem<T>::load(tile + j * RS + c);
@@ -91,9 +96,9 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ x,
 }
 
 template <typename T, int D>
-static int gather_t(int H, int N, int BK, const void* x, const int32_t* perm, void* xp, void* xpt,
-                    float* xbar, hipStream_t st) {
-  const int nb = cdiv(N, BK);
+static int gather_t(int H, int N, int Nv, int BK, const void* x, const int32_t* perm, void* xp,
+                    void* xpt, float* xbar, hipStream_t st) {
+  const int nb = cdiv(Nv, BK), nbt = nb + cdiv(N - Nv, BK);
   constexpr int PAD = 16 / sizeof(T);
   const size_t lds = (size_t)BK * (D + PAD) * sizeof(T);
   static bool attr = false;
@@ -101,18 +106,19 @@ static int gather_t(int H, int N, int BK, const void* x, const int32_t* perm, vo
     hipFuncSetAttribute((const void*)gather_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
     attr = true;
   }
-  hipLaunchKernelGGL((gather_kernel<T, D>), dim3(H * nb), dim3(256), lds, st, (const T*)x, perm,
-                     (T*)xp, (T*)xpt, xbar, N, BK, nb, perm == nullptr ? 1 : 0);
+  hipLaunchKernelGGL((gather_kernel<T, D>), dim3(H * nbt), dim3(256), lds, st, (const T*)x, perm,
+                     (T*)xp, (T*)xpt, xbar, N, Nv, BK, nb, nbt, perm == nullptr ? 1 : 0);
   return spark_check_launch("gather");
 }
 
-int gather_launch(int H, int N, int D, int BK, int dtype, const void* x, const int32_t* perm,
-                  void* xp, void* xpt, float* xbar, hipStream_t st) {
+// Nv = N: the plain layout; Nv < N: tokens [Nv, N) are context blocks.
+int gather_launch(int H, int N, int Nv, int D, int BK, int dtype, const void* x,
+                  const int32_t* perm, void* xp, void* xpt, float* xbar, hipStream_t st) {
   if (dtype == SPARK_F32)
-    return D == 128 ? gather_t<float, 128>(H, N, BK, x, perm, xp, xpt, xbar, st)
-                    : gather_t<float, 64>(H, N, BK, x, perm, xp, xpt, xbar, st);
-  return D == 128 ? gather_t<uint16_t, 128>(H, N, BK, x, perm, xp, xpt, xbar, st)
-                  : gather_t<uint16_t, 64>(H, N, BK, x, perm, xp, xpt, xbar, st);
+    return D == 128 ? gather_t<float, 128>(H, N, Nv, BK, x, perm, xp, xpt, xbar, st)
+                    : gather_t<float, 64>(H, N, Nv, BK, x, perm, xp, xpt, xbar, st);
+  return D == 128 ? gather_t<uint16_t, 128>(H, N, Nv, BK, x, perm, xp, xpt, xbar, st)
+                  : gather_t<uint16_t, 64>(H, N, Nv, BK, x, perm, xp, xpt, xbar, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -128,7 +134,7 @@ __global__ __launch_bounds__(256) void summarize_kernel(const T* __restrict__ kp
                                                         float* __restrict__ ksum,
                                                         float* __restrict__ vsum,
                                                         float* __restrict__ bias, int N, int BK,
-                                                        int nb, int mean_mode, float rsd) {
+                                                        int nb, int nbt, int mean_mode, float rsd) {
   __shared__ float s_anchor[D];
   __shared__ float s_w[128];
   __shared__ float s_t[128];
@@ -137,9 +143,9 @@ __global__ __launch_bounds__(256) void summarize_kernel(const T* __restrict__ kp
   const int h = blockIdx.x / nb, B = blockIdx.x % nb;
   const int tid = threadIdx.x;
   const int n_real = min(BK, N - B * BK);
-  const long Np = (long)nb * BK;
+  const long Np = (long)nbt * BK;   // k_p / v_pt may hold nbt - nb context blocks after these
   const T* kblk = kp + ((long)h * Np + (long)B * BK) * D;
-  const T* vblk = vpt + ((long)h * nb + B) * (long)D * BK;
+  const T* vblk = vpt + ((long)h * nbt + B) * (long)D * BK;
   constexpr int CPR = D / 8;           // chunks per row
   constexpr int RPP = 256 / CPR;       // rows per pass
 
@@ -234,23 +240,26 @@ __global__ __launch_bounds__(256) void summarize_kernel(const T* __restrict__ kp
 }
 
 template <typename T, int D>
-static int summarize_t(int H, int N, int BK, const void* kp, const void* vpt, const float* anchor,
-                       float* ksum, float* vsum, float* bias, int mean_mode, hipStream_t st) {
+static int summarize_t(int H, int N, int nbc, int BK, const void* kp, const void* vpt,
+                       const float* anchor, float* ksum, float* vsum, float* bias, int mean_mode,
+                       hipStream_t st) {
   const int nb = cdiv(N, BK);
   hipLaunchKernelGGL((summarize_kernel<T, D>), dim3(H * nb), dim3(256), 0, st, (const T*)kp,
-                     (const T*)vpt, anchor, ksum, vsum, bias, N, BK, nb, mean_mode,
+                     (const T*)vpt, anchor, ksum, vsum, bias, N, BK, nb, nb + nbc, mean_mode,
                      1.f / sqrtf((float)D));
   return spark_check_launch("summarize");
 }
 
-int summarize_launch(int H, int N, int D, int BK, int dtype, const void* kp, const void* vpt,
-                     const float* anchor, float* ksum, float* vsum, float* bias, int mean_mode,
-                     hipStream_t st) {
+// Summaries of the ceil(N / BK) blocks of N (video) tokens; k_p / v_pt carry
+// nbc further (context) blocks per head, which are not summarised.
+int summarize_launch(int H, int N, int nbc, int D, int BK, int dtype, const void* kp,
+                     const void* vpt, const float* anchor, float* ksum, float* vsum, float* bias,
+                     int mean_mode, hipStream_t st) {
   if (dtype == SPARK_F32)
-    return D == 128 ? summarize_t<float, 128>(H, N, BK, kp, vpt, anchor, ksum, vsum, bias, mean_mode, st)
-                    : summarize_t<float, 64>(H, N, BK, kp, vpt, anchor, ksum, vsum, bias, mean_mode, st);
-  return D == 128 ? summarize_t<uint16_t, 128>(H, N, BK, kp, vpt, anchor, ksum, vsum, bias, mean_mode, st)
-                  : summarize_t<uint16_t, 64>(H, N, BK, kp, vpt, anchor, ksum, vsum, bias, mean_mode, st);
+    return D == 128 ? summarize_t<float, 128>(H, N, nbc, BK, kp, vpt, anchor, ksum, vsum, bias, mean_mode, st)
+                    : summarize_t<float, 64>(H, N, nbc, BK, kp, vpt, anchor, ksum, vsum, bias, mean_mode, st);
+  return D == 128 ? summarize_t<uint16_t, 128>(H, N, nbc, BK, kp, vpt, anchor, ksum, vsum, bias, mean_mode, st)
+                  : summarize_t<uint16_t, 64>(H, N, nbc, BK, kp, vpt, anchor, ksum, vsum, bias, mean_mode, st);
 }
 
 // anchor[h] = mean of query rows [0, n_anchor) (column sums in row order)
@@ -323,10 +332,10 @@ static void anchor_t(int H, int N, const void* q, float* anchor, int n_anchor, f
   hipLaunchKernelGGL(anchor_reduce, dim3(H), dim3(D), 0, st, scratch, anchor, D, nchunk, stride, n_anchor);
 }
 
-// scratch: [H, ceil(N / BK), D] fp32 (e.g. the qbar output, written later)
-int anchor_launch(int H, int N, int D, int BK, int dtype, const void* q, float* anchor, int n_anchor,
-                  float* scratch, hipStream_t st) {
-  const int nb = cdiv(N, BK);
+// scratch: [H, scratch_nb, D] fp32 (e.g. the qbar output, written later)
+int anchor_launch(int H, int N, int D, int dtype, const void* q, float* anchor, int n_anchor,
+                  float* scratch, int scratch_nb, hipStream_t st) {
+  const int nb = scratch_nb;
   if (dtype == SPARK_F32) {
     if (D == 128) anchor_t<float, 128>(H, N, q, anchor, n_anchor, scratch, nb, st);
     else anchor_t<float, 64>(H, N, q, anchor, n_anchor, scratch, nb, st);

@@ -81,14 +81,16 @@ __device__ __forceinline__ uint64_t argmin_key(float v, int id) {
 }
 
 // ---- global-level passes ----------------------------------------------------
-// ids[t][i] = i; trees t >= split_at go to hi (offset by split_at trees).
+// ids[t][from + i] = from + i for i < n, rows of ld entries; trees
+// t >= split_at go to hi (offset by split_at trees).
 __global__ void iota_kernel(int32_t* __restrict__ lo, int32_t* __restrict__ hi, int split_at,
-                            int N, long total) {
+                            int n, long ld, int from, long total) {
   for (long e = blockIdx.x * (long)blockDim.x + threadIdx.x; e < total;
        e += (long)gridDim.x * blockDim.x) {
-    const long t = e / N;
-    int32_t* dst = (t < split_at) ? lo + e : hi + (e - (long)split_at * N);
-    *dst = (int32_t)(e % N);
+    const long t = e / n;
+    const int i = from + (int)(e % n);
+    int32_t* row = (t < split_at) ? lo + t * ld : hi + (t - split_at) * ld;
+    row[i] = i;
   }
 }
 
@@ -486,7 +488,7 @@ __global__ __launch_bounds__(FIN_T) void finisher(const T* __restrict__ xh,
                                                   const int32_t* __restrict__ ids_in,
                                                   int32_t* __restrict__ perm_lo,
                                                   int32_t* __restrict__ perm_hi, int split_at,
-                                                  int N, int BK, int nb, int level) {
+                                                  int N, int BK, int nb, int level, long perm_ld) {
   constexpr int VE = Chunk<T>::VE, CPR = D / VE, RPP = FIN_T / CPR, NW = FIN_T / 64;
   constexpr int RS = D + 16 / (int)sizeof(T);  // padded row stride (elements)
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -737,7 +739,7 @@ __global__ __launch_bounds__(FIN_T) void finisher(const T* __restrict__ xh,
     }
     if (!any) break;
   }
-  int32_t* perm = (t < split_at) ? perm_lo + (long)t * N : perm_hi + (long)(t - split_at) * N;
+  int32_t* perm = (t < split_at) ? perm_lo + (long)t * perm_ld : perm_hi + (long)(t - split_at) * perm_ld;
   for (int i = tid; i < n; i += FIN_T) perm[g0 + i] = s_oid[s_lid[i]];
 }
 
@@ -782,7 +784,7 @@ size_t split_ws_bytes(int count, int N, int D, int BK, int dtype) {
 
 template <typename T, int D>
 static int split_t(int count, int N, int BK, const void* xhv, int32_t* perm_lo,
-                   int32_t* perm_hi, int split_at, void* ws, hipStream_t st) {
+                   int32_t* perm_hi, int split_at, long perm_ld, void* ws, hipStream_t st) {
   const T* xh = (const T*)xhv;
   const SplitPlan p = split_plan(N, D, BK, sizeof(T));
   char* w = (char*)ws;
@@ -797,12 +799,12 @@ static int split_t(int count, int N, int BK, const void* xhv, int32_t* perm_lo,
   int32_t* poleB = (int32_t*)w;
   const long total = (long)count * N;
   if (p.nb <= 1) {
-    hipLaunchKernelGGL(iota_kernel, dim3((int)std::min<long>((total + 255) / 256, 8192)), dim3(256), 0, st, perm_lo, perm_hi, split_at, N, total);
+    hipLaunchKernelGGL(iota_kernel, dim3((int)std::min<long>((total + 255) / 256, 8192)), dim3(256), 0, st, perm_lo, perm_hi, split_at, N, perm_ld, 0, total);
     return spark_check_launch("split iota");
   }
   int32_t* cur = nullptr;
   if (p.Lf > 0) {
-    hipLaunchKernelGGL(iota_kernel, dim3((int)std::min<long>((total + 255) / 256, 8192)), dim3(256), 0, st, ids_a, ids_a, count, N, total);
+    hipLaunchKernelGGL(iota_kernel, dim3((int)std::min<long>((total + 255) / 256, 8192)), dim3(256), 0, st, ids_a, ids_a, count, N, (long)N, 0, total);
     cur = ids_a;
     int32_t* nxt = ids_b;
     for (int lev = 0; lev < p.Lf; ++lev) {
@@ -829,7 +831,7 @@ static int split_t(int count, int N, int BK, const void* xhv, int32_t* perm_lo,
     hipFuncSetAttribute((const void*)finisher<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize, FIN_LDS);
     attr = true;
   }
-  hipLaunchKernelGGL((finisher<T, D>), dim3(SF, count), dim3(FIN_T), lds, st, xh, cur, perm_lo, perm_hi, split_at, N, BK, p.nb, p.Lf);
+  hipLaunchKernelGGL((finisher<T, D>), dim3(SF, count), dim3(FIN_T), lds, st, xh, cur, perm_lo, perm_hi, split_at, N, BK, p.nb, p.Lf, perm_ld);
   return spark_check_launch("split finisher");
 }
 
@@ -844,20 +846,25 @@ int copy_perm_launch(long count, const int32_t* src, int32_t* dst, hipStream_t s
   return spark_check_launch("copy_perm");
 }
 
-int iota_launch(int count, int N, int32_t* lo, int32_t* hi, int split_at, hipStream_t st) {
-  const long total = (long)count * N;
-  hipLaunchKernelGGL(iota_kernel, dim3((int)std::min<long>((total + 255) / 256, 8192)), dim3(256), 0, st, lo, hi, split_at, N, total);
+// rows of ld entries: row[from + i] = from + i for i < n (the identity on
+// positions [from, from + n))
+int iota_launch(int count, int n, long ld, int from, int32_t* lo, int32_t* hi, int split_at,
+                hipStream_t st) {
+  const long total = (long)count * n;
+  if (total == 0) return SPARK_OK;
+  hipLaunchKernelGGL(iota_kernel, dim3((int)std::min<long>((total + 255) / 256, 8192)), dim3(256), 0, st, lo, hi, split_at, n, ld, from, total);
   return spark_check_launch("iota");
 }
 
-// Trees [0, split_at) write to perm_lo, trees [split_at, count) to perm_hi.
+// Trees [0, split_at) write to perm_lo, trees [split_at, count) to perm_hi,
+// N entries per tree at a stride of perm_ld >= N.
 int split_launch(int count, int N, int D, int BK, int dtype, const void* xh, int32_t* perm_lo,
-                 int32_t* perm_hi, int split_at, void* ws, hipStream_t st) {
+                 int32_t* perm_hi, int split_at, long perm_ld, void* ws, hipStream_t st) {
   if (dtype == SPARK_BF16)
-    return D == 128 ? split_t<uint16_t, 128>(count, N, BK, xh, perm_lo, perm_hi, split_at, ws, st)
-                    : split_t<uint16_t, 64>(count, N, BK, xh, perm_lo, perm_hi, split_at, ws, st);
-  return D == 128 ? split_t<float, 128>(count, N, BK, xh, perm_lo, perm_hi, split_at, ws, st)
-                  : split_t<float, 64>(count, N, BK, xh, perm_lo, perm_hi, split_at, ws, st);
+    return D == 128 ? split_t<uint16_t, 128>(count, N, BK, xh, perm_lo, perm_hi, split_at, perm_ld, ws, st)
+                    : split_t<uint16_t, 64>(count, N, BK, xh, perm_lo, perm_hi, split_at, perm_ld, ws, st);
+  return D == 128 ? split_t<float, 128>(count, N, BK, xh, perm_lo, perm_hi, split_at, perm_ld, ws, st)
+                  : split_t<float, 64>(count, N, BK, xh, perm_lo, perm_hi, split_at, perm_ld, ws, st);
 }
 
 }  // namespace spark

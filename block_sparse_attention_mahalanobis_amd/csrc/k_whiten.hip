@@ -387,7 +387,7 @@ constexpr int WH_ROWS = 1024;  // rows per workgroup: 8 rounds of 4 waves x 32
 template <int D>
 __global__ __launch_bounds__(256, 4) void whiten_mfma(const uint16_t* __restrict__ x,
                                                    const float* __restrict__ W,
-                                                   uint16_t* __restrict__ xh, int N) {
+                                                   uint16_t* __restrict__ xh, int N, int xrows) {
   constexpr int RS = D + 8;
   __shared__ __attribute__((aligned(16))) uint16_t sW[D * RS];
   const int t = blockIdx.y;
@@ -400,7 +400,7 @@ __global__ __launch_bounds__(256, 4) void whiten_mfma(const uint16_t* __restrict
     const long row = (long)blockIdx.x * WH_ROWS + r0 + wave * 32 + l32;
     if ((long)blockIdx.x * WH_ROWS + r0 >= N) break;  // uniform across the workgroup
     const bool ok = row < N;
-    const uint16_t* xr = x + ((long)t * N + (ok ? row : 0)) * D;
+    const uint16_t* xr = x + ((long)t * xrows + (ok ? row : 0)) * D;
     bf16x8 xb[D / 16];
 #pragma unroll
     for (int s2 = 0; s2 < D / 16; ++s2) xb[s2] = *reinterpret_cast<const bf16x8*>(xr + 16 * s2 + 8 * hf);
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(256, 4) void whiten_mfma(const uint16_t* __restrict
 template <int D>
 __global__ __launch_bounds__(256) void whiten_f32(const float* __restrict__ x,
                                                   const float* __restrict__ W,
-                                                  float* __restrict__ xh, int N) {
+                                                  float* __restrict__ xh, int N, int xrows) {
   __shared__ float sW[D * (D + 1)];
   const int t = blockIdx.y, tid = threadIdx.x;
   const float* w = W + (long)t * D * D;
@@ -449,7 +449,7 @@ __global__ __launch_bounds__(256) void whiten_f32(const float* __restrict__ x,
   // one thread per row
   const long row = (long)blockIdx.x * 256 + tid;
   if (row >= N) return;
-  const float* xr = x + ((long)t * N + row) * D;
+  const float* xr = x + ((long)t * xrows + row) * D;
   float xv[D];
 #pragma unroll
   for (int c = 0; c < D; ++c) xv[c] = xr[c];
@@ -466,20 +466,23 @@ __global__ __launch_bounds__(256) void whiten_f32(const float* __restrict__ x,
   for (int c = 0; c < D; ++c) dst[c] *= inv;
 }
 
-int whiten_launch(int count, int N, int D, int dtype, const void* x, const float* W, void* xh,
-                  hipStream_t st) {
+// Rows [0, N) of each of the `count` input matrices, whose head stride is
+// xrows >= N rows (xrows > N: the rows past N are context tokens, not
+// whitened); xh is [count, N, D].
+int whiten_launch(int count, int N, int xrows, int D, int dtype, const void* x, const float* W,
+                  void* xh, hipStream_t st) {
   if (dtype == SPARK_BF16) {
     dim3 grid(cdiv(N, WH_ROWS), count);
     if (D == 128)
-      hipLaunchKernelGGL(whiten_mfma<128>, grid, dim3(256), 0, st, (const uint16_t*)x, W, (uint16_t*)xh, N);
+      hipLaunchKernelGGL(whiten_mfma<128>, grid, dim3(256), 0, st, (const uint16_t*)x, W, (uint16_t*)xh, N, xrows);
     else
-      hipLaunchKernelGGL(whiten_mfma<64>, grid, dim3(256), 0, st, (const uint16_t*)x, W, (uint16_t*)xh, N);
+      hipLaunchKernelGGL(whiten_mfma<64>, grid, dim3(256), 0, st, (const uint16_t*)x, W, (uint16_t*)xh, N, xrows);
   } else {
     dim3 grid(cdiv(N, 256), count);
     if (D == 128)
-      hipLaunchKernelGGL(whiten_f32<128>, grid, dim3(256), 0, st, (const float*)x, W, (float*)xh, N);
+      hipLaunchKernelGGL(whiten_f32<128>, grid, dim3(256), 0, st, (const float*)x, W, (float*)xh, N, xrows);
     else
-      hipLaunchKernelGGL(whiten_f32<64>, grid, dim3(256), 0, st, (const float*)x, W, (float*)xh, N);
+      hipLaunchKernelGGL(whiten_f32<64>, grid, dim3(256), 0, st, (const float*)x, W, (float*)xh, N, xrows);
   }
   return spark_check_launch("whiten");
 }

@@ -12,20 +12,19 @@
 
 namespace spark {
 // kernels (k_*.hip)
-int attn_launch(int H, int N, int D, int BK, int dtype, const void* qp, const void* kp,
+int attn_launch(int H, int N, int Nv, int D, int BK, int dtype, const void* qp, const void* kp,
                 const void* vpt, const int32_t* idx, int topk, const float* ksum,
                 const float* vsum, const float* bias, const int32_t* perm_q, void* out, void* ws,
                 hipStream_t st);
 size_t attn_ws_bytes(int H, int N, int D, int BK, int dtype);
 bool attn_uses_mfma(int dtype, int BK);
-int gather_launch(int H, int N, int D, int BK, int dtype, const void* x, const int32_t* perm,
-                  void* xp, void* xpt, float* xbar, hipStream_t st);
-int summarize_launch(int H, int N, int D, int BK, int dtype, const void* kp, const void* vpt,
-                     const float* anchor, float* ksum, float* vsum, float* bias, int mean_mode,
-                     hipStream_t st);
-int anchor_launch(int H, int N, int D, int BK, int dtype, const void* q, float* anchor, int n_anchor,
-                  float* scratch,
-                  hipStream_t st);
+int gather_launch(int H, int N, int Nv, int D, int BK, int dtype, const void* x,
+                  const int32_t* perm, void* xp, void* xpt, float* xbar, hipStream_t st);
+int summarize_launch(int H, int N, int nbc, int D, int BK, int dtype, const void* kp,
+                     const void* vpt, const float* anchor, float* ksum, float* vsum, float* bias,
+                     int mean_mode, hipStream_t st);
+int anchor_launch(int H, int N, int D, int dtype, const void* q, float* anchor, int n_anchor,
+                  float* scratch, int scratch_nb, hipStream_t st);
 int select_launch(int H, int N, int D, int BK, const float* qbar, const float* kbar,
                   const float* scores_in, int topk, int32_t* idx, float* scores_out,
                   hipStream_t st);
@@ -35,12 +34,13 @@ int moments_launch(int H, int N, int D, int dtype, const void* q, const void* k,
 int copy_perm_launch(long count, const int32_t* src, int32_t* dst, hipStream_t st);
 size_t msqrt_ws_bytes(int count, int D);
 int msqrt_launch(int count, int D, const float* M, float* W, float* Tscr, hipStream_t st);
-int whiten_launch(int count, int N, int D, int dtype, const void* x, const float* W, void* xh,
-                  hipStream_t st);
+int whiten_launch(int count, int N, int xrows, int D, int dtype, const void* x, const float* W,
+                  void* xh, hipStream_t st);
 size_t split_ws_bytes(int count, int N, int D, int BK, int dtype);
 int split_launch(int count, int N, int D, int BK, int dtype, const void* xh, int32_t* perm_lo,
-                 int32_t* perm_hi, int split_at, void* ws, hipStream_t st);
-int iota_launch(int count, int N, int32_t* lo, int32_t* hi, int split_at, hipStream_t st);
+                 int32_t* perm_hi, int split_at, long perm_ld, void* ws, hipStream_t st);
+int iota_launch(int count, int n, long ld, int from, int32_t* lo, int32_t* hi, int split_at,
+                hipStream_t st);
 int diag_launch(int H, int N, int D, int BK, int dtype, const void* qp, const void* kp,
                 const int32_t* idx, int topk, const float* ksum, const float* bias, float* recall,
                 float* logmass, hipStream_t st);
@@ -103,7 +103,8 @@ int check_args(const spark_args* a, const char* fn) {
   if (a->n_anchor < 1 || a->n_anchor > a->N)
     return spark_set_error(SPARK_E_SHAPE, "%s: n_anchor=%d not in [1, N=%d]", fn, a->n_anchor, a->N);
   const uint32_t layout = a->flags & SPARK_LAYOUT_MASK;
-  if (layout > SPARK_LAYOUT_Q_REUSE_K || (a->flags & ~(SPARK_LAYOUT_MASK | SPARK_SUMMARY_MEAN)))
+  if (layout > SPARK_LAYOUT_Q_REUSE_K ||
+      (a->flags & ~(SPARK_LAYOUT_MASK | SPARK_SUMMARY_MEAN | SPARK_CONTEXT_EXACT)))
     return spark_set_error(SPARK_E_ARG, "%s: bad flags 0x%x", fn, a->flags);
   const long nb = (a->N + (long)a->block - 1) / a->block;
   if ((long)a->H * nb > 0x7fffffffL || (long)a->N * a->d > 0x7fffffffL)
@@ -111,18 +112,39 @@ int check_args(const spark_args* a, const char* fn) {
   return SPARK_OK;
 }
 
-int nblocks(const spark_args* a) { return (a->N + a->block - 1) / a->block; }
+// Token geometry: Nv video tokens in nb blocks (all N tokens unless
+// SPARK_CONTEXT_EXACT), then nbc context blocks; nbt = nb + nbc blocks in
+// q_p / k_p / v_pt.
+struct Geo {
+  int Nv, nb, nbc, nbt;
+};
+Geo geo(const spark_args* a) {
+  Geo g;
+  g.Nv = (a->flags & SPARK_CONTEXT_EXACT) ? a->n_anchor : a->N;
+  g.nb = (g.Nv + a->block - 1) / a->block;
+  g.nbc = (a->N - g.Nv + a->block - 1) / a->block;
+  g.nbt = g.nb + g.nbc;
+  return g;
+}
+
+int nblocks(const spark_args* a) { return geo(a).nb; }
+
+int reject_context(const spark_args* a, const char* fn) {
+  if (a->flags & SPARK_CONTEXT_EXACT)
+    return spark_set_error(SPARK_E_UNSUPPORTED, "%s: SPARK_CONTEXT_EXACT is not supported here", fn);
+  return SPARK_OK;
+}
 
 size_t reblock_ws(const spark_args* a) {
   const uint32_t layout = a->flags & SPARK_LAYOUT_MASK;
   if (layout != SPARK_LAYOUT_REBLOCK && layout != SPARK_LAYOUT_Q_REUSE_K) return 0;
-  const int H = a->H, N = a->N, D = a->d;
+  const int H = a->H, N = a->N, D = a->d, Nv = geo(a).Nv;
   size_t b = 0;
   b += up((size_t)2 * H * D * D * 4);                     // moments [MK | MQ]
   b += up((size_t)2 * H * D * D * 4);                     // roots  [W_Q | W_K]
   b += up(std::max(moments_ws_bytes(H, N, D), msqrt_ws_bytes(2 * H, D)));
-  b += up((size_t)2 * H * N * D * esize(a->dtype));       // whitened rows
-  b += up(split_ws_bytes(2 * H, N, D, a->block, a->dtype));
+  b += up((size_t)2 * H * Nv * D * esize(a->dtype));      // whitened (video) rows
+  b += up(split_ws_bytes(2 * H, Nv, D, a->block, a->dtype));
   return b;
 }
 
@@ -134,8 +156,9 @@ struct LayerBufs {
 };
 
 size_t layer_bufs(const spark_args* a, int topk, char* base, LayerBufs* o) {
-  const int H = a->H, N = a->N, D = a->d, nb = nblocks(a);
-  const size_t Np = (size_t)nb * a->block;
+  const Geo g = geo(a);
+  const int H = a->H, N = a->N, D = a->d, nb = g.nb;
+  const size_t Np = (size_t)g.nbt * a->block;
   const int es = esize(a->dtype);
   size_t off = 0;
   auto take = [&](size_t bytes) -> char* {
@@ -148,7 +171,7 @@ size_t layer_bufs(const spark_args* a, int topk, char* base, LayerBufs* o) {
   b.perm_k = (int32_t*)take((size_t)H * N * 4);
   b.q_p = take((size_t)H * Np * D * es);
   b.k_p = take((size_t)H * Np * D * es);
-  b.v_pt = take((size_t)H * Np * D * es);
+  b.v_pt = take((size_t)H * Np * D * es);   // [H, nbt, D, block]
   b.qbar = (float*)take((size_t)H * nb * D * 4);
   b.kbar = (float*)take((size_t)H * nb * D * 4);
   b.anchor = (float*)take((size_t)H * D * 4);
@@ -158,7 +181,7 @@ size_t layer_bufs(const spark_args* a, int topk, char* base, LayerBufs* o) {
   b.bias = (float*)take((size_t)H * nb * 4);
   b.scratch = take(0);
   if (o) *o = b;
-  return off + std::max(reblock_ws(a), attn_ws_bytes(H, N, D, a->block, a->dtype));
+  return off + std::max(reblock_ws(a), attn_ws_bytes(H, g.Nv, D, a->block, a->dtype));
 }
 
 }  // namespace
@@ -204,7 +227,7 @@ size_t spark_workspace_bytes(const spark_args* a, int op, int32_t topk) {
     case SPARK_OP_REBLOCK: return reblock_ws(a);
     case SPARK_OP_SELECT: return 0;
     case SPARK_OP_SUMMARIZE: return 0;
-    case SPARK_OP_ATTN: return attn_ws_bytes(a->H, a->N, a->d, a->block, a->dtype);
+    case SPARK_OP_ATTN: return attn_ws_bytes(a->H, geo(a).Nv, a->d, a->block, a->dtype);
     case SPARK_OP_SPLIT: return split_ws_bytes(2 * a->H, a->N, a->d, a->block, a->dtype);
     case SPARK_OP_LAYER:
       if (topk < 1 || topk > nb) {
@@ -223,6 +246,7 @@ int spark_moments(const spark_args* a, const void* q, const void* k, float* MQ, 
                   float* anchor, void* ws, size_t ws_bytes, spark_stream_t stream) {
   const char* fn = "spark_moments";
   CHECK(check_args(a, fn));
+  CHECK(reject_context(a, fn));
   CHECK(check_ptr(q, fn, "q"));
   CHECK(check_ptr(k, fn, "k"));
   CHECK(check_ptr(MQ, fn, "MQ"));
@@ -251,37 +275,42 @@ int spark_whiten(const spark_args* a, int32_t count, const void* x, const float*
                  spark_stream_t stream) {
   const char* fn = "spark_whiten";
   CHECK(check_args(a, fn));
+  CHECK(reject_context(a, fn));
   if (count < 1) return spark_set_error(SPARK_E_SHAPE, "%s: count=%d", fn, count);
   CHECK(check_ptr(x, fn, "x"));
   CHECK(check_ptr(W, fn, "W"));
   CHECK(check_ptr(xhat, fn, "xhat"));
-  return whiten_launch(count, a->N, a->d, a->dtype, x, W, xhat, (hipStream_t)stream);
+  return whiten_launch(count, a->N, a->N, a->d, a->dtype, x, W, xhat, (hipStream_t)stream);
 }
 
 int spark_split(const spark_args* a, int32_t count, const void* xhat, int32_t* perm, void* ws,
                 size_t ws_bytes, spark_stream_t stream) {
   const char* fn = "spark_split";
   CHECK(check_args(a, fn));
+  CHECK(reject_context(a, fn));
   if (count < 1) return spark_set_error(SPARK_E_SHAPE, "%s: count=%d", fn, count);
   CHECK(check_ptr(xhat, fn, "xhat"));
   CHECK(check_ptr(perm, fn, "perm"));
   const size_t need = split_ws_bytes(count, a->N, a->d, a->block, a->dtype);
   CHECK(check_ptr(ws, fn, "ws"));
   if (ws_bytes < need) return spark_set_error(SPARK_E_WORKSPACE, "%s: ws_bytes %zu < %zu", fn, ws_bytes, need);
-  return split_launch(count, a->N, a->d, a->block, a->dtype, xhat, perm, perm, count, ws, (hipStream_t)stream);
+  return split_launch(count, a->N, a->d, a->block, a->dtype, xhat, perm, perm, count, a->N, ws,
+                      (hipStream_t)stream);
 }
 
 int spark_gather(const spark_args* a, const void* x, const int32_t* perm, void* x_p, void* x_pt,
                  float* xbar, spark_stream_t stream) {
   const char* fn = "spark_gather";
   CHECK(check_args(a, fn));
+  CHECK(reject_context(a, fn));
   CHECK(check_ptr(x, fn, "x"));
   CHECK(check_ptr(perm, fn, "perm"));
   CHECK(check_ptr(x_p, fn, "x_p", true));
   CHECK(check_ptr(x_pt, fn, "x_pt", true));
   CHECK(check_ptr(xbar, fn, "xbar", true));
   if (!x_p && !x_pt && !xbar) return SPARK_OK;
-  return gather_launch(a->H, a->N, a->d, a->block, a->dtype, x, perm, x_p, x_pt, xbar, (hipStream_t)stream);
+  return gather_launch(a->H, a->N, a->N, a->d, a->block, a->dtype, x, perm, x_p, x_pt, xbar,
+                       (hipStream_t)stream);
 }
 
 // ---- the four steps -----------------------------------------------------------------
@@ -310,23 +339,27 @@ int spark_reblock(const spark_args* a, const void* q, const void* k, const void*
   }
   hipStream_t st = (hipStream_t)stream;
   const int H = a->H, N = a->N, D = a->d, BK = a->block;
+  const Geo g = geo(a);
+  const int Nv = g.Nv;   // tokens that are partitioned (the video tokens)
   const int32_t *pq = perm_q, *pk = perm_k;
   if (layout == SPARK_LAYOUT_REBLOCK) {
     char* w = (char*)ws;
     float* Ms = (float*)w;  w += up((size_t)2 * H * D * D * 4);   // [MK | MQ]
     float* Ws = (float*)w;  w += up((size_t)2 * H * D * D * 4);   // [W_Q | W_K]
     void* scr = w;          w += up(std::max(moments_ws_bytes(H, N, D), msqrt_ws_bytes(2 * H, D)));
-    void* xh = w;           w += up((size_t)2 * H * N * D * esize(a->dtype));
+    void* xh = w;           w += up((size_t)2 * H * Nv * D * esize(a->dtype));
     void* sws = w;
     float* MK = Ms;
     float* MQ = Ms + (size_t)H * D * D;
-    // queries are whitened by M_K^{1/2} (first H roots), keys by M_Q^{1/2}
+    // moments over all N tokens; queries are whitened by M_K^{1/2} (first H
+    // roots), keys by M_Q^{1/2}; only the Nv video rows are whitened and split
     CHECK(moments_launch(H, N, D, a->dtype, q, k, MQ, MK, anchor, a->n_anchor, scr, st));
     CHECK(msqrt_launch(2 * H, D, Ms, Ws, (float*)scr, st));
-    CHECK(whiten_launch(H, N, D, a->dtype, q, Ws, xh, st));
-    CHECK(whiten_launch(H, N, D, a->dtype, k, Ws + (size_t)H * D * D,
-                        (char*)xh + (size_t)H * N * D * esize(a->dtype), st));
-    CHECK(split_launch(2 * H, N, D, BK, a->dtype, xh, perm_q, perm_k, H, sws, st));
+    CHECK(whiten_launch(H, Nv, N, D, a->dtype, q, Ws, xh, st));
+    CHECK(whiten_launch(H, Nv, N, D, a->dtype, k, Ws + (size_t)H * D * D,
+                        (char*)xh + (size_t)H * Nv * D * esize(a->dtype), st));
+    CHECK(split_launch(2 * H, Nv, D, BK, a->dtype, xh, perm_q, perm_k, H, N, sws, st));
+    CHECK(iota_launch(2 * H, N - Nv, N, Nv, perm_q, perm_k, H, st));   // context stays in place
   } else if (layout == SPARK_LAYOUT_Q_REUSE_K) {
     // the same key side as REBLOCK (keys whitened by M_Q^{1/2}); the query
     // moments are still needed for M_Q and the anchor, the key moments not
@@ -334,13 +367,14 @@ int spark_reblock(const spark_args* a, const void* q, const void* k, const void*
     float* Ms = (float*)w;  w += up((size_t)2 * H * D * D * 4);
     float* Ws = (float*)w;  w += up((size_t)2 * H * D * D * 4);
     void* scr = w;          w += up(std::max(moments_ws_bytes(H, N, D), msqrt_ws_bytes(2 * H, D)));
-    void* xh = w;           w += up((size_t)2 * H * N * D * esize(a->dtype));
+    void* xh = w;           w += up((size_t)2 * H * Nv * D * esize(a->dtype));
     void* sws = w;
     float* MQ = Ms;
     CHECK(moments_launch(H, N, D, a->dtype, q, nullptr, MQ, nullptr, anchor, a->n_anchor, scr, st));
     CHECK(msqrt_launch(H, D, MQ, Ws, (float*)scr, st));
-    CHECK(whiten_launch(H, N, D, a->dtype, k, Ws, xh, st));
-    CHECK(split_launch(H, N, D, BK, a->dtype, xh, perm_k, perm_k, H, sws, st));
+    CHECK(whiten_launch(H, Nv, N, D, a->dtype, k, Ws, xh, st));
+    CHECK(split_launch(H, Nv, D, BK, a->dtype, xh, perm_k, perm_k, H, N, sws, st));
+    CHECK(iota_launch(H, N - Nv, N, Nv, perm_k, perm_k, H, st));
     CHECK(copy_perm_launch((long)H * N, perm_k, perm_q, st));
     pq = perm_k;
   } else {
@@ -349,12 +383,12 @@ int spark_reblock(const spark_args* a, const void* q, const void* k, const void*
       pk = nullptr;
     }
     // qbar (written by the gather below) holds the anchor's chunk sums
-    if (anchor) CHECK(anchor_launch(H, N, D, BK, a->dtype, q, anchor, a->n_anchor, qbar, st));
+    if (anchor) CHECK(anchor_launch(H, N, D, a->dtype, q, anchor, a->n_anchor, qbar, g.nb, st));
   }
-  CHECK(gather_launch(H, N, D, BK, a->dtype, q, pq, q_p, nullptr, qbar, st));
-  CHECK(gather_launch(H, N, D, BK, a->dtype, k, pk, k_p, nullptr, kbar, st));
-  CHECK(gather_launch(H, N, D, BK, a->dtype, v, pk, nullptr, v_pt, nullptr, st));
-  if (layout == SPARK_LAYOUT_IDENTITY) CHECK(iota_launch(2 * H, N, perm_q, perm_k, H, st));
+  CHECK(gather_launch(H, N, Nv, D, BK, a->dtype, q, pq, q_p, nullptr, qbar, st));
+  CHECK(gather_launch(H, N, Nv, D, BK, a->dtype, k, pk, k_p, nullptr, kbar, st));
+  CHECK(gather_launch(H, N, Nv, D, BK, a->dtype, v, pk, nullptr, v_pt, nullptr, st));
+  if (layout == SPARK_LAYOUT_IDENTITY) CHECK(iota_launch(2 * H, N, N, 0, perm_q, perm_k, H, st));
   return SPARK_OK;
 }
 
@@ -371,7 +405,8 @@ int spark_select(const spark_args* a, const float* qbar, const float* kbar, cons
   }
   CHECK(check_ptr(idx, fn, "idx"));
   CHECK(check_ptr(scores_out, fn, "scores_out", true));
-  return select_launch(a->H, a->N, a->d, a->block, qbar, kbar, scores_in, topk, idx, scores_out, (hipStream_t)stream);
+  return select_launch(a->H, geo(a).Nv, a->d, a->block, qbar, kbar, scores_in, topk, idx, scores_out,
+                       (hipStream_t)stream);
 }
 
 int spark_summarize(const spark_args* a, const void* k_p, const void* v_pt, const float* anchor,
@@ -385,7 +420,9 @@ int spark_summarize(const spark_args* a, const void* k_p, const void* v_pt, cons
   CHECK(check_ptr(ksum, fn, "ksum"));
   CHECK(check_ptr(vsum, fn, "vsum"));
   CHECK(check_ptr(bias, fn, "bias"));
-  return summarize_launch(a->H, a->N, a->d, a->block, a->dtype, k_p, v_pt, anchor, ksum, vsum, bias, mean_mode, (hipStream_t)stream);
+  const Geo g = geo(a);
+  return summarize_launch(a->H, g.Nv, g.nbc, a->d, a->block, a->dtype, k_p, v_pt, anchor, ksum, vsum,
+                          bias, mean_mode, (hipStream_t)stream);
 }
 
 int spark_attn(const spark_args* a, const void* q_p, const void* k_p, const void* v_pt,
@@ -405,12 +442,14 @@ int spark_attn(const spark_args* a, const void* q_p, const void* k_p, const void
   CHECK(check_ptr(bias, fn, "bias"));
   CHECK(check_ptr(perm_q, fn, "perm_q", true));
   CHECK(check_ptr(out, fn, "out"));
-  const size_t need = attn_ws_bytes(a->H, a->N, a->d, a->block, a->dtype);
+  const int Nv = geo(a).Nv;
+  const size_t need = attn_ws_bytes(a->H, Nv, a->d, a->block, a->dtype);
   if (need > 0) {
     CHECK(check_ptr(ws, fn, "ws"));
     if (ws_bytes < need) return spark_set_error(SPARK_E_WORKSPACE, "%s: ws_bytes %zu < %zu", fn, ws_bytes, need);
   }
-  return attn_launch(a->H, a->N, a->d, a->block, a->dtype, q_p, k_p, v_pt, idx, topk, ksum, vsum, bias, perm_q, out, ws, (hipStream_t)stream);
+  return attn_launch(a->H, a->N, Nv, a->d, a->block, a->dtype, q_p, k_p, v_pt, idx, topk, ksum, vsum,
+                     bias, perm_q, out, ws, (hipStream_t)stream);
 }
 
 int spark_layer(const spark_args* a, const void* q, const void* k, const void* v, int32_t topk,
@@ -446,6 +485,7 @@ int spark_diagnostics(const spark_args* a, const void* q_p, const void* k_p, con
                       float* logmass, spark_stream_t stream) {
   const char* fn = "spark_diagnostics";
   CHECK(check_args(a, fn));
+  CHECK(reject_context(a, fn));
   const int nb = nblocks(a);
   if (topk < 1 || topk > nb) return spark_set_error(SPARK_E_SHAPE, "%s: topk=%d not in [1, %d]", fn, topk, nb);
   CHECK(check_ptr(q_p, fn, "q_p"));

@@ -76,6 +76,26 @@ typedef enum spark_dtype { SPARK_F32 = 0, SPARK_BF16 = 1 } spark_dtype;
 /* flags: compressed-branch estimator */
 #define SPARK_SUMMARY_REWEIGHT 0x0u /* Spark-Reweight ([blog] 02 / Method: Spark-Reweight)          */
 #define SPARK_SUMMARY_MEAN 0x4u     /* uniform block means, no bias (BSA / Sol-Attn estimator)      */
+/* flags: context/sink tokens ([blog] 01 / Method: Spark-Reblock: context/sink
+ * tokens stay exact and lie outside the video-block Top-K budget).  Tokens
+ * [n_anchor, N) of every head are context tokens, [0, n_anchor) video tokens:
+ *   - only the video tokens are partitioned, pooled, scored, routed and
+ *     summarised: n_b = ceil(n_anchor / block) video blocks, and topk,
+ *     qbar, kbar, idx, ksum, vsum, bias all count video blocks;
+ *   - the n_c = ceil((N - n_anchor) / block) context blocks follow the video
+ *     blocks in q_p, k_p and v_pt (context tokens in original order), so
+ *     those hold n_t = n_b + n_c blocks: q_p, k_p [H, n_t * block, d],
+ *     v_pt [H, n_t, d, block];
+ *   - perm_q / perm_k keep the context tokens in place (perm[p] = p for
+ *     p >= n_anchor); the moments still use all N tokens;
+ *   - every video query attends exactly to all context keys besides its
+ *     selected blocks; a context query's row is exact dense attention over
+ *     all N keys.
+ * Honoured by spark_reblock, spark_select, spark_summarize, spark_attn,
+ * spark_layer and spark_workspace_bytes; the stage entry points and
+ * spark_diagnostics reject it (SPARK_E_UNSUPPORTED).  With n_anchor = N it
+ * changes nothing. */
+#define SPARK_CONTEXT_EXACT 0x8u
 
 typedef struct spark_args {
   int32_t H;        /* heads                                                  */
@@ -84,7 +104,7 @@ typedef struct spark_args {
   int32_t block;    /* tokens per block, 1..128                               */
   int32_t dtype;    /* spark_dtype of q, k, v                                 */
   int32_t n_anchor; /* the anchor averages query rows [0, n_anchor); 1..N     */
-  uint32_t flags;   /* SPARK_LAYOUT_* | SPARK_SUMMARY_*                       */
+  uint32_t flags;   /* SPARK_LAYOUT_* | SPARK_SUMMARY_* | SPARK_CONTEXT_EXACT */
   int32_t reserved; /* must be 0                                              */
 } spark_args;
 
@@ -146,7 +166,8 @@ size_t spark_workspace_bytes(const spark_args* args, int op, int32_t topk);
  * reblock_layout=q_reuse_k setting of the [news] page's Workflows section)
  * and writes that permutation to both perm_k and perm_q; IDENTITY writes
  * perm = 0..N-1; GIVEN reads perm_q/perm_k (inputs, each a permutation of
- * 0..N-1 per head; not checked).
+ * 0..N-1 per head; not checked; with SPARK_CONTEXT_EXACT only entries
+ * [0, n_anchor) are read, each a permutation of 0..n_anchor-1).
  * q_p and anchor may be NULL (not written).  ws: spark_workspace_bytes(args,
  * SPARK_OP_REBLOCK, 0) bytes (0 for IDENTITY and GIVEN). */
 int spark_reblock(const spark_args* args, const void* q, const void* k, const void* v,
@@ -187,7 +208,8 @@ int spark_summarize(const spark_args* args, const void* k_p, const void* v_pt,
  *         / (the same sums without the values),
  * computed with an online softmax, then scattered: out[h][perm_q[h][p]] =
  * o_p.  If perm_q is NULL the output stays in permuted order and `out` is
- * [H, Np, d] (padding rows written as 0).  idx rows must be strictly
+ * [H, Np, d] (padding rows written as 0; Np = n_t * block with
+ * SPARK_CONTEXT_EXACT).  idx rows must be strictly
  * ascending block ids in [0, n_b) (not checked on the device).
  * ws: spark_workspace_bytes(args, SPARK_OP_ATTN, topk) bytes. */
 int spark_attn(const spark_args* args, const void* q_p, const void* k_p, const void* v_pt,

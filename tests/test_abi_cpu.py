@@ -93,7 +93,7 @@ def test_null_misaligned_topk_and_workspace_errors(lib):
     rc = lib.spark_select(ctypes.byref(a), None, FAKE, None, 4, FAKE, None, None)
     assert rc == -1 and "qbar" in L.last_error()
     bad_flags = _args()
-    bad_flags.flags = 0x8
+    bad_flags.flags = 0x10
     rc = lib.spark_reblock(ctypes.byref(bad_flags), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
                            FAKE, None, FAKE, 1 << 40, None)
     assert rc == -1
@@ -119,6 +119,34 @@ def test_workspace_sizes_are_consistent(lib):
     assert L.workspace_bytes(ident, L.OP_REBLOCK) == 0
     assert lib.spark_workspace_bytes(ctypes.byref(a), 99, 0) == ctypes.c_size_t(-1).value
     assert lib.spark_workspace_bytes(ctypes.byref(a), L.OP_LAYER, 0) == ctypes.c_size_t(-1).value
+
+
+def test_context_mode_validation(lib):
+    """SPARK_CONTEXT_EXACT: topk counts video blocks (ceil(n_anchor / block)),
+    the stage entry points and the diagnostics refuse the flag, and the
+    layer workspace grows by the context blocks' gathered copies."""
+    N, nv, b = 1000, 700, 64
+    a = _args(dtype=1)
+    a.N, a.n_anchor, a.block = N, nv, b
+    a.flags = L.CONTEXT_EXACT
+    nbv = O.n_blocks(nv, b)
+    for k in (0, nbv + 1):
+        assert lib.spark_attn(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, k, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                              1 << 40, None) == -2
+        assert lib.spark_select(ctypes.byref(a), FAKE, FAKE, None, k, FAKE, None, None) == -2
+    assert L.workspace_bytes(a, L.OP_LAYER, nbv) > 0
+    assert lib.spark_workspace_bytes(ctypes.byref(a), L.OP_LAYER, nbv + 1) == ctypes.c_size_t(-1).value
+    assert lib.spark_diagnostics(ctypes.byref(a), FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, None) == -4
+    assert lib.spark_whiten(ctypes.byref(a), 1, FAKE, FAKE, FAKE, None) == -4
+    assert lib.spark_split(ctypes.byref(a), 1, FAKE, FAKE, FAKE, 1 << 40, None) == -4
+    assert lib.spark_gather(ctypes.byref(a), FAKE, FAKE, FAKE, None, None, None) == -4
+    assert lib.spark_moments(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None) == -4
+    # the 768p layer plus two 48x84 reference frames as context tokens
+    ref = L.make_args(40, 254016, 128, 128, 1, 245952, context=True)
+    plain = L.make_args(40, 254016, 128, 128, 1, 245952)
+    k_ref = L.topk_from_ratio(0.2, O.n_blocks(245952, 128))
+    assert L.workspace_bytes(ref, L.OP_LAYER, k_ref) < L.workspace_bytes(plain, L.OP_LAYER, k_ref)
+    assert L.workspace_bytes(ref, L.OP_REBLOCK) < L.workspace_bytes(plain, L.OP_REBLOCK)
 
 
 def test_diagnostics_validation(lib):
