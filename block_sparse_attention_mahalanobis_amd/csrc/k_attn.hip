@@ -383,6 +383,9 @@ __device__ __forceinline__ void d128_pipeline() {
 }
 constexpr int D128_LDS_TILES = 2 * 128 * 256;   // K + V^T, 64 KB
 
+// CTX = false (no context blocks) compiles the tile bookkeeping of the plain
+// layer: one compare less per tile and the idx load unconditional.
+template <bool CTX>
 __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
     const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vpt, const int32_t* __restrict__ idx, int topk,
@@ -395,6 +398,7 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
   unsigned char* sV = smem + 128 * 256;
   float* sBias = reinterpret_cast<float*>(smem + D128_LDS_TILES);
 
+  if constexpr (!CTX) nbc = 0;
   int h, A;
   if (!d128_map(blockIdx.x, nb, nbc, h, A)) return;
   const int tid = threadIdx.x;
@@ -402,7 +406,15 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
   const int l32 = lane & 31, hf = lane >> 5;
   const int nbt = nb + nbc;
   const long Np = (long)nbt * BK;
-  const TilePlan tp = tile_plan(A, nb, nbc, topk, nbp / BK);
+  TilePlan tp;
+  if constexpr (CTX) {
+    tp = tile_plan(A, nb, nbc, topk, nbp / BK);
+  } else {
+    tp.nidx = topk;
+    tp.nex = topk;
+    tp.bofs = 0;
+    tp.nct = (topk < nb) ? nbp / BK : 0;
+  }
   const int nct = tp.nct;
   const int ntiles = tp.nex + nct;
   const int32_t* myidx = (A < nb) ? idx + ((long)h * nb + A) * topk : idx;
@@ -430,7 +442,7 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
   }
   auto tile_base = [&](int t, const char*& kb, const char*& vb) {
     if (t < tp.nex) {
-      const int B = (t < tp.nidx) ? myidx[t] : t + tp.bofs;
+      const int B = (!CTX || t < tp.nidx) ? myidx[t] : t + tp.bofs;
       kb = reinterpret_cast<const char*>(kp + ((long)h * Np + (long)B * BK) * D);
       vb = reinterpret_cast<const char*>(vpt + ((long)h * nbt + B) * (long)D * BK);
     } else {
@@ -515,10 +527,16 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
       issue(kb1, koff, sK);
     }
 
-    float mx;
+    // P against the lazy reference m_ref: p = 2^(logit * log2 e - m_ref).
+    // Every p of a row half is at most that half's sum, so a sum <= 2^12
+    // shows that no p exceeds 2^12 (bf16 P and the fp32 sums hold that with
+    // room to spare) and m_ref can stay -- no per-tile maximum.  Otherwise
+    // (the first tile, or logits that rose by more than ~12 in log2 units)
+    // the exact tile maximum is taken, the running sums are rescaled and P
+    // is recomputed.
     if (exact) {
-      const int B = (t < tp.nidx) ? myidx[t] : t + tp.bofs;
-      const int valid = block_rows(B, nb, nbt, N, Nv, BK);
+      const int B = (!CTX || t < tp.nidx) ? myidx[t] : t + tp.bofs;
+      const int valid = CTX ? block_rows(B, nb, nbt, N, Nv, BK) : ((B == nb - 1) ? Nv - (nb - 1) * BK : BK);
       if (valid < BK) {
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt)
@@ -528,28 +546,42 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
             if (j >= valid) sacc[jt][v] = -INFINITY;
           }
       }
-      float mr = sacc[0][0];
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mr = fmaxf(mr, sacc[jt][v]);
-      mx = mr * scale_log2;
     } else {
       const float* bb = sBias + (t - tp.nex) * BK;
-      mx = -INFINITY;
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int j = 32 * jt + ((v < 8) ? 8 * hf + v : 16 + 8 * hf + v - 8);
-          const float s2 = fmaf(sacc[jt][v], scale_log2, bb[j]);
-          sacc[jt][v] = s2;
-          mx = fmaxf(mx, s2);
+          sacc[jt][v] = fmaf(sacc[jt][v], scale_log2, bb[j]);
         }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const bool need = mx > m_ref + 8.f;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+    bf16x8 pop[8];
+    float psum;
+    // exact tiles hold raw logits (the scale is folded into the exp
+    // argument), compressed tiles already-scaled, biased ones
+#define SPARK_D128_P()                                                                   \
+    {                                                                                   \
+      const float nm = -m_ref;                                                          \
+      const float sc = exact ? scale_log2 : 1.f;                                        \
+      psum = 0.f;                                                                       \
+      _Pragma("unroll") for (int jt = 0; jt < 4; ++jt)                                  \
+      _Pragma("unroll") for (int hh = 0; hh < 2; ++hh)                                  \
+      _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                   \
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[jt][8 * hh + e], sc, nm));     \
+        psum += p;                                                                      \
+        pop[2 * jt + hh][e] = (__bf16)p;                                                \
+      }                                                                                 \
+    }
+    SPARK_D128_P()
+    if (__builtin_amdgcn_ballot_w64(!(psum <= 4096.f)) != 0) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[jt][v]);
+      if (exact) mx *= scale_log2;
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_new = fmaxf(m_ref, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
       m_ref = m_new;
@@ -558,32 +590,10 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
+      SPARK_D128_P()
     }
-    bf16x8 pop[8];
-    if (exact) {
-      const float nm = -m_ref;
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[jt][8 * hh + e], scale_log2, nm));
-            l_run += p;
-            pop[2 * jt + hh][e] = (__bf16)p;
-          }
-    } else {
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float p = __builtin_amdgcn_exp2f(sacc[jt][8 * hh + e] - m_ref);
-            l_run += p;
-            pop[2 * jt + hh][e] = (__bf16)p;
-          }
-    }
+#undef SPARK_D128_P
+    l_run += psum;
 
     // V(t) landed: only this wave's 8 K(t+1) loads may be outstanding
     if (t + 1 < ntiles) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
@@ -809,16 +819,23 @@ static int launch_d128(const void* qp, const void* kp, const void* vpt, const in
   const size_t lds = D128_LDS_TILES + (size_t)nbp * 4;
   static bool attr_set = false;
   if (!attr_set) {
-    hipFuncSetAttribute((const void*)attn_mfma_d128, hipFuncAttributeMaxDynamicSharedMemorySize,
+    hipFuncSetAttribute((const void*)attn_mfma_d128<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        80 * 1024);
+    hipFuncSetAttribute((const void*)attn_mfma_d128<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                         80 * 1024);
     attr_set = true;
   }
   const float scale_log2 = kLog2e / sqrtf(128.f);
   const long slots = 8L * (((nbc + 7) >> 3) + ((nb + 7) >> 3));   // d128_slots
   if ((long)H * slots > 0x7fffffffL) return spark_set_error(SPARK_E_SHAPE, "spark_attn: grid too large");
-  hipLaunchKernelGGL(attn_mfma_d128, dim3((unsigned)(H * slots)), dim3(D128_NT), lds, st, (const uint16_t*)qp,
-                     (const uint16_t*)kp, (const uint16_t*)vpt, idx, topk, ks16, vs16t, bias2,
-                     perm_q, (uint16_t*)out, H, N, Nv, nb, nbc, nbp, scale_log2);
+  if (nbc > 0)
+    hipLaunchKernelGGL(attn_mfma_d128<true>, dim3((unsigned)(H * slots)), dim3(D128_NT), lds, st,
+                       (const uint16_t*)qp, (const uint16_t*)kp, (const uint16_t*)vpt, idx, topk, ks16,
+                       vs16t, bias2, perm_q, (uint16_t*)out, H, N, Nv, nb, nbc, nbp, scale_log2);
+  else
+    hipLaunchKernelGGL(attn_mfma_d128<false>, dim3((unsigned)(H * slots)), dim3(D128_NT), lds, st,
+                       (const uint16_t*)qp, (const uint16_t*)kp, (const uint16_t*)vpt, idx, topk, ks16,
+                       vs16t, bias2, perm_q, (uint16_t*)out, H, N, Nv, nb, nbc, nbp, scale_log2);
   return spark_check_launch("attn_mfma_d128");
 }
 
