@@ -51,6 +51,9 @@ def parse():
                    help="token partition: separate query/key Spark-Reblock, or the key partition reused")
     p.add_argument("--sweep", action="store_true",
                    help="the density / noise sweep at the draft shape instead of the layer line")
+    p.add_argument("--context", action="store_true",
+                   help="tokens from n_anchor on (the ref2va reference frames) are context tokens: "
+                        "exact for every query, outside the video-block top-k")
     return p.parse_args()
 
 
@@ -67,58 +70,75 @@ def load_inputs(w, torch, dtype, threads):
     return out
 
 
-def attn_flops(idx, N, b, d):
+def attn_flops(idx, N, b, d, Nv=None):
     """Algorithmic flops of the fused attention: 4 d per (query row, exact
-    key) plus 4 d per (query row, unselected block summary)."""
+    key) plus 4 d per (query row, unselected block summary).  With context
+    tokens (Nv < N) every video row also takes the N - Nv context keys
+    exactly and every context row all N keys."""
+    Nv = N if Nv is None else Nv
     H, nb, k = idx.shape
     sizes = np.full(nb, b, dtype=np.int64)
-    sizes[-1] = N - (nb - 1) * b
-    keys_per_qblock = sizes[idx].sum(axis=2)                  # [H, nb]
-    exact = 4 * d * int((keys_per_qblock * sizes[None, :]).sum())
-    comp = 4 * d * int(H * N * (nb - k))
+    sizes[-1] = Nv - (nb - 1) * b
+    keys_per_qblock = sizes[idx].sum(axis=2) + (N - Nv)      # [H, nb]
+    exact = 4 * d * int((keys_per_qblock * sizes[None, :]).sum()) + 4 * d * H * (N - Nv) * N
+    comp = 4 * d * int(H * Nv * (nb - k))
     return exact, comp
 
 
-def reblock_bytes(H, N, d, b, es, levels_global, nb, sides=2):
+def reblock_bytes(H, N, d, b, es, levels_global, nb, sides=2, Nv=None):
     """Algorithmic HBM bytes of reblock + summaries (per layer); sides = 1
-    for q_reuse_k (moments of q only, keys whitened and split)."""
+    for q_reuse_k (moments of q only, keys whitened and split).  With
+    context tokens only the Nv video rows are whitened, split and summarised."""
+    Nv = N if Nv is None else Nv
     vol = H * N * d * es                      # one [H, N, d] tensor
+    volv = H * Nv * d * es                    # its video rows
     moments = sides * vol
-    whiten = 2 * sides * vol
-    split = sides * (levels_global * 4 * vol + vol)     # 4 row passes per global level + finisher
+    whiten = 2 * sides * volv
+    split = sides * (levels_global * 4 * volv + volv)   # 4 row passes per global level + finisher
     gather = 6 * vol
-    summ = 2 * vol
+    summ = 2 * volv
     return moments + whiten + split + gather + summ
 
 
-def cpu_baseline(w, topk, sample_blocks):
+def cpu_baseline(w, topk, sample_blocks, context=False):
     """The fp64 oracle as it stands, timed on this host: head 0 end to end
     (reblock of both sides, pooling, scores, top-k, summaries) plus the
-    two-branch attention of `sample_blocks` query blocks, scaled to the whole
-    layer (H heads, all query blocks)."""
+    two-branch attention of `sample_blocks` query blocks (and, with context
+    tokens, the dense rows of up to 1024 context queries), scaled to the
+    whole layer (H heads, all query blocks and context rows)."""
     import oracle as O
     from block_sparse_attention_mahalanobis_amd.workload import make_head
     cores = len(os.sched_getaffinity(0))
     q, k, v = make_head(w, 0)
     b = w.block
-    nb = O.n_blocks(w.N, b)
+    nv = w.n_anchor if context else w.N
+    nb = O.n_blocks(nv, b)
     t0 = time.perf_counter()
-    pq, pk = O.reblock_head(q, k, b)
-    qp, qbar = O.gather_pool(q, pq, b)
-    kp, kbar = O.gather_pool(k, pk, b)
-    vp = np.asarray(v, np.float64)[pk]
+    pq, pk = O.reblock_head(q, k, b, n_split=nv)
+    qp, qbar = O.gather_pool(q[:nv], pq, b)
+    kp, kbar = O.gather_pool(k[:nv], pk, b)
+    vp = np.asarray(v[:nv], np.float64)[pk]
     S = O.block_scores(qbar, kbar)
     idx = O.select_topk(S, topk)
     ks, vs, beta = O.reweight_summaries(kp, vp, O.anchor_query(q, w.n_anchor), b)
     t1 = time.perf_counter()
     nsamp = min(sample_blocks, nb)
-    O.sparse_attention(qp, kp, vp, idx, ks, vs, beta, b, qblocks=range(nsamp))
+    O.sparse_attention(qp, kp, vp, idx, ks, vs, beta, b, qblocks=range(nsamp),
+                       extra_k=k[nv:] if nv < w.N else None, extra_v=v[nv:] if nv < w.N else None)
     t2 = time.perf_counter()
     per_head = (t1 - t0) + (t2 - t1) * (nb / nsamp)
+    extra = ""
+    if nv < w.N:
+        nc = w.N - nv
+        ncs = min(1024, nc)
+        O.dense_attention(q[nv:nv + ncs], k, v)
+        t3 = time.perf_counter()
+        per_head += (t3 - t2) * (nc / ncs)
+        extra = f" + dense rows of {ncs}/{nc} context queries ({t3 - t2:.1f} s)"
     layer_ms = per_head * w.H * 1e3
     return {"value": round(layer_ms, 1), "unit": "ms", "cores": cores, "kind": "oracle",
             "sample": (f"head 0 of {w.H}: full reblock/select/summaries ({t1 - t0:.1f} s) + attention "
-                       f"of {nsamp}/{nb} query blocks ({t2 - t1:.1f} s), scaled x{nb / nsamp:.1f} blocks "
+                       f"of {nsamp}/{nb} query blocks ({t2 - t1:.1f} s){extra}, scaled to all blocks "
                        f"and x{w.H} heads; numpy fp64, BLAS threads = {cores}")}
 
 
@@ -227,22 +247,24 @@ def main():
     dtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     es = 2 if w.dtype == "bf16" else 4
     H, N, d, b = w.H, w.N, w.d, w.block
-    nb = L.n_blocks(N, b)
+    ctx = args.context and w.n_anchor < N
+    Nv, nb, nbt = L.geometry(N, b, w.n_anchor, ctx)
     topk = L.topk_from_ratio(w.ratio, nb)
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
-    log(f"workload {w.name}: H={H} N={N} d={d} block={b} n_b={nb} topk={topk} dtype={w.dtype}")
+    log(f"workload {w.name}: H={H} N={N} d={d} block={b} n_b={nb} topk={topk} dtype={w.dtype}"
+        + (f"; context tokens {N - Nv} ({nbt - nb} blocks)" if ctx else ""))
     t = time.perf_counter()
     q, k, v = load_inputs(w, torch, dtype, threads)
     log(f"inputs resident ({time.perf_counter() - t:.1f} s)")
 
     # buffers and workspaces, allocated once
-    Np = nb * b
+    Np = nbt * b
     dev = "cuda:0"
     perm_q = torch.empty((H, N), dtype=torch.int32, device=dev)
     perm_k = torch.empty((H, N), dtype=torch.int32, device=dev)
     q_p = torch.empty((H, Np, d), dtype=dtype, device=dev)
     k_p = torch.empty((H, Np, d), dtype=dtype, device=dev)
-    v_pt = torch.empty((H, nb, d, b), dtype=dtype, device=dev)
+    v_pt = torch.empty((H, nbt, d, b), dtype=dtype, device=dev)
     qbar = torch.empty((H, nb, d), dtype=torch.float32, device=dev)
     kbar = torch.empty((H, nb, d), dtype=torch.float32, device=dev)
     anchor = torch.empty((H, d), dtype=torch.float32, device=dev)
@@ -251,7 +273,7 @@ def main():
     vsum = torch.empty((H, nb, d), dtype=torch.float32, device=dev)
     bias = torch.empty((H, nb), dtype=torch.float32, device=dev)
     out = torch.empty_like(q)
-    a = L.make_args(H, N, d, b, dtype, w.n_anchor, args.layout)
+    a = L.make_args(H, N, d, b, dtype, w.n_anchor, args.layout, context=ctx)
     ws_r = L.workspace_bytes(a, L.OP_REBLOCK)
     ws_a = L.workspace_bytes(a, L.OP_ATTN)
     ws = torch.empty(max(ws_r, ws_a, 256), dtype=torch.uint8, device=dev)
@@ -301,7 +323,7 @@ def main():
     log(f"layer {layer_ms:.2f} ms; reblock {st_mean[0]:.2f} select {st_mean[1]:.2f} "
         f"summarize {st_mean[2]:.2f} attn {st_mean[3]:.2f} ms")
 
-    exact, comp = attn_flops(idx.cpu().numpy(), N, b, d)
+    exact, comp = attn_flops(idx.cpu().numpy(), N, b, d, Nv)
     attn_s = st_mean[3] * 1e-3
     exact_tf = exact / attn_s / 1e12
     alg_tf = (exact + comp) / attn_s / 1e12
@@ -315,7 +337,7 @@ def main():
     while mx > F:
         mx = (mx + 1) // 2
         lev += 1
-    rb_bytes = reblock_bytes(H, N, d, b, es, lev, nb, 1 if args.layout == "q_reuse_k" else 2)
+    rb_bytes = reblock_bytes(H, N, d, b, es, lev, nb, 1 if args.layout == "q_reuse_k" else 2, Nv)
     rb_ms = st_mean[0] + st_mean[2]
     csrc = os.path.join(ROOT, "block_sparse_attention_mahalanobis_amd", "csrc")
     traffic = load_traffic("attn_full768_traffic.txt",
@@ -329,7 +351,7 @@ def main():
     base = None
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a sample (cpu_baseline)")
-        base = cpu_baseline(w, topk, args.cpu_sample_blocks)
+        base = cpu_baseline(w, topk, args.cpu_sample_blocks, ctx)
         log(f"cpu baseline {base['value']:.0f} ms projected ({base['sample']})")
 
     rec = {
@@ -346,7 +368,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded clustered Gaussian-mixture q/k on the latent grid, v ~ N(0,1))",
         "config": {"workload": w.name, "H": H, "N": N, "d": d, "block": b, "n_blocks": nb,
-                   "topk": topk, "density": w.ratio, "layout": args.layout, "summary": "reweight"},
+                   "topk": topk, "density": w.ratio, "layout": args.layout, "summary": "reweight",
+                   **({"context_tokens": N - Nv, "context_blocks": nbt - nb} if ctx else {})},
         "exact_mfma_pct_peak": round(100.0 * exact_tf / PEAK_BF16_TFLOPS, 2),
         "stages_ms": {"reblock": round(st_mean[0], 3), "select": round(st_mean[1], 3),
                       "summarize": round(st_mean[2], 3), "attn": round(st_mean[3], 3)},
