@@ -383,6 +383,24 @@ __device__ __forceinline__ void d128_pipeline() {
 }
 constexpr int D128_LDS_TILES = 2 * 128 * 256;   // K + V^T, 64 KB
 
+// Sum of the 64 bf16 P values a lane holds, two bf16 per dot-product step
+// (against (1, 1)), in two interleaved partial sums: the softmax denominator
+// is summed from the same rounded P that multiplies V.
+__device__ __forceinline__ float rowsum_bf16(const bf16x8 (&pop)[8]) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t one = {(__bf16)1.f, (__bf16)1.f};
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bf16x8 v = pop[i];
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, s1, false);
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, s1, false);
+  }
+  return s0 + s1;
+}
+
 // CTX = false (no context blocks) compiles the tile bookkeeping of the plain
 // layer: one compare less per tile and the idx load unconditional.
 template <bool CTX>
@@ -564,14 +582,11 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
     {                                                                                   \
       const float nm = -m_ref;                                                          \
       const float sc = exact ? scale_log2 : 1.f;                                        \
-      psum = 0.f;                                                                       \
       _Pragma("unroll") for (int jt = 0; jt < 4; ++jt)                                  \
       _Pragma("unroll") for (int hh = 0; hh < 2; ++hh)                                  \
-      _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                   \
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[jt][8 * hh + e], sc, nm));     \
-        psum += p;                                                                      \
-        pop[2 * jt + hh][e] = (__bf16)p;                                                \
-      }                                                                                 \
+      _Pragma("unroll") for (int e = 0; e < 8; ++e)                                     \
+        pop[2 * jt + hh][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[jt][8 * hh + e], sc, nm)); \
+      psum = rowsum_bf16(pop);                                                          \
     }
     SPARK_D128_P()
     if (__builtin_amdgcn_ballot_w64(!(psum <= 4096.f)) != 0) {
