@@ -384,26 +384,57 @@ int msqrt_launch(int count, int D, const float* M, float* W, float* Tscr, hipStr
 // ---------------------------------------------------------------------------
 constexpr int WH_ROWS = 1024;  // rows per workgroup: 8 rounds of 4 waves x 32
 
+// Each wave whitens 32 consecutive rows per round.  The rows (8 KB for
+// d = 128, contiguous in HBM) come in with 16-byte lane loads, four rows per
+// instruction, are staged in the wave's own LDS slice, and feed the MFMA B
+// operand from there; the bf16 results go back through the same slice and
+// out as coalesced 16-byte stores.  The next round's rows are loaded into
+// registers while the current round runs.  A wave's LDS accesses are ordered
+// by wave_lds_sync(), so past the W load there is no workgroup barrier.
 template <int D>
-__global__ __launch_bounds__(256, 4) void whiten_mfma(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(256, 2) void whiten_mfma(const uint16_t* __restrict__ x,
                                                    const float* __restrict__ W,
                                                    uint16_t* __restrict__ xh, int N, int xrows) {
-  constexpr int RS = D + 8;
+  constexpr int RS = D + 8;            // LDS row stride (bf16), 16-byte pad
+  constexpr int CPR = D / 8;           // 16-byte chunks per row
+  constexpr int CPL = 32 * CPR / 64;   // chunks per lane per round (d = 128: 8)
   __shared__ __attribute__((aligned(16))) uint16_t sW[D * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t sX[4][32 * RS];
   const int t = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const float* w = W + (long)t * D * D;
   for (int e = tid; e < D * D; e += 256) sW[(e / D) * RS + e % D] = f2bf(w[e]);
   __syncthreads();
+  uint16_t* sx = sX[wave];
+  const uint16_t* xt = x + (long)t * xrows * D;
+  uint16_t* ht = xh + (long)t * N * D;
+  const long wbase = (long)blockIdx.x * WH_ROWS + wave * 32;   // this wave's first row, round 0
+
+  uint4 pf[CPL];
+  auto load = [&](long base) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = i * 64 + lane, rr = c / CPR, cc = c % CPR;
+      pf[i] = (base + rr < N) ? *reinterpret_cast<const uint4*>(xt + (base + rr) * D + cc * 8)
+                              : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  if (wbase < N) load(wbase);
   for (int r0 = 0; r0 < WH_ROWS; r0 += 128) {
-    const long row = (long)blockIdx.x * WH_ROWS + r0 + wave * 32 + l32;
-    if ((long)blockIdx.x * WH_ROWS + r0 >= N) break;  // uniform across the workgroup
-    const bool ok = row < N;
-    const uint16_t* xr = x + ((long)t * xrows + (ok ? row : 0)) * D;
+    const long base = wbase + r0;
+    if (base >= N) break;   // uniform across the wave
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = i * 64 + lane, rr = c / CPR, cc = c % CPR;
+      *reinterpret_cast<uint4*>(sx + rr * RS + cc * 8) = pf[i];
+    }
+    if (r0 + 128 < WH_ROWS && base + 128 < N) load(base + 128);
+    wave_lds_sync();
     bf16x8 xb[D / 16];
 #pragma unroll
-    for (int s2 = 0; s2 < D / 16; ++s2) xb[s2] = *reinterpret_cast<const bf16x8*>(xr + 16 * s2 + 8 * hf);
+    for (int s2 = 0; s2 < D / 16; ++s2)
+      xb[s2] = *reinterpret_cast<const bf16x8*>(sx + l32 * RS + 16 * s2 + 8 * hf);
     f32x16 acc[D / 32];
 #pragma unroll
     for (int ct = 0; ct < D / 32; ++ct) {
@@ -422,18 +453,24 @@ __global__ __launch_bounds__(256, 4) void whiten_mfma(const uint16_t* __restrict
       for (int v = 0; v < 16; ++v) ss = fmaf(acc[ct][v], acc[ct][v], ss);
     ss = group_sum<64, 32>(ss);
     const float inv = (ss > 0.f) ? 1.f / sqrtf(ss) : 0.f;
-    if (ok) {
-      uint16_t* dst = xh + ((long)t * N + row) * D;
+    wave_lds_sync();   // every lane has read its B operand rows
 #pragma unroll
-      for (int ct = 0; ct < D / 32; ++ct)
+    for (int ct = 0; ct < D / 32; ++ct)
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          uint2 p;
-          p.x = pack_bf2(acc[ct][4 * a] * inv, acc[ct][4 * a + 1] * inv);
-          p.y = pack_bf2(acc[ct][4 * a + 2] * inv, acc[ct][4 * a + 3] * inv);
-          *reinterpret_cast<uint2*>(dst + 32 * ct + 8 * a + 4 * hf) = p;
-        }
+      for (int a = 0; a < 4; ++a) {
+        uint2 p;
+        p.x = pack_bf2(acc[ct][4 * a] * inv, acc[ct][4 * a + 1] * inv);
+        p.y = pack_bf2(acc[ct][4 * a + 2] * inv, acc[ct][4 * a + 3] * inv);
+        *reinterpret_cast<uint2*>(sx + l32 * RS + 32 * ct + 8 * a + 4 * hf) = p;
+      }
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = i * 64 + lane, rr = c / CPR, cc = c % CPR;
+      if (base + rr < N)
+        *reinterpret_cast<uint4*>(ht + (base + rr) * D + cc * 8) = *reinterpret_cast<const uint4*>(sx + rr * RS + cc * 8);
     }
+    wave_lds_sync();   // the slice is free for the next round
   }
 }
 
