@@ -26,33 +26,39 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ x,
   T* tile = reinterpret_cast<T*>(smem);  // [BK][D + pad]
   constexpr int PAD = 16 / sizeof(T);
   constexpr int RS = D + PAD;
+  constexpr int C16 = D * (int)sizeof(T) / 16;   // 16-byte chunks per row
+  constexpr int MAXC = 128 * C16 / 256;          // chunks per thread for a 128-row block
   const int h = blockIdx.x / nbt, B = blockIdx.x % nbt;
   const int tid = threadIdx.x;
   const bool ctx = B >= nb;
   const long p0 = ctx ? (long)Nv + (long)(B - nb) * BK : (long)B * BK;  // first source position
   const int n_real = (int)min((long)BK, (ctx ? (long)N : (long)Nv) - p0);
   const long Np = (long)nbt * BK;
-  constexpr int CPR = D / 8;  // 8-element chunks per row
-  for (int ch = tid; ch < BK * CPR; ch += blockDim.x) {
-    const int j = ch / CPR, c = (ch % CPR) * 8;
-    float v[8];
-    if (j < n_real) {
-      const long p = p0 + j;
-      const long src = (identity || ctx) ? p : (long)perm[(long)h * N + p];
-      load8(x + ((long)h * N + src) * D + c, v);
-    } else {
+  // all of this thread's row loads are issued before any store, so up to
+  // MAXC 16-byte loads per thread are in flight
+  long src[MAXC];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = 0.f;
-    }
-    if (xp) store8(xp + ((long)h * Np + (long)B * BK + j) * D + c, v);
-    if (sizeof(T) == 2) {
-      uint16_t* t16 = reinterpret_cast<uint16_t*>(tile + j * RS + c);
+  for (int i = 0; i < MAXC; ++i) {
+    const int ch = tid + i * 256, j = ch / C16;
+    src[i] = -1;
+    if (ch < BK * C16 && j < n_real)
+      src[i] = (identity || ctx) ? p0 + j : (long)perm[(long)h * N + p0 + j];
+  }
+  uint4 buf[MAXC];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) t16[e] = f2bf(v[e]);  // exact: v came from bf16
-    } else {
-      float* t32 = reinterpret_cast<float*>(tile + j * RS + c);
+  for (int i = 0; i < MAXC; ++i) {
+    const int ch = tid + i * 256, cc = ch % C16;
+    buf[i] = (src[i] >= 0)
+                 ? *reinterpret_cast<const uint4*>(x + ((long)h * N + src[i]) * D + cc * (16 / (int)sizeof(T)))
+                 : make_uint4(0u, 0u, 0u, 0u);
+  }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) t32[e] = v[e];
+  for (int i = 0; i < MAXC; ++i) {
+    const int ch = tid + i * 256, j = ch / C16, cc = ch % C16;
+    if (ch < BK * C16) {
+      if (xp)
+        *reinterpret_cast<uint4*>(xp + ((long)h * Np + (long)B * BK + j) * D + cc * (16 / (int)sizeof(T))) = buf[i];
+      *reinterpret_cast<uint4*>(tile + j * RS + cc * (16 / (int)sizeof(T))) = buf[i];
     }
   }
   __syncthreads();
