@@ -162,17 +162,43 @@ __global__ __launch_bounds__(SPL_T) void cent_partial(const T* __restrict__ xh,
   }
 }
 
-// Per group: centroid = sum of its blocks' partials, in block order.
+// Per group: centroid = sum of its blocks' partials.  CR_T threads: column
+// c = tid % D, block stride G = CR_T / D; each thread keeps 8 partial sums
+// (8 loads in flight), then the G partials are added in a fixed order
+// (deterministic).  The top levels have few groups with thousands of blocks.
+constexpr int CR_T = 1024;
 template <int D>
-__global__ __launch_bounds__(D) void cent_reduce(const float* __restrict__ cpart,
-                                                 float* __restrict__ cen, int nb, int level,
-                                                 int S) {
-  const int slot = blockIdx.x, t = blockIdx.y, c = threadIdx.x;
+__global__ __launch_bounds__(CR_T) void cent_reduce(const float* __restrict__ cpart,
+                                                    float* __restrict__ cen, int nb, int level,
+                                                    int S) {
+  constexpr int G = CR_T / D;
+  __shared__ float s_p[G][D];
+  const int slot = blockIdx.x, t = blockIdx.y;
+  const int c = threadIdx.x % D, g = threadIdx.x / D;
   int start, nbg;
   if (!group_of_slot(slot, level, nb, start, nbg) || nbg < 2) return;
-  float s = 0.f;
-  for (int b = start; b < start + nbg; ++b) s += cpart[((long)t * nb + b) * D + c];
-  cen[((long)t * S + slot) * D + c] = s;
+  const int end = start + nbg;
+  const float* src = cpart + (long)t * nb * D + c;
+  float a[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) a[u] = 0.f;
+  int b = start + g;
+  for (; b + 7 * G < end; b += 8 * G) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[(long)(b + u * G) * D];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a[u] += v[u];
+  }
+  for (; b < end; b += G) a[0] += src[(long)b * D];
+  s_p[g][c] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+  __syncthreads();
+  if (g == 0) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < G; ++i) s += s_p[i][c];
+    cen[((long)t * S + slot) * D + c] = s;
+  }
 }
 
 // Per chunk: min over rows of (x^_i . vec_g, id), vec_g = cen[slot] (mode 0)
@@ -293,7 +319,8 @@ __global__ __launch_bounds__(SPL_T) void score_kernel(const T* __restrict__ xh,
 }
 
 // ---- workgroup helpers (radix select + stable partition) ---------------------
-// Exclusive scan of one int per thread over SPL_T threads; returns the total.
+// Exclusive scan of one int per thread over NT threads; returns the total.
+template <int NT = SPL_T>
 __device__ __forceinline__ int wg_exscan(int v, int* s_tmp, int& total) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int incl = v;
@@ -306,7 +333,7 @@ __device__ __forceinline__ int wg_exscan(int v, int* s_tmp, int& total) {
   __syncthreads();
   int base = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < SPL_T / 64; ++i) {
+  for (int i = 0; i < NT / 64; ++i) {
     if (i < w) base += s_tmp[i];
     tot += s_tmp[i];
   }
@@ -369,14 +396,17 @@ __device__ __forceinline__ void radix_pick(const int* s_hist, uint32_t* s_prefix
 }
 
 // One workgroup per group: radix-select the c_L-th key of the group's scores
-// (streamed from global), then stable-partition the ids.
-__global__ __launch_bounds__(SPL_T) void select_partition(const float* __restrict__ s,
-                                                          const int32_t* __restrict__ ids_in,
-                                                          int32_t* __restrict__ ids_out, int N,
-                                                          int BK, int nb, int level) {
+// (streamed from global), then stable-partition the ids.  NT threads: 1024
+// for the top levels (a few groups of up to N tokens, where the loads in
+// flight per group decide the speed), SPL_T below.
+template <int NT>
+__global__ __launch_bounds__(NT) void select_partition(const float* __restrict__ s,
+                                                       const int32_t* __restrict__ ids_in,
+                                                       int32_t* __restrict__ ids_out, int N,
+                                                       int BK, int nb, int level) {
   __shared__ int s_hist[256];
-  __shared__ int s_whist[SPL_T / 64][256];  // one histogram per wave (less atomic contention)
-  __shared__ int s_tmp[SPL_T / 64];
+  __shared__ int s_whist[NT / 64][256];  // one histogram per wave (less atomic contention)
+  __shared__ int s_tmp[NT / 64];
   __shared__ uint32_t s_prefix;
   __shared__ int s_need;
   const int slot = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
@@ -387,7 +417,7 @@ __global__ __launch_bounds__(SPL_T) void select_partition(const float* __restric
   const int n = (int)(min((long)N, (long)(start + nbg) * BK) - g0);
   const long base = (long)t * N + g0;
   if (nbg < 2) {  // a leaf carried through this level: copy
-    for (int i = tid; i < n; i += SPL_T) ids_out[base + i] = ids_in[base + i];
+    for (int i = tid; i < n; i += NT) ids_out[base + i] = ids_in[base + i];
     return;
   }
   const int cL = ((nbg + 1) >> 1) * BK;
@@ -396,30 +426,30 @@ __global__ __launch_bounds__(SPL_T) void select_partition(const float* __restric
     s_need = cL;
   }
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < (SPL_T / 64) * 256; i += SPL_T) (&s_whist[0][0])[i] = 0;
+    for (int i = tid; i < (NT / 64) * 256; i += NT) (&s_whist[0][0])[i] = 0;
     __syncthreads();
     const uint32_t pre = s_prefix;
     const uint32_t hmask = (shift == 24) ? 0u : (0xffffffffu << (shift + 8));
     constexpr int U = 8;  // independent loads in flight per thread
-    for (int i0 = 0; i0 < n; i0 += U * SPL_T) {
+    for (int i0 = 0; i0 < n; i0 += U * NT) {
       float v[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * SPL_T + tid;
+        const int i = i0 + u * NT + tid;
         v[u] = (i < n) ? s[base + i] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * SPL_T + tid;
+        const int i = i0 + u * NT + tid;
         const uint32_t k = pref_key_desc(v[u]);
         if (i < n && (k & hmask) == pre) atomicAdd(&s_whist[wave][(k >> shift) & 255], 1);
       }
     }
     __syncthreads();
-    for (int i = tid; i < 256; i += SPL_T) {
+    for (int i = tid; i < 256; i += NT) {
       int c = 0;
 #pragma unroll
-      for (int w = 0; w < SPL_T / 64; ++w) c += s_whist[w][i];
+      for (int w = 0; w < NT / 64; ++w) c += s_whist[w][i];
       s_hist[i] = c;
     }
     __syncthreads();
@@ -428,10 +458,10 @@ __global__ __launch_bounds__(SPL_T) void select_partition(const float* __restric
   }
   const uint32_t thr = s_prefix;
   const int ties_needed = s_need;
-  // stable partition in tiles of SPL_T * E positions, E consecutive per thread
+  // stable partition in tiles of NT * E positions, E consecutive per thread
   constexpr int E = 8;
   int run_left = 0, run_eq = 0;  // lefts / ties before this tile
-  for (int p0 = 0; p0 < n; p0 += SPL_T * E) {
+  for (int p0 = 0; p0 < n; p0 += NT * E) {
     uint32_t k[E];
     int nl = 0, ne = 0;
 #pragma unroll
@@ -443,7 +473,7 @@ __global__ __launch_bounds__(SPL_T) void select_partition(const float* __restric
     }
     // a tie goes left iff its rank among ties < ties_needed
     int tot_eq;
-    const int eq_before = run_eq + wg_exscan(ne, s_tmp, tot_eq);
+    const int eq_before = run_eq + wg_exscan<NT>(ne, s_tmp, tot_eq);
     int ce = eq_before;
     bool left[E];
 #pragma unroll
@@ -459,7 +489,7 @@ __global__ __launch_bounds__(SPL_T) void select_partition(const float* __restric
       nl += l;
     }
     int tot_l;
-    const int l_before = run_left + wg_exscan(nl, s_tmp, tot_l);
+    const int l_before = run_left + wg_exscan<NT>(nl, s_tmp, tot_l);
     int cl = l_before;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -811,13 +841,17 @@ static int split_t(int count, int N, int BK, const void* xhv, int32_t* perm_lo,
       const int S = 1 << lev;
       dim3 gc(p.nb, count), gs(S, count);
       hipLaunchKernelGGL((cent_partial<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, cpart, N, BK, p.nb, lev);
-      hipLaunchKernelGGL((cent_reduce<D>), gs, dim3(D), 0, st, cpart, cen, p.nb, lev, p.S);
+      hipLaunchKernelGGL((cent_reduce<D>), gs, dim3(CR_T), 0, st, cpart, cen, p.nb, lev, p.S);
       hipLaunchKernelGGL((argmin_partial<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, cen, poleA, mpart, N, BK, p.nb, lev, p.S, 0);
       hipLaunchKernelGGL((argmin_reduce<T, D>), gs, dim3(64), 0, st, mpart, xh, poleA, poleB, diff, N, p.nb, lev, p.S, 0);
       hipLaunchKernelGGL((argmin_partial<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, cen, poleA, mpart, N, BK, p.nb, lev, p.S, 1);
       hipLaunchKernelGGL((argmin_reduce<T, D>), gs, dim3(64), 0, st, mpart, xh, poleA, poleB, diff, N, p.nb, lev, p.S, 1);
       hipLaunchKernelGGL((score_kernel<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, diff, s, N, BK, p.nb, lev, p.S);
-      hipLaunchKernelGGL(select_partition, gs, dim3(SPL_T), 0, st, s, cur, nxt, N, BK, p.nb, lev);
+      // groups of more than 64 blocks: the wide variant
+      if ((p.nb >> lev) > 64)
+        hipLaunchKernelGGL(select_partition<1024>, gs, dim3(1024), 0, st, s, cur, nxt, N, BK, p.nb, lev);
+      else
+        hipLaunchKernelGGL(select_partition<SPL_T>, gs, dim3(SPL_T), 0, st, s, cur, nxt, N, BK, p.nb, lev);
       int rc = spark_check_launch("split level");
       if (rc) return rc;
       std::swap(cur, nxt);
