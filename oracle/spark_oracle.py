@@ -38,6 +38,12 @@ Readings taken where the pages are silent:
     the BSA multiplicity |B| (the all-ones vector in K~_A);
   * anchor = mean of the first ``n_anchor`` raw queries (video tokens);
   * moments are uncentred and use all N tokens;
+  * fp8 mode (the Benchmark Results' FP8 runs; precision otherwise
+    unstated): every attention logit q . k is taken from OCP E4M3 values --
+    queries quantised per row, keys per block of b rows, summary keys per
+    group of b consecutive blocks -- each group scaled by the smallest power
+    of two that brings its largest magnitude to <= 448, rounded to nearest
+    (ties to even); P and V stay in the bf16 path;
   * context mode ([blog] Spark-Reblock: context/sink tokens stay exact and
     lie outside the video-block Top-K budget): tokens [n_anchor, N) are
     context tokens.  Only the video tokens are partitioned, pooled, scored,
@@ -63,6 +69,7 @@ __all__ = [
     "block_scores", "select_topk", "anchor_query", "reweight_summaries",
     "mean_summaries", "sparse_attention", "dense_attention", "forward_head",
     "forward", "attention_mass_recall", "log_mass_error", "HeadResult",
+    "E4M3_MAX", "e4m3_round", "pow2_scale", "quantize_e4m3_groups",
 ]
 
 
@@ -304,11 +311,65 @@ def mean_summaries(kp: np.ndarray, vp: np.ndarray, b: int):
 
 
 # ----------------------------------------------------------------------------
+# FP8 (OCP E4M3) logits ([blog] Benchmark Results: the DiT also runs in FP8)
+# ----------------------------------------------------------------------------
+
+E4M3_MAX = 448.0   # largest finite E4M3 magnitude: 1.75 * 2^8
+
+
+def e4m3_round(x):
+    """Round to the nearest OCP E4M3 value, ties to the even code: 3 mantissa
+    bits, exponent bias 7, so normal numbers (|x| >= 2^-6) sit on a grid of
+    2^(e-3) in the binade [2^e, 2^(e+1)) and subnormals on a grid of 2^-9.
+    Inputs must satisfy |x| <= 448 (the callers scale them there)."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(np.abs(x) > E4M3_MAX):
+        raise ValueError("e4m3_round: |x| > 448")
+    a = np.abs(x)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    # log2 can misplace exact powers of two by one ulp: fix e so 2^e <= a < 2^(e+1)
+    e = np.where(np.exp2(e) > a, e - 1, e)
+    e = np.where(np.exp2(e + 1) <= a, e + 1, e)
+    quantum = np.where(a >= 2.0 ** -6, np.exp2(e - 3), 2.0 ** -9)
+    return np.round(x / quantum) * quantum       # numpy rounds halves to even
+
+
+def pow2_scale(amax):
+    """Smallest power of two s with amax <= 448 s (1 for amax = 0): exact in
+    any binary floating point, so every implementation picks the same s."""
+    amax = float(amax)
+    if amax == 0.0:
+        return 1.0
+    e = math.frexp(amax)[1] - 9
+    while amax > E4M3_MAX * 2.0 ** e:
+        e += 1
+    while amax <= E4M3_MAX * 2.0 ** (e - 1):
+        e -= 1
+    return 2.0 ** e
+
+
+def quantize_e4m3_groups(x, group: int):
+    """Rows of x in consecutive groups of ``group`` rows (the last may be
+    short), each group scaled by pow2_scale of its largest magnitude and
+    rounded to E4M3.  Returns (the dequantised rows, the per-group scales)."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros_like(x)
+    n = x.shape[0]
+    scales = np.zeros(max(1, -(-n // group)))
+    for g0 in range(0, n, group):
+        blk = x[g0:g0 + group]
+        sc = pow2_scale(np.abs(blk).max() if blk.size else 0.0)
+        scales[g0 // group] = sc
+        out[g0:g0 + group] = e4m3_round(blk / sc) * sc
+    return out, scales
+
+
+# ----------------------------------------------------------------------------
 # Two-branch attention ([blog] Spark-Reblock section, BSA(Q_A) equations)
 # ----------------------------------------------------------------------------
 
 def sparse_attention(qp, kp, vp, idx, ksum, vsum, bias, b: int, qblocks=None,
-                     extra_k=None, extra_v=None) -> np.ndarray:
+                     extra_k=None, extra_v=None, fp8: bool = False) -> np.ndarray:
     """BSA(Q_A) = Softmax(Q_A K~_A^T / sqrt(d)) V~_A with one row-wise softmax
     over the concatenation, per key block B, of
         B in S_A : the exact rows K_B, V_B;
@@ -316,6 +377,9 @@ def sparse_attention(qp, kp, vp, idx, ksum, vsum, bias, b: int, qblocks=None,
                        all-ones vector), its logit shifted by beta_B;
     plus, when given, the rows of ``extra_k`` / ``extra_v`` exactly for
     every query block (context/sink tokens: exact, outside the Top-K budget).
+    fp8: the logits use E4M3 queries (per row), keys (per block of b rows,
+    context keys per block of b rows of their own) and summary keys (per b
+    consecutive blocks); values and weights are unchanged.
     The |B| identical summary rows are carried as one row of weight |B|.
     Returns the output in permuted order [N, d].  ``qblocks`` (optional)
     restricts the work to those query blocks; other rows stay 0."""
@@ -332,6 +396,12 @@ def sparse_attention(qp, kp, vp, idx, ksum, vsum, bias, b: int, qblocks=None,
     else:
         xk = np.asarray(extra_k, np.float64)
         xv = np.asarray(extra_v, np.float64)
+    if fp8:
+        qp = quantize_e4m3_groups(qp, 1)[0]
+        kp = quantize_e4m3_groups(kp, b)[0]
+        ksum = quantize_e4m3_groups(ksum, b)[0]
+        if xk.shape[0]:
+            xk = quantize_e4m3_groups(xk, b)[0]
     out = np.zeros((N, d))
     for A in (range(nb) if qblocks is None else qblocks):
         rows = slice(A * b, min(N, (A + 1) * b))
@@ -387,7 +457,7 @@ class HeadResult:
 def forward_head(q, k, v, b: int, topk: int, n_anchor: Optional[int] = None,
                  layout: str = "reblock", perm_q=None, perm_k=None,
                  summary: str = "reweight", scores_in=None,
-                 context: bool = False) -> HeadResult:
+                 context: bool = False, fp8: bool = False) -> HeadResult:
     """Reblock -> select -> summarise -> attend -> scatter, one head.
     layout: "reblock" (Spark-Reblock), "q_reuse_k" (the key partition reused
     for the queries), "identity" (consecutive blocks, the
@@ -400,7 +470,11 @@ def forward_head(q, k, v, b: int, topk: int, n_anchor: Optional[int] = None,
     counts video blocks), every video query attends exactly to all context
     keys, and each context query's row is dense attention over all N keys.
     The permutations then fix the context tokens (perm[p] = p, p >= n_anchor);
-    qp / kp / vp and the block arrays hold the video tokens only."""
+    qp / kp / vp and the block arrays hold the video tokens only.
+    fp8: the attention logits come from E4M3 operands (see sparse_attention);
+    a context query's dense row then uses E4M3 queries (per row) and keys
+    (video keys per block of the permuted order, context keys per block of
+    their own), like the video rows."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -434,11 +508,17 @@ def forward_head(q, k, v, b: int, topk: int, n_anchor: Optional[int] = None,
     else:
         raise ValueError(summary)
     op = sparse_attention(qp, kp, vp, idx, ks, vs, beta, b,
-                          extra_k=k[nv:] if nv < N else None, extra_v=v[nv:] if nv < N else None)
+                          extra_k=k[nv:] if nv < N else None, extra_v=v[nv:] if nv < N else None,
+                          fp8=fp8)
     out = np.zeros((N, q.shape[1]))
     out[perm_q] = op
     if nv < N:
-        out[nv:] = dense_attention(q[nv:], k, v)
+        if fp8:
+            kq = np.concatenate([quantize_e4m3_groups(kp, b)[0], quantize_e4m3_groups(k[nv:], b)[0]])
+            out[nv:] = dense_attention(quantize_e4m3_groups(q[nv:], 1)[0], kq,
+                                       np.concatenate([vp, v[nv:]]))
+        else:
+            out[nv:] = dense_attention(q[nv:], k, v)
         tail = np.arange(nv, N)
         perm_q = np.concatenate([perm_q, tail])
         perm_k = np.concatenate([perm_k, tail])

@@ -524,3 +524,170 @@ def test_context_moments_use_every_token():
     video_only = O.split_partition(O.whiten(qv, O.psd_sqrt(O.second_moment(kv))), b)
     assert np.array_equal(video_only, np.arange(Nv))    # all ties: id order
     assert not runs_of_angles(video_only)
+
+
+# --- fp8 (OCP E4M3) logits ------------------------------------------------------
+
+def _e4m3_grid():
+    """Every finite OCP E4M3 value from the format's definition (1 sign bit,
+    4 exponent bits with bias 7, 3 mantissa bits, code 0x7f/0xff NaN), with
+    its code, enumerated directly."""
+    vals = []
+    for code in range(256):
+        s, e, m = code >> 7, (code >> 3) & 15, code & 7
+        if e == 15 and m == 7:
+            continue
+        v = (m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+        vals.append((-v if s else v, code))
+    return vals
+
+
+def test_e4m3_round_is_nearest_with_ties_to_even():
+    grid = _e4m3_grid()
+    values = np.array([v for v, _ in grid])
+    assert values.max() == O.E4M3_MAX == 448.0 and values.min() == -448.0
+    # every representable value is a fixed point
+    np.testing.assert_array_equal(O.e4m3_round(values), values)
+    # halfway points go to the neighbour with the even code (mantissa lsb 0)
+    pos = sorted((v, c) for v, c in grid if v > 0)
+    for (lo, clo), (hi, chi) in zip(pos, pos[1:]):
+        mid = (lo + hi) / 2
+        want = lo if (clo & 1) == 0 else hi
+        assert O.e4m3_round(np.array([mid]))[0] == want
+        assert O.e4m3_round(np.array([-mid]))[0] == -want
+    # random inputs: the nearest grid value by brute force
+    rng = _rng(40)
+    x = rng.uniform(-1, 1, 4000) * np.exp2(rng.integers(-12, 9, 4000))
+    x = np.clip(x, -448, 448)
+    got = O.e4m3_round(x)
+    d = np.abs(x[:, None] - values[None, :])
+    best = d.min(axis=1)
+    assert np.all(np.abs(got - x) == best)
+    # spot values from the definition
+    np.testing.assert_array_equal(O.e4m3_round(np.array([1.0625, 1.1875, 17.0, 2.0 ** -10, 3 * 2.0 ** -10, 0.3])),
+                                  [1.0, 1.25, 16.0, 0.0, 2.0 ** -8, 0.3125])
+    with pytest.raises(ValueError):
+        O.e4m3_round(np.array([449.0]))
+
+
+def test_pow2_scale_is_the_smallest_power_of_two():
+    rng = _rng(41)
+    for amax in list(rng.uniform(0, 1, 200) * np.exp2(rng.integers(-30, 30, 200))) + [448.0, 224.0, 449.0, 1.0]:
+        s = O.pow2_scale(amax)
+        assert math.frexp(s)[0] == 0.5                      # a power of two
+        assert amax <= 448.0 * s and amax > 224.0 * s
+    assert O.pow2_scale(0.0) == 1.0
+
+
+def test_group_quantisation_shares_scales_and_bounds_the_error():
+    rng = _rng(42)
+    x = rng.standard_normal((300, 16)) * np.exp2(rng.integers(-5, 5, (300, 1)))
+    deq, sc = O.quantize_e4m3_groups(x, 64)
+    assert sc.shape == (5,)
+    for g in range(5):
+        blk = x[64 * g:64 * (g + 1)]
+        assert sc[g] == O.pow2_scale(np.abs(blk).max())
+        # normal range: relative error <= 2^-4; subnormal range: <= half the 2^-9 quantum
+        err = np.abs(deq[64 * g:64 * (g + 1)] - blk)
+        bound = np.maximum(np.abs(blk) * 2.0 ** -4, 2.0 ** -10 * sc[g])
+        assert np.all(err <= bound * (1 + 1e-12))
+
+
+def test_fp8_logits_exact_on_representable_inputs():
+    """Query rows and key blocks whose entries are multiples of 2^-3 up to
+    7/8 (row / block maximum 7/8): the power-of-two scale 2^-9 maps them to
+    64 x {-7..7}, all E4M3 values.  Keys constant within each block make the
+    mean summaries equal to those rows, so they are representable too, and
+    the fp8 mode must equal the plain one -- wiring errors (wrong groups,
+    scales not undone, the wrong side quantised) break that.  Generic inputs
+    differ from the plain mode by the E4M3 rounding, at the percent level."""
+    rng = _rng(43)
+    N, d, b, topk = 384, 16, 64, 2
+    q = rng.integers(-7, 8, (N, d)) / 8.0
+    k = rng.integers(-7, 8, (N, d)) / 8.0
+    q[:, 0] = 7 / 8.0
+    k[:, 0] = -7 / 8.0
+    for B in range(N // b):
+        k[B * b:(B + 1) * b] = k[B * b]
+    v = rng.standard_normal((N, d))
+    for kw in ({"layout": "identity", "summary": "mean"}, {"layout": "identity", "summary": "mean", "context": True}):
+        a = O.forward_head(q, k, v, b, topk, n_anchor=320, fp8=True, **kw)
+        c = O.forward_head(q, k, v, b, topk, n_anchor=320, **kw)
+        np.testing.assert_allclose(a.out, c.out, rtol=0, atol=1e-12)
+    qg, kg, vg = (rng.standard_normal((N, d)) * s for s in (1.0, 1.5, 1.0))
+    a = O.forward_head(qg, kg, vg, b, topk, fp8=True)
+    c = O.forward_head(qg, kg, vg, b, topk)
+    rel = np.linalg.norm(a.out - c.out) / np.linalg.norm(c.out)
+    assert 1e-4 < rel < 0.1
+
+
+def test_fp8_query_rows_are_quantised_on_their_own():
+    """Per-row query scaling: enlarging one query row (to the largest
+    magnitude of its block) leaves every other row's output bit-identical;
+    a shared block scale would re-round its neighbours."""
+    rng = _rng(44)
+    N, d, b = 256, 16, 64
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    S = rng.standard_normal((4, 4))               # routing fixed, no anchor: only the logits move
+    kw = dict(layout="identity", summary="mean", scores_in=S, fp8=True)
+    a = O.forward_head(q, k, v, b, 2, **kw)
+    q2 = q.copy()
+    q2[5] *= 37.3
+    c = O.forward_head(q2, k, v, b, 2, **kw)
+    keep = np.arange(N) != 5
+    np.testing.assert_array_equal(a.out[keep], c.out[keep])
+
+
+def _ratio_pair(q_row, k, v, b, topk, scores=None, summary="reweight"):
+    r = O.forward_head(np.tile(q_row, (k.shape[0], 1)), k, v, b, topk, layout="identity",
+                       summary=summary, scores_in=scores, fp8=True)
+    return r.out[0, 0] / r.out[0, 1]
+
+
+def test_fp8_keys_are_quantised_per_block():
+    """The same key vector u in two exactly attended blocks, one of which also
+    holds a 2^12 times larger key: with one scale per block, u's entries land
+    in the subnormal range there (powers of two commute with the rounding of
+    normal numbers, not of subnormals), so its two copies get different
+    logits (seen through one-hot values e0 / e1); u representable at both
+    scales gives equal logits (ratio 1)."""
+    rng = _rng(45)
+    N, d, b = 128, 16, 32
+    k = rng.standard_normal((N, d)) * 0.01
+    v = np.zeros((N, d))
+    q = rng.standard_normal(d)
+    u = rng.standard_normal(d)
+    for uu, want_equal in ((u, False), (np.round(u * 2) / 2, True)):
+        kk = k.copy()
+        kk[3], kk[40] = uu, uu                    # blocks 0 and 1
+        kk[41] = 4096 * np.abs(uu).max() * np.ones(d)
+        vv = v.copy()
+        vv[3, 0], vv[40, 1] = 1.0, 1.0
+        ratio = _ratio_pair(q, kk, vv, b, O.n_blocks(N, b))
+        assert (abs(ratio - 1.0) < 1e-12) == want_equal
+
+
+def test_fp8_summary_keys_are_quantised_per_group_of_b_blocks():
+    """Two compressed blocks with identical keys (hence identical mean
+    summaries) in different summary groups of b = 4 blocks, one group also
+    holding a block of 2^12 times larger keys: the shared summary's entries
+    fall into the subnormal range in that group, so the two blocks'
+    compressed logits differ (one-hot values); the plain mode gives ratio 1."""
+    rng = _rng(46)
+    b, nb = 4, 12
+    N, d = b * nb, 8
+    u = rng.standard_normal(d)
+    k = rng.standard_normal((N, d)) * 0.01
+    k[4:8] = u                                    # block 1 (summary group 0)
+    k[20:24] = u                                  # block 5 (summary group 1)
+    k[24:28] = 4096 * np.abs(u).max()             # block 6 (summary group 1)
+    v = np.zeros((N, d))
+    v[4:8, 0] = 1.0
+    v[20:24, 1] = 1.0
+    S = np.zeros((nb, nb))
+    S[:, 0] = 1.0                                 # only block 0 attended exactly
+    q = rng.standard_normal(d)
+    ratio = _ratio_pair(q, k, v, b, 1, scores=S, summary="mean")
+    assert abs(ratio - 1.0) > 1e-6
+    r = O.forward_head(np.tile(q, (N, 1)), k, v, b, 1, layout="identity", summary="mean", scores_in=S)
+    assert abs(r.out[0, 0] / r.out[0, 1] - 1.0) < 1e-12
