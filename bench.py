@@ -51,6 +51,8 @@ def parse():
                    help="token partition: separate query/key Spark-Reblock, or the key partition reused")
     p.add_argument("--sweep", action="store_true",
                    help="the density / noise sweep at the draft shape instead of the layer line")
+    p.add_argument("--fp8", action="store_true",
+                   help="attention logits from E4M3 operands (queries per row, keys per block)")
     p.add_argument("--context", action="store_true",
                    help="tokens from n_anchor on (the ref2va reference frames) are context tokens: "
                         "exact for every query, outside the video-block top-k")
@@ -273,7 +275,7 @@ def main():
     vsum = torch.empty((H, nb, d), dtype=torch.float32, device=dev)
     bias = torch.empty((H, nb), dtype=torch.float32, device=dev)
     out = torch.empty_like(q)
-    a = L.make_args(H, N, d, b, dtype, w.n_anchor, args.layout, context=ctx)
+    a = L.make_args(H, N, d, b, dtype, w.n_anchor, args.layout, context=ctx, fp8=args.fp8)
     ws_r = L.workspace_bytes(a, L.OP_REBLOCK)
     ws_a = L.workspace_bytes(a, L.OP_ATTN)
     ws = torch.empty(max(ws_r, ws_a, 256), dtype=torch.uint8, device=dev)
@@ -369,7 +371,8 @@ def main():
         "data": "synthetic (seeded clustered Gaussian-mixture q/k on the latent grid, v ~ N(0,1))",
         "config": {"workload": w.name, "H": H, "N": N, "d": d, "block": b, "n_blocks": nb,
                    "topk": topk, "density": w.ratio, "layout": args.layout, "summary": "reweight",
-                   **({"context_tokens": N - Nv, "context_blocks": nbt - nb} if ctx else {})},
+                   **({"context_tokens": N - Nv, "context_blocks": nbt - nb} if ctx else {}),
+                   **({"logits": "fp8 e4m3 (QK^T on fp8 MFMA, P V bf16)"} if args.fp8 else {})},
         "exact_mfma_pct_peak": round(100.0 * exact_tf / PEAK_BF16_TFLOPS, 2),
         "stages_ms": {"reblock": round(st_mean[0], 3), "select": round(st_mean[1], 3),
                       "summarize": round(st_mean[2], 3), "attn": round(st_mean[3], 3)},

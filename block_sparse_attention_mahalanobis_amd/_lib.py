@@ -21,6 +21,7 @@ SPARK_F32, SPARK_BF16 = 0, 1
 LAYOUT_REBLOCK, LAYOUT_IDENTITY, LAYOUT_GIVEN, LAYOUT_Q_REUSE_K = 0x0, 0x1, 0x2, 0x3
 SUMMARY_REWEIGHT, SUMMARY_MEAN = 0x0, 0x4
 CONTEXT_EXACT = 0x8
+EXACT_FP8 = 0x10
 OP_REBLOCK, OP_SELECT, OP_SUMMARIZE, OP_ATTN, OP_SPLIT, OP_LAYER = range(6)
 _LAYOUTS = {"reblock": LAYOUT_REBLOCK, "identity": LAYOUT_IDENTITY, "given": LAYOUT_GIVEN,
             "q_reuse_k": LAYOUT_Q_REUSE_K}
@@ -30,7 +31,7 @@ EXPORTED = [
     "spark_version", "spark_status_string", "spark_last_error", "spark_block_count",
     "spark_topk_from_ratio", "spark_workspace_bytes", "spark_reblock", "spark_select",
     "spark_summarize", "spark_attn", "spark_layer", "spark_moments", "spark_msqrt",
-    "spark_whiten", "spark_split", "spark_gather", "spark_diagnostics",
+    "spark_whiten", "spark_split", "spark_gather", "spark_diagnostics", "spark_quant_e4m3",
 ]
 
 
@@ -79,6 +80,7 @@ def lib() -> ctypes.CDLL:
         "spark_split": ([_A, _I, _P, _P, _P, _Z, _P], ctypes.c_int),
         "spark_gather": ([_A, _P, _P, _P, _P, _P, _P], ctypes.c_int),
         "spark_diagnostics": ([_A, _P, _P, _P, _I, _P, _P, _P, _P, _P], ctypes.c_int),
+        "spark_quant_e4m3": ([_I, _I, _I, _I, _P, _P, _P, _P], ctypes.c_int),
     }
     for name, (argt, rest) in sig.items():
         f = getattr(L, name)
@@ -120,10 +122,12 @@ def _dtype_code(dt: torch.dtype) -> int:
 
 
 def make_args(H: int, N: int, d: int, block: int, dtype, n_anchor: Optional[int] = None,
-              layout: str = "reblock", summary: str = "reweight", context: bool = False) -> SparkArgs:
+              layout: str = "reblock", summary: str = "reweight", context: bool = False,
+              fp8: bool = False) -> SparkArgs:
     code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
     return SparkArgs(H, N, d, block, code, N if n_anchor is None else n_anchor,
-                     _LAYOUTS[layout] | _SUMMARIES[summary] | (CONTEXT_EXACT if context else 0), 0)
+                     _LAYOUTS[layout] | _SUMMARIES[summary] | (CONTEXT_EXACT if context else 0)
+                     | (EXACT_FP8 if fp8 else 0), 0)
 
 
 def n_blocks(N: int, block: int) -> int:
@@ -226,12 +230,12 @@ def spark_summarize(k_p, v_pt, anchor, N: int, block: int, summary: str = "rewei
 
 
 def spark_attn(q_p, k_p, v_pt, idx, ksum, vsum, bias, N: int, block: int, perm_q=None, out=None,
-               ws=None, n_anchor: Optional[int] = None, context: bool = False):
+               ws=None, n_anchor: Optional[int] = None, context: bool = False, fp8: bool = False):
     """Fused two-branch attention; [H, N, d] in original order if perm_q is
-    given, else [H, Np, d] in permuted order."""
+    given, else [H, Np, d] in permuted order.  fp8: E4M3 logits."""
     H, Np, d = q_p.shape
     topk = idx.shape[2]
-    a = make_args(H, N, d, block, q_p.dtype, n_anchor, context=context)
+    a = make_args(H, N, d, block, q_p.dtype, n_anchor, context=context, fp8=fp8)
     dev = q_p.device
     if out is None:
         out = torch.empty((H, N if perm_q is not None else Np, d), dtype=q_p.dtype, device=dev)
@@ -259,10 +263,11 @@ def spark_diagnostics(q_p, k_p, idx, ksum, bias, N: int, block: int):
 
 
 def spark_layer(q, k, v, block: int, topk: int, layout: str = "reblock", summary: str = "reweight",
-                n_anchor: Optional[int] = None, out=None, ws=None, context: bool = False):
+                n_anchor: Optional[int] = None, out=None, ws=None, context: bool = False,
+                fp8: bool = False):
     """The whole layer in one call; intermediates live in the workspace."""
     H, N, d = q.shape
-    a = make_args(H, N, d, block, q.dtype, n_anchor, layout, summary, context)
+    a = make_args(H, N, d, block, q.dtype, n_anchor, layout, summary, context, fp8)
     nws = workspace_bytes(a, OP_LAYER, topk)
     if ws is None:
         ws = _ws(nws, q.device)
@@ -331,3 +336,14 @@ def spark_gather(x, perm, block: int, want_rows=True, want_transposed=False, wan
     _check(lib().spark_gather(ctypes.byref(a), _ptr(x), _ptr(perm), _ptr(xp), _ptr(xpt), _ptr(xbar), _stream()),
            "spark_gather")
     return xp, xpt, xbar
+
+
+def spark_quant_e4m3(x, group: int):
+    """E4M3 bytes [rows, d] (uint8) and per-group power-of-two scales of the
+    rows of x [rows, d] (bf16 or fp32), groups of ``group`` rows."""
+    rows, d = x.shape
+    x8 = torch.empty((rows, d), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((-(-rows // group),), dtype=torch.float32, device=x.device)
+    _check(lib().spark_quant_e4m3(rows, d, group, _dtype_code(x.dtype), _ptr(x), _ptr(x8), _ptr(scales),
+                                  _stream()), "spark_quant_e4m3")
+    return x8, scales

@@ -383,6 +383,32 @@ __device__ __forceinline__ void d128_pipeline() {
 }
 constexpr int D128_LDS_TILES = 2 * 128 * 256;   // K + V^T, 64 KB
 
+// fp8 logits: issue order of the QK block (16 LDS reads of 16 bytes, 8
+// 32x32x64 MFMAs): the first k step's reads, then each MFMA of that step
+// followed by two reads of the second step, then the second step's MFMAs.
+__device__ __forceinline__ void d128_pipeline_fp8() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+}
+
+// Smallest power of two s with amax <= 448 s (the E4M3 group scale; 1 for
+// amax = 0 or not finite).
+__device__ __forceinline__ float attn_pow2_scale(float amax) {
+  if (!(amax > 0.f) || !(amax < INFINITY)) return 1.f;
+  int e;
+  frexpf(amax, &e);
+  e -= 9;
+  while (amax > 448.f * ldexpf(1.f, e)) ++e;
+  while (amax <= 448.f * ldexpf(1.f, e - 1)) --e;
+  return ldexpf(1.f, e);
+}
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
 // Sum of the 64 bf16 P values a lane holds, two bf16 per dot-product step
 // (against (1, 1)), in two interleaved partial sums: the softmax denominator
 // is summed from the same rounded P that multiplies V.
@@ -403,13 +429,19 @@ __device__ __forceinline__ float rowsum_bf16(const bf16x8 (&pop)[8]) {
 
 // CTX = false (no context blocks) compiles the tile bookkeeping of the plain
 // layer: one compare less per tile and the idx load unconditional.
-template <bool CTX>
+// FP8: the logits come from E4M3 operands ([blog] Benchmark Results' FP8
+// runs): kp / ks16 then point at E4M3 key tiles (16 KB, one power-of-two
+// scale per tile in kscale / ksscale), each query row is rounded to E4M3
+// with its own scale in registers, and S^T runs on 32x32x64 fp8 MFMAs;
+// P V stays bf16.
+template <bool CTX, bool FP8>
 __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
     const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vpt, const int32_t* __restrict__ idx, int topk,
     const uint16_t* __restrict__ ks16, const uint16_t* __restrict__ vs16t,
     const float* __restrict__ bias2, const int32_t* __restrict__ perm_q,
-    uint16_t* __restrict__ out, int H, int N, int Nv, int nb, int nbc, int nbp, float scale_log2) {
+    uint16_t* __restrict__ out, int H, int N, int Nv, int nb, int nbc, int nbp, float scale_log2,
+    const float* __restrict__ kscale, const float* __restrict__ ksscale) {
   constexpr int D = 128, BK = 128;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   unsigned char* sK = smem;
@@ -458,16 +490,40 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
     koff[i] = (uint32_t)(grow * D + lc * 8) * 2u;
     voff[i] = (uint32_t)(srow * BK + lc * 8) * 2u;
   }
+  if constexpr (FP8) {
+    // E4M3 K tile: 128 rows of 128 bytes; load i of this wave fills LDS rows
+    // 32 wave + 8 i .. +7, the 16-byte chunk slot XOR-swizzled by (row >> 1) & 7
+    // (16 consecutive rows then hit 16 distinct bank groups); rows in the
+    // same permuted order as the bf16 tiles
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int srow = 32 * wave + 8 * i + (lane >> 3);
+      const int c = (lane & 7) ^ ((srow >> 1) & 7);
+      const int grow = (srow & ~31) + ((((srow & 31) >> 3) >> 1) << 4) + (((srow >> 2) & 1) << 3) +
+                       ((((srow & 31) >> 3) & 1) << 2) + (srow & 3);
+      koff[i] = (uint32_t)(grow * 128 + c * 16);
+    }
+  }
+  constexpr int KES = FP8 ? 1 : 2;   // bytes per key element
   auto tile_base = [&](int t, const char*& kb, const char*& vb) {
     if (t < tp.nex) {
       const int B = (!CTX || t < tp.nidx) ? myidx[t] : t + tp.bofs;
-      kb = reinterpret_cast<const char*>(kp + ((long)h * Np + (long)B * BK) * D);
+      kb = reinterpret_cast<const char*>(kp) + ((long)h * Np + (long)B * BK) * D * KES;
       vb = reinterpret_cast<const char*>(vpt + ((long)h * nbt + B) * (long)D * BK);
     } else {
       const int c = t - tp.nex;
-      kb = reinterpret_cast<const char*>(ks16 + ((long)h * nbp + (long)c * BK) * D);
+      kb = reinterpret_cast<const char*>(ks16) + ((long)h * nbp + (long)c * BK) * D * KES;
       vb = reinterpret_cast<const char*>(vs16t + ((long)h * (nbp / BK) + c) * (long)D * BK);
     }
+  };
+  // one 16 KB E4M3 key tile, four 1 KB direct loads per wave
+  auto issue8 = [&](const char* base, unsigned char* dst) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 128 * 128, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (void __attribute__((address_space(3)))*)(dst + (4 * wave + i) * 1024), 16, koff[i], 0, 0, 0);
   };
   // one 32 KB tile through a buffer resource (scalar base, 32-bit lane
   // offsets; bytes past the tile would read as 0)
@@ -482,10 +538,41 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
   };
 
   const long qrow = (long)h * Np + (long)A * BK + wave * 32 + l32;
-  bf16x8 qop[D / 16];
+  bf16x8 qop[FP8 ? 1 : D / 16];
+  i32x8 q8[2];       // E4M3 query, lane (l32, hf): d = 64 s + 32 hf + 0..31
+  float qscale = 1.f;
+  if constexpr (FP8) {
+    bf16x8 raw[2][4];
+    float amax = 0.f;
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s)
-    qop[s] = *reinterpret_cast<const bf16x8*>(qp + qrow * D + 16 * s + 8 * hf);
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        raw[s2][u] = *reinterpret_cast<const bf16x8*>(qp + qrow * D + 64 * s2 + 32 * hf + 8 * u);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)raw[s2][u][e]));
+      }
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    qscale = attn_pow2_scale(amax);
+    const float inv = 1.f / qscale;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const bf16x8 r = raw[s2][u];
+          const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32((float)r[4 * w] * inv,
+                                                                         (float)r[4 * w + 1] * inv, 0, false) & 0xffffu;
+          const uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32((float)r[4 * w + 2] * inv,
+                                                                         (float)r[4 * w + 3] * inv, 0, false) & 0xffffu;
+          q8[s2][2 * u + w] = (int)(lo | (hi << 16));
+        }
+  } else {
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      qop[s] = *reinterpret_cast<const bf16x8*>(qp + qrow * D + 16 * s + 8 * hf);
+  }
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -499,11 +586,18 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
   int ro[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) ro[s] = sw_off(l32, 2 * s + hf);
+  // E4M3 K operand reads: row 32 jt + l32, logical chunks 4 s + 2 hf + u
+  int ro8[2][2];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) ro8[s2][u] = l32 * 128 + (((4 * s2 + 2 * hf + u) ^ ((l32 >> 1) & 7)) << 4);
 
   {
     const char *kb, *vb;
     tile_base(0, kb, vb);
-    issue(kb, koff, sK);
+    if constexpr (FP8) issue8(kb, sK);
+    else issue(kb, koff, sK);
     issue(vb, voff, sV);
   }
 
@@ -519,7 +613,25 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
       for (int v = 0; v < 16; ++v) sacc[jt][v] = 0.f;
     }
     __builtin_amdgcn_s_setprio(2);  // favour the wave that feeds the matrix core
-    {
+    if constexpr (FP8) {
+      i32x8 kop8[2][4];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          const uint4 lo = *reinterpret_cast<const uint4*>(sK + ro8[s2][0] + jt * 4096);
+          const uint4 hi = *reinterpret_cast<const uint4*>(sK + ro8[s2][1] + jt * 4096);
+          kop8[s2][jt] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                               (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt)
+          sacc[jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop8[s2][jt], q8[s2], sacc[jt], 0, 0, 0,
+                                                                     0, 0, 0);
+      d128_pipeline_fp8();
+    } else {
       // all 32 K operand reads and MFMAs are written out; the group barriers
       // below fix the issue order: the reads of steps 0..D128_PF-1 first,
       // then each MFMA of step s followed by one read of step s+D128_PF, so
@@ -542,7 +654,8 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
     const char *kb1 = nullptr, *vb1 = nullptr;
     if (t + 1 < ntiles) {
       tile_base(t + 1, kb1, vb1);
-      issue(kb1, koff, sK);
+      if constexpr (FP8) issue8(kb1, sK);
+      else issue(kb1, koff, sK);
     }
 
     // P against the lazy reference m_ref: p = 2^(logit * log2 e - m_ref).
@@ -552,8 +665,10 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
     // (the first tile, or logits that rose by more than ~12 in log2 units)
     // the exact tile maximum is taken, the running sums are rescaled and P
     // is recomputed.
+    float lsc = scale_log2;   // logit -> log2 units (fp8: times the two group scales)
     if (exact) {
       const int B = (!CTX || t < tp.nidx) ? myidx[t] : t + tp.bofs;
+      if constexpr (FP8) lsc = scale_log2 * qscale * kscale[(long)h * nbt + B];
       const int valid = CTX ? block_rows(B, nb, nbt, N, Nv, BK) : ((B == nb - 1) ? Nv - (nb - 1) * BK : BK);
       if (valid < BK) {
 #pragma unroll
@@ -566,12 +681,13 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
       }
     } else {
       const float* bb = sBias + (t - tp.nex) * BK;
+      if constexpr (FP8) lsc = scale_log2 * qscale * ksscale[(long)h * (nbp / BK) + (t - tp.nex)];
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int j = 32 * jt + ((v < 8) ? 8 * hf + v : 16 + 8 * hf + v - 8);
-          sacc[jt][v] = fmaf(sacc[jt][v], scale_log2, bb[j]);
+          sacc[jt][v] = fmaf(sacc[jt][v], lsc, bb[j]);
         }
     }
     bf16x8 pop[8];
@@ -581,7 +697,7 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
 #define SPARK_D128_P()                                                                   \
     {                                                                                   \
       const float nm = -m_ref;                                                          \
-      const float sc = exact ? scale_log2 : 1.f;                                        \
+      const float sc = exact ? lsc : 1.f;                                               \
       _Pragma("unroll") for (int jt = 0; jt < 4; ++jt)                                  \
       _Pragma("unroll") for (int hh = 0; hh < 2; ++hh)                                  \
       _Pragma("unroll") for (int e = 0; e < 8; ++e)                                     \
@@ -595,7 +711,7 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
       for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[jt][v]);
-      if (exact) mx *= scale_log2;
+      if (exact) mx *= lsc;
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_new = fmaxf(m_ref, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
@@ -610,9 +726,13 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
 #undef SPARK_D128_P
     l_run += psum;
 
-    // V(t) landed: only this wave's 8 K(t+1) loads may be outstanding
-    if (t + 1 < ntiles) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // V(t) landed: only this wave's K(t+1) loads (8 bf16 / 4 fp8) may be outstanding
+    if (t + 1 < ntiles) {
+      if constexpr (FP8) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     __syncthreads();
     __builtin_amdgcn_s_setprio(2);
     {
@@ -788,16 +908,38 @@ __global__ __launch_bounds__(128) void attn_generic(
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-// N here is the number of video tokens (all tokens without context).
-size_t attn_ws_bytes(int H, int N, int D, int BK, int dtype) {
-  if (dtype != SPARK_BF16 || (BK != 32 && BK != 64 && BK != 128)) return 0;
-  const int nb = cdiv(N, BK);
-  const int nbp = cdiv(nb, BK) * BK;
-  const size_t a = (size_t)H * nbp * D * 2;  // ks16
-  const size_t b = (size_t)H * nbp * D * 2;  // vs16t
-  const size_t c = (size_t)H * nbp * 4;      // bias2
+// Workspace of attn_launch: the bf16 summary tiles, and in fp8 mode the E4M3
+// key tiles (all nbt blocks) and summary tiles with their scales.
+struct AttnWs {
+  size_t ks16, vs16t, bias2, k8, kscale, ks8, ksscale, total;
+};
+static AttnWs attn_ws_plan(int H, int N, int Nv, int D, int BK, bool fp8) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  return up(a) + up(b) + up(c);
+  const int nb = cdiv(Nv, BK), nbt = nb + cdiv(N - Nv, BK);
+  const int nbp = cdiv(nb, BK) * BK;
+  AttnWs w;
+  size_t o = 0;
+  w.ks16 = o;    o += up((size_t)H * nbp * D * 2);
+  w.vs16t = o;   o += up((size_t)H * nbp * D * 2);
+  w.bias2 = o;   o += up((size_t)H * nbp * 4);
+  w.k8 = o;      o += fp8 ? up((size_t)H * nbt * BK * D) : 0;
+  w.kscale = o;  o += fp8 ? up((size_t)H * nbt * 4) : 0;
+  w.ks8 = o;     o += fp8 ? up((size_t)H * nbp * D) : 0;
+  w.ksscale = o; o += fp8 ? up((size_t)H * (nbp / BK) * 4) : 0;
+  w.total = o;
+  return w;
+}
+
+// Nv video tokens of N (Nv = N without context tokens).
+size_t attn_ws_bytes(int H, int N, int Nv, int D, int BK, int dtype, bool fp8) {
+  if (dtype != SPARK_BF16 || (BK != 32 && BK != 64 && BK != 128)) return 0;
+  return attn_ws_plan(H, N, Nv, D, BK, fp8).total;
+}
+
+bool attn_fp8_supported(int H, int N, int Nv, int D, int BK, int dtype) {
+  const int nb = cdiv(Nv, BK), nbp = cdiv(nb, BK) * BK;
+  return dtype == SPARK_BF16 && D == 128 && BK == 128 &&
+         (size_t)D128_LDS_TILES + (size_t)nbp * 4 <= 80 * 1024;
 }
 
 bool attn_uses_mfma(int dtype, int BK) {
@@ -827,30 +969,36 @@ static int launch_mfma(const void* qp, const void* kp, const void* vpt, const in
   return spark_check_launch("attn_mfma");
 }
 
+// kp / ks16: bf16 tiles, or (fp8) E4M3 tiles with their scales kscale / ksscale
 static int launch_d128(const void* qp, const void* kp, const void* vpt, const int32_t* idx, int topk,
                      const uint16_t* ks16, const uint16_t* vs16t, const float* bias2,
                      const int32_t* perm_q, void* out, int H, int N, int Nv, int nb, int nbc,
-                     int nbp, hipStream_t st) {
+                     int nbp, bool fp8, const float* kscale, const float* ksscale, hipStream_t st) {
   const size_t lds = D128_LDS_TILES + (size_t)nbp * 4;
   static bool attr_set = false;
   if (!attr_set) {
-    hipFuncSetAttribute((const void*)attn_mfma_d128<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        80 * 1024);
-    hipFuncSetAttribute((const void*)attn_mfma_d128<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        80 * 1024);
+    hipFuncSetAttribute((const void*)attn_mfma_d128<false, false>, hipFuncAttributeMaxDynamicSharedMemorySize, 80 * 1024);
+    hipFuncSetAttribute((const void*)attn_mfma_d128<true, false>, hipFuncAttributeMaxDynamicSharedMemorySize, 80 * 1024);
+    hipFuncSetAttribute((const void*)attn_mfma_d128<false, true>, hipFuncAttributeMaxDynamicSharedMemorySize, 80 * 1024);
+    hipFuncSetAttribute((const void*)attn_mfma_d128<true, true>, hipFuncAttributeMaxDynamicSharedMemorySize, 80 * 1024);
     attr_set = true;
   }
   const float scale_log2 = kLog2e / sqrtf(128.f);
   const long slots = 8L * (((nbc + 7) >> 3) + ((nb + 7) >> 3));   // d128_slots
   if ((long)H * slots > 0x7fffffffL) return spark_set_error(SPARK_E_SHAPE, "spark_attn: grid too large");
-  if (nbc > 0)
-    hipLaunchKernelGGL(attn_mfma_d128<true>, dim3((unsigned)(H * slots)), dim3(D128_NT), lds, st,
-                       (const uint16_t*)qp, (const uint16_t*)kp, (const uint16_t*)vpt, idx, topk, ks16,
-                       vs16t, bias2, perm_q, (uint16_t*)out, H, N, Nv, nb, nbc, nbp, scale_log2);
-  else
-    hipLaunchKernelGGL(attn_mfma_d128<false>, dim3((unsigned)(H * slots)), dim3(D128_NT), lds, st,
-                       (const uint16_t*)qp, (const uint16_t*)kp, (const uint16_t*)vpt, idx, topk, ks16,
-                       vs16t, bias2, perm_q, (uint16_t*)out, H, N, Nv, nb, nbc, nbp, scale_log2);
+  const dim3 grid((unsigned)(H * slots)), block(D128_NT);
+#define SPARK_D128_LAUNCH(C, F)                                                                    \
+  hipLaunchKernelGGL((attn_mfma_d128<C, F>), grid, block, lds, st, (const uint16_t*)qp,             \
+                     (const uint16_t*)kp, (const uint16_t*)vpt, idx, topk, ks16, vs16t, bias2, perm_q, \
+                     (uint16_t*)out, H, N, Nv, nb, nbc, nbp, scale_log2, kscale, ksscale)
+  if (nbc > 0) {
+    if (fp8) SPARK_D128_LAUNCH(true, true);
+    else SPARK_D128_LAUNCH(true, false);
+  } else {
+    if (fp8) SPARK_D128_LAUNCH(false, true);
+    else SPARK_D128_LAUNCH(false, false);
+  }
+#undef SPARK_D128_LAUNCH
   return spark_check_launch("attn_mfma_d128");
 }
 
@@ -868,27 +1016,46 @@ static int launch_generic(const void* qp, const void* kp, const void* vpt, const
   return spark_check_launch("attn_generic");
 }
 
-// Nv = N: the plain layer; Nv < N: tokens [Nv, N) are context tokens.
+int quant_e4m3_launch(int H, long in_rows, long out_rows, int D, int G, int dtype, const void* x,
+                      uint8_t* x8, float* scales, hipStream_t st);
+
+// Nv = N: the plain layer; Nv < N: tokens [Nv, N) are context tokens.  fp8:
+// E4M3 logits (the caller has checked attn_fp8_supported).
 int attn_launch(int H, int N, int Nv, int D, int BK, int dtype, const void* qp, const void* kp,
                 const void* vpt, const int32_t* idx, int topk, const float* ksum,
                 const float* vsum, const float* bias, const int32_t* perm_q, void* out, void* ws,
-                hipStream_t st) {
+                bool fp8, hipStream_t st) {
   const int nb = cdiv(Nv, BK), nbc = cdiv(N - Nv, BK);
   if (attn_uses_mfma(dtype, BK)) {
     const int nbp = cdiv(nb, BK) * BK;
-    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    uint16_t* ks16 = (uint16_t*)ws;
-    uint16_t* vs16t = (uint16_t*)((char*)ws + up((size_t)H * nbp * D * 2));
-    float* bias2 = (float*)((char*)ws + 2 * up((size_t)H * nbp * D * 2));
+    const AttnWs w = attn_ws_plan(H, N, Nv, D, BK, fp8);
+    char* wb = (char*)ws;
+    uint16_t* ks16 = (uint16_t*)(wb + w.ks16);
+    uint16_t* vs16t = (uint16_t*)(wb + w.vs16t);
+    float* bias2 = (float*)(wb + w.bias2);
     const long total = (long)H * nbp * D;
     const int grid = (int)std::min<long>((total + 255) / 256, 4096);
     hipLaunchKernelGGL(attn_prep_summaries, dim3(grid), dim3(256), 0, st, ksum, vsum, bias, ks16,
                        vs16t, bias2, H, Nv, D, BK, nb, nbp);
     int rc = spark_check_launch("attn_prep_summaries");
     if (rc) return rc;
+    if (fp8) {
+      uint8_t* k8 = (uint8_t*)(wb + w.k8);
+      uint8_t* ks8 = (uint8_t*)(wb + w.ks8);
+      float* kscale = (float*)(wb + w.kscale);
+      float* ksscale = (float*)(wb + w.ksscale);
+      const long rows = (long)(nb + nbc) * BK;
+      rc = quant_e4m3_launch(H, rows, rows, D, BK, SPARK_BF16, kp, k8, kscale, st);
+      if (rc) return rc;
+      rc = quant_e4m3_launch(H, nb, nbp, D, BK, SPARK_F32, ksum, ks8, ksscale, st);
+      if (rc) return rc;
+      return launch_d128(qp, k8, vpt, idx, topk, (const uint16_t*)ks8, vs16t, bias2, perm_q, out, H, N, Nv,
+                         nb, nbc, nbp, true, kscale, ksscale, st);
+    }
     if (D == 128) {
       if (BK == 128 && (size_t)D128_LDS_TILES + (size_t)nbp * 4 <= 80 * 1024)
-        return launch_d128(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, Nv, nb, nbc, nbp, st);
+        return launch_d128(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, Nv, nb, nbc, nbp,
+                           false, nullptr, nullptr, st);
       if (BK == 128) return launch_mfma<128, 128>(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, Nv, nb, nbc, nbp, st);
       if (BK == 64) return launch_mfma<128, 64>(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, Nv, nb, nbc, nbp, st);
       return launch_mfma<128, 32>(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, Nv, nb, nbc, nbp, st);

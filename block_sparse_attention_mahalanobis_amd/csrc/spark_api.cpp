@@ -15,8 +15,11 @@ namespace spark {
 int attn_launch(int H, int N, int Nv, int D, int BK, int dtype, const void* qp, const void* kp,
                 const void* vpt, const int32_t* idx, int topk, const float* ksum,
                 const float* vsum, const float* bias, const int32_t* perm_q, void* out, void* ws,
-                hipStream_t st);
-size_t attn_ws_bytes(int H, int N, int D, int BK, int dtype);
+                bool fp8, hipStream_t st);
+size_t attn_ws_bytes(int H, int N, int Nv, int D, int BK, int dtype, bool fp8);
+bool attn_fp8_supported(int H, int N, int Nv, int D, int BK, int dtype);
+int quant_e4m3_launch(int H, long in_rows, long out_rows, int D, int G, int dtype, const void* x,
+                      uint8_t* x8, float* scales, hipStream_t st);
 bool attn_uses_mfma(int dtype, int BK);
 int gather_launch(int H, int N, int Nv, int D, int BK, int dtype, const void* x,
                   const int32_t* perm, void* xp, void* xpt, float* xbar, hipStream_t st);
@@ -104,7 +107,7 @@ int check_args(const spark_args* a, const char* fn) {
     return spark_set_error(SPARK_E_SHAPE, "%s: n_anchor=%d not in [1, N=%d]", fn, a->n_anchor, a->N);
   const uint32_t layout = a->flags & SPARK_LAYOUT_MASK;
   if (layout > SPARK_LAYOUT_Q_REUSE_K ||
-      (a->flags & ~(SPARK_LAYOUT_MASK | SPARK_SUMMARY_MEAN | SPARK_CONTEXT_EXACT)))
+      (a->flags & ~(SPARK_LAYOUT_MASK | SPARK_SUMMARY_MEAN | SPARK_CONTEXT_EXACT | SPARK_EXACT_FP8)))
     return spark_set_error(SPARK_E_ARG, "%s: bad flags 0x%x", fn, a->flags);
   const long nb = (a->N + (long)a->block - 1) / a->block;
   if ((long)a->H * nb > 0x7fffffffL || (long)a->N * a->d > 0x7fffffffL)
@@ -128,6 +131,18 @@ Geo geo(const spark_args* a) {
 }
 
 int nblocks(const spark_args* a) { return geo(a).nb; }
+
+bool fp8_of(const spark_args* a) { return (a->flags & SPARK_EXACT_FP8) != 0; }
+
+// SPARK_EXACT_FP8 runs on the d = 128, block 128 bf16 kernel only
+int check_fp8(const spark_args* a, const char* fn) {
+  if (!fp8_of(a)) return SPARK_OK;
+  const Geo g = geo(a);
+  if (!attn_fp8_supported(a->H, a->N, g.Nv, a->d, a->block, a->dtype))
+    return spark_set_error(SPARK_E_UNSUPPORTED,
+                           "%s: SPARK_EXACT_FP8 needs bf16, d = 128, block = 128 and at most 4096 video blocks", fn);
+  return SPARK_OK;
+}
 
 int reject_context(const spark_args* a, const char* fn) {
   if (a->flags & SPARK_CONTEXT_EXACT)
@@ -181,7 +196,7 @@ size_t layer_bufs(const spark_args* a, int topk, char* base, LayerBufs* o) {
   b.bias = (float*)take((size_t)H * nb * 4);
   b.scratch = take(0);
   if (o) *o = b;
-  return off + std::max(reblock_ws(a), attn_ws_bytes(H, g.Nv, D, a->block, a->dtype));
+  return off + std::max(reblock_ws(a), attn_ws_bytes(H, N, g.Nv, D, a->block, a->dtype, fp8_of(a)));
 }
 
 }  // namespace
@@ -227,7 +242,7 @@ size_t spark_workspace_bytes(const spark_args* a, int op, int32_t topk) {
     case SPARK_OP_REBLOCK: return reblock_ws(a);
     case SPARK_OP_SELECT: return 0;
     case SPARK_OP_SUMMARIZE: return 0;
-    case SPARK_OP_ATTN: return attn_ws_bytes(a->H, geo(a).Nv, a->d, a->block, a->dtype);
+    case SPARK_OP_ATTN: return attn_ws_bytes(a->H, a->N, geo(a).Nv, a->d, a->block, a->dtype, fp8_of(a));
     case SPARK_OP_SPLIT: return split_ws_bytes(2 * a->H, a->N, a->d, a->block, a->dtype);
     case SPARK_OP_LAYER:
       if (topk < 1 || topk > nb) {
@@ -442,14 +457,15 @@ int spark_attn(const spark_args* a, const void* q_p, const void* k_p, const void
   CHECK(check_ptr(bias, fn, "bias"));
   CHECK(check_ptr(perm_q, fn, "perm_q", true));
   CHECK(check_ptr(out, fn, "out"));
+  CHECK(check_fp8(a, fn));
   const int Nv = geo(a).Nv;
-  const size_t need = attn_ws_bytes(a->H, Nv, a->d, a->block, a->dtype);
+  const size_t need = attn_ws_bytes(a->H, a->N, Nv, a->d, a->block, a->dtype, fp8_of(a));
   if (need > 0) {
     CHECK(check_ptr(ws, fn, "ws"));
     if (ws_bytes < need) return spark_set_error(SPARK_E_WORKSPACE, "%s: ws_bytes %zu < %zu", fn, ws_bytes, need);
   }
   return attn_launch(a->H, a->N, Nv, a->d, a->block, a->dtype, q_p, k_p, v_pt, idx, topk, ksum, vsum,
-                     bias, perm_q, out, ws, (hipStream_t)stream);
+                     bias, perm_q, out, ws, fp8_of(a), (hipStream_t)stream);
 }
 
 int spark_layer(const spark_args* a, const void* q, const void* k, const void* v, int32_t topk,
@@ -460,6 +476,7 @@ int spark_layer(const spark_args* a, const void* q, const void* k, const void* v
     return spark_set_error(SPARK_E_ARG, "%s: SPARK_LAYOUT_GIVEN needs spark_reblock", fn);
   const int nb = nblocks(a);
   if (topk < 1 || topk > nb) return spark_set_error(SPARK_E_SHAPE, "%s: topk=%d not in [1, %d]", fn, topk, nb);
+  CHECK(check_fp8(a, fn));
   CHECK(check_ptr(q, fn, "q"));
   CHECK(check_ptr(k, fn, "k"));
   CHECK(check_ptr(v, fn, "v"));
@@ -486,6 +503,7 @@ int spark_diagnostics(const spark_args* a, const void* q_p, const void* k_p, con
   const char* fn = "spark_diagnostics";
   CHECK(check_args(a, fn));
   CHECK(reject_context(a, fn));
+  if (fp8_of(a)) return spark_set_error(SPARK_E_UNSUPPORTED, "%s: SPARK_EXACT_FP8 is not supported here", fn);
   const int nb = nblocks(a);
   if (topk < 1 || topk > nb) return spark_set_error(SPARK_E_SHAPE, "%s: topk=%d not in [1, %d]", fn, topk, nb);
   CHECK(check_ptr(q_p, fn, "q_p"));
@@ -498,4 +516,18 @@ int spark_diagnostics(const spark_args* a, const void* q_p, const void* k_p, con
   if (recall == nullptr && logmass == nullptr)
     return spark_set_error(SPARK_E_ARG, "%s: recall and logmass are both NULL", fn);
   return diag_launch(a->H, a->N, a->d, a->block, a->dtype, q_p, k_p, idx, topk, ksum, bias, recall, logmass, (hipStream_t)stream);
+}
+
+int spark_quant_e4m3(int32_t rows, int32_t d, int32_t group, int32_t dtype, const void* x, uint8_t* x8,
+                     float* scales, spark_stream_t stream) {
+  const char* fn = "spark_quant_e4m3";
+  if (rows < 1 || group < 1) return spark_set_error(SPARK_E_SHAPE, "%s: rows=%d group=%d", fn, rows, group);
+  if (d != 64 && d != 128) return spark_set_error(SPARK_E_UNSUPPORTED, "%s: d=%d not in {64, 128}", fn, d);
+  if (dtype != SPARK_F32 && dtype != SPARK_BF16)
+    return spark_set_error(SPARK_E_DTYPE, "%s: dtype %d is not SPARK_F32/SPARK_BF16", fn, dtype);
+  CHECK(check_ptr(x, fn, "x"));
+  if (x8 == nullptr || scales == nullptr) return spark_set_error(SPARK_E_ARG, "%s: x8 or scales is NULL", fn);
+  if (reinterpret_cast<uintptr_t>(x8) % 4 != 0)
+    return spark_set_error(SPARK_E_ARG, "%s: x8 is not 4-byte aligned", fn);
+  return quant_e4m3_launch(1, rows, rows, d, group, dtype, x, x8, scales, (hipStream_t)stream);
 }

@@ -96,6 +96,16 @@ typedef enum spark_dtype { SPARK_F32 = 0, SPARK_BF16 = 1 } spark_dtype;
  * spark_diagnostics reject it (SPARK_E_UNSUPPORTED).  With n_anchor = N it
  * changes nothing. */
 #define SPARK_CONTEXT_EXACT 0x8u
+/* flags: fp8 attention logits ([blog] 03 / Evaluation: Benchmark Results, the
+ * DiT's FP8 runs; the pages give no further detail).  Every attention logit
+ * q . k is computed from OCP E4M3 operands: each query row, each key block
+ * (block rows) and each group of `block` consecutive summary keys is scaled
+ * by the smallest power of two s with max |x| <= 448 s and rounded to the
+ * nearest E4M3 value (ties to even); the logit is s_q s_k (q8 . k8).  P and
+ * V keep the bf16 path.  Supported for bf16, d = 128, block = 128 (the
+ * spark_attn / spark_layer kernels); SPARK_E_UNSUPPORTED otherwise, and
+ * from spark_diagnostics. */
+#define SPARK_EXACT_FP8 0x10u
 
 typedef struct spark_args {
   int32_t H;        /* heads                                                  */
@@ -104,7 +114,8 @@ typedef struct spark_args {
   int32_t block;    /* tokens per block, 1..128                               */
   int32_t dtype;    /* spark_dtype of q, k, v                                 */
   int32_t n_anchor; /* the anchor averages query rows [0, n_anchor); 1..N     */
-  uint32_t flags;   /* SPARK_LAYOUT_* | SPARK_SUMMARY_* | SPARK_CONTEXT_EXACT */
+  uint32_t flags;   /* SPARK_LAYOUT_* | SPARK_SUMMARY_* | SPARK_CONTEXT_EXACT |
+                       SPARK_EXACT_FP8 */
   int32_t reserved; /* must be 0                                              */
 } spark_args;
 
@@ -262,6 +273,16 @@ int spark_split(const spark_args* args, int32_t count, const void* xhat, int32_t
  * real rows. */
 int spark_gather(const spark_args* args, const void* x, const int32_t* perm, void* x_p,
                  void* x_pt, float* xbar, spark_stream_t stream);
+
+/* E4M3 quantisation as SPARK_EXACT_FP8 applies it: `rows` rows of d values
+ * (x: SPARK_BF16 or SPARK_F32 per dtype, d in {64, 128}) in consecutive
+ * groups of `group` rows (the last may be short); group g is scaled by the
+ * smallest power of two s_g with max |x| <= 448 s_g (s_g = 1 for an all-zero
+ * group) and x / s_g is rounded to the nearest OCP E4M3 value, ties to even.
+ * Writes x8 [rows, d] bytes (4-byte aligned) and scales [ceil(rows / group)]
+ * fp32 (the s_g).  Device pointers, enqueued on the stream. */
+int spark_quant_e4m3(int32_t rows, int32_t d, int32_t group, int32_t dtype, const void* x,
+                     uint8_t* x8, float* scales, spark_stream_t stream);
 
 /* ---- routing diagnostics (outside the layer; dense cost) ---------------- */
 

@@ -21,7 +21,7 @@ MISALIGNED = ctypes.c_void_p(0x10008)
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(spark_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(spark_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -93,7 +93,7 @@ def test_null_misaligned_topk_and_workspace_errors(lib):
     rc = lib.spark_select(ctypes.byref(a), None, FAKE, None, 4, FAKE, None, None)
     assert rc == -1 and "qbar" in L.last_error()
     bad_flags = _args()
-    bad_flags.flags = 0x10
+    bad_flags.flags = 0x20
     rc = lib.spark_reblock(ctypes.byref(bad_flags), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
                            FAKE, None, FAKE, 1 << 40, None)
     assert rc == -1
@@ -147,6 +147,26 @@ def test_context_mode_validation(lib):
     k_ref = L.topk_from_ratio(0.2, O.n_blocks(245952, 128))
     assert L.workspace_bytes(ref, L.OP_LAYER, k_ref) < L.workspace_bytes(plain, L.OP_LAYER, k_ref)
     assert L.workspace_bytes(ref, L.OP_REBLOCK) < L.workspace_bytes(plain, L.OP_REBLOCK)
+
+
+def test_fp8_validation(lib):
+    """SPARK_EXACT_FP8 needs bf16, d = 128, block = 128; the diagnostics
+    refuse it; spark_quant_e4m3 validates its arguments before any launch."""
+    ok = L.make_args(2, 1000, 128, 128, 1, fp8=True)
+    assert L.workspace_bytes(ok, L.OP_ATTN) > L.workspace_bytes(L.make_args(2, 1000, 128, 128, 1), L.OP_ATTN)
+    for bad in (L.make_args(2, 1000, 128, 128, 0, fp8=True), L.make_args(2, 1000, 128, 64, 1, fp8=True),
+                L.make_args(2, 1000, 64, 128, 1, fp8=True)):
+        rc = lib.spark_attn(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                            1 << 40, None)
+        assert rc == -4 and "FP8" in L.last_error()
+        assert lib.spark_layer(ctypes.byref(bad), FAKE, FAKE, FAKE, 2, FAKE, FAKE, 1 << 40, None) == -4
+    assert lib.spark_diagnostics(ctypes.byref(ok), FAKE, FAKE, FAKE, 2, FAKE, FAKE, FAKE, FAKE, None) == -4
+    q = lib.spark_quant_e4m3
+    assert q(0, 128, 128, 1, FAKE, FAKE, FAKE, None) == -2
+    assert q(10, 96, 128, 1, FAKE, FAKE, FAKE, None) == -4
+    assert q(10, 128, 128, 7, FAKE, FAKE, FAKE, None) == -3
+    assert q(10, 128, 128, 1, None, FAKE, FAKE, None) == -1
+    assert q(10, 128, 128, 1, FAKE, None, FAKE, None) == -1
 
 
 def test_diagnostics_validation(lib):
