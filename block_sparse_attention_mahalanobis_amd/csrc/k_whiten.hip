@@ -15,7 +15,7 @@
 
 namespace spark {
 
-constexpr int MOM_TOK = 64;      // rows staged per LDS round
+constexpr int MOM_TOK = 128;     // rows staged per LDS round
 
 // Rows per moment partial: enough chunks that both sides of all heads give
 // about 2048 workgroups (the chip holds 256 CUs x several), a multiple of
@@ -57,30 +57,31 @@ __global__ __launch_bounds__(256) void moments_mfma(const uint16_t* __restrict__
   const bool want_cs = cpart != nullptr && t < H;
   float cs[8] = {0, 0, 0, 0, 0, 0, 0, 0};   // column sums of rows < n_anchor
 
-  // staging: thread -> (4-row group, 8-col chunk)
+  // staging: thread -> (RPG-row group, 8-col chunk); the next round's rows
+  // (32 KB per workgroup for d = 128) are in flight while this round runs
   constexpr int CPR = D / 8;                 // 16 or 8
-  constexpr int RG = 256 / CPR;              // 4-row groups per round: 16 or 32
-  static_assert(RG * 4 >= MOM_TOK, "staging covers the round");
+  constexpr int RG = 256 / CPR;              // row groups per round: 16 or 32
+  constexpr int RPG = MOM_TOK / RG;          // rows per group: 8 or 4
+  static_assert(RPG == 8 || RPG == 4, "staging layout");
   const int g = tid / CPR, cc = (tid % CPR) * 8;
-  const bool stager = g * 4 < MOM_TOK;
+  constexpr bool stager = true;
 
-  uint4 pf[4];
+  uint4 pf[RPG];
   auto fetch = [&](long rb) {
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const long row = rb + g * 4 + rr;
-      pf[rr] = (stager && row < r1) ? *reinterpret_cast<const uint4*>(xt + row * D + cc)
-                                    : make_uint4(0, 0, 0, 0);
+    for (int rr = 0; rr < RPG; ++rr) {
+      const long row = rb + g * RPG + rr;
+      pf[rr] = (row < r1) ? *reinterpret_cast<const uint4*>(xt + row * D + cc) : make_uint4(0, 0, 0, 0);
     }
   };
   fetch(r0);
   for (long rb = r0; rb < r1; rb += MOM_TOK) {
     __syncthreads();  // the previous round's MFMAs are done with sXT
     if (stager) {
-      uint16_t vals[4][8];
+      uint16_t vals[RPG][8];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const long row = rb + g * 4 + rr;
+      for (int rr = 0; rr < RPG; ++rr) {
+        const long row = rb + g * RPG + rr;
         const uint32_t w[4] = {pf[rr].x, pf[rr].y, pf[rr].z, pf[rr].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -94,10 +95,19 @@ __global__ __launch_bounds__(256) void moments_mfma(const uint16_t* __restrict__
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        uint2 p;
-        p.x = (uint32_t)vals[0][e] | ((uint32_t)vals[1][e] << 16);
-        p.y = (uint32_t)vals[2][e] | ((uint32_t)vals[3][e] << 16);
-        *reinterpret_cast<uint2*>(sXT + (cc + e) * RS + g * 4) = p;
+        if constexpr (RPG == 8) {
+          uint4 p;
+          p.x = (uint32_t)vals[0][e] | ((uint32_t)vals[1][e] << 16);
+          p.y = (uint32_t)vals[2][e] | ((uint32_t)vals[3][e] << 16);
+          p.z = (uint32_t)vals[4][e] | ((uint32_t)vals[5][e] << 16);
+          p.w = (uint32_t)vals[6][e] | ((uint32_t)vals[7][e] << 16);
+          *reinterpret_cast<uint4*>(sXT + (cc + e) * RS + g * RPG) = p;
+        } else {
+          uint2 p;
+          p.x = (uint32_t)vals[0][e] | ((uint32_t)vals[1][e] << 16);
+          p.y = (uint32_t)vals[2][e] | ((uint32_t)vals[3][e] << 16);
+          *reinterpret_cast<uint2*>(sXT + (cc + e) * RS + g * RPG) = p;
+        }
       }
     }
     __syncthreads();
@@ -136,7 +146,7 @@ __global__ __launch_bounds__(256) void moments_mfma(const uint16_t* __restrict__
 #pragma unroll
       for (int e = 0; e < 8; ++e) sf[g * D + cc + e] = cs[e];
     __syncthreads();
-    const int ng = MOM_TOK / 4;
+    const int ng = RG;
     for (int c = tid; c < D; c += 256) {
       float s = 0.f;
       for (int gg = 0; gg < ng; ++gg) s += sf[gg * D + c];
