@@ -20,6 +20,7 @@ __device__ __forceinline__ uint32_t pref_key(float s) {
 }
 
 constexpr int SEL_QB = 8;   // query blocks per workgroup (they share each k_bar read)
+constexpr int SEL_KB = 4;   // key blocks per lane (they share each query-mean read)
 
 template <int D>
 __global__ __launch_bounds__(SEL_T) void select_kernel(const float* __restrict__ qbar,
@@ -47,36 +48,54 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(const float* __restrict__
       }
     }
   } else {
-    // one key block per lane: the nq query means sit in LDS (broadcast
-    // reads), the lane streams its k_bar row; no cross-lane reductions
+    // SEL_KB key blocks per lane: the nq query means sit in LDS (broadcast
+    // reads, each one used for SEL_KB blocks), the lane streams its k_bar
+    // rows; no cross-lane reductions.  Every score is one fp32 FMA chain
+    // over d in ascending order.
     float* s_q = reinterpret_cast<float*>(smem + (size_t)qb * nb * 4);   // [qb][D]
     for (int e = tid; e < nq * D; e += SEL_T) s_q[e] = qbar[((long)h * nb + A0) * D + e];
     __syncthreads();
-    for (int B = tid; B < nb; B += SEL_T) {
-      const float* kr = kbar + ((long)h * nb + B) * D;
-      float acc[SEL_QB];
+    for (int B0 = 0; B0 < nb; B0 += SEL_T * SEL_KB) {
+      const float* kr[SEL_KB];
 #pragma unroll
-      for (int q = 0; q < SEL_QB; ++q) acc[q] = 0.f;
-#pragma unroll 4
+      for (int r = 0; r < SEL_KB; ++r)
+        kr[r] = kbar + ((long)h * nb + min(B0 + r * SEL_T + tid, nb - 1)) * D;   // tail lanes reread a row
+      float acc[SEL_KB][SEL_QB];
+#pragma unroll
+      for (int r = 0; r < SEL_KB; ++r)
+#pragma unroll
+        for (int q = 0; q < SEL_QB; ++q) acc[r][q] = 0.f;
+#pragma unroll 2
       for (int c = 0; c < D; c += 4) {
-        const float4 kv = *reinterpret_cast<const float4*>(kr + c);
+        float4 kv[SEL_KB];
+#pragma unroll
+        for (int r = 0; r < SEL_KB; ++r) kv[r] = *reinterpret_cast<const float4*>(kr[r] + c);
 #pragma unroll
         for (int q = 0; q < SEL_QB; ++q) {
           if (q < nq) {
             const float4 qv = *reinterpret_cast<const float4*>(s_q + q * D + c);
-            acc[q] = fmaf(qv.x, kv.x, acc[q]);
-            acc[q] = fmaf(qv.y, kv.y, acc[q]);
-            acc[q] = fmaf(qv.z, kv.z, acc[q]);
-            acc[q] = fmaf(qv.w, kv.w, acc[q]);
+#pragma unroll
+            for (int r = 0; r < SEL_KB; ++r) {
+              acc[r][q] = fmaf(qv.x, kv[r].x, acc[r][q]);
+              acc[r][q] = fmaf(qv.y, kv[r].y, acc[r][q]);
+              acc[r][q] = fmaf(qv.z, kv[r].z, acc[r][q]);
+              acc[r][q] = fmaf(qv.w, kv[r].w, acc[r][q]);
+            }
           }
         }
       }
 #pragma unroll
-      for (int q = 0; q < SEL_QB; ++q) {
-        if (q < nq) {
-          const float sc = acc[q] * rsd;
-          if (scores_out) scores_out[((long)h * nb + A0 + q) * nb + B] = sc;
-          s_keys[q * nb + B] = pref_key(sc);
+      for (int r = 0; r < SEL_KB; ++r) {
+        const int B = B0 + r * SEL_T + tid;
+        if (B < nb) {
+#pragma unroll
+          for (int q = 0; q < SEL_QB; ++q) {
+            if (q < nq) {
+              const float sc = acc[r][q] * rsd;
+              if (scores_out) scores_out[((long)h * nb + A0 + q) * nb + B] = sc;
+              s_keys[q * nb + B] = pref_key(sc);
+            }
+          }
         }
       }
     }
