@@ -364,6 +364,31 @@ __device__ __forceinline__ int fin_exscan(int v, int* s_tmp, int& total) {
   return base + incl - v;
 }
 
+// Exclusive scan over the NT threads of one team (waves w0 .. w0 + NT/64 - 1
+// of the workgroup; s_tmp is indexed by workgroup wave).  Every thread of the
+// workgroup must call it (two barriers).
+template <int NT>
+__device__ __forceinline__ int team_exscan(int v, int* s_tmp, int w0, int& total) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) s_tmp[w] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    if (w0 + i < w) base += s_tmp[w0 + i];
+    tot += s_tmp[w0 + i];
+  }
+  __syncthreads();
+  total = tot;
+  return base + incl - v;
+}
+
 // After a histogram round: find the digit where the running count reaches
 // *need (wave 0 only), updating *prefix and *need.
 __device__ __forceinline__ void radix_pick(const int* s_hist, uint32_t* s_prefix, int* s_need,
@@ -526,15 +551,17 @@ __global__ __launch_bounds__(FIN_T) void finisher(const T* __restrict__ xh,
   __shared__ int32_t s_oid[FIN_MAX];    // original id of local row r
   __shared__ int16_t s_lid[FIN_MAX];    // current local order (row indices)
   __shared__ int16_t s_tmp_lid[FIN_MAX];
-  __shared__ float s_val[FIN_MAX];
-  __shared__ int s_hist[256];
-  __shared__ float s_vec[D];
-  __shared__ float s_part[NW][D];
-  __shared__ uint64_t s_min[NW];
-  __shared__ int s_tmp[NW];
-  __shared__ uint32_t s_prefix;
-  __shared__ int s_need;
-  __shared__ int s_pole;
+  __shared__ float s_val[FIN_MAX];      // score of local position (group-relative)
+  // per team: below the first level the two independent splits of a level
+  // run side by side, one in each half of the workgroup
+  __shared__ int s_hist[2][256];
+  __shared__ float s_vec[2][D];
+  __shared__ float s_part[NW][D];       // by workgroup wave
+  __shared__ uint64_t s_min[NW];        // by workgroup wave
+  __shared__ int s_tmp[NW];             // by workgroup wave
+  __shared__ uint32_t s_prefix[2];
+  __shared__ int s_need[2];
+  __shared__ int s_pole[2];
 
   const int slot = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -594,178 +621,210 @@ __global__ __launch_bounds__(FIN_T) void finisher(const T* __restrict__ xh,
   }
   __syncthreads();
 
-  const int rslot = tid / CPR, cc = (tid % CPR) * VE;
-  // dot of every row of [a, a+len) with s_vec; calls f(i, r, dot) on the
-  // lane that owns the row's first chunk
-  auto rows_dot = [&](int a, int len, auto&& f) {
-    float vec[VE];
+  // One split of the local positions [a, a + len) (capacity cL to the left)
+  // by a team of NT threads (team 0 = the whole workgroup when NT = FIN_T).
+  // Every barrier is a workgroup barrier: both teams run this with the same
+  // NT and pass the same barriers (a team without a split runs it with
+  // len = 0).
+  auto split = [&](auto ntc, int team, int a, int len, int cL) {
+    constexpr int NT = decltype(ntc)::value;
+    constexpr int TW = NT / 64, RPT = NT / CPR;
+    const int ttid = tid - team * NT, w0 = team * TW;
+    const int rslot = ttid / CPR, cc = (ttid % CPR) * VE;
+    int* hist = s_hist[team];
+    float* vecs = s_vec[team];
+    if (ttid == 0) s_pole[team] = 0;
+    // dot of every row of [a, a+len) with vecs; calls f(i, r, dot) on the
+    // lane that owns the row's first chunk
+    auto rows_dot = [&](auto&& f) {
+      float vec[VE];
 #pragma unroll
-    for (int e = 0; e < VE; ++e) vec[e] = s_vec[cc + e];
-    // 4 row steps per iteration: index reads, then chunk reads, then math,
-    // so the LDS latencies overlap
-    constexpr int UR = 4;
-    for (int i0 = 0; i0 < len; i0 += UR * RPP) {
-      int rr[UR];
+      for (int e = 0; e < VE; ++e) vec[e] = vecs[cc + e];
+      // 4 row steps per iteration: index reads, then chunk reads, then math,
+      // so the LDS latencies overlap
+      constexpr int UR = 4;
+      for (int i0 = 0; i0 < len; i0 += UR * RPT) {
+        int rr[UR];
 #pragma unroll
-      for (int u = 0; u < UR; ++u) {
-        const int i = i0 + u * RPP + rslot;
-        rr[u] = (i < len) ? s_lid[a + i] : 0;
+        for (int u = 0; u < UR; ++u) {
+          const int i = i0 + u * RPT + rslot;
+          rr[u] = (i < len) ? s_lid[a + i] : 0;
+        }
+        float v[UR][VE];
+#pragma unroll
+        for (int u = 0; u < UR; ++u) Chunk<T>::load(sX + rr[u] * RS + cc, v[u]);
+        float acc[UR];
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+          acc[u] = 0.f;
+#pragma unroll
+          for (int e = 0; e < VE; ++e) acc[u] = fmaf(v[u][e], vec[e], acc[u]);
+          acc[u] = group_sum<CPR>(acc[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+          const int i = i0 + u * RPT + rslot;
+          if (i < len && (ttid % CPR) == 0) f(i, rr[u], acc[u]);
+        }
       }
-      float v[UR][VE];
+    };
+    // argmin over [a, a+len) of (row . vecs, original id) -> local row
+    auto argmin_range = [&]() -> int {
+      uint64_t best = ~0ull;
+      rows_dot([&](int, int r, float dv) {
+        const uint64_t k = argmin_key(dv, s_oid[r]);
+        best = k < best ? k : best;
+      });
+      best = group_min_u64<64>(best);
+      if (lane == 0) s_min[wave] = best;
+      __syncthreads();
+      uint64_t b = s_min[w0];
 #pragma unroll
-      for (int u = 0; u < UR; ++u) Chunk<T>::load(sX + rr[u] * RS + cc, v[u]);
-      float acc[UR];
+      for (int w = 1; w < TW; ++w) b = s_min[w0 + w] < b ? s_min[w0 + w] : b;
+      const int id = (int)(uint32_t)(b & 0xffffffffu);
+      for (int i = ttid; i < len; i += NT) {
+        const int r = s_lid[a + i];
+        if (s_oid[r] == id) s_pole[team] = r;
+      }
+      __syncthreads();
+      const int rp = s_pole[team];
+      __syncthreads();
+      return rp;
+    };
+    // centroid: per-lane partial sums over independent rows, then lanes with
+    // the same chunk (shuffles), then the team's waves (LDS), all in a fixed
+    // order
+    {
+      float acc[VE];
 #pragma unroll
-      for (int u = 0; u < UR; ++u) {
-        acc[u] = 0.f;
+      for (int e = 0; e < VE; ++e) acc[e] = 0.f;
+      for (int i0 = rslot; i0 < len; i0 += 4 * RPT) {
+        int rr[4];
 #pragma unroll
-        for (int e = 0; e < VE; ++e) acc[u] = fmaf(v[u][e], vec[e], acc[u]);
-        acc[u] = group_sum<CPR>(acc[u]);
+        for (int u = 0; u < 4; ++u) rr[u] = (i0 + u * RPT < len) ? s_lid[a + i0 + u * RPT] : -1;
+        float v[4][VE];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) Chunk<T>::load(sX + (rr[u] < 0 ? 0 : rr[u]) * RS + cc, v[u]);
+        // rows in a fixed order (u ascending), absent rows add nothing
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int e = 0; e < VE; ++e) acc[e] += (rr[u] < 0) ? 0.f : v[u][e];
       }
 #pragma unroll
-      for (int u = 0; u < UR; ++u) {
-        const int i = i0 + u * RPP + rslot;
-        if (i < len && (tid % CPR) == 0) f(i, rr[u], acc[u]);
+      for (int e = 0; e < VE; ++e) acc[e] = group_sum<64, CPR>(acc[e]);
+      if (lane < CPR)
+#pragma unroll
+        for (int e = 0; e < VE; ++e) s_part[wave][cc + e] = acc[e];
+      __syncthreads();
+      for (int c = ttid; c < D; c += NT) {
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < TW; ++w) sum += s_part[w0 + w][c];
+        vecs[c] = sum;
       }
+      __syncthreads();
     }
-  };
-  // argmin over [a, a+len) of (row . s_vec, original id) -> local row
-  auto argmin_range = [&](int a, int len) -> int {
-    uint64_t best = ~0ull;
-    rows_dot(a, len, [&](int, int r, float dv) {
-      const uint64_t k = argmin_key(dv, s_oid[r]);
-      best = k < best ? k : best;
-    });
-    best = group_min_u64<64>(best);
-    if (lane == 0) s_min[wave] = best;
+    const int rA = argmin_range();
+    for (int c = ttid; c < D; c += NT) vecs[c] = Elem<T>::load(sX + rA * RS + c);
     __syncthreads();
-    uint64_t b = s_min[0];
+    const int rB = argmin_range();
+    for (int c = ttid; c < D; c += NT)
+      vecs[c] = Elem<T>::load(sX + rA * RS + c) - Elem<T>::load(sX + rB * RS + c);
+    __syncthreads();
+    rows_dot([&](int i, int, float dv) { s_val[a + i] = dv; });
+    __syncthreads();
+    // the cL-th key: radix select, 8 bits per round, the team's threads
+    // counting into its LDS histogram, its first wave picking the digit
+    if (ttid == 0) {
+      s_prefix[team] = 0;
+      s_need[team] = cL;
+    }
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int i = ttid; i < 256; i += NT) hist[i] = 0;
+      __syncthreads();
+      const uint32_t pre = s_prefix[team];
+      const uint32_t hmask = (shift == 24) ? 0u : (0xffffffffu << (shift + 8));
+      for (int i = ttid; i < len; i += NT) {
+        const uint32_t k = pref_key_desc(s_val[a + i]);
+        if ((k & hmask) == pre) atomicAdd(&hist[(k >> shift) & 255], 1);
+      }
+      __syncthreads();
+      if (ttid < 64) radix_pick(hist, &s_prefix[team], &s_need[team], shift);
+      __syncthreads();
+    }
+    const uint32_t thr = s_prefix[team];
+    const int ties_needed = s_need[team];
+    // stable partition: E consecutive positions per thread
+    constexpr int EMAX = FIN_MAX / NT;
+    const int E = (len + NT - 1) / NT;
+    int ne = 0;
+    for (int e = 0; e < E; ++e) {
+      const int p = ttid * E + e;
+      if (p < len && pref_key_desc(s_val[a + p]) == thr) ++ne;
+    }
+    int tot;
+    int ce = team_exscan<NT>(ne, s_tmp, w0, tot);
+    int nl = 0;
+    bool left[EMAX];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) b = s_min[w] < b ? s_min[w] : b;
-    const int id = (int)(uint32_t)(b & 0xffffffffu);
-    for (int i = tid; i < len; i += FIN_T) {
-      const int r = s_lid[a + i];
-      if (s_oid[r] == id) s_pole = r;
+    for (int e = 0; e < EMAX; ++e) {
+      const int p = ttid * E + e;
+      bool l = false;
+      if (e < E && p < len) {
+        const uint32_t k = pref_key_desc(s_val[a + p]);
+        if (k < thr) l = true;
+        else if (k == thr) { l = ce < ties_needed; ++ce; }
+      }
+      left[e] = l;
+      nl += l;
+    }
+    int cl = team_exscan<NT>(nl, s_tmp, w0, tot);
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) {
+      const int p = ttid * E + e;
+      if (e >= E || p >= len) continue;
+      const int dst = left[e] ? cl : cL + (p - cl);
+      if (dst < len) s_tmp_lid[a + dst] = s_lid[a + p];
+      cl += left[e];
     }
     __syncthreads();
-    const int rp = s_pole;
+    for (int i = ttid; i < len; i += NT) s_lid[a + i] = s_tmp_lid[a + i];
     __syncthreads();
-    return rp;
   };
 
-  for (int sub = 0;; ++sub) {
+  // group geometry of `path` at sub-level `sub` below this group: false if
+  // that subgroup is a single block (or does not exist)
+  auto sub_group = [&](int sub, int path, int& a, int& len, int& cL) {
+    int sstart = 0, snb = nbg;
+    for (int l = sub - 1; l >= 0; --l) {
+      if (snb <= 1) return false;
+      const int nl = (snb + 1) >> 1;
+      if ((path >> l) & 1) { sstart += nl; snb -= nl; } else snb = nl;
+    }
+    if (snb < 2) return false;
+    a = sstart * BK;
+    len = min(n, (sstart + snb) * BK) - a;
+    cL = ((snb + 1) >> 1) * BK;
+    return true;
+  };
+  {
+    int a, len, cL;
+    if (sub_group(0, 0, a, len, cL)) split(std::integral_constant<int, FIN_T>{}, 0, a, len, cL);
+  }
+  const int team = tid / (FIN_T / 2);
+  for (int sub = 1;; ++sub) {
     bool any = false;
-    for (int path = 0; path < (1 << sub); ++path) {
-      int sstart = 0, snb = nbg;
-      bool exists = true;
-      for (int l = sub - 1; l >= 0; --l) {
-        if (snb <= 1) { exists = false; break; }
-        const int nl = (snb + 1) >> 1;
-        if ((path >> l) & 1) { sstart += nl; snb -= nl; } else snb = nl;
-      }
-      if (!exists || snb < 2) continue;
+    for (int p2 = 0; p2 < (1 << sub); p2 += 2) {
+      int a0, len0, cL0, a1, len1, cL1;
+      const bool e0 = sub_group(sub, p2, a0, len0, cL0);
+      const bool e1 = sub_group(sub, p2 + 1, a1, len1, cL1);
+      if (!e0 && !e1) continue;
       any = true;
-      const int a = sstart * BK;
-      const int len = min(n, (sstart + snb) * BK) - a;
-      const int cL = ((snb + 1) >> 1) * BK;
-      // centroid: per-lane partial sums over independent rows, then lanes with
-      // the same chunk (shuffles), then waves (LDS), all in a fixed order
-      {
-        float acc[VE];
-#pragma unroll
-        for (int e = 0; e < VE; ++e) acc[e] = 0.f;
-        for (int i0 = rslot; i0 < len; i0 += 4 * RPP) {
-          int rr[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) rr[u] = (i0 + u * RPP < len) ? s_lid[a + i0 + u * RPP] : -1;
-          float v[4][VE];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) Chunk<T>::load(sX + (rr[u] < 0 ? 0 : rr[u]) * RS + cc, v[u]);
-          // rows in a fixed order (u ascending), absent rows add nothing
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int e = 0; e < VE; ++e) acc[e] += (rr[u] < 0) ? 0.f : v[u][e];
-        }
-#pragma unroll
-        for (int e = 0; e < VE; ++e) acc[e] = group_sum<64, CPR>(acc[e]);
-        if (lane < CPR)
-#pragma unroll
-          for (int e = 0; e < VE; ++e) s_part[wave][cc + e] = acc[e];
-        __syncthreads();
-        for (int c = tid; c < D; c += FIN_T) {
-          float sum = 0.f;
-#pragma unroll
-          for (int w = 0; w < NW; ++w) sum += s_part[w][c];
-          s_vec[c] = sum;
-        }
-        __syncthreads();
-      }
-      const int rA = argmin_range(a, len);
-      for (int c = tid; c < D; c += FIN_T) s_vec[c] = Elem<T>::load(sX + rA * RS + c);
-      __syncthreads();
-      const int rB = argmin_range(a, len);
-      for (int c = tid; c < D; c += FIN_T)
-        s_vec[c] = Elem<T>::load(sX + rA * RS + c) - Elem<T>::load(sX + rB * RS + c);
-      __syncthreads();
-      rows_dot(a, len, [&](int i, int, float dv) { s_val[i] = dv; });
-      __syncthreads();
-      // the cL-th key: radix select, 8 bits per round, all threads counting
-      // into an LDS histogram, wave 0 picking the digit
-      if (tid == 0) {
-        s_prefix = 0;
-        s_need = cL;
-      }
-      for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = tid; i < 256; i += FIN_T) s_hist[i] = 0;
-        __syncthreads();
-        const uint32_t pre = s_prefix;
-        const uint32_t hmask = (shift == 24) ? 0u : (0xffffffffu << (shift + 8));
-        for (int i = tid; i < len; i += FIN_T) {
-          const uint32_t k = pref_key_desc(s_val[i]);
-          if ((k & hmask) == pre) atomicAdd(&s_hist[(k >> shift) & 255], 1);
-        }
-        __syncthreads();
-        if (tid < 64) radix_pick(s_hist, &s_prefix, &s_need, shift);
-        __syncthreads();
-      }
-      const uint32_t thr = s_prefix;
-      const int ties_needed = s_need;
-      // stable partition: E consecutive positions per thread (E <= 2)
-      const int E = (len + FIN_T - 1) / FIN_T;
-      int ne = 0;
-      for (int e = 0; e < E; ++e) {
-        const int p = tid * E + e;
-        if (p < len && pref_key_desc(s_val[p]) == thr) ++ne;
-      }
-      int tot;
-      int ce = fin_exscan(ne, s_tmp, tot);
-      int nl = 0;
-      bool left[FIN_MAX / FIN_T];
-#pragma unroll
-      for (int e = 0; e < FIN_MAX / FIN_T; ++e) {
-        const int p = tid * E + e;
-        bool l = false;
-        if (e < E && p < len) {
-          const uint32_t k = pref_key_desc(s_val[p]);
-          if (k < thr) l = true;
-          else if (k == thr) { l = ce < ties_needed; ++ce; }
-        }
-        left[e] = l;
-        nl += l;
-      }
-      int cl = fin_exscan(nl, s_tmp, tot);
-#pragma unroll
-      for (int e = 0; e < FIN_MAX / FIN_T; ++e) {
-        const int p = tid * E + e;
-        if (e >= E || p >= len) continue;
-        const int dst = left[e] ? cl : cL + (p - cl);
-        if (dst < len) s_tmp_lid[a + dst] = s_lid[a + p];
-        cl += left[e];
-      }
-      __syncthreads();
-      for (int i = tid; i < len; i += FIN_T) s_lid[a + i] = s_tmp_lid[a + i];
-      __syncthreads();
+      int a = 0, len = 0, cL = 0;
+      if (team == 0 && e0) { a = a0; len = len0; cL = cL0; }
+      if (team == 1 && e1) { a = a1; len = len1; cL = cL1; }
+      split(std::integral_constant<int, FIN_T / 2>{}, team, a, len, cL);
     }
     if (!any) break;
   }
