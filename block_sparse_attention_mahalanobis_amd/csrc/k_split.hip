@@ -96,22 +96,35 @@ __global__ void iota_kernel(int32_t* __restrict__ lo, int32_t* __restrict__ hi, 
 
 // Rows of one block (chunk) of the current order, gathered by id: every lane
 // loads its NIT row chunks up front (ids staged in LDS first), so all the
-// row reads of the block are in flight together.
+// row reads of the block are in flight together.  The chunks stay as loaded
+// (16 bytes: 8 bf16 or 4 fp32) and are widened to fp32 where they are used,
+// which halves the registers a bf16 pass holds and lets 8 waves per SIMD
+// keep their reads in flight.
 template <typename T, int D>
 struct ChunkRows {
   static constexpr int VE = Chunk<T>::VE, CPR = D / VE, RPP = SPL_T / CPR, NIT = 128 / RPP;
-  float v[NIT][VE];
+  uint4 raw[NIT];
   __device__ __forceinline__ void load(const T* __restrict__ xt, const int32_t* s_ids, int n_real,
                                        int rg, int c) {
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int j = it * RPP + rg;
-      if (j < n_real) {
-        Chunk<T>::load(xt + (long)s_ids[j] * D + c, v[it]);
-      } else {
+      raw[it] = (j < n_real) ? *reinterpret_cast<const uint4*>(xt + (long)s_ids[j] * D + c)
+                             : uint4{0u, 0u, 0u, 0u};
+    }
+  }
+  // chunk `it` as fp32 (absent rows are zero)
+  __device__ __forceinline__ void get(int it, float (&v)[VE]) const {
+    const uint32_t w[4] = {raw[it].x, raw[it].y, raw[it].z, raw[it].w};
+    if constexpr (sizeof(T) == 2) {
 #pragma unroll
-        for (int e = 0; e < VE; ++e) v[it][e] = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(w[i]);
     }
   }
 };
@@ -144,9 +157,12 @@ __global__ __launch_bounds__(SPL_T) void cent_partial(const T* __restrict__ xh,
 #pragma unroll
   for (int e = 0; e < VE; ++e) acc[e] = 0.f;
 #pragma unroll
-  for (int it = 0; it < CR::NIT; ++it)
+  for (int it = 0; it < CR::NIT; ++it) {
+    float v[VE];
+    rows.get(it, v);
 #pragma unroll
-    for (int e = 0; e < VE; ++e) acc[e] += rows.v[it][e];
+    for (int e = 0; e < VE; ++e) acc[e] += v[e];
+  }
   // lanes holding the same chunk: fold within the wave, then across waves
 #pragma unroll
   for (int e = 0; e < VE; ++e) acc[e] = group_sum<64, CPR>(acc[e]);
@@ -235,9 +251,11 @@ __global__ __launch_bounds__(SPL_T) void argmin_partial(const T* __restrict__ xh
 #pragma unroll
   for (int it = 0; it < CR::NIT; ++it) {
     const int j = it * RPP + rg;
+    float v[VE];
+    rows.get(it, v);
     float acc = 0.f;
 #pragma unroll
-    for (int e = 0; e < VE; ++e) acc = fmaf(rows.v[it][e], vec[e], acc);
+    for (int e = 0; e < VE; ++e) acc = fmaf(v[e], vec[e], acc);
     acc = group_sum<CPR>(acc);
     if (j < n_real) {
       const uint64_t k = argmin_key(acc, s_ids[j]);
@@ -310,9 +328,11 @@ __global__ __launch_bounds__(SPL_T) void score_kernel(const T* __restrict__ xh,
 #pragma unroll
   for (int it = 0; it < CR::NIT; ++it) {
     const int j = it * RPP + rg;
+    float v[VE];
+    rows.get(it, v);
     float acc = 0.f;
 #pragma unroll
-    for (int e = 0; e < VE; ++e) acc = fmaf(rows.v[it][e], vec[e], acc);
+    for (int e = 0; e < VE; ++e) acc = fmaf(v[e], vec[e], acc);
     acc = group_sum<CPR>(acc);
     if (j < n_real && (tid % CPR) == 0) s[pos0 + j] = acc;
   }
