@@ -221,12 +221,28 @@ __global__ __launch_bounds__(256) void summarize_kernel(const T* __restrict__ kp
     for (int r = 0; r < 16; ++r) kval += s_part[r][tid];
     ksum[((long)h * nb + B) * D + tid] = kval;
   }
-  // vsum from the transposed block: row c of vpt holds the block's values of column c
-  for (int c = tid; c < D; c += 256) {
-    const T* row = vblk + (long)c * BK;
-    float acc = 0.f;
-    for (int j = 0; j < n_real; ++j) acc = fmaf(s_w[j], Elem<T>::load(row + j), acc);
-    vsum[((long)h * nb + B) * D + c] = acc;
+  // vsum from the transposed block: row c of vpt holds the block's values of
+  // column c.  16 lanes per row, 8 consecutive tokens each (one 16-byte
+  // load), then a fixed shuffle tree over the 16 lanes; tokens past n_real
+  // are skipped.
+  {
+    const int rr = tid / 16, jc = (tid % 16) * 8;
+    float wv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wv[e] = (jc + e < n_real) ? s_w[jc + e] : 0.f;
+    for (int c0 = 0; c0 < D; c0 += 16) {
+      const int c = c0 + rr;
+      float acc = 0.f;
+      if (jc < n_real) {
+        float v[8];
+        load8(vblk + (long)c * BK + jc, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (jc + e < n_real) acc = fmaf(wv[e], v[e], acc);
+      }
+      acc = group_sum<16>(acc);
+      if ((tid & 15) == 0) vsum[((long)h * nb + B) * D + c] = acc;
+    }
   }
   if (mean_mode) {
     if (tid == 0) bias[(long)h * nb + B] = 0.f;
