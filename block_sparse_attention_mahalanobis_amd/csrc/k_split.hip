@@ -557,6 +557,7 @@ __global__ __launch_bounds__(NT) void select_partition(const float* __restrict__
 // row (one 16-byte chunk each) reduced with shuffles; the centroid sums
 // independent rows per lane; all reductions run in a fixed order.
 constexpr int FIN_T = 512;
+constexpr int FIN_KR = 16;   // rows per lane slot a split holds in registers (host-checked)
 
 template <typename T, int D>
 __global__ __launch_bounds__(FIN_T) void finisher(const T* __restrict__ xh,
@@ -581,7 +582,7 @@ __global__ __launch_bounds__(FIN_T) void finisher(const T* __restrict__ xh,
   __shared__ int s_tmp[NW];             // by workgroup wave
   __shared__ uint32_t s_prefix[2];
   __shared__ int s_need[2];
-  __shared__ int s_pole[2];
+  __shared__ int s_minr[NW];           // by workgroup wave
 
   const int slot = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -653,63 +654,83 @@ __global__ __launch_bounds__(FIN_T) void finisher(const T* __restrict__ xh,
     const int rslot = ttid / CPR, cc = (ttid % CPR) * VE;
     int* hist = s_hist[team];
     float* vecs = s_vec[team];
-    if (ttid == 0) s_pole[team] = 0;
-    // dot of every row of [a, a+len) with vecs; calls f(i, r, dot) on the
-    // lane that owns the row's first chunk
+    // this lane's 16-byte chunk of the rows at positions a + rslot + k RPT,
+    // their local row numbers and original ids: read from LDS once for the
+    // four row passes below
+    uint4 rw[FIN_KR];
+    int rid[FIN_KR], oid[FIN_KR];
+#pragma unroll
+    for (int k = 0; k < FIN_KR; ++k) {
+      const int i = rslot + k * RPT;
+      rid[k] = (i < len) ? (int)s_lid[a + i] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < FIN_KR; ++k) {
+      rw[k] = *reinterpret_cast<const uint4*>(sX + rid[k] * RS + cc);
+      oid[k] = s_oid[rid[k]];
+    }
+    auto widen = [&](const uint4& q, float (&v)[VE]) {
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = __uint_as_float(w[i] << 16);
+          v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(w[i]);
+      }
+    };
+    // dot of every row of [a, a+len) with vecs; calls f(i, k, dot) on the
+    // lane that owns the row's first chunk (k: the row's cache slot)
     auto rows_dot = [&](auto&& f) {
       float vec[VE];
 #pragma unroll
       for (int e = 0; e < VE; ++e) vec[e] = vecs[cc + e];
-      // 4 row steps per iteration: index reads, then chunk reads, then math,
-      // so the LDS latencies overlap
-      constexpr int UR = 4;
-      for (int i0 = 0; i0 < len; i0 += UR * RPT) {
-        int rr[UR];
 #pragma unroll
-        for (int u = 0; u < UR; ++u) {
-          const int i = i0 + u * RPT + rslot;
-          rr[u] = (i < len) ? s_lid[a + i] : 0;
-        }
-        float v[UR][VE];
+      for (int k = 0; k < FIN_KR; ++k) {
+        if (k * RPT < len) {   // uniform
+          float v[VE];
+          widen(rw[k], v);
+          float acc = 0.f;
 #pragma unroll
-        for (int u = 0; u < UR; ++u) Chunk<T>::load(sX + rr[u] * RS + cc, v[u]);
-        float acc[UR];
-#pragma unroll
-        for (int u = 0; u < UR; ++u) {
-          acc[u] = 0.f;
-#pragma unroll
-          for (int e = 0; e < VE; ++e) acc[u] = fmaf(v[u][e], vec[e], acc[u]);
-          acc[u] = group_sum<CPR>(acc[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < UR; ++u) {
-          const int i = i0 + u * RPT + rslot;
-          if (i < len && (ttid % CPR) == 0) f(i, rr[u], acc[u]);
+          for (int e = 0; e < VE; ++e) acc = fmaf(v[e], vec[e], acc);
+          acc = group_sum<CPR>(acc);
+          const int i = rslot + k * RPT;
+          if (i < len && (ttid % CPR) == 0) f(i, k, acc);
         }
       }
     };
-    // argmin over [a, a+len) of (row . vecs, original id) -> local row
+    // argmin over [a, a+len) of (row . vecs, original id) -> local row: the
+    // winning row rides along the reduction, so one barrier suffices
     auto argmin_range = [&]() -> int {
       uint64_t best = ~0ull;
-      rows_dot([&](int, int r, float dv) {
-        const uint64_t k = argmin_key(dv, s_oid[r]);
-        best = k < best ? k : best;
+      int brow = 0;
+      rows_dot([&](int, int k, float dv) {
+        const uint64_t key = argmin_key(dv, oid[k]);
+        if (key < best) {
+          best = key;
+          brow = rid[k];
+        }
       });
-      best = group_min_u64<64>(best);
-      if (lane == 0) s_min[wave] = best;
-      __syncthreads();
-      uint64_t b = s_min[w0];
-#pragma unroll
-      for (int w = 1; w < TW; ++w) b = s_min[w0 + w] < b ? s_min[w0 + w] : b;
-      const int id = (int)(uint32_t)(b & 0xffffffffu);
-      for (int i = ttid; i < len; i += NT) {
-        const int r = s_lid[a + i];
-        if (s_oid[r] == id) s_pole[team] = r;
+      const uint64_t wb = group_min_u64<64>(best);
+      const uint64_t holders = __builtin_amdgcn_ballot_w64(best == wb);
+      const int wrow = __builtin_amdgcn_readlane(brow, __builtin_ctzll(holders));
+      if (lane == 0) {
+        s_min[wave] = wb;
+        s_minr[wave] = wrow;
       }
       __syncthreads();
-      const int rp = s_pole[team];
-      __syncthreads();
-      return rp;
+      uint64_t b = s_min[w0];
+      int r = s_minr[w0];
+#pragma unroll
+      for (int w = 1; w < TW; ++w)
+        if (s_min[w0 + w] < b) {
+          b = s_min[w0 + w];
+          r = s_minr[w0 + w];
+        }
+      return r;
     };
     // centroid: per-lane partial sums over independent rows, then lanes with
     // the same chunk (shuffles), then the team's waves (LDS), all in a fixed
@@ -718,18 +739,21 @@ __global__ __launch_bounds__(FIN_T) void finisher(const T* __restrict__ xh,
       float acc[VE];
 #pragma unroll
       for (int e = 0; e < VE; ++e) acc[e] = 0.f;
-      for (int i0 = rslot; i0 < len; i0 += 4 * RPT) {
-        int rr[4];
+      // rows in a fixed order (k ascending, in groups of 4), absent rows of a
+      // started group add +0
 #pragma unroll
-        for (int u = 0; u < 4; ++u) rr[u] = (i0 + u * RPT < len) ? s_lid[a + i0 + u * RPT] : -1;
-        float v[4][VE];
+      for (int k0 = 0; k0 < FIN_KR; k0 += 4) {
+        if (rslot + k0 * RPT < len) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) Chunk<T>::load(sX + (rr[u] < 0 ? 0 : rr[u]) * RS + cc, v[u]);
-        // rows in a fixed order (u ascending), absent rows add nothing
+          for (int u = 0; u < 4; ++u) {
+            const int k = k0 + u;
+            float v[VE];
+            widen(rw[k], v);
+            const bool in = rslot + k * RPT < len;
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int e = 0; e < VE; ++e) acc[e] += (rr[u] < 0) ? 0.f : v[u][e];
+            for (int e = 0; e < VE; ++e) acc[e] += in ? v[e] : 0.f;
+          }
+        }
       }
 #pragma unroll
       for (int e = 0; e < VE; ++e) acc[e] = group_sum<64, CPR>(acc[e]);
@@ -864,6 +888,10 @@ static SplitPlan split_plan(int N, int D, int BK, int esz) {
   fb = std::min(fb, FIN_MAX / BK);
   int F = 1;
   while (F * 2 <= fb) F *= 2;
+  // a split keeps at most FIN_KR rows per lane slot in registers: FIN_T
+  // threads on the group, FIN_T / 2 on each group of the levels below
+  const int rpt = FIN_T / (D / (16 / esz));
+  while (F > 1 && (F * BK > FIN_KR * rpt || ((F + 1) / 2) * BK > FIN_KR * (rpt / 2))) F >>= 1;
   p.F = std::max(F, 1);
   // first level whose largest group has <= F blocks
   int L = 0, mx = p.nb;
