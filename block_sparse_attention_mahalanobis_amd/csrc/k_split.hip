@@ -452,6 +452,7 @@ __global__ __launch_bounds__(NT) void select_partition(const float* __restrict__
   __shared__ int s_hist[256];
   __shared__ int s_whist[NT / 64][256];  // one histogram per wave (less atomic contention)
   __shared__ int s_tmp[NT / 64];
+  __shared__ int32_t s_stage[NT * 8];     // one partition tile's ids in output order
   __shared__ uint32_t s_prefix;
   __shared__ int s_need;
   const int slot = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
@@ -503,50 +504,94 @@ __global__ __launch_bounds__(NT) void select_partition(const float* __restrict__
   }
   const uint32_t thr = s_prefix;
   const int ties_needed = s_need;
-  // stable partition in tiles of NT * E positions, E consecutive per thread
+  // stable partition in tiles of NT * E positions, E consecutive per thread.
+  // Before position p, lt(p) keys are below the threshold and eq(p) equal to
+  // it; a tie goes left iff its rank among ties is < ties_needed, so the
+  // lefts before p number lt(p) + min(eq(p), ties_needed): one scan of the
+  // packed (lt, eq) counts per tile places every element.  Each tile's keys
+  // and ids are loaded one tile ahead.
   constexpr int E = 8;
-  int run_left = 0, run_eq = 0;  // lefts / ties before this tile
+  int run_lt = 0, run_eq = 0;  // below / equal before this tile
+  uint32_t kn[E];
+  int32_t idn[E];
+  const bool vec_ok = (base & 3) == 0;   // 16-byte aligned rows of this group
+  auto fetch = [&](int p0) {
+    const int q = p0 + tid * E;
+    if (vec_ok && q + E <= n) {   // two 16-byte loads per array
+      const float4 s0 = *reinterpret_cast<const float4*>(s + base + q);
+      const float4 s1 = *reinterpret_cast<const float4*>(s + base + q + 4);
+      const int4 i0 = *reinterpret_cast<const int4*>(ids_in + base + q);
+      const int4 i1 = *reinterpret_cast<const int4*>(ids_in + base + q + 4);
+      const float sv[E] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      const int32_t iv[E] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        kn[e] = pref_key_desc(sv[e]);
+        idn[e] = iv[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int p = q + e;
+        kn[e] = (p < n) ? pref_key_desc(s[base + p]) : 0xffffffffu;
+        idn[e] = (p < n) ? ids_in[base + p] : 0;
+      }
+    }
+  };
+  fetch(0);
   for (int p0 = 0; p0 < n; p0 += NT * E) {
     uint32_t k[E];
-    int nl = 0, ne = 0;
+    int32_t idv[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const int p = p0 + tid * E + e;
-      k[e] = (p < n) ? pref_key_desc(s[base + p]) : 0xffffffffu;
-      const bool valid = p < n;
-      ne += (valid && k[e] == thr);
+      k[e] = kn[e];
+      idv[e] = idn[e];
     }
-    // a tie goes left iff its rank among ties < ties_needed
-    int tot_eq;
-    const int eq_before = run_eq + wg_exscan<NT>(ne, s_tmp, tot_eq);
-    int ce = eq_before;
-    bool left[E];
+    if (p0 + NT * E < n) fetch(p0 + NT * E);
+    int lt = 0, eq = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const int p = p0 + tid * E + e;
-      const bool valid = p < n;
-      bool l = false;
-      if (valid) {
-        if (k[e] < thr) l = true;
-        else if (k[e] == thr) { l = ce < ties_needed; ++ce; }
-      }
-      left[e] = l;
-      nl += l;
+      const bool valid = p0 + tid * E + e < n;
+      lt += (valid && k[e] < thr);
+      eq += (valid && k[e] == thr);
     }
-    int tot_l;
-    const int l_before = run_left + wg_exscan<NT>(nl, s_tmp, tot_l);
-    int cl = l_before;
+    int tot;
+    const int packed = wg_exscan<NT>((lt << 16) | eq, s_tmp, tot);   // tile counts < 2^16
+    int lt_c = run_lt + (packed >> 16), eq_c = run_eq + (packed & 0xffff);
+    // the tile's lefts land in one run, its rights in another: stage the ids
+    // in LDS in output order, then write both runs with contiguous stores
+    const int tile_n = min(NT * E, n - p0);
+    const int lb_tile = run_lt + min(run_eq, ties_needed);               // lefts before the tile
+    const int la_tile = run_lt + (tot >> 16) + min(run_eq + (tot & 0xffff), ties_needed);
+    const int nl_tile = la_tile - lb_tile;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int p = p0 + tid * E + e;
       if (p >= n) continue;
-      const int r_before = p - cl;  // rights before p
-      const int dst = left[e] ? cl : cL + r_before;
-      if (dst < n) ids_out[base + dst] = ids_in[base + p];
-      cl += left[e];
+      const int left_before = lt_c + min(eq_c, ties_needed);
+      bool l;
+      if (k[e] < thr) {
+        l = true;
+        ++lt_c;
+      } else if (k[e] == thr) {
+        l = eq_c < ties_needed;
+        ++eq_c;
+      } else {
+        l = false;
+      }
+      // position in the tile's output: lefts first, then rights, both in order
+      const int j = l ? left_before - lb_tile : nl_tile + (p - left_before) - (p0 - lb_tile);
+      s_stage[j] = idv[e];
     }
-    run_left += tot_l;
-    run_eq += tot_eq;
+    __syncthreads();
+    const int rb_tile = p0 - lb_tile;                                     // rights before the tile
+    for (int j = tid; j < tile_n; j += NT) {
+      const int dst = (j < nl_tile) ? lb_tile + j : cL + rb_tile + (j - nl_tile);
+      if (dst < n) ids_out[base + dst] = s_stage[j];
+    }
+    __syncthreads();   // the stage is rewritten by the next tile
+    run_lt += tot >> 16;
+    run_eq += tot & 0xffff;
   }
 }
 
