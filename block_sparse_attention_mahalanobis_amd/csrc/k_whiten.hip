@@ -39,8 +39,15 @@ __global__ __launch_bounds__(256) void moments_mfma(const uint16_t* __restrict__
                                                     float* __restrict__ part,
                                                     float* __restrict__ cpart, int H, int N,
                                                     int n_anchor, int nchunk, int rpc) {
-  constexpr int RS = MOM_TOK + 8;  // LDS row stride (bf16) of X^T
+  // X^T in LDS, one row per column of X.  d = 128: rows of MOM_TOK tokens
+  // as 16 chunks of 8, chunk slot XOR-swizzled by (row + row / 8) mod 16, so
+  // the transposed stores (16 rows 8 apart, 4 chunk groups per wave) and
+  // the MFMA operand reads (32 consecutive rows, one chunk each) both spread
+  // over all banks.  d = 64: rows padded by 8 tokens.
+  constexpr bool SWZ = (D == 128);
+  constexpr int RS = SWZ ? MOM_TOK : MOM_TOK + 8;   // LDS row stride (bf16) of X^T
   __shared__ __attribute__((aligned(16))) uint16_t sXT[D * RS];
+  auto xt_sw = [](int r) { return SWZ ? ((r + (r >> 3)) & 15) : 0; };
   const int t = blockIdx.y, chunk = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
@@ -101,7 +108,7 @@ __global__ __launch_bounds__(256) void moments_mfma(const uint16_t* __restrict__
           p.y = (uint32_t)vals[2][e] | ((uint32_t)vals[3][e] << 16);
           p.z = (uint32_t)vals[4][e] | ((uint32_t)vals[5][e] << 16);
           p.w = (uint32_t)vals[6][e] | ((uint32_t)vals[7][e] << 16);
-          *reinterpret_cast<uint4*>(sXT + (cc + e) * RS + g * RPG) = p;
+          *reinterpret_cast<uint4*>(sXT + (cc + e) * RS + ((g ^ xt_sw(cc + e)) * RPG)) = p;
         } else {
           uint2 p;
           p.x = (uint32_t)vals[0][e] | ((uint32_t)vals[1][e] << 16);
@@ -119,8 +126,9 @@ __global__ __launch_bounds__(256) void moments_mfma(const uint16_t* __restrict__
         const int tile = wave * TPW + i;
         const int mt = tile / MT, nt = tile % MT;
         if (tile >= MT * MT) continue;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sXT + (32 * mt + l32) * RS + 16 * ks + 8 * hf);
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(sXT + (32 * nt + l32) * RS + 16 * ks + 8 * hf);
+        const int ra = 32 * mt + l32, rb2 = 32 * nt + l32;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sXT + ra * RS + (((2 * ks + hf) ^ xt_sw(ra)) * 8));
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(sXT + rb2 * RS + (((2 * ks + hf) ^ xt_sw(rb2)) * 8));
         acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
       }
     }
