@@ -277,23 +277,27 @@ int moments_launch(int H, int N, int D, int dtype, const void* q, const void* k,
 // energy.  Y and Z live in LDS; T goes through a per-matrix global scratch
 // (L2-resident).  Stops when max|ZY - I| < 3e-5, after at most 40 iterations.
 // ---------------------------------------------------------------------------
+constexpr int MSQ_T = 512;
 template <int D>
-__global__ __launch_bounds__(256) void msqrt_kernel(const float* __restrict__ M,
+__global__ __launch_bounds__(MSQ_T) void msqrt_kernel(const float* __restrict__ M,
                                                     float* __restrict__ W,
                                                     float* __restrict__ Tscr) {
-  constexpr int SUB = (D == 128) ? 8 : 4;
+  // each thread owns an SI x SJ block of every product: 8 x 4 (d = 128) or
+  // 4 x 2 (d = 64) with MSQ_T threads, two waves per SIMD
+  constexpr int SI = (D == 128) ? 8 : 4, SJ = SI / 2;
+  constexpr int NW = MSQ_T / 64;
   __shared__ float sY[D * D];
   __shared__ float sZ[D * D];
-  __shared__ float s_red[4];
+  __shared__ float s_red[NW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const long off = (long)blockIdx.x * D * D;
   const float* m = M + off;
   float* tg = Tscr + off;
-  const int bi = (tid / (D / SUB)) * SUB, bj = (tid % (D / SUB)) * SUB;
+  const int bi = (tid / (D / SJ)) * SI, bj = (tid % (D / SJ)) * SJ;
 
   // Frobenius norm (symmetrised input)
   float ss = 0.f;
-  for (int e = tid; e < D * D; e += 256) {
+  for (int e = tid; e < D * D; e += MSQ_T) {
     const int r = e / D, c = e % D;
     const float v = 0.5f * (m[r * D + c] + m[c * D + r]);
     sY[e] = v;
@@ -302,14 +306,17 @@ __global__ __launch_bounds__(256) void msqrt_kernel(const float* __restrict__ M,
   ss = wave_sum(ss);
   if (lane == 0) s_red[wave] = ss;
   __syncthreads();
-  const float fro = sqrtf(s_red[0] + s_red[1] + s_red[2] + s_red[3]);
+  float ssum = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) ssum += s_red[w];
+  const float fro = sqrtf(ssum);
   if (!(fro > 0.f) || !isfinite(fro)) {
-    for (int e = tid; e < D * D; e += 256) W[off + e] = (fro == 0.f) ? 0.f : NAN;
+    for (int e = tid; e < D * D; e += MSQ_T) W[off + e] = (fro == 0.f) ? 0.f : NAN;
     return;
   }
   const float inv = 1.f / fro;
   constexpr float kRidge = 1e-6f;
-  for (int e = tid; e < D * D; e += 256) {
+  for (int e = tid; e < D * D; e += MSQ_T) {
     const bool diag = (e / D == e % D);
     sY[e] = sY[e] * inv + (diag ? kRidge : 0.f);
     sZ[e] = diag ? 1.f : 0.f;
@@ -317,26 +324,28 @@ __global__ __launch_bounds__(256) void msqrt_kernel(const float* __restrict__ M,
   __syncthreads();
 
   for (int it = 0; it < 40; ++it) {
-    // P = Z Y (this thread's SUB x SUB block), T = (3I - P)/2 to global
-    float acc[SUB][SUB];
+    // P = Z Y (this thread's block), T = (3I - P)/2 to global
+    float acc[SI][SJ];
 #pragma unroll
-    for (int i = 0; i < SUB; ++i)
+    for (int i = 0; i < SI; ++i)
 #pragma unroll
-      for (int j = 0; j < SUB; ++j) acc[i][j] = 0.f;
+      for (int j = 0; j < SJ; ++j) acc[i][j] = 0.f;
     for (int kx = 0; kx < D; ++kx) {
-      float a[SUB], b[SUB];
+      float a[SI], b[SJ];
 #pragma unroll
-      for (int i = 0; i < SUB; ++i) { a[i] = sZ[(bi + i) * D + kx]; b[i] = sY[kx * D + bj + i]; }
+      for (int i = 0; i < SI; ++i) a[i] = sZ[(bi + i) * D + kx];
 #pragma unroll
-      for (int i = 0; i < SUB; ++i)
+      for (int j = 0; j < SJ; ++j) b[j] = sY[kx * D + bj + j];
 #pragma unroll
-        for (int j = 0; j < SUB; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+      for (int i = 0; i < SI; ++i)
+#pragma unroll
+        for (int j = 0; j < SJ; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
     }
     float dev = 0.f;
 #pragma unroll
-    for (int i = 0; i < SUB; ++i)
+    for (int i = 0; i < SI; ++i)
 #pragma unroll
-      for (int j = 0; j < SUB; ++j) {
+      for (int j = 0; j < SJ; ++j) {
         const float id = (bi + i == bj + j) ? 1.f : 0.f;
         dev = fmaxf(dev, fabsf(acc[i][j] - id));
         tg[(bi + i) * D + bj + j] = 0.5f * (3.f * id - acc[i][j]);
@@ -344,43 +353,48 @@ __global__ __launch_bounds__(256) void msqrt_kernel(const float* __restrict__ M,
     dev = wave_max(dev);
     if (lane == 0) s_red[wave] = dev;
     __syncthreads();  // T visible to the workgroup; s_red ready
-    const float gdev = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    float gdev = s_red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) gdev = fmaxf(gdev, s_red[w]);
     if (gdev < 3e-5f) break;
     // Ynew = Y T, Znew = T Z
-    float ay[SUB][SUB], az[SUB][SUB];
+    float ay[SI][SJ], az[SI][SJ];
 #pragma unroll
-    for (int i = 0; i < SUB; ++i)
+    for (int i = 0; i < SI; ++i)
 #pragma unroll
-      for (int j = 0; j < SUB; ++j) { ay[i][j] = 0.f; az[i][j] = 0.f; }
+      for (int j = 0; j < SJ; ++j) { ay[i][j] = 0.f; az[i][j] = 0.f; }
     for (int kx = 0; kx < D; ++kx) {
-      float ya[SUB], tb[SUB], ta[SUB], zb[SUB];
+      float ya[SI], tb[SJ], ta[SI], zb[SJ];
 #pragma unroll
-      for (int i = 0; i < SUB; ++i) {
+      for (int i = 0; i < SI; ++i) {
         ya[i] = sY[(bi + i) * D + kx];
-        tb[i] = tg[kx * D + bj + i];
         ta[i] = tg[(bi + i) * D + kx];
-        zb[i] = sZ[kx * D + bj + i];
       }
 #pragma unroll
-      for (int i = 0; i < SUB; ++i)
+      for (int j = 0; j < SJ; ++j) {
+        tb[j] = tg[kx * D + bj + j];
+        zb[j] = sZ[kx * D + bj + j];
+      }
 #pragma unroll
-        for (int j = 0; j < SUB; ++j) {
+      for (int i = 0; i < SI; ++i)
+#pragma unroll
+        for (int j = 0; j < SJ; ++j) {
           ay[i][j] = fmaf(ya[i], tb[j], ay[i][j]);
           az[i][j] = fmaf(ta[i], zb[j], az[i][j]);
         }
     }
     __syncthreads();  // everyone done reading old Y, Z and T
 #pragma unroll
-    for (int i = 0; i < SUB; ++i)
+    for (int i = 0; i < SI; ++i)
 #pragma unroll
-      for (int j = 0; j < SUB; ++j) {
+      for (int j = 0; j < SJ; ++j) {
         sY[(bi + i) * D + bj + j] = ay[i][j];
         sZ[(bi + i) * D + bj + j] = az[i][j];
       }
     __syncthreads();
   }
   const float sc = sqrtf(fro);
-  for (int e = tid; e < D * D; e += 256) {
+  for (int e = tid; e < D * D; e += MSQ_T) {
     const int r = e / D, c = e % D;
     W[off + e] = 0.5f * (sY[r * D + c] + sY[c * D + r]) * sc;
   }
@@ -390,9 +404,9 @@ size_t msqrt_ws_bytes(int count, int D) { return (size_t)count * D * D * 4; }
 
 int msqrt_launch(int count, int D, const float* M, float* W, float* Tscr, hipStream_t st) {
   if (D == 128)
-    hipLaunchKernelGGL(msqrt_kernel<128>, dim3(count), dim3(256), 0, st, M, W, Tscr);
+    hipLaunchKernelGGL(msqrt_kernel<128>, dim3(count), dim3(MSQ_T), 0, st, M, W, Tscr);
   else
-    hipLaunchKernelGGL(msqrt_kernel<64>, dim3(count), dim3(256), 0, st, M, W, Tscr);
+    hipLaunchKernelGGL(msqrt_kernel<64>, dim3(count), dim3(MSQ_T), 0, st, M, W, Tscr);
   return spark_check_launch("msqrt");
 }
 
