@@ -414,7 +414,7 @@ int msqrt_launch(int count, int D, const float* M, float* W, float* Tscr, hipStr
 // whiten: xhat = normalize(W x) row by row.  bf16: x^T-side MFMA with W (bf16)
 // as the A operand: O^T[c][i] = sum_k W[c][k] x_i[k]; lane l32 owns row i.
 // ---------------------------------------------------------------------------
-constexpr int WH_ROWS = 1024;  // rows per workgroup: 8 rounds of 4 waves x 32
+constexpr int WH_ROWS = 4096;  // rows per workgroup: 32 rounds of 4 waves x 32 (the W setup is paid per workgroup)
 
 // Each wave whitens 32 consecutive rows per round.  The rows (8 KB for
 // d = 128, contiguous in HBM) come in with 16-byte lane loads, four rows per
