@@ -844,38 +844,42 @@ __global__ __launch_bounds__(FIN_T) void finisher(const T* __restrict__ xh,
     }
     const uint32_t thr = s_prefix[team];
     const int ties_needed = s_need[team];
-    // stable partition: E consecutive positions per thread
+    // stable partition: E consecutive positions per thread.  Before position
+    // p, lt(p) keys are below the threshold and eq(p) equal to it; a tie
+    // goes left iff its rank among ties is < ties_needed, so the lefts before
+    // p number lt(p) + min(eq(p), ties_needed): one scan of the packed
+    // (lt, eq) counts places every position.
     constexpr int EMAX = FIN_MAX / NT;
     const int E = (len + NT - 1) / NT;
-    int ne = 0;
-    for (int e = 0; e < E; ++e) {
-      const int p = ttid * E + e;
-      if (p < len && pref_key_desc(s_val[a + p]) == thr) ++ne;
-    }
-    int tot;
-    int ce = team_exscan<NT>(ne, s_tmp, w0, tot);
-    int nl = 0;
-    bool left[EMAX];
+    uint32_t kk[EMAX];
+    int lt = 0, eq = 0;
 #pragma unroll
     for (int e = 0; e < EMAX; ++e) {
       const int p = ttid * E + e;
-      bool l = false;
-      if (e < E && p < len) {
-        const uint32_t k = pref_key_desc(s_val[a + p]);
-        if (k < thr) l = true;
-        else if (k == thr) { l = ce < ties_needed; ++ce; }
-      }
-      left[e] = l;
-      nl += l;
+      kk[e] = (e < E && p < len) ? pref_key_desc(s_val[a + p]) : 0xffffffffu;
+      lt += (e < E && p < len && kk[e] < thr);
+      eq += (e < E && p < len && kk[e] == thr);
     }
-    int cl = team_exscan<NT>(nl, s_tmp, w0, tot);
+    int tot;
+    const int packed = team_exscan<NT>((lt << 16) | eq, s_tmp, w0, tot);   // counts < 2^16
+    int lt_c = packed >> 16, eq_c = packed & 0xffff;
 #pragma unroll
     for (int e = 0; e < EMAX; ++e) {
       const int p = ttid * E + e;
       if (e >= E || p >= len) continue;
-      const int dst = left[e] ? cl : cL + (p - cl);
+      const int left_before = lt_c + min(eq_c, ties_needed);
+      bool l;
+      if (kk[e] < thr) {
+        l = true;
+        ++lt_c;
+      } else if (kk[e] == thr) {
+        l = eq_c < ties_needed;
+        ++eq_c;
+      } else {
+        l = false;
+      }
+      const int dst = l ? left_before : cL + (p - left_before);
       if (dst < len) s_tmp_lid[a + dst] = s_lid[a + p];
-      cl += left[e];
     }
     __syncthreads();
     for (int i = ttid; i < len; i += NT) s_lid[a + i] = s_tmp_lid[a + i];
