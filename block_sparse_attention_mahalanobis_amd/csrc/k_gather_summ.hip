@@ -127,6 +127,35 @@ int gather_launch(int H, int N, int Nv, int D, int BK, int dtype, const void* x,
                   : gather_t<uint16_t, 64>(H, N, Nv, BK, x, perm, xp, xpt, xbar, st);
 }
 
+// 8 consecutive elements as loaded (16 bytes of bf16, 32 of fp32), widened
+// to fp32 on use.
+template <typename T> struct Raw8;
+template <> struct Raw8<uint16_t> {
+  uint4 q;
+  __device__ __forceinline__ void load(const uint16_t* p) { q = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void zero() { q = make_uint4(0u, 0u, 0u, 0u); }
+  __device__ __forceinline__ void widen(float (&v)[8]) const {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+template <> struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ __forceinline__ void widen(float (&v)[8]) const {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
 // ---------------------------------------------------------------------------
 // summaries.  REWEIGHT:  t_j = anchor.k_j / sqrt(d);  w = softmax_B(t);
 //   ksum = sum w_j k_j;  vsum = sum w_j v_j;
@@ -154,22 +183,44 @@ __global__ __launch_bounds__(256) void summarize_kernel(const T* __restrict__ kp
   const T* vblk = vpt + ((long)h * nbt + B) * (long)D * BK;
   constexpr int CPR = D / 8;           // chunks per row
   constexpr int RPP = 256 / CPR;       // rows per pass
+  constexpr int NR = 128 / RPP;        // row passes of a block of up to 128 tokens
+  // the block's key chunks (rows rg + RPP i) and transposed value chunks
+  // (rows c + 16 i, tokens jc .. jc + 7), all loaded up front: a workgroup
+  // then has its whole block in flight, and the keys serve both key passes
+  const int rg = tid / CPR, ck = (tid % CPR) * 8;
+  const int rv = tid / 16, jc = (tid % 16) * 8;
+  Raw8<T> kraw[NR], vraw[D / 16];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int j = rg + RPP * i;
+    if (j < n_real) kraw[i].load(kblk + (long)j * D + ck);
+    else kraw[i].zero();
+  }
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) {
+    if (jc < n_real) vraw[i].load(vblk + (long)(rv + 16 * i) * BK + jc);
+    else vraw[i].zero();
+  }
+  auto widen8 = [](const Raw8<T>& q, float (&v)[8]) { q.widen(v); };
 
   if (!mean_mode) {
     for (int c = tid; c < D; c += 256) s_anchor[c] = anchor[(long)h * D + c];
     __syncthreads();
     // t_j: CPR lanes per row, reduced with shuffles (CPR is 8 or 16)
-    for (int j0 = 0; j0 < n_real; j0 += RPP) {
-      const int j = j0 + tid / CPR, c = (tid % CPR) * 8;
-      float acc = 0.f;
-      if (j < n_real) {
-        float v[8];
-        load8(kblk + (long)j * D + c, v);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fmaf(v[e], s_anchor[c + e], acc);
+    for (int i = 0; i < NR; ++i) {
+      if (RPP * i < n_real) {   // uniform
+        const int j = rg + RPP * i;
+        float acc = 0.f;
+        if (j < n_real) {
+          float v[8];
+          widen8(kraw[i], v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc = fmaf(v[e], s_anchor[ck + e], acc);
+        }
+        acc = group_sum<CPR>(acc);
+        if (j < n_real && (tid % CPR) == 0) s_w[j] = acc * rsd;
       }
-      acc = group_sum<CPR>(acc);
-      if (j < n_real && (tid % CPR) == 0) s_w[j] = acc * rsd;
     }
     __syncthreads();
     if (tid < 64) {
@@ -195,14 +246,18 @@ __global__ __launch_bounds__(256) void summarize_kernel(const T* __restrict__ kp
 
   // ksum: row-chunk partials over RPP row groups, then a fixed-order reduce
   {
-    const int rg = tid / CPR, c = (tid % CPR) * 8;
+    const int c = ck;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = rg; j < n_real; j += RPP) {
-      float v[8];
-      load8(kblk + (long)j * D + c, v);
-      const float w = s_w[j];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, v[e], acc[e]);
+    for (int i = 0; i < NR; ++i) {
+      const int j = rg + RPP * i;
+      if (j < n_real) {
+        float v[8];
+        widen8(kraw[i], v);
+        const float w = s_w[j];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, v[e], acc[e]);
+      }
     }
     if (rg < 16) {
 #pragma unroll
@@ -226,16 +281,16 @@ __global__ __launch_bounds__(256) void summarize_kernel(const T* __restrict__ kp
   // load), then a fixed shuffle tree over the 16 lanes; tokens past n_real
   // are skipped.
   {
-    const int rr = tid / 16, jc = (tid % 16) * 8;
     float wv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) wv[e] = (jc + e < n_real) ? s_w[jc + e] : 0.f;
-    for (int c0 = 0; c0 < D; c0 += 16) {
-      const int c = c0 + rr;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      const int c = rv + 16 * i;
       float acc = 0.f;
       if (jc < n_real) {
         float v[8];
-        load8(vblk + (long)c * BK + jc, v);
+        widen8(vraw[i], v);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (jc + e < n_real) acc = fmaf(wv[e], v[e], acc);
