@@ -83,39 +83,6 @@ __device__ __forceinline__ uint32_t float_key_asc(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// k-th smallest (1-based) of n <= 64 * KPL uint32 keys, found by ONE wave:
-// every lane copies its keys (i = lane + 64 j) into registers, then a
-// bisection over the key space runs 32 rounds of count(key <= mid) -- register
-// compares plus a wave reduction; no atomics, no barriers, no LDS traffic.
-// Returns the key; *ties_needed = k - count(key < result).  Padding slots
-// hold 0xffffffff and never count below a real threshold (k <= n).
-template <int KPL>
-__device__ __forceinline__ uint32_t wave_kth_key(const uint32_t* keys, int n, int k,
-                                                 int* ties_needed) {
-  const int lane = threadIdx.x & 63;
-  uint32_t r[KPL];
-#pragma unroll
-  for (int j = 0; j < KPL; ++j) {
-    const int i = lane + 64 * j;
-    r[j] = (i < n) ? keys[i] : 0xffffffffu;
-  }
-  uint32_t lo = 0u, hi = 0xffffffffu;
-  while (lo < hi) {
-    const uint32_t mid = lo + ((hi - lo) >> 1);
-    // wave-wide count as a sum of ballot popcounts (scalar unit, no shuffles);
-    // padding keys (0xffffffff) never count: mid < 0xffffffff inside the loop
-    int c = 0;
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) c += __builtin_popcountll(__builtin_amdgcn_ballot_w64(r[j] <= mid));
-    if (c >= k) hi = mid; else lo = mid + 1;
-  }
-  int less = 0;
-#pragma unroll
-  for (int j = 0; j < KPL; ++j) less += __builtin_popcountll(__builtin_amdgcn_ballot_w64(r[j] < lo));
-  *ties_needed = k - less;
-  return lo;
-}
-
 // k-th smallest (1-based) of n uint32 keys in LDS, found by ONE wave with a
 // private 256-int LDS histogram: 4 radix rounds of 8 bits (count the keys
 // that match the prefix so far, then pick the digit holding rank k).
@@ -174,29 +141,6 @@ __device__ __forceinline__ uint32_t wave_radix_kth(const uint32_t* keys, int n, 
   }
   *ties_needed = need;
   return prefix;
-}
-
-// Same result for any n, reading the keys from LDS every round (slower).
-__device__ __forceinline__ uint32_t wave_kth_key_lds(const uint32_t* keys, int n, int k,
-                                                     int* ties_needed) {
-  const int lane = threadIdx.x & 63;
-  uint32_t lo = 0u, hi = 0xffffffffu;
-  while (lo < hi) {
-    const uint32_t mid = lo + ((hi - lo) >> 1);
-    int c = 0;
-    for (int i0 = 0; i0 < n; i0 += 64) {
-      const int i = i0 + lane;
-      c += __builtin_popcountll(__builtin_amdgcn_ballot_w64(i < n && keys[i] <= mid));
-    }
-    if (c >= k) hi = mid; else lo = mid + 1;
-  }
-  int less = 0;
-  for (int i0 = 0; i0 < n; i0 += 64) {
-    const int i = i0 + lane;
-    less += __builtin_popcountll(__builtin_amdgcn_ballot_w64(i < n && keys[i] < lo));
-  }
-  *ties_needed = k - less;
-  return lo;
 }
 
 // Butterfly reductions over aligned groups of G lanes (G a power of two,

@@ -3,10 +3,13 @@
 // attention; 01 / Method: Spark-Reblock: a fixed Top-K budget per query block).
 //
 // One workgroup per (head, 8 consecutive query blocks): the rows S[A, :] =
-// qbar_A . kbar_B / sqrt(d) are computed into LDS (each k_bar chunk read once
-// for all 8 rows; or read from scores_in); then one wave per row finds the
-// k-th best order key (score desc, block asc) by bisection and writes the
-// selected blocks in ascending order with ballot prefix sums.  Integer decisions only; bit-exact for given scores.
+// qbar_A . kbar_B / sqrt(d) are computed into LDS (each lane scores four key
+// blocks against all 8 query means, so every k_bar read serves 8 rows and
+// every query-mean read 4 blocks; or read from scores_in); then one wave per
+// row finds the k-th best order key (score desc, block asc) by a radix
+// select over the 32-bit keys and writes the selected blocks in ascending
+// order with ballot prefix sums.  Integer decisions only; bit-exact for given
+// scores.
 #include "common.hpp"
 
 namespace spark {
