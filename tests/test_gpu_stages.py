@@ -320,6 +320,7 @@ def test_split_hand_fixtures_exact():
     (torch.float32, 3000, 64, 64, 2),
     (torch.bfloat16, 700, 64, 32, 2),
     (torch.float32, 257, 64, 1, 1),          # block 1: N leaves
+    (torch.bfloat16, 2051, 128, 5, 2),       # odd N, block 5: group starts not 16-byte aligned
 ])
 def test_split_bit_exact_on_integer_embeddings(dt, N, d, b, count):
     """Small-integer vectors: every sum and dot is exact in fp32, so the
