@@ -87,6 +87,26 @@ def attn_flops(idx, N, b, d, Nv=None):
     return exact, comp
 
 
+def split_rows_read(Nv, b, levels_global):
+    """Rows one side's global split levels read: the centroid, pole-A, pole-B
+    and score passes over every group that splits (>= 2 blocks), except that
+    below the root the centroid pass skips right children (a right child's
+    sum is its parent's minus its sibling's)."""
+    def nrows(start, n):
+        return min(Nv, (start + n) * b) - start * b
+    groups, rows = [(0, -(-Nv // b), False)], 0
+    for _ in range(levels_global):
+        nxt = []
+        for start, n, right in groups:
+            if n < 2:
+                continue
+            rows += (3 if right else 4) * nrows(start, n)
+            nl = (n + 1) // 2
+            nxt += [(start, nl, False), (start + nl, n - nl, True)]
+        groups = nxt
+    return rows
+
+
 def reblock_bytes(H, N, d, b, es, levels_global, nb, sides=2, Nv=None):
     """Algorithmic HBM bytes of reblock + summaries (per layer); sides = 1
     for q_reuse_k (moments of q only, keys whitened and split).  With
@@ -96,7 +116,7 @@ def reblock_bytes(H, N, d, b, es, levels_global, nb, sides=2, Nv=None):
     volv = H * Nv * d * es                    # its video rows
     moments = sides * vol
     whiten = 2 * sides * volv
-    split = sides * (levels_global * 4 * volv + volv)   # 4 row passes per global level + finisher
+    split = sides * (H * split_rows_read(Nv, b, levels_global) * d * es + volv)   # + finisher
     gather = 6 * vol
     summ = 2 * volv
     return moments + whiten + split + gather + summ
@@ -330,11 +350,14 @@ def main():
     exact_tf = exact / attn_s / 1e12
     alg_tf = (exact + comp) / attn_s / 1e12
     # deepest global split level: groups must fit the LDS finisher
-    fb = (140 * 1024) // (b * (d * es + 16))
+    fb = (136 * 1024) // (b * (d * es + 16))
     fb = min(fb, 1024 // b)
     F = 1
     while F * 2 <= fb:
         F *= 2
+    rpt = 512 // (d // (16 // es))            # finisher rows per lane slot; 16 held per split
+    while F > 1 and (F * b > 16 * rpt or ((F + 1) // 2) * b > 16 * (rpt // 2)):
+        F //= 2
     lev, mx = 0, nb
     while mx > F:
         mx = (mx + 1) // 2

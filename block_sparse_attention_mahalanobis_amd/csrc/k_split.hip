@@ -16,8 +16,10 @@
 // left/right path) by walking down from the root; no tables are needed.
 //
 // Large groups (global levels) use level-synchronous passes over all trees:
-//   cent_partial  -> per-block partial centroid sums (rows gathered by id)
-//   cent_reduce   -> per-group centroid (fixed chunk order: deterministic)
+//   cent_partial  -> per-block partial centroid sums (rows gathered by id;
+//                    below the root only the left children's blocks)
+//   cent_reduce   -> per-group centroid sum in fp64 (fixed chunk order:
+//                    deterministic); a right child's is parent - left
 //   argmin_partial/argmin_reduce (twice: pole A, pole B; 64-bit (key, id) mins)
 //   score         -> s_i for every position
 //   select_partition (one workgroup per group): exact radix select of the
@@ -148,6 +150,7 @@ __global__ __launch_bounds__(SPL_T) void cent_partial(const T* __restrict__ xh,
   const int cb = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
   int start, nbg, slot;
   if (!group_of_block(cb, level, nb, start, nbg, slot)) return;
+  if (level > 0 && (slot & 1)) return;   // a right child: parent - left (cent_reduce)
   const int n_real = min(BK, N - cb * BK);
   const int rg = tid / CPR, c = (tid % CPR) * VE;
   stage_ids(s_ids, ids + (long)t * N + (long)cb * BK, n_real);
@@ -178,42 +181,55 @@ __global__ __launch_bounds__(SPL_T) void cent_partial(const T* __restrict__ xh,
   }
 }
 
-// Per group: centroid = sum of its blocks' partials.  CR_T threads: column
+// Per group: centroid sum, in fp64.  At the root, the sum of its blocks'
+// partials.  Below it, one workgroup per parent: the left child's sum comes
+// from its blocks' partials and the right child's is the parent's sum minus
+// the left's, which is the same sum in exact arithmetic and saves reading the
+// right half's rows; in fp64 the subtraction stays far below fp32 rounding.
+// The left child holds ceil(nb_g / 2) blocks, so whenever the right child
+// still splits (>= 2 blocks) the left has been summed.  CR_T threads: column
 // c = tid % D, block stride G = CR_T / D; each thread keeps 8 partial sums
 // (8 loads in flight), then the G partials are added in a fixed order
 // (deterministic).  The top levels have few groups with thousands of blocks.
 constexpr int CR_T = 1024;
 template <int D>
 __global__ __launch_bounds__(CR_T) void cent_reduce(const float* __restrict__ cpart,
-                                                    float* __restrict__ cen, int nb, int level,
+                                                    const double* __restrict__ cen_up,
+                                                    double* __restrict__ cen, int nb, int level,
                                                     int S) {
   constexpr int G = CR_T / D;
-  __shared__ float s_p[G][D];
-  const int slot = blockIdx.x, t = blockIdx.y;
+  __shared__ double s_p[G][D];
+  const int par = blockIdx.x, t = blockIdx.y;
+  const int lslot = level == 0 ? 0 : 2 * par;   // the root, or the parent's left child
   const int c = threadIdx.x % D, g = threadIdx.x / D;
   int start, nbg;
-  if (!group_of_slot(slot, level, nb, start, nbg) || nbg < 2) return;
+  if (!group_of_slot(lslot, level, nb, start, nbg) || nbg < 2) return;
   const int end = start + nbg;
   const float* src = cpart + (long)t * nb * D + c;
-  float a[8];
+  double a[8];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) a[u] = 0.f;
+  for (int u = 0; u < 8; ++u) a[u] = 0.0;
   int b = start + g;
   for (; b + 7 * G < end; b += 8 * G) {
     float v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) v[u] = src[(long)(b + u * G) * D];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) a[u] += v[u];
+    for (int u = 0; u < 8; ++u) a[u] += (double)v[u];
   }
-  for (; b < end; b += G) a[0] += src[(long)b * D];
+  for (; b < end; b += G) a[0] += (double)src[(long)b * D];
   s_p[g][c] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
   __syncthreads();
   if (g == 0) {
-    float s = 0.f;
+    double sl = 0.0;
 #pragma unroll
-    for (int i = 0; i < G; ++i) s += s_p[i][c];
-    cen[((long)t * S + slot) * D + c] = s;
+    for (int i = 0; i < G; ++i) sl += s_p[i][c];
+    cen[((long)t * S + lslot) * D + c] = sl;
+    if (level > 0) {
+      int rstart, rnb;
+      if (group_of_slot(lslot + 1, level, nb, rstart, rnb) && rnb >= 2)
+        cen[((long)t * S + lslot + 1) * D + c] = cen_up[((long)t * S + par) * D + c] - sl;
+    }
   }
 }
 
@@ -222,7 +238,7 @@ __global__ __launch_bounds__(CR_T) void cent_reduce(const float* __restrict__ cp
 template <typename T, int D>
 __global__ __launch_bounds__(SPL_T) void argmin_partial(const T* __restrict__ xh,
                                                         const int32_t* __restrict__ ids,
-                                                        const float* __restrict__ cen,
+                                                        const double* __restrict__ cen,
                                                         const int32_t* __restrict__ poleA,
                                                         uint64_t* __restrict__ mpart, int N,
                                                         int BK, int nb, int level, int S,
@@ -240,7 +256,7 @@ __global__ __launch_bounds__(SPL_T) void argmin_partial(const T* __restrict__ xh
   float vec[VE];
   if (mode == 0) {
 #pragma unroll
-    for (int e = 0; e < VE; ++e) vec[e] = cen[((long)t * S + slot) * D + c + e];
+    for (int e = 0; e < VE; ++e) vec[e] = (float)cen[((long)t * S + slot) * D + c + e];
   } else {
     Chunk<T>::load(xt + (long)poleA[(long)t * S + slot] * D + c, vec);
   }
@@ -963,7 +979,8 @@ size_t split_ws_bytes(int count, int N, int D, int BK, int dtype) {
   b += up256((size_t)count * N * 4);                // s
   b += up256((size_t)count * p.nb * D * 4);         // cpart
   b += up256((size_t)count * p.nb * 8);             // mpart
-  b += 2 * up256((size_t)count * p.S * D * 4);      // cen, diff
+  b += 2 * up256((size_t)count * p.S * D * 8);      // cen (fp64), one per level parity
+  b += up256((size_t)count * p.S * D * 4);          // diff
   b += 2 * up256((size_t)count * p.S * 4);          // poleA, poleB
   return b;
 }
@@ -979,7 +996,9 @@ static int split_t(int count, int N, int BK, const void* xhv, int32_t* perm_lo,
   float* s = (float*)w; w += up256((size_t)count * N * 4);
   float* cpart = (float*)w; w += up256((size_t)count * p.nb * D * 4);
   uint64_t* mpart = (uint64_t*)w; w += up256((size_t)count * p.nb * 8);
-  float* cen = (float*)w; w += up256((size_t)count * p.S * D * 4);
+  double* cen_ab[2];
+  cen_ab[0] = (double*)w; w += up256((size_t)count * p.S * D * 8);
+  cen_ab[1] = (double*)w; w += up256((size_t)count * p.S * D * 8);
   float* diff = (float*)w; w += up256((size_t)count * p.S * D * 4);
   int32_t* poleA = (int32_t*)w; w += up256((size_t)count * p.S * 4);
   int32_t* poleB = (int32_t*)w;
@@ -995,9 +1014,10 @@ static int split_t(int count, int N, int BK, const void* xhv, int32_t* perm_lo,
     int32_t* nxt = ids_b;
     for (int lev = 0; lev < p.Lf; ++lev) {
       const int S = 1 << lev;
-      dim3 gc(p.nb, count), gs(S, count);
+      dim3 gc(p.nb, count), gs(S, count), gp(lev == 0 ? 1 : S / 2, count);
+      double* cen = cen_ab[lev & 1];             // this level's sums; the parents' in the other
       hipLaunchKernelGGL((cent_partial<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, cpart, N, BK, p.nb, lev);
-      hipLaunchKernelGGL((cent_reduce<D>), gs, dim3(CR_T), 0, st, cpart, cen, p.nb, lev, p.S);
+      hipLaunchKernelGGL((cent_reduce<D>), gp, dim3(CR_T), 0, st, cpart, cen_ab[(lev + 1) & 1], cen, p.nb, lev, p.S);
       hipLaunchKernelGGL((argmin_partial<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, cen, poleA, mpart, N, BK, p.nb, lev, p.S, 0);
       hipLaunchKernelGGL((argmin_reduce<T, D>), gs, dim3(64), 0, st, mpart, xh, poleA, poleB, diff, N, p.nb, lev, p.S, 0);
       hipLaunchKernelGGL((argmin_partial<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, cen, poleA, mpart, N, BK, p.nb, lev, p.S, 1);
