@@ -83,10 +83,12 @@ __device__ __forceinline__ uint32_t float_key_asc(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// k-th smallest (1-based) of n uint32 keys in LDS, found by ONE wave with a
-// private 256-int LDS histogram: 4 radix rounds of 8 bits (count the keys
-// that match the prefix so far, then pick the digit holding rank k).
-// Returns the key; *ties_needed = k - count(key < result).
+// k-th smallest (1-based) of n uint32 keys, found by ONE wave with a private
+// 256-int LDS histogram: 4 radix rounds of 8 bits (count the keys that match
+// the prefix so far, then pick the digit holding rank k).  Returns the key;
+// *ties_needed = k - count(key < result).  count(prefix, hmask, shift)
+// adds, for every key with (key & hmask) == prefix, one to
+// hist[(key >> shift) & 255]; the keys may sit in LDS or in registers.
 //
 // The hardware runs one wave's LDS instructions in issue order, but to the
 // compiler the other lanes' atomics race with the plain reads: without an
@@ -95,8 +97,9 @@ __device__ __forceinline__ uint32_t float_key_asc(float f) {
 // the wave's LDS operations and is a compiler memory barrier.
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-__device__ __forceinline__ uint32_t wave_radix_kth(const uint32_t* keys, int n, int k, int* hist,
-                                                   int* ties_needed) {
+template <typename CountFn>
+__device__ __forceinline__ uint32_t wave_radix_select(int k, int* hist, int* ties_needed,
+                                                      CountFn&& count) {
   const int lane = threadIdx.x & 63;
   uint32_t prefix = 0;
   int need = k;
@@ -105,10 +108,7 @@ __device__ __forceinline__ uint32_t wave_radix_kth(const uint32_t* keys, int n, 
     for (int j = 0; j < 4; ++j) hist[4 * lane + j] = 0;
     wave_lds_sync();
     const uint32_t hmask = (shift == 24) ? 0u : (0xffffffffu << (shift + 8));
-    for (int i = lane; i < n; i += 64) {
-      const uint32_t key = keys[i];
-      if ((key & hmask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
-    }
+    count(prefix, hmask, shift);
     wave_lds_sync();
     int c[4], run = 0;
 #pragma unroll
@@ -141,6 +141,18 @@ __device__ __forceinline__ uint32_t wave_radix_kth(const uint32_t* keys, int n, 
   }
   *ties_needed = need;
   return prefix;
+}
+
+// The n keys in LDS, lane i counting keys i, i + 64, ...
+__device__ __forceinline__ uint32_t wave_radix_kth(const uint32_t* keys, int n, int k, int* hist,
+                                                   int* ties_needed) {
+  const int lane = threadIdx.x & 63;
+  return wave_radix_select(k, hist, ties_needed, [&](uint32_t prefix, uint32_t hmask, int shift) {
+    for (int i = lane; i < n; i += 64) {
+      const uint32_t key = keys[i];
+      if ((key & hmask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+    }
+  });
 }
 
 // Butterfly reductions over aligned groups of G lanes (G a power of two,

@@ -7,9 +7,9 @@
 // blocks against all 8 query means, so every k_bar read serves 8 rows and
 // every query-mean read 4 blocks; or read from scores_in); then one wave per
 // row finds the k-th best order key (score desc, block asc) by a radix
-// select over the 32-bit keys and writes the selected blocks in ascending
-// order with ballot prefix sums.  Integer decisions only; bit-exact for given
-// scores.
+// select over the 32-bit keys, held in registers, and writes the selected
+// blocks in ascending order with ballot prefix sums.  Integer decisions
+// only; bit-exact for given scores.
 #include "common.hpp"
 
 namespace spark {
@@ -20,6 +20,60 @@ constexpr int SEL_T = 256;
 __device__ __forceinline__ uint32_t pref_key(float s) {
   if (s != s) return 0xffffffffu;
   return ~float_key_asc(s);
+}
+
+// One row's top-k by one wave: the key of rank topk (radix select), then
+// the blocks below it and the first ties_needed blocks equal to it, in
+// ascending block order, each placed by a ballot prefix sum.  KPL > 0: the
+// row's keys are first loaded into registers (block B in lane B % 64, slot
+// B / 64; nb <= 64 KPL), so neither the radix rounds nor the emission read
+// LDS per key; KPL = 0: the keys are read from LDS.
+template <int KPL>
+__device__ __forceinline__ void row_topk(const uint32_t* s_key, int nb, int topk, int* hist,
+                                         int32_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  int ties_needed;
+  uint32_t thr;
+  uint32_t kr[KPL > 0 ? KPL : 1];
+  if constexpr (KPL > 0) {
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int B = 64 * j + lane;
+      kr[j] = (B < nb) ? s_key[B] : 0xffffffffu;
+    }
+    thr = wave_radix_select(topk, hist, &ties_needed, [&](uint32_t prefix, uint32_t hmask, int shift) {
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        const int B = 64 * j + lane;
+        if (B < nb && (kr[j] & hmask) == prefix) atomicAdd(&hist[(kr[j] >> shift) & 255], 1);
+      }
+    });
+  } else {
+    thr = wave_radix_kth(s_key, nb, topk, hist, &ties_needed);
+  }
+  int taken = 0, ties_seen = 0;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  auto step = [&](int B, uint32_t k) {
+    const bool tie = (B < nb) && (k == thr);
+    const uint64_t tmask = __builtin_amdgcn_ballot_w64(tie);
+    const int tie_rank = ties_seen + __builtin_popcountll(tmask & below);
+    const bool sel = (B < nb) && (k < thr || (tie && tie_rank < ties_needed));
+    const uint64_t smask = __builtin_amdgcn_ballot_w64(sel);
+    const int pos = taken + __builtin_popcountll(smask & below);
+    if (sel && pos < topk) out[pos] = B;
+    taken += __builtin_popcountll(smask);
+    ties_seen += __builtin_popcountll(tmask);
+  };
+  if constexpr (KPL > 0) {
+#pragma unroll
+    for (int j = 0; j < KPL; ++j)
+      if (64 * j < nb) step(64 * j + lane, kr[j]);   // uniform
+  } else {
+    for (int B0 = 0; B0 < nb; B0 += 64) {
+      const int B = B0 + lane;
+      step(B, (B < nb) ? s_key[B] : 0xffffffffu);
+    }
+  }
 }
 
 constexpr int SEL_QB = 8;   // query blocks per workgroup (they share each k_bar read)
@@ -54,7 +108,10 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(const float* __restrict__
     // SEL_KB key blocks per lane: the nq query means sit in LDS (broadcast
     // reads, each one used for SEL_KB blocks), the lane streams its k_bar
     // rows; no cross-lane reductions.  Every score is one fp32 FMA chain
-    // over d in ascending order.
+    // over d in ascending order.  A lane's row reads are per-lane 16-byte
+    // loads, 64 rows apart across the wave: the four loads that cover 64
+    // bytes of a row are issued together, so they share the cache lines
+    // they fetch instead of fetching them again on later steps.
     float* s_q = reinterpret_cast<float*>(smem + (size_t)qb * nb * 4);   // [qb][D]
     for (int e = tid; e < nq * D; e += SEL_T) s_q[e] = qbar[((long)h * nb + A0) * D + e];
     __syncthreads();
@@ -68,21 +125,26 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(const float* __restrict__
       for (int r = 0; r < SEL_KB; ++r)
 #pragma unroll
         for (int q = 0; q < SEL_QB; ++q) acc[r][q] = 0.f;
-#pragma unroll 2
-      for (int c = 0; c < D; c += 4) {
-        float4 kv[SEL_KB];
+      for (int c0 = 0; c0 < D; c0 += 16) {
+        float4 kv[SEL_KB][4];
 #pragma unroll
-        for (int r = 0; r < SEL_KB; ++r) kv[r] = *reinterpret_cast<const float4*>(kr[r] + c);
+        for (int r = 0; r < SEL_KB; ++r)
 #pragma unroll
-        for (int q = 0; q < SEL_QB; ++q) {
-          if (q < nq) {
-            const float4 qv = *reinterpret_cast<const float4*>(s_q + q * D + c);
+          for (int u = 0; u < 4; ++u) kv[r][u] = *reinterpret_cast<const float4*>(kr[r] + c0 + 4 * u);
 #pragma unroll
-            for (int r = 0; r < SEL_KB; ++r) {
-              acc[r][q] = fmaf(qv.x, kv[r].x, acc[r][q]);
-              acc[r][q] = fmaf(qv.y, kv[r].y, acc[r][q]);
-              acc[r][q] = fmaf(qv.z, kv[r].z, acc[r][q]);
-              acc[r][q] = fmaf(qv.w, kv[r].w, acc[r][q]);
+        for (int u = 0; u < 4; ++u) {
+          const int c = c0 + 4 * u;
+#pragma unroll
+          for (int q = 0; q < SEL_QB; ++q) {
+            if (q < nq) {
+              const float4 qv = *reinterpret_cast<const float4*>(s_q + q * D + c);
+#pragma unroll
+              for (int r = 0; r < SEL_KB; ++r) {
+                acc[r][q] = fmaf(qv.x, kv[r][u].x, acc[r][q]);
+                acc[r][q] = fmaf(qv.y, kv[r][u].y, acc[r][q]);
+                acc[r][q] = fmaf(qv.z, kv[r][u].z, acc[r][q]);
+                acc[r][q] = fmaf(qv.w, kv[r][u].w, acc[r][q]);
+              }
             }
           }
         }
@@ -106,27 +168,21 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(const float* __restrict__
   __syncthreads();
 
   // one wave per row: radix select of the threshold key, then ballot prefix
-  // sums emit the selected blocks in ascending order (no barriers)
+  // sums emit the selected blocks in ascending order (no barriers); rows of
+  // up to 4096 blocks hold their keys in registers
   for (int q = wave; q < nq; q += SEL_T / 64) {
     const uint32_t* s_key = s_keys + q * nb;
-    int ties_needed;
-    const uint32_t thr = wave_radix_kth(s_key, nb, topk, s_whist[wave], &ties_needed);
     int32_t* out = idx + ((long)h * nb + A0 + q) * topk;
-    int taken = 0, ties_seen = 0;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int B0 = 0; B0 < nb; B0 += 64) {
-      const int B = B0 + lane;
-      const uint32_t k = (B < nb) ? s_key[B] : 0xffffffffu;
-      const bool tie = (B < nb) && (k == thr);
-      const uint64_t tmask = __builtin_amdgcn_ballot_w64(tie);
-      const int tie_rank = ties_seen + __builtin_popcountll(tmask & below);
-      const bool sel = (B < nb) && (k < thr || (tie && tie_rank < ties_needed));
-      const uint64_t smask = __builtin_amdgcn_ballot_w64(sel);
-      const int pos = taken + __builtin_popcountll(smask & below);
-      if (sel && pos < topk) out[pos] = B;
-      taken += __builtin_popcountll(smask);
-      ties_seen += __builtin_popcountll(tmask);
-    }
+    if (nb <= 64 * 8)
+      row_topk<8>(s_key, nb, topk, s_whist[wave], out);
+    else if (nb <= 64 * 16)
+      row_topk<16>(s_key, nb, topk, s_whist[wave], out);
+    else if (nb <= 64 * 32)
+      row_topk<32>(s_key, nb, topk, s_whist[wave], out);
+    else if (nb <= 64 * 64)
+      row_topk<64>(s_key, nb, topk, s_whist[wave], out);
+    else
+      row_topk<0>(s_key, nb, topk, s_whist[wave], out);
   }
 }
 

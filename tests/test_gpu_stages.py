@@ -180,6 +180,25 @@ def test_topk_ties_nan_and_full_density():
             assert np.array_equal(got[h], want), (h, topk)
 
 
+@pytest.mark.parametrize("nb", [64, 65, 1922, 4096, 4097])
+def test_topk_row_lengths(nb):
+    """Rows of up to 4096 blocks keep their keys in registers, in slots of
+    64; longer rows read them from LDS.  Both forms, at the slot boundaries,
+    with ties and NaNs, select exactly what the oracle selects."""
+    rng = np.random.default_rng(nb)
+    S = rng.standard_normal((1, nb, nb)).astype(np.float32)
+    S[0, :, ::7] = np.round(S[0, :, ::7])           # many equal scores
+    S[0, 3, 10:20] = np.nan
+    topk = max(1, nb // 10)
+    say(f"[select] nb={nb} topk={topk}")
+    got = host(L.spark_select(None, None, topk, nb, 1, scores_in=torch.from_numpy(S).to(DEV)))
+    rows = sorted(set(range(min(nb, 24))) | set(range(max(0, nb - 24), nb))
+                  | set(rng.integers(0, nb, 16).tolist()))
+    for A in rows:
+        want = O.select_topk(S[0, A:A + 1].astype(np.float64), topk)[0]
+        assert np.array_equal(got[0, A], want), A
+
+
 @pytest.mark.parametrize("name", ["tiny_f32", "draft_bf16"])
 def test_scores_from_means_match_oracle(name, oracle_runs):
     q, k, v, dt, b, topk, res = oracle_runs(name)
