@@ -17,14 +17,15 @@ namespace spark {
 
 constexpr int MOM_TOK = 128;     // rows staged per LDS round
 
-// Rows per moment partial: enough chunks that both sides of all heads give
-// about 2048 workgroups (the chip holds 256 CUs x several), a multiple of
-// MOM_TOK, at least 256 rows.
+// Rows per moment partial: both sides of all heads give at most 2048
+// workgroups, four full waves of the 512 that the chip holds at once (256
+// CUs x 2; the kernel's registers allow two per CU), so no wave runs a
+// small remainder alone; a multiple of MOM_TOK, at least 256 rows.
 struct MomPlan {
   int nchunk, rpc;
 };
 static MomPlan mom_plan(int H, int N) {
-  const int want = std::max(1, cdiv(2048, 2 * H));
+  const int want = std::max(1, 2048 / (2 * H));
   int rpc = std::max(256, cdiv(N, want));
   rpc = cdiv(rpc, MOM_TOK) * MOM_TOK;
   return {cdiv(N, rpc), rpc};
