@@ -17,16 +17,17 @@ namespace spark {
 
 constexpr int MOM_TOK = 128;     // rows staged per LDS round
 
-// Rows per moment partial: both sides of all heads give at most 2048
-// workgroups, four full waves of the 512 that the chip holds at once (256
-// CUs x 2; the kernel's registers allow two per CU), so no wave runs a
-// small remainder alone; a multiple of MOM_TOK, at least 256 rows.
+// Rows per moment partial: a function of N alone, so a head's moments (and
+// everything computed from them) do not depend on how many heads are
+// processed together.  At most 25 chunks per matrix: the 768p layer's 80
+// matrices give 2000 workgroups, four full waves of the 512 that the chip
+// holds at once (two per CU), so no wave runs a small remainder alone; a
+// multiple of MOM_TOK, at least 256 rows.
 struct MomPlan {
   int nchunk, rpc;
 };
-static MomPlan mom_plan(int H, int N) {
-  const int want = std::max(1, 2048 / (2 * H));
-  int rpc = std::max(256, cdiv(N, want));
+static MomPlan mom_plan(int N) {
+  int rpc = std::max(256, cdiv(N, 25));
   rpc = cdiv(rpc, MOM_TOK) * MOM_TOK;
   return {cdiv(N, rpc), rpc};
 }
@@ -237,7 +238,7 @@ __global__ void moments_reduce(const float* __restrict__ part, const float* __re
 }
 
 size_t moments_ws_bytes(int H, int N, int D) {
-  const int nchunk = mom_plan(H, N).nchunk;
+  const int nchunk = mom_plan(N).nchunk;
   return (size_t)2 * H * nchunk * D * D * 4 + (size_t)2 * H * nchunk * D * 4 + 512;
 }
 
@@ -245,7 +246,7 @@ size_t moments_ws_bytes(int H, int N, int D) {
 // be NULL: then only the query side, M_Q and the anchor).
 int moments_launch(int H, int N, int D, int dtype, const void* q, const void* k, float* MQ,
                    float* MK, float* anchor, int n_anchor, void* ws, hipStream_t st) {
-  const MomPlan mp = mom_plan(H, N);
+  const MomPlan mp = mom_plan(N);
   const int nchunk = mp.nchunk;
   float* part = (float*)ws;
   float* cpart = part + (size_t)2 * H * nchunk * D * D;

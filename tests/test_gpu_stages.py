@@ -180,6 +180,24 @@ def test_topk_ties_nan_and_full_density():
             assert np.array_equal(got[h], want), (h, topk)
 
 
+def test_head_results_do_not_depend_on_the_head_batch():
+    """Every step works per head and every launch plan depends on (N, d,
+    block) only, so a head's layer output is the same whether it is
+    processed alone, with one other head or with three.  N = 70,000: a plan
+    that followed the head count would give 2 and 4 heads different moment
+    chunks, hence different fp32 rounding."""
+    rng = np.random.default_rng(11)
+    H, N, d, b = 4, 70000, 128, 128
+    q, k, v = (dev(rng.standard_normal((H, N, d)), torch.bfloat16) for _ in range(3))
+    topk = L.topk_from_ratio(0.1, L.n_blocks(N, b))
+    say(f"[batch] H={H} N={N} topk={topk}")
+    full = L.spark_layer(q, k, v, b, topk)
+    parts = [L.spark_layer(q[h0:h1].contiguous(), k[h0:h1].contiguous(), v[h0:h1].contiguous(), b, topk)
+             for h0, h1 in ((0, 2), (2, 3), (3, 4))]
+    torch.cuda.synchronize()
+    assert torch.equal(full, torch.cat(parts))
+
+
 @pytest.mark.parametrize("nb", [64, 65, 1922, 4096, 4097])
 def test_topk_row_lengths(nb):
     """Rows of up to 4096 blocks keep their keys in registers, in slots of
