@@ -187,17 +187,17 @@ __global__ __launch_bounds__(SPL_T) void cent_partial(const T* __restrict__ xh,
 // the left's, which is the same sum in exact arithmetic and saves reading the
 // right half's rows; in fp64 the subtraction stays far below fp32 rounding.
 // The left child holds ceil(nb_g / 2) blocks, so whenever the right child
-// still splits (>= 2 blocks) the left has been summed.  CR_T threads: column
-// c = tid % D, block stride G = CR_T / D; each thread keeps 8 partial sums
+// still splits (>= 2 blocks) the left has been summed.  NT threads: column
+// c = tid % D, block stride G = NT / D; each thread keeps 8 partial sums
 // (8 loads in flight), then the G partials are added in a fixed order
-// (deterministic).  The top levels have few groups with thousands of blocks.
-constexpr int CR_T = 1024;
-template <int D>
-__global__ __launch_bounds__(CR_T) void cent_reduce(const float* __restrict__ cpart,
+// (deterministic).  The top levels have few groups with thousands of blocks
+// (NT = 1024); the deep levels many groups of a few dozen (NT = D).
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void cent_reduce(const float* __restrict__ cpart,
                                                     const double* __restrict__ cen_up,
                                                     double* __restrict__ cen, int nb, int level,
                                                     int S) {
-  constexpr int G = CR_T / D;
+  constexpr int G = NT / D;
   __shared__ double s_p[G][D];
   const int par = blockIdx.x, t = blockIdx.y;
   const int lslot = level == 0 ? 0 : 2 * par;   // the root, or the parent's left child
@@ -1017,7 +1017,10 @@ static int split_t(int count, int N, int BK, const void* xhv, int32_t* perm_lo,
       dim3 gc(p.nb, count), gs(S, count), gp(lev == 0 ? 1 : S / 2, count);
       double* cen = cen_ab[lev & 1];             // this level's sums; the parents' in the other
       hipLaunchKernelGGL((cent_partial<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, cpart, N, BK, p.nb, lev);
-      hipLaunchKernelGGL((cent_reduce<D>), gp, dim3(CR_T), 0, st, cpart, cen_ab[(lev + 1) & 1], cen, p.nb, lev, p.S);
+      if ((p.nb >> lev) > 64)
+        hipLaunchKernelGGL((cent_reduce<D, 1024>), gp, dim3(1024), 0, st, cpart, cen_ab[(lev + 1) & 1], cen, p.nb, lev, p.S);
+      else
+        hipLaunchKernelGGL((cent_reduce<D, D>), gp, dim3(D), 0, st, cpart, cen_ab[(lev + 1) & 1], cen, p.nb, lev, p.S);
       hipLaunchKernelGGL((argmin_partial<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, cen, poleA, mpart, N, BK, p.nb, lev, p.S, 0);
       hipLaunchKernelGGL((argmin_reduce<T, D>), gs, dim3(64), 0, st, mpart, xh, poleA, poleB, diff, N, p.nb, lev, p.S, 0);
       hipLaunchKernelGGL((argmin_partial<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, cen, poleA, mpart, N, BK, p.nb, lev, p.S, 1);
