@@ -23,7 +23,9 @@
 //   argmin_partial/argmin_reduce (twice: pole A, pole B; 64-bit (key, id) mins)
 //   score         -> s_i for every position
 //   select_partition (one workgroup per group): exact radix select of the
-//                 c_L-th key, then a stable partition of the ids.
+//                 c_L-th key, then a stable partition of the ids; groups of
+//                 more than 512 blocks get the key from radix_hist /
+//                 radix_pick_groups rounds over many workgroups first.
 // Once every group fits in LDS (<= FIN_MAX tokens) one workgroup per group
 // loads its rows once and finishes all remaining levels in LDS.
 #include "common.hpp"
@@ -460,11 +462,121 @@ __device__ __forceinline__ void radix_pick(const int* s_hist, uint32_t* s_prefix
 // (streamed from global), then stable-partition the ids.  NT threads: 1024
 // for the top levels (a few groups of up to N tokens, where the loads in
 // flight per group decide the speed), SPL_T below.
+// Capacity select of the large groups by many workgroups, four radix rounds
+// of two launches each, synchronised by the launch boundaries alone (no
+// cross-workgroup fences or atomics, which cost an L2 write-back per
+// workgroup on this multi-XCD part).  radix_hist: every workgroup takes
+// RG_SEG positions of its group, counts the keys that match the prefix so
+// far into per-wave LDS histograms and stores its 256 counts in its own
+// slot of hpart.  radix_pick: one workgroup per group adds its segments'
+// counts in segment order and picks the digit exactly as the one-workgroup
+// form does (hpart is indexed by the level's groups, rec by the deepest
+// level's slot count S, as select_partition reads it).  Per (tree, group)
+// the record rec[RG_REC] holds the prefix and
+// the rank still needed; after the last round it holds the c_L-th key and
+// the number of ties that go left, which select_partition takes as given.
+constexpr int RG_REC = 2;
+constexpr int RG_SEG = 8192;
+constexpr int RG_T = 256;
+
+__global__ __launch_bounds__(RG_T) void radix_hist(const float* __restrict__ s, const int* __restrict__ rec,
+                                                  int* __restrict__ hpart, int N, int BK, int nb, int level,
+                                                  int S, int nseg_max, int shift) {
+  __shared__ int s_whist[RG_T / 64][256];
+  const int slot = blockIdx.x / nseg_max, seg = blockIdx.x % nseg_max, t = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  int start, nbg;
+  if (!group_of_slot(slot, level, nb, start, nbg) || nbg < 2) return;
+  const long g0 = (long)start * BK;
+  const int n = (int)(min((long)N, (long)(start + nbg) * BK) - g0);
+  const int i0 = seg * RG_SEG;
+  if (i0 >= n) return;
+  const int i1 = min(n, i0 + RG_SEG);
+  const uint32_t pre = (shift == 24) ? 0u : (uint32_t)rec[((long)t * S + slot) * RG_REC];
+  for (int i = tid; i < (RG_T / 64) * 256; i += RG_T) (&s_whist[0][0])[i] = 0;
+  __syncthreads();
+  const uint32_t hmask = (shift == 24) ? 0u : (0xffffffffu << (shift + 8));
+  const long base = (long)t * N + g0;
+  constexpr int U = 8;
+  for (int j0 = i0; j0 < i1; j0 += U * RG_T) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = j0 + u * RG_T + tid;
+      v[u] = (i < i1) ? s[base + i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = j0 + u * RG_T + tid;
+      const uint32_t k = pref_key_desc(v[u]);
+      if (i < i1 && (k & hmask) == pre) atomicAdd(&s_whist[wave][(k >> shift) & 255], 1);
+    }
+  }
+  __syncthreads();
+  int* hp = hpart + (((long)t * (1 << level) + slot) * nseg_max + seg) * 256;   // this level's groups
+  for (int b = tid; b < 256; b += RG_T) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < RG_T / 64; ++w) c += s_whist[w][b];
+    hp[b] = c;
+  }
+}
+
+__global__ __launch_bounds__(RG_T) void radix_pick_groups(int* __restrict__ rec, const int* __restrict__ hpart,
+                                                         int N, int BK, int nb, int level, int S,
+                                                         int nseg_max, int shift) {
+  __shared__ int s_hist[256];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_need;
+  const int slot = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+  int start, nbg;
+  if (!group_of_slot(slot, level, nb, start, nbg) || nbg < 2) return;
+  const long g0 = (long)start * BK;
+  const int n = (int)(min((long)N, (long)(start + nbg) * BK) - g0);
+  const int nseg = (n + RG_SEG - 1) / RG_SEG;
+  int* r = rec + ((long)t * S + slot) * RG_REC;
+  const int* hp = hpart + ((long)t * (1 << level) + slot) * nseg_max * 256;
+  for (int b = tid; b < 256; b += RG_T) {
+    int c = 0;
+    for (int g = 0; g < nseg; ++g) c += hp[g * 256 + b];
+    s_hist[b] = c;
+  }
+  if (tid == 0) {
+    s_prefix = (shift == 24) ? 0u : (uint32_t)r[0];
+    s_need = (shift == 24) ? ((nbg + 1) >> 1) * BK : r[1];
+  }
+  __syncthreads();
+  if (tid < 64) radix_pick(s_hist, &s_prefix, &s_need, shift);
+  __syncthreads();
+  if (tid == 0) {
+    r[0] = (int)s_prefix;
+    r[1] = s_need;
+  }
+}
+
+// The levels whose groups exceed 512 blocks take the threshold from the
+// many-workgroup rounds (at the 768p layer: the top level 408 -> 280 us;
+// below 512 blocks the extra passes over the scores cost more than the
+// one-workgroup select).
+static bool wide_select(int nb, int lev) { return (nb >> lev) > 512; }
+
+// Largest radix_hist grid (groups x segments) over the levels that use it.
+static long radix_hist_slots(int N, int BK, int nb, int Lf) {
+  long mx = 0;
+  for (int lev = 0; lev < Lf; ++lev) {
+    if (!wide_select(nb, lev)) continue;
+    const long gmax = (nb + (1L << lev) - 1) >> lev;
+    mx = std::max(mx, (1L << lev) * ((gmax * BK + RG_SEG - 1) / RG_SEG));
+  }
+  return mx;
+}
+
 template <int NT>
 __global__ __launch_bounds__(NT) void select_partition(const float* __restrict__ s,
                                                        const int32_t* __restrict__ ids_in,
                                                        int32_t* __restrict__ ids_out, int N,
-                                                       int BK, int nb, int level) {
+                                                       int BK, int nb, int level,
+                                                       const int* __restrict__ given, int S) {
   __shared__ int s_hist[256];
   __shared__ int s_whist[NT / 64][256];  // one histogram per wave (less atomic contention)
   __shared__ int s_tmp[NT / 64];
@@ -484,10 +596,10 @@ __global__ __launch_bounds__(NT) void select_partition(const float* __restrict__
   }
   const int cL = ((nbg + 1) >> 1) * BK;
   if (tid == 0) {
-    s_prefix = 0;
-    s_need = cL;
+    s_prefix = given ? (uint32_t)given[((long)t * S + slot) * RG_REC] : 0u;
+    s_need = given ? given[((long)t * S + slot) * RG_REC + 1] : cL;
   }
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  for (int shift = 24; shift >= 0 && !given; shift -= 8) {
     for (int i = tid; i < (NT / 64) * 256; i += NT) (&s_whist[0][0])[i] = 0;
     __syncthreads();
     const uint32_t pre = s_prefix;
@@ -518,6 +630,7 @@ __global__ __launch_bounds__(NT) void select_partition(const float* __restrict__
     if (tid < 64) radix_pick(s_hist, &s_prefix, &s_need, shift);
     __syncthreads();
   }
+  if (given) __syncthreads();
   const uint32_t thr = s_prefix;
   const int ties_needed = s_need;
   // stable partition in tiles of NT * E positions, E consecutive per thread.
@@ -982,6 +1095,8 @@ size_t split_ws_bytes(int count, int N, int D, int BK, int dtype) {
   b += 2 * up256((size_t)count * p.S * D * 8);      // cen (fp64), one per level parity
   b += up256((size_t)count * p.S * D * 4);          // diff
   b += 2 * up256((size_t)count * p.S * 4);          // poleA, poleB
+  b += up256((size_t)count * p.S * RG_REC * 4);     // capacity-select records
+  b += up256((size_t)count * radix_hist_slots(N, BK, p.nb, p.Lf) * 256 * 4);   // their segment counts
   return b;
 }
 
@@ -1001,7 +1116,9 @@ static int split_t(int count, int N, int BK, const void* xhv, int32_t* perm_lo,
   cen_ab[1] = (double*)w; w += up256((size_t)count * p.S * D * 8);
   float* diff = (float*)w; w += up256((size_t)count * p.S * D * 4);
   int32_t* poleA = (int32_t*)w; w += up256((size_t)count * p.S * 4);
-  int32_t* poleB = (int32_t*)w;
+  int32_t* poleB = (int32_t*)w; w += up256((size_t)count * p.S * 4);
+  int* rec = (int*)w; w += up256((size_t)count * p.S * RG_REC * 4);
+  int* hpart = (int*)w;
   const long total = (long)count * N;
   if (p.nb <= 1) {
     hipLaunchKernelGGL(iota_kernel, dim3((int)std::min<long>((total + 255) / 256, 8192)), dim3(256), 0, st, perm_lo, perm_hi, split_at, N, perm_ld, 0, total);
@@ -1026,11 +1143,26 @@ static int split_t(int count, int N, int BK, const void* xhv, int32_t* perm_lo,
       hipLaunchKernelGGL((argmin_partial<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, cen, poleA, mpart, N, BK, p.nb, lev, p.S, 1);
       hipLaunchKernelGGL((argmin_reduce<T, D>), gs, dim3(64), 0, st, mpart, xh, poleA, poleB, diff, N, p.nb, lev, p.S, 1);
       hipLaunchKernelGGL((score_kernel<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, diff, s, N, BK, p.nb, lev, p.S);
-      // groups of more than 64 blocks: the wide variant
-      if ((p.nb >> lev) > 64)
-        hipLaunchKernelGGL(select_partition<1024>, gs, dim3(1024), 0, st, s, cur, nxt, N, BK, p.nb, lev);
-      else
-        hipLaunchKernelGGL(select_partition<SPL_T>, gs, dim3(SPL_T), 0, st, s, cur, nxt, N, BK, p.nb, lev);
+      // the largest groups: the threshold by many workgroups per group, then
+      // the wide partition; groups of more than 64 blocks: the wide form
+      if (wide_select(p.nb, lev)) {
+        const int gmax = (p.nb + (1 << lev) - 1) >> lev;   // largest group, blocks
+        const int nseg_max = (int)(((long)gmax * BK + RG_SEG - 1) / RG_SEG);
+        for (int shift = 24; shift >= 0; shift -= 8) {
+          hipLaunchKernelGGL(radix_hist, dim3(S * nseg_max, count), dim3(RG_T), 0, st, s, rec, hpart, N, BK,
+                             p.nb, lev, p.S, nseg_max, shift);
+          hipLaunchKernelGGL(radix_pick_groups, gs, dim3(RG_T), 0, st, rec, hpart, N, BK, p.nb, lev, p.S,
+                             nseg_max, shift);
+        }
+        hipLaunchKernelGGL(select_partition<1024>, gs, dim3(1024), 0, st, s, cur, nxt, N, BK, p.nb, lev,
+                           (const int*)rec, p.S);
+      } else if ((p.nb >> lev) > 64) {
+        hipLaunchKernelGGL(select_partition<1024>, gs, dim3(1024), 0, st, s, cur, nxt, N, BK, p.nb, lev,
+                           (const int*)nullptr, p.S);
+      } else {
+        hipLaunchKernelGGL(select_partition<SPL_T>, gs, dim3(SPL_T), 0, st, s, cur, nxt, N, BK, p.nb, lev,
+                           (const int*)nullptr, p.S);
+      }
       int rc = spark_check_launch("split level");
       if (rc) return rc;
       std::swap(cur, nxt);

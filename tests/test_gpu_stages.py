@@ -358,6 +358,9 @@ def test_split_hand_fixtures_exact():
     (torch.bfloat16, 700, 64, 32, 2),
     (torch.float32, 257, 64, 1, 1),          # block 1: N leaves
     (torch.bfloat16, 2051, 128, 5, 2),       # odd N, block 5: group starts not 16-byte aligned
+    (torch.bfloat16, 20000, 128, 128, 2),    # groups of > 64 blocks: the wide one-workgroup select
+    (torch.bfloat16, 70000, 128, 128, 1),    # a group of > 512 blocks: the threshold by several workgroups
+    (torch.float32, 20000, 64, 1, 2),        # six levels of > 512-block groups, 3 to 1 segments each
 ])
 def test_split_bit_exact_on_integer_embeddings(dt, N, d, b, count):
     """Small-integer vectors: every sum and dot is exact in fp32, so the
