@@ -17,6 +17,10 @@
  *    with spark_workspace_bytes().  Pointers must be 16-byte aligned.
  *  - Calls are asynchronous and ordered on `stream` (a hipStream_t; NULL is
  *    the null stream).  The library keeps no state between calls.
+ *  - Results are deterministic: every reduction runs in a fixed order, so
+ *    the same inputs give bit-identical outputs on every call, whatever
+ *    the workspace held before; a head's outputs do not depend on how many
+ *    heads the call holds.
  *  - Return value: SPARK_OK (0) or a negative spark_status.  All argument
  *    checks run before anything is enqueued, so a failed call enqueues
  *    nothing.  A failed launch returns SPARK_E_HIP.  spark_last_error()
