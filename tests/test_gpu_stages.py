@@ -78,6 +78,9 @@ def _case(name):
     if name == "draft_bf16_b32":
         q, k, v = make_workload(WORKLOADS["draft"], heads=[7])
         return q[:, :4000], k[:, :4000], v[:, :4000], torch.bfloat16, 32, 13
+    if name in ("draft_bf16_r20", "draft_bf16_r30"):   # the density sweep's 20% and 30%
+        q, k, v = make_workload(WORKLOADS["draft"], heads=[9 if name.endswith("20") else 10])
+        return q, k, v, torch.bfloat16, 128, O.topk_from_ratio(0.2 if name.endswith("20") else 0.3, 126)
     if name == "draft_bf16_b100":        # generic kernel (block not a multiple of 32)
         q, k, v = make_workload(WORKLOADS["draft"], heads=[8])
         return q[:, :3000], k[:, :3000], v[:, :3000], torch.bfloat16, 100, 4
@@ -85,7 +88,7 @@ def _case(name):
 
 
 CASES = ["tiny_f32", "tiny_f32_ragged", "tiny_f32_tail1", "tiny_bf16_b64", "draft_bf16",
-         "draft_bf16_ragged", "draft_bf16_b32", "draft_bf16_b100"]
+         "draft_bf16_ragged", "draft_bf16_b32", "draft_bf16_b100", "draft_bf16_r20", "draft_bf16_r30"]
 
 
 @pytest.fixture(scope="module")
