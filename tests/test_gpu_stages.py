@@ -183,6 +183,22 @@ def test_topk_ties_nan_and_full_density():
             assert np.array_equal(got[h], want), (h, topk)
 
 
+@pytest.mark.parametrize("name", ["tiny_f32_ragged", "draft_bf16_ragged"])
+def test_reblock_equals_its_stages(name):
+    """spark_reblock equals its public stages composed: spark_moments, the
+    two square roots (queries whitened by M_K^(1/2), keys by M_Q^(1/2)),
+    spark_whiten and spark_split, permutations bit for bit."""
+    q, k, v, dt, b, topk = _case(name)
+    qd, kd, vd = dev(q, dt), dev(k, dt), dev(v, dt)
+    g = L.spark_reblock(qd, kd, vd, b)
+    MQ, MK, _ = L.spark_moments(qd, kd)
+    pq = L.spark_split(L.spark_whiten(qd, L.spark_msqrt(MK)), b)
+    pk = L.spark_split(L.spark_whiten(kd, L.spark_msqrt(MQ)), b)
+    torch.cuda.synchronize()
+    say(f"[stages] {name}: reblock vs composed stages")
+    assert torch.equal(pq, g["perm_q"]) and torch.equal(pk, g["perm_k"])
+
+
 def test_head_results_do_not_depend_on_the_head_batch():
     """Every step works per head and every launch plan depends on (N, d,
     block) only, so a head's layer output is the same whether it is
