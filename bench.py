@@ -87,11 +87,12 @@ def attn_flops(idx, N, b, d, Nv=None):
     return exact, comp
 
 
-def split_rows_read(Nv, b, levels_global):
+def split_rows_read(Nv, b, levels_global, root_fused=False):
     """Rows one side's global split levels read: the centroid, pole-A, pole-B
     and score passes over every group that splits (>= 2 blocks), except that
     below the root the centroid pass skips right children (a right child's
-    sum is its parent's minus its sibling's)."""
+    sum is its parent's minus its sibling's), and with root_fused the root's
+    centroid comes from the whitening pass (no read)."""
     def nrows(start, n):
         return min(Nv, (start + n) * b) - start * b
     groups, rows = [(0, -(-Nv // b), False)], 0
@@ -100,7 +101,7 @@ def split_rows_read(Nv, b, levels_global):
         for start, n, right in groups:
             if n < 2:
                 continue
-            rows += (3 if right else 4) * nrows(start, n)
+            rows += (3 if right or (root_fused and start == 0 and n == -(-Nv // b)) else 4) * nrows(start, n)
             nl = (n + 1) // 2
             nxt += [(start, nl, False), (start + nl, n - nl, True)]
         groups = nxt
@@ -116,7 +117,8 @@ def reblock_bytes(H, N, d, b, es, levels_global, nb, sides=2, Nv=None):
     volv = H * Nv * d * es                    # its video rows
     moments = sides * vol
     whiten = 2 * sides * volv
-    split = sides * (H * split_rows_read(Nv, b, levels_global) * d * es + volv)   # + finisher
+    fused = es == 2 and d == 128 and b == 128   # the whitening pass sums the root's blocks
+    split = sides * (H * split_rows_read(Nv, b, levels_global, fused) * d * es + volv)   # + finisher
     gather = 6 * vol
     summ = 2 * volv
     return moments + whiten + split + gather + summ

@@ -1102,7 +1102,8 @@ size_t split_ws_bytes(int count, int N, int D, int BK, int dtype) {
 
 template <typename T, int D>
 static int split_t(int count, int N, int BK, const void* xhv, int32_t* perm_lo,
-                   int32_t* perm_hi, int split_at, long perm_ld, void* ws, hipStream_t st) {
+                   int32_t* perm_hi, int split_at, long perm_ld, void* ws, hipStream_t st,
+                   bool level0_given) {
   const T* xh = (const T*)xhv;
   const SplitPlan p = split_plan(N, D, BK, sizeof(T));
   char* w = (char*)ws;
@@ -1133,7 +1134,8 @@ static int split_t(int count, int N, int BK, const void* xhv, int32_t* perm_lo,
       const int S = 1 << lev;
       dim3 gc(p.nb, count), gs(S, count), gp(lev == 0 ? 1 : S / 2, count);
       double* cen = cen_ab[lev & 1];             // this level's sums; the parents' in the other
-      hipLaunchKernelGGL((cent_partial<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, cpart, N, BK, p.nb, lev);
+      if (lev > 0 || !level0_given)   // else the whitening pass stored the root's partials
+        hipLaunchKernelGGL((cent_partial<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, cpart, N, BK, p.nb, lev);
       if ((p.nb >> lev) > 64)
         hipLaunchKernelGGL((cent_reduce<D, 1024>), gp, dim3(1024), 0, st, cpart, cen_ab[(lev + 1) & 1], cen, p.nb, lev, p.S);
       else
@@ -1203,13 +1205,26 @@ int iota_launch(int count, int n, long ld, int from, int32_t* lo, int32_t* hi, i
 
 // Trees [0, split_at) write to perm_lo, trees [split_at, count) to perm_hi,
 // N entries per tree at a stride of perm_ld >= N.
+// level0_given: the root's per-block partial centroid sums are already in
+// the workspace (split_level0_partials), stored by the whitening pass.
 int split_launch(int count, int N, int D, int BK, int dtype, const void* xh, int32_t* perm_lo,
-                 int32_t* perm_hi, int split_at, long perm_ld, void* ws, hipStream_t st) {
+                 int32_t* perm_hi, int split_at, long perm_ld, void* ws, hipStream_t st,
+                 bool level0_given) {
   if (dtype == SPARK_BF16)
-    return D == 128 ? split_t<uint16_t, 128>(count, N, BK, xh, perm_lo, perm_hi, split_at, perm_ld, ws, st)
-                    : split_t<uint16_t, 64>(count, N, BK, xh, perm_lo, perm_hi, split_at, perm_ld, ws, st);
-  return D == 128 ? split_t<float, 128>(count, N, BK, xh, perm_lo, perm_hi, split_at, perm_ld, ws, st)
-                  : split_t<float, 64>(count, N, BK, xh, perm_lo, perm_hi, split_at, perm_ld, ws, st);
+    return D == 128 ? split_t<uint16_t, 128>(count, N, BK, xh, perm_lo, perm_hi, split_at, perm_ld, ws, st, level0_given)
+                    : split_t<uint16_t, 64>(count, N, BK, xh, perm_lo, perm_hi, split_at, perm_ld, ws, st, level0_given);
+  return D == 128 ? split_t<float, 128>(count, N, BK, xh, perm_lo, perm_hi, split_at, perm_ld, ws, st, level0_given)
+                  : split_t<float, 64>(count, N, BK, xh, perm_lo, perm_hi, split_at, perm_ld, ws, st, level0_given);
+}
+
+// Where split_launch keeps its per-block partial centroid sums
+// ([count][n_b][D] fp32) inside ws; NULL when the tree has a single block
+// (no global level runs).
+float* split_level0_partials(void* ws, int count, int N, int D, int BK, int dtype) {
+  const int esz = dtype == SPARK_BF16 ? 2 : 4;
+  const SplitPlan p = split_plan(N, D, BK, esz);
+  if (p.nb <= 1 || p.Lf == 0) return nullptr;
+  return (float*)((char*)ws + 3 * up256((size_t)count * N * 4));   // after ids_a, ids_b, s
 }
 
 }  // namespace spark

@@ -428,12 +428,14 @@ constexpr int WH_ROWS = 4096;  // rows per workgroup: 32 rounds of 4 waves x 32 
 template <int D>
 __global__ __launch_bounds__(256, 2) void whiten_mfma(const uint16_t* __restrict__ x,
                                                    const float* __restrict__ W,
-                                                   uint16_t* __restrict__ xh, int N, int xrows) {
+                                                   uint16_t* __restrict__ xh, int N, int xrows,
+                                                   float* __restrict__ cpart, int tree_off, int nb) {
   constexpr int RS = D + 8;            // LDS row stride (bf16), 16-byte pad
   constexpr int CPR = D / 8;           // 16-byte chunks per row
   constexpr int CPL = 32 * CPR / 64;   // chunks per lane per round (d = 128: 8)
   __shared__ __attribute__((aligned(16))) uint16_t sW[D * RS];
   __shared__ __attribute__((aligned(16))) uint16_t sX[4][32 * RS];
+  __shared__ float s_cp[4][D];
   const int t = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
@@ -457,7 +459,10 @@ __global__ __launch_bounds__(256, 2) void whiten_mfma(const uint16_t* __restrict
   if (wbase < N) load(wbase);
   for (int r0 = 0; r0 < WH_ROWS; r0 += 128) {
     const long base = wbase + r0;
-    if (base >= N) break;   // uniform across the wave
+    // uniform across the workgroup (the partial sums below take barriers): a
+    // wave whose rows all lie past N runs the round on ignored data, with
+    // every load, store and sum guarded by row < N
+    if ((long)blockIdx.x * WH_ROWS + r0 >= N) break;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       const int c = i * 64 + lane, rr = c / CPR, cc = c % CPR;
@@ -504,6 +509,43 @@ __global__ __launch_bounds__(256, 2) void whiten_mfma(const uint16_t* __restrict
       if (base + rr < N)
         *reinterpret_cast<uint4*>(ht + (base + rr) * D + cc * 8) = *reinterpret_cast<const uint4*>(sx + rr * RS + cc * 8);
     }
+    if (cpart) {
+      // The round's 128 rows are one block of the split's first level (block
+      // 128, identity order): its partial centroid sum, computed as the
+      // split's own centroid pass does (lane (rg, chunk c) adds rows
+      // it * 16 + rg, absent rows as +0; then the lanes of a chunk; then the
+      // waves in order), so the sums are bit-identical to that pass's.
+      __syncthreads();   // the four slices hold the round's rows
+      const long row0 = (long)blockIdx.x * WH_ROWS + r0;
+      const int rg = tid / CPR, c = (tid % CPR) * 8;
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int j = it * 16 + rg;
+        uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+        if (row0 + j < N) raw = *reinterpret_cast<const uint4*>(&sX[j >> 5][(j & 31) * RS + c]);
+        const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+          acc[2 * q2] += __uint_as_float(wv[q2] << 16);
+          acc[2 * q2 + 1] += __uint_as_float(wv[q2] & 0xffff0000u);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = group_sum<64, CPR>(acc[e]);
+      if (lane < CPR)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_cp[wave][c + e] = acc[e];
+      __syncthreads();   // also: every slice read is done before the next round
+      for (int cc2 = tid; cc2 < D; cc2 += 256) {
+        float sum = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) sum += s_cp[w2][cc2];
+        cpart[((long)(tree_off + t) * nb + row0 / 128) * D + cc2] = sum;
+      }
+    }
     wave_lds_sync();   // the slice is free for the next round
   }
 }
@@ -540,14 +582,20 @@ __global__ __launch_bounds__(256) void whiten_f32(const float* __restrict__ x,
 // Rows [0, N) of each of the `count` input matrices, whose head stride is
 // xrows >= N rows (xrows > N: the rows past N are context tokens, not
 // whitened); xh is [count, N, D].
+// cpart (bf16, d = 128 only; else NULL): also store the split's first-level
+// partial centroid sums of 128-row blocks, for trees tree_off .. tree_off +
+// count - 1 of a [trees][ceil(N / 128)][D] array.
 int whiten_launch(int count, int N, int xrows, int D, int dtype, const void* x, const float* W,
-                  void* xh, hipStream_t st) {
+                  void* xh, hipStream_t st, float* cpart, int tree_off) {
   if (dtype == SPARK_BF16) {
     dim3 grid(cdiv(N, WH_ROWS), count);
+    const int nb = cdiv(N, 128);
     if (D == 128)
-      hipLaunchKernelGGL(whiten_mfma<128>, grid, dim3(256), 0, st, (const uint16_t*)x, W, (uint16_t*)xh, N, xrows);
+      hipLaunchKernelGGL(whiten_mfma<128>, grid, dim3(256), 0, st, (const uint16_t*)x, W, (uint16_t*)xh, N, xrows,
+                         cpart, tree_off, nb);
     else
-      hipLaunchKernelGGL(whiten_mfma<64>, grid, dim3(256), 0, st, (const uint16_t*)x, W, (uint16_t*)xh, N, xrows);
+      hipLaunchKernelGGL(whiten_mfma<64>, grid, dim3(256), 0, st, (const uint16_t*)x, W, (uint16_t*)xh, N, xrows,
+                         (float*)nullptr, 0, nb);
   } else {
     dim3 grid(cdiv(N, 256), count);
     if (D == 128)

@@ -38,10 +38,12 @@ int copy_perm_launch(long count, const int32_t* src, int32_t* dst, hipStream_t s
 size_t msqrt_ws_bytes(int count, int D);
 int msqrt_launch(int count, int D, const float* M, float* W, float* Tscr, hipStream_t st);
 int whiten_launch(int count, int N, int xrows, int D, int dtype, const void* x, const float* W,
-                  void* xh, hipStream_t st);
+                  void* xh, hipStream_t st, float* cpart, int tree_off);
 size_t split_ws_bytes(int count, int N, int D, int BK, int dtype);
 int split_launch(int count, int N, int D, int BK, int dtype, const void* xh, int32_t* perm_lo,
-                 int32_t* perm_hi, int split_at, long perm_ld, void* ws, hipStream_t st);
+                 int32_t* perm_hi, int split_at, long perm_ld, void* ws, hipStream_t st,
+                 bool level0_given);
+float* split_level0_partials(void* ws, int count, int N, int D, int BK, int dtype);
 int iota_launch(int count, int n, long ld, int from, int32_t* lo, int32_t* hi, int split_at,
                 hipStream_t st);
 int diag_launch(int H, int N, int D, int BK, int dtype, const void* qp, const void* kp,
@@ -148,6 +150,12 @@ int reject_context(const spark_args* a, const char* fn) {
   if (a->flags & SPARK_CONTEXT_EXACT)
     return spark_set_error(SPARK_E_UNSUPPORTED, "%s: SPARK_CONTEXT_EXACT is not supported here", fn);
   return SPARK_OK;
+}
+
+// The whitening pass can hand the split its root partial centroid sums when
+// a 128-row whitening round is exactly one block (bf16, d = 128, block 128).
+static bool level0_fusable(const spark_args* a) {
+  return a->dtype == SPARK_BF16 && a->d == 128 && a->block == 128;
 }
 
 size_t reblock_ws(const spark_args* a) {
@@ -295,7 +303,7 @@ int spark_whiten(const spark_args* a, int32_t count, const void* x, const float*
   CHECK(check_ptr(x, fn, "x"));
   CHECK(check_ptr(W, fn, "W"));
   CHECK(check_ptr(xhat, fn, "xhat"));
-  return whiten_launch(count, a->N, a->N, a->d, a->dtype, x, W, xhat, (hipStream_t)stream);
+  return whiten_launch(count, a->N, a->N, a->d, a->dtype, x, W, xhat, (hipStream_t)stream, nullptr, 0);
 }
 
 int spark_split(const spark_args* a, int32_t count, const void* xhat, int32_t* perm, void* ws,
@@ -310,7 +318,7 @@ int spark_split(const spark_args* a, int32_t count, const void* xhat, int32_t* p
   CHECK(check_ptr(ws, fn, "ws"));
   if (ws_bytes < need) return spark_set_error(SPARK_E_WORKSPACE, "%s: ws_bytes %zu < %zu", fn, ws_bytes, need);
   return split_launch(count, a->N, a->d, a->block, a->dtype, xhat, perm, perm, count, a->N, ws,
-                      (hipStream_t)stream);
+                      (hipStream_t)stream, false);
 }
 
 int spark_gather(const spark_args* a, const void* x, const int32_t* perm, void* x_p, void* x_pt,
@@ -370,10 +378,13 @@ int spark_reblock(const spark_args* a, const void* q, const void* k, const void*
     // roots), keys by M_Q^{1/2}; only the Nv video rows are whitened and split
     CHECK(moments_launch(H, N, D, a->dtype, q, k, MQ, MK, anchor, a->n_anchor, scr, st));
     CHECK(msqrt_launch(2 * H, D, Ms, Ws, (float*)scr, st));
-    CHECK(whiten_launch(H, Nv, N, D, a->dtype, q, Ws, xh, st));
+    // bf16, d = 128, block 128: the whitening pass also stores the split's
+    // root partial centroid sums (the split then skips that pass)
+    float* cp0 = level0_fusable(a) ? split_level0_partials(sws, 2 * H, Nv, D, BK, a->dtype) : nullptr;
+    CHECK(whiten_launch(H, Nv, N, D, a->dtype, q, Ws, xh, st, cp0, 0));
     CHECK(whiten_launch(H, Nv, N, D, a->dtype, k, Ws + (size_t)H * D * D,
-                        (char*)xh + (size_t)H * Nv * D * esize(a->dtype), st));
-    CHECK(split_launch(2 * H, Nv, D, BK, a->dtype, xh, perm_q, perm_k, H, N, sws, st));
+                        (char*)xh + (size_t)H * Nv * D * esize(a->dtype), st, cp0, H));
+    CHECK(split_launch(2 * H, Nv, D, BK, a->dtype, xh, perm_q, perm_k, H, N, sws, st, cp0 != nullptr));
     CHECK(iota_launch(2 * H, N - Nv, N, Nv, perm_q, perm_k, H, st));   // context stays in place
   } else if (layout == SPARK_LAYOUT_Q_REUSE_K) {
     // the same key side as REBLOCK (keys whitened by M_Q^{1/2}); the query
@@ -387,8 +398,9 @@ int spark_reblock(const spark_args* a, const void* q, const void* k, const void*
     float* MQ = Ms;
     CHECK(moments_launch(H, N, D, a->dtype, q, nullptr, MQ, nullptr, anchor, a->n_anchor, scr, st));
     CHECK(msqrt_launch(H, D, MQ, Ws, (float*)scr, st));
-    CHECK(whiten_launch(H, Nv, N, D, a->dtype, k, Ws, xh, st));
-    CHECK(split_launch(H, Nv, D, BK, a->dtype, xh, perm_k, perm_k, H, N, sws, st));
+    float* cp0 = level0_fusable(a) ? split_level0_partials(sws, H, Nv, D, BK, a->dtype) : nullptr;
+    CHECK(whiten_launch(H, Nv, N, D, a->dtype, k, Ws, xh, st, cp0, 0));
+    CHECK(split_launch(H, Nv, D, BK, a->dtype, xh, perm_k, perm_k, H, N, sws, st, cp0 != nullptr));
     CHECK(iota_launch(H, N - Nv, N, Nv, perm_k, perm_k, H, st));
     CHECK(copy_perm_launch((long)H * N, perm_k, perm_q, st));
     pq = perm_k;
