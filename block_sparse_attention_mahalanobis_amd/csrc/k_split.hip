@@ -110,9 +110,14 @@ struct ChunkRows {
   uint4 raw[NIT];
   __device__ __forceinline__ void load(const T* __restrict__ xt, const int32_t* s_ids, int n_real,
                                        int rg, int c) {
+    load_rows(xt, s_ids, n_real, rg, RPP, c);
+  }
+  // chunk `it` holds row j0 + it * step
+  __device__ __forceinline__ void load_rows(const T* __restrict__ xt, const int32_t* s_ids, int n_real,
+                                            int j0, int step, int c) {
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      const int j = it * RPP + rg;
+      const int j = j0 + it * step;
       raw[it] = (j < n_real) ? *reinterpret_cast<const uint4*>(xt + (long)s_ids[j] * D + c)
                              : uint4{0u, 0u, 0u, 0u};
     }
@@ -154,10 +159,14 @@ __global__ __launch_bounds__(SPL_T) void cent_partial(const T* __restrict__ xh,
   if (!group_of_block(cb, level, nb, start, nbg, slot)) return;
   if (level > 0 && (slot & 1)) return;   // a right child: parent - left (cent_reduce)
   const int n_real = min(BK, N - cb * BK);
-  const int rg = tid / CPR, c = (tid % CPR) * VE;
+  // wave w sums rows [32 w, 32 w + 32) of the 128-row block: lane (rl, chunk
+  // c) rows 32 w + RGW it + rl (the whitening pass, which holds each wave's
+  // 32 rows, reproduces this order for the root)
+  constexpr int RGW = 64 / CPR;   // row groups per wave
+  const int lane = tid & 63, rl = lane / CPR, c = (tid % CPR) * VE;
   stage_ids(s_ids, ids + (long)t * N + (long)cb * BK, n_real);
   CR rows;
-  rows.load(xh + (long)t * N * D, s_ids, n_real, rg, c);
+  rows.load_rows(xh + (long)t * N * D, s_ids, n_real, 32 * (tid >> 6) + rl, RGW, c);
   float acc[VE];
 #pragma unroll
   for (int e = 0; e < VE; ++e) acc[e] = 0.f;

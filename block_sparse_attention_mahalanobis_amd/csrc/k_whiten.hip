@@ -435,7 +435,7 @@ __global__ __launch_bounds__(256, 2) void whiten_mfma(const uint16_t* __restrict
   constexpr int CPL = 32 * CPR / 64;   // chunks per lane per round (d = 128: 8)
   __shared__ __attribute__((aligned(16))) uint16_t sW[D * RS];
   __shared__ __attribute__((aligned(16))) uint16_t sX[4][32 * RS];
-  __shared__ float s_cp[4][D];
+  __shared__ float s_cp[2][4][D];   // by round parity
   const int t = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
@@ -511,21 +511,20 @@ __global__ __launch_bounds__(256, 2) void whiten_mfma(const uint16_t* __restrict
     }
     if (cpart) {
       // The round's 128 rows are one block of the split's first level (block
-      // 128, identity order): its partial centroid sum, computed as the
-      // split's own centroid pass does (lane (rg, chunk c) adds rows
-      // it * 16 + rg, absent rows as +0; then the lanes of a chunk; then the
+      // 128, identity order): its partial centroid sum in the split's own
+      // centroid-pass order (wave w: lane (rl, chunk c) adds its slice rows
+      // 4 it + rl, absent rows as +0; then the lanes of a chunk; then the
       // waves in order), so the sums are bit-identical to that pass's.
-      __syncthreads();   // the four slices hold the round's rows
       const long row0 = (long)blockIdx.x * WH_ROWS + r0;
-      const int rg = tid / CPR, c = (tid % CPR) * 8;
+      const int rl = lane / CPR, c = (lane % CPR) * 8, par = (r0 >> 7) & 1;
       float acc[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
-        const int j = it * 16 + rg;
+        const int j = 4 * it + rl;   // this wave's slice row
         uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-        if (row0 + j < N) raw = *reinterpret_cast<const uint4*>(&sX[j >> 5][(j & 31) * RS + c]);
+        if (base + j < N) raw = *reinterpret_cast<const uint4*>(sx + j * RS + c);
         const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
         for (int q2 = 0; q2 < 4; ++q2) {
@@ -537,12 +536,12 @@ __global__ __launch_bounds__(256, 2) void whiten_mfma(const uint16_t* __restrict
       for (int e = 0; e < 8; ++e) acc[e] = group_sum<64, CPR>(acc[e]);
       if (lane < CPR)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s_cp[wave][c + e] = acc[e];
-      __syncthreads();   // also: every slice read is done before the next round
+        for (int e = 0; e < 8; ++e) s_cp[par][wave][c + e] = acc[e];
+      __syncthreads();   // the four waves' sums (the other parity is free again)
       for (int cc2 = tid; cc2 < D; cc2 += 256) {
         float sum = 0.f;
 #pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) sum += s_cp[w2][cc2];
+        for (int w2 = 0; w2 < 4; ++w2) sum += s_cp[par][w2][cc2];
         cpart[((long)(tree_off + t) * nb + row0 / 128) * D + cc2] = sum;
       }
     }
