@@ -8,7 +8,8 @@ H=40, d=128, block 128, density 0.1 (top 193 of 1922 key blocks), bf16,
 seeded synthetic clustered q/k (see block_sparse_attention_mahalanobis_amd/
 workload.py).  Inputs are resident in HBM before timing starts.
 
-Prints ONE JSON line.  `value` is the layer latency in ms (lower is better);
+Prints ONE JSON line.  `value` is the median layer latency in ms over the
+timed steps (HIP events; lower is better);
 the exact-branch MFMA fraction of the bf16 dense peak, per-stage times, the
 attention kernel's roofline and the fp64 CPU oracle baseline ride along.
 """
@@ -342,10 +343,16 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     stages = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs])  # ms
-    layer_ms = wall * 1e3 / args.steps
-    st_mean = stages.mean(axis=0)
-    log(f"layer {layer_ms:.2f} ms; reblock {st_mean[0]:.2f} select {st_mean[1]:.2f} "
-        f"summarize {st_mean[2]:.2f} attn {st_mean[3]:.2f} ms")
+    per_step = np.array([e[0].elapsed_time(e[4]) for e in evs])                        # ms
+    # the median over the timed steps (HIP events on the launch stream); the
+    # wall-clock mean over the same steps rides along
+    layer_ms = float(np.median(per_step))
+    wall_ms = wall * 1e3 / args.steps
+    st_mean = np.median(stages, axis=0)
+    log(f"layer {layer_ms:.2f} ms (median of {args.steps}; wall mean {wall_ms:.2f}); reblock {st_mean[0]:.2f} "
+        f"select {st_mean[1]:.2f} summarize {st_mean[2]:.2f} attn {st_mean[3]:.2f} ms")
+    peak_meas = L.mfma_peak_tflops()
+    log(f"measured bf16 MFMA rate (register-only loop): {peak_meas:.0f} TFLOP/s")
 
     exact, comp = attn_flops(idx.cpu().numpy(), N, b, d, Nv)
     attn_s = st_mean[3] * 1e-3
@@ -389,6 +396,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(layer_ms, 3),
+        "wall_ms_per_step": round(wall_ms, 3),
+        "step_ms_min_max": [round(float(per_step.min()), 3), round(float(per_step.max()), 3)],
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -399,6 +408,7 @@ def main():
                    **({"context_tokens": N - Nv, "context_blocks": nbt - nb} if ctx else {}),
                    **({"logits": "fp8 e4m3 (QK^T on fp8 MFMA, P V bf16)"} if args.fp8 else {})},
         "exact_mfma_pct_peak": round(100.0 * exact_tf / PEAK_BF16_TFLOPS, 2),
+        "exact_mfma_pct_measured_peak": round(100.0 * exact_tf / peak_meas, 2),
         "stages_ms": {"reblock": round(st_mean[0], 3), "select": round(st_mean[1], 3),
                       "summarize": round(st_mean[2], 3), "attn": round(st_mean[3], 3)},
         "attn_tflops": {"exact": round(exact_tf, 1), "exact_plus_compressed": round(alg_tf, 1),
@@ -409,7 +419,10 @@ def main():
                                   "traffic_gb": None if rb_traffic is None else round(rb_traffic / 1e9, 1)},
         "roofline": {"kernel": "attn_mfma_d128 (spark_attn)", "bound": "mfma",
                      "achieved": round(alg_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(alg_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+                     "frac": round(alg_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "measured_peak": round(peak_meas, 1),
+                     "measured_peak_note": "register-only v_mfma_f32_32x32x16_bf16 loop on this GPU "
+                                           "(spark_mfma_peak_probe), best of 5 launches"},
         "cpu_baseline": base,
     }
     print(json.dumps(rec), flush=True)

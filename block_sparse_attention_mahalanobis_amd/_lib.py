@@ -32,6 +32,8 @@ EXPORTED = [
     "spark_topk_from_ratio", "spark_workspace_bytes", "spark_reblock", "spark_select",
     "spark_summarize", "spark_attn", "spark_layer", "spark_moments", "spark_msqrt",
     "spark_whiten", "spark_split", "spark_gather", "spark_diagnostics", "spark_quant_e4m3",
+    "spark_debug_partition_ws_bytes", "spark_debug_partition_level", "spark_debug_argmin",
+    "spark_mfma_peak_probe",
 ]
 
 
@@ -81,6 +83,10 @@ def lib() -> ctypes.CDLL:
         "spark_gather": ([_A, _P, _P, _P, _P, _P, _P], ctypes.c_int),
         "spark_diagnostics": ([_A, _P, _P, _P, _I, _P, _P, _P, _P, _P], ctypes.c_int),
         "spark_quant_e4m3": ([_I, _I, _I, _I, _P, _P, _P, _P], ctypes.c_int),
+        "spark_debug_partition_ws_bytes": ([_I, _I, _I], _Z),
+        "spark_debug_partition_level": ([_I, _I, _I, _P, _P, _P, _P, _Z, _P], ctypes.c_int),
+        "spark_debug_argmin": ([_I, _I, _P, _P, _P, _P], ctypes.c_int),
+        "spark_mfma_peak_probe": ([_I, _I, _P, _P], ctypes.c_double),
     }
     for name, (argt, rest) in sig.items():
         f = getattr(L, name)
@@ -347,3 +353,44 @@ def spark_quant_e4m3(x, group: int):
     _check(lib().spark_quant_e4m3(rows, d, group, _dtype_code(x.dtype), _ptr(x), _ptr(x8), _ptr(scales),
                                   _stream()), "spark_quant_e4m3")
     return x8, scales
+
+
+def spark_debug_partition_level(s, ids, block: int):
+    """One capacity partition per row of s [count, n] fp32 with ids [count, n]
+    int32 (ascending per row): left child's ids then the right child's."""
+    count, n = s.shape
+    nws = lib().spark_debug_partition_ws_bytes(count, n, block)
+    if nws == ctypes.c_size_t(-1).value:
+        raise SparkError(f"spark_debug_partition_ws_bytes: {last_error()}")
+    ws = _ws(nws, s.device)
+    out = torch.empty((count, n), dtype=torch.int32, device=s.device)
+    _check(lib().spark_debug_partition_level(count, n, block, _ptr(s), _ptr(ids), _ptr(out), _ptr(ws), nws,
+                                             _stream()), "spark_debug_partition_level")
+    return out
+
+
+def spark_debug_argmin(vals, ids):
+    """Per row of vals [count, n] fp32 / ids [count, n] int32: the id of the
+    minimum (-0 = +0, NaN last, ties to the lower id)."""
+    count, n = vals.shape
+    out = torch.empty((count,), dtype=torch.int32, device=vals.device)
+    _check(lib().spark_debug_argmin(count, n, _ptr(vals), _ptr(ids), _ptr(out), _stream()), "spark_debug_argmin")
+    return out
+
+
+def mfma_peak_tflops(workgroups: int = 512, iters: int = 16384, repeats: int = 5) -> float:
+    """Sustained bf16 MFMA rate of this GPU (TFLOP/s): the best of `repeats`
+    event-timed launches of the library's register-only MFMA loop."""
+    sink = torch.empty(workgroups * 256, dtype=torch.float32, device="cuda:0")
+    best = 0.0
+    for _ in range(repeats + 1):                      # the first launch warms up
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        flops = lib().spark_mfma_peak_probe(workgroups, iters, _ptr(sink), _stream())
+        e1.record()
+        if flops < 0:
+            raise SparkError(f"spark_mfma_peak_probe: {last_error()}")
+        torch.cuda.synchronize()
+        best = max(best, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return best

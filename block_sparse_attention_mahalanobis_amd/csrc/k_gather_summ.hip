@@ -133,6 +133,18 @@ template <typename T> struct Raw8;
 template <> struct Raw8<uint16_t> {
   uint4 q;
   __device__ __forceinline__ void load(const uint16_t* p) { q = *reinterpret_cast<const uint4*>(p); }
+  // the first cnt (1..8) elements one by one, the rest zero: for rows whose
+  // length is not a multiple of 8 (no read past the row, no 16-byte alignment)
+  __device__ __forceinline__ void load_n(const uint16_t* p, int cnt) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = (2 * i < cnt) ? p[2 * i] : 0u;
+      const uint32_t hi = (2 * i + 1 < cnt) ? p[2 * i + 1] : 0u;
+      w[i] = lo | (hi << 16);
+    }
+    q = make_uint4(w[0], w[1], w[2], w[3]);
+  }
   __device__ __forceinline__ void zero() { q = make_uint4(0u, 0u, 0u, 0u); }
   __device__ __forceinline__ void widen(float (&v)[8]) const {
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
@@ -148,6 +160,13 @@ template <> struct Raw8<float> {
   __device__ __forceinline__ void load(const float* p) {
     a = *reinterpret_cast<const float4*>(p);
     b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void load_n(const float* p, int cnt) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (i < cnt) ? p[i] : 0.f;
+    a = make_float4(v[0], v[1], v[2], v[3]);
+    b = make_float4(v[4], v[5], v[6], v[7]);
   }
   __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
   __device__ __forceinline__ void widen(float (&v)[8]) const {
@@ -196,10 +215,16 @@ __global__ __launch_bounds__(256) void summarize_kernel(const T* __restrict__ kp
     if (j < n_real) kraw[i].load(kblk + (long)j * D + ck);
     else kraw[i].zero();
   }
+  // a transposed row holds BK tokens: with BK % 8 == 0 every 8-token chunk
+  // is 16-byte aligned and inside the row; otherwise the chunk is read
+  // element by element up to the block's last real token
+  const bool vec_rows = (BK & 7) == 0;
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) {
-    if (jc < n_real) vraw[i].load(vblk + (long)(rv + 16 * i) * BK + jc);
-    else vraw[i].zero();
+    const T* src = vblk + (long)(rv + 16 * i) * BK + jc;
+    if (jc >= n_real) vraw[i].zero();
+    else if (vec_rows) vraw[i].load(src);
+    else vraw[i].load_n(src, min(8, n_real - jc));
   }
   auto widen8 = [](const Raw8<T>& q, float (&v)[8]) { q.widen(v); };
 

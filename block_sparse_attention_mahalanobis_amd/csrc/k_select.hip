@@ -77,6 +77,13 @@ __device__ __forceinline__ void row_topk(const uint32_t* s_key, int nb, int topk
 }
 
 constexpr int SEL_QB = 8;   // query blocks per workgroup (they share each k_bar read)
+constexpr size_t SEL_LDS = 128 * 1024;   // dynamic LDS of a select workgroup
+
+// Byte offset of the query means after the qb rows of nb keys, rounded up to
+// 16 bytes.
+__host__ __device__ __forceinline__ size_t sel_qoff(int qb, int nb) {
+  return ((size_t)qb * nb * 4 + 15) & ~(size_t)15;
+}
 constexpr int SEL_KB = 4;   // key blocks per lane (they share each query-mean read)
 
 template <int D>
@@ -112,7 +119,9 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(const float* __restrict__
     // loads, 64 rows apart across the wave: the four loads that cover 64
     // bytes of a row are issued together, so they share the cache lines
     // they fetch instead of fetching them again on later steps.
-    float* s_q = reinterpret_cast<float*>(smem + (size_t)qb * nb * 4);   // [qb][D]
+    // [qb][D], 16-byte aligned for the float4 reads (qb * nb need not be a
+    // multiple of 4)
+    float* s_q = reinterpret_cast<float*>(smem + sel_qoff(qb, nb));
     for (int e = tid; e < nq * D; e += SEL_T) s_q[e] = qbar[((long)h * nb + A0) * D + e];
     __syncthreads();
     for (int B0 = 0; B0 < nb; B0 += SEL_T * SEL_KB) {
@@ -190,16 +199,17 @@ int select_launch(int H, int N, int D, int BK, const float* qbar, const float* k
                   const float* scores_in, int topk, int32_t* idx, float* scores_out,
                   hipStream_t st) {
   const int nb = cdiv(N, BK);
-  if ((size_t)nb * 4 + 128 * 4 > 128 * 1024)
+  // the 16 bytes cover the alignment padding of the query means
+  if ((size_t)nb * 4 + 128 * 4 + 16 > SEL_LDS)
     return spark_set_error(SPARK_E_SHAPE, "spark_select: %d blocks exceed the LDS row buffer", nb);
-  int qb = (int)std::min<size_t>(SEL_QB, (size_t)(128 * 1024) / ((size_t)nb * 4 + (size_t)D * 4));
+  int qb = (int)std::min<size_t>(SEL_QB, (SEL_LDS - 16) / ((size_t)nb * 4 + (size_t)D * 4));
   qb = std::max(qb, 1);
-  const size_t lds = (size_t)qb * nb * 4 + (size_t)qb * D * 4;
+  const size_t lds = sel_qoff(qb, nb) + (size_t)qb * D * 4;
   const float rsd = 1.f / sqrtf((float)D);
   static bool attr = false;
   if (!attr) {
-    hipFuncSetAttribute((const void*)select_kernel<128>, hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
-    hipFuncSetAttribute((const void*)select_kernel<64>, hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+    hipFuncSetAttribute((const void*)select_kernel<128>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)SEL_LDS);
+    hipFuncSetAttribute((const void*)select_kernel<64>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)SEL_LDS);
     attr = true;
   }
   const int grid = H * ((nb + qb - 1) / qb);

@@ -1226,6 +1226,71 @@ int split_launch(int count, int N, int D, int BK, int dtype, const void* xh, int
                   : split_t<float, 64>(count, N, BK, xh, perm_lo, perm_hi, split_at, perm_ld, ws, st, level0_given);
 }
 
+// ---- test hooks: the split's argmin and capacity partition on caller values ----
+// Argmin of caller values per row with the splitter's 64-bit (key, id)
+// ordering and wave reduction: -0 equals +0, NaN ranks last, ties to the
+// lower id.  One workgroup per row.
+__global__ __launch_bounds__(SPL_T) void debug_argmin_kernel(const float* __restrict__ vals,
+                                                             const int32_t* __restrict__ ids, int n,
+                                                             int32_t* __restrict__ out) {
+  __shared__ uint64_t s_min[SPL_T / 64];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  uint64_t best = ~0ull;
+  for (int i = tid; i < n; i += SPL_T) {
+    const uint64_t k = argmin_key(vals[(long)t * n + i], ids[(long)t * n + i]);
+    best = k < best ? k : best;
+  }
+  best = group_min_u64<64>(best);
+  if ((tid & 63) == 0) s_min[tid >> 6] = best;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t b = s_min[0];
+    for (int w = 1; w < SPL_T / 64; ++w) b = s_min[w] < b ? s_min[w] : b;
+    out[t] = (int32_t)(uint32_t)(b & 0xffffffffu);
+  }
+}
+
+int debug_argmin_launch(int count, int n, const float* vals, const int32_t* ids, int32_t* out,
+                        hipStream_t st) {
+  hipLaunchKernelGGL(debug_argmin_kernel, dim3(count), dim3(SPL_T), 0, st, vals, ids, n, out);
+  return spark_check_launch("debug argmin");
+}
+
+// One capacity partition per row of n scores: the split's level-0 kernels
+// (the many-workgroup threshold above 512 blocks, the 1024-thread select
+// above 64 blocks, the 256-thread one below), with the capacity of a group of
+// ceil(n / BK) blocks.
+size_t debug_partition_ws_bytes(int count, int n, int BK) {
+  const int nb = cdiv(n, BK);
+  const long nseg = wide_select(nb, 0) ? ((long)nb * BK + RG_SEG - 1) / RG_SEG : 0;
+  return up256((size_t)count * RG_REC * 4) + up256((size_t)count * nseg * 256 * 4);
+}
+
+int debug_partition_launch(int count, int n, int BK, const float* s, const int32_t* ids_in,
+                           int32_t* ids_out, void* ws, hipStream_t st) {
+  const int nb = cdiv(n, BK);
+  int* rec = (int*)ws;
+  int* hpart = (int*)((char*)ws + up256((size_t)count * RG_REC * 4));
+  const dim3 gs(1, count);
+  if (wide_select(nb, 0)) {
+    const int nseg_max = (int)(((long)nb * BK + RG_SEG - 1) / RG_SEG);
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      hipLaunchKernelGGL(radix_hist, dim3(nseg_max, count), dim3(RG_T), 0, st, s, rec, hpart, n, BK, nb, 0, 1,
+                         nseg_max, shift);
+      hipLaunchKernelGGL(radix_pick_groups, gs, dim3(RG_T), 0, st, rec, hpart, n, BK, nb, 0, 1, nseg_max, shift);
+    }
+    hipLaunchKernelGGL(select_partition<1024>, gs, dim3(1024), 0, st, s, ids_in, ids_out, n, BK, nb, 0,
+                       (const int*)rec, 1);
+  } else if (nb > 64) {
+    hipLaunchKernelGGL(select_partition<1024>, gs, dim3(1024), 0, st, s, ids_in, ids_out, n, BK, nb, 0,
+                       (const int*)nullptr, 1);
+  } else {
+    hipLaunchKernelGGL(select_partition<SPL_T>, gs, dim3(SPL_T), 0, st, s, ids_in, ids_out, n, BK, nb, 0,
+                       (const int*)nullptr, 1);
+  }
+  return spark_check_launch("debug partition");
+}
+
 // Where split_launch keeps its per-block partial centroid sums
 // ([count][n_b][D] fp32) inside ws; NULL when the tree has a single block
 // (no global level runs).

@@ -46,6 +46,12 @@ int split_launch(int count, int N, int D, int BK, int dtype, const void* xh, int
 float* split_level0_partials(void* ws, int count, int N, int D, int BK, int dtype);
 int iota_launch(int count, int n, long ld, int from, int32_t* lo, int32_t* hi, int split_at,
                 hipStream_t st);
+int debug_argmin_launch(int count, int n, const float* vals, const int32_t* ids, int32_t* out,
+                        hipStream_t st);
+size_t debug_partition_ws_bytes(int count, int n, int BK);
+int debug_partition_launch(int count, int n, int BK, const float* s, const int32_t* ids_in,
+                           int32_t* ids_out, void* ws, hipStream_t st);
+int mfma_peak_launch(int workgroups, int iters, float* sink, hipStream_t st);
 int diag_launch(int H, int N, int D, int BK, int dtype, const void* qp, const void* kp,
                 const int32_t* idx, int topk, const float* ksum, const float* bias, float* recall,
                 float* logmass, hipStream_t st);
@@ -542,4 +548,50 @@ int spark_quant_e4m3(int32_t rows, int32_t d, int32_t group, int32_t dtype, cons
   if (reinterpret_cast<uintptr_t>(x8) % 4 != 0)
     return spark_set_error(SPARK_E_ARG, "%s: x8 is not 4-byte aligned", fn);
   return quant_e4m3_launch(1, rows, rows, d, group, dtype, x, x8, scales, (hipStream_t)stream);
+}
+
+// ---- test hooks ---------------------------------------------------------------------
+size_t spark_debug_partition_ws_bytes(int32_t count, int32_t n, int32_t block) {
+  if (count < 1 || n < 1 || block < 1 || block > 128 || (long)count * n > 0x7fffffffL) {
+    spark_set_error(SPARK_E_SHAPE, "spark_debug_partition_ws_bytes: count=%d n=%d block=%d", count, n, block);
+    return (size_t)-1;
+  }
+  return debug_partition_ws_bytes(count, n, block);
+}
+
+int spark_debug_partition_level(int32_t count, int32_t n, int32_t block, const float* s,
+                                const int32_t* ids_in, int32_t* ids_out, void* ws, size_t ws_bytes,
+                                spark_stream_t stream) {
+  const char* fn = "spark_debug_partition_level";
+  if (count < 1 || n < 1 || block < 1 || block > 128 || (long)count * n > 0x7fffffffL)
+    return spark_set_error(SPARK_E_SHAPE, "%s: count=%d n=%d block=%d", fn, count, n, block);
+  CHECK(check_ptr(s, fn, "s"));
+  CHECK(check_ptr(ids_in, fn, "ids_in"));
+  CHECK(check_ptr(ids_out, fn, "ids_out"));
+  const size_t need = debug_partition_ws_bytes(count, n, block);
+  CHECK(check_ptr(ws, fn, "ws"));
+  if (ws_bytes < need) return spark_set_error(SPARK_E_WORKSPACE, "%s: ws_bytes %zu < %zu", fn, ws_bytes, need);
+  return debug_partition_launch(count, n, block, s, ids_in, ids_out, ws, (hipStream_t)stream);
+}
+
+int spark_debug_argmin(int32_t count, int32_t n, const float* vals, const int32_t* ids, int32_t* out,
+                       spark_stream_t stream) {
+  const char* fn = "spark_debug_argmin";
+  if (count < 1 || n < 1 || (long)count * n > 0x7fffffffL)
+    return spark_set_error(SPARK_E_SHAPE, "%s: count=%d n=%d", fn, count, n);
+  CHECK(check_ptr(vals, fn, "vals"));
+  CHECK(check_ptr(ids, fn, "ids"));
+  CHECK(check_ptr(out, fn, "out"));
+  return debug_argmin_launch(count, n, vals, ids, out, (hipStream_t)stream);
+}
+
+// ---- measurement helper ---------------------------------------------------------------
+double spark_mfma_peak_probe(int32_t workgroups, int32_t iters, float* sink, spark_stream_t stream) {
+  if (workgroups < 1 || iters < 1) {
+    spark_set_error(SPARK_E_SHAPE, "spark_mfma_peak_probe: workgroups=%d iters=%d", workgroups, iters);
+    return -1.0;
+  }
+  if (check_ptr(sink, "spark_mfma_peak_probe", "sink")) return -1.0;
+  if (mfma_peak_launch(workgroups, iters, sink, (hipStream_t)stream)) return -1.0;
+  return (double)workgroups * 4 * 4 * (double)iters * (32.0 * 32.0 * 16.0 * 2.0);
 }

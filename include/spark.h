@@ -288,6 +288,50 @@ int spark_gather(const spark_args* args, const void* x, const int32_t* perm, voi
 int spark_quant_e4m3(int32_t rows, int32_t d, int32_t group, int32_t dtype, const void* x,
                      uint8_t* x8, float* scales, spark_stream_t stream);
 
+/* ---- test hooks: the splitter's selection rules on caller values -------- */
+
+/* One capacity partition, as every split of spark_reblock performs it
+ * ([blog] 01 / Method: Spark-Reblock, the partitioner paragraph: each group
+ * is split by the distance while the child capacities are enforced; the
+ * two-pole rule and its tie rules are this library's reading).  For each of
+ * `count` rows of n positions (s: fp32 scores, ids_in: int32 token ids, both
+ * [count, n]; within a row the ids must be ascending, as in every group of
+ * the splitter, since ties are ranked by position): the left child is the
+ * c_L = ceil(ceil(n / block) / 2) * block positions first in (s descending,
+ * id ascending) order, where -0 equals +0 and NaN ranks after every number;
+ * ids_out [count, n] receives the left child's ids, then the right child's,
+ * each in input order.  Runs the kernels the splitter's top level uses for a
+ * group of that many blocks.  ws: spark_debug_partition_ws_bytes(count, n,
+ * block) bytes (SPARK_E_WORKSPACE if smaller).  Device pointers, 16-byte
+ * aligned; enqueued on the stream. */
+size_t spark_debug_partition_ws_bytes(int32_t count, int32_t n, int32_t block);
+int spark_debug_partition_level(int32_t count, int32_t n, int32_t block, const float* s,
+                                const int32_t* ids_in, int32_t* ids_out, void* ws, size_t ws_bytes,
+                                spark_stream_t stream);
+
+/* The pole choice of every split (same passage and reading as above: pole A
+ * is the member farthest from the group centroid, pole B the member
+ * farthest from A, both an argmin of a dot product): for each of `count`
+ * rows of n fp32 values vals [count, n] with int32 ids [count, n] (ids >= 0),
+ * out[row] = the id of the minimum value, where -0 equals +0, NaN ranks
+ * after every number and equal values go to the lower id; the same 64-bit
+ * (value key, id) ordering and wave reduction as the splitter's argmin
+ * passes.  Device pointers, 16-byte aligned; enqueued on the stream. */
+int spark_debug_argmin(int32_t count, int32_t n, const float* vals, const int32_t* ids, int32_t* out,
+                       spark_stream_t stream);
+
+/* ---- measurement helper (not part of the layer) -------------------------- */
+
+/* Enqueues one launch of a register-only bf16 matrix-core loop
+ * (v_mfma_f32_32x32x16_bf16, four independent accumulator chains per wave,
+ * `workgroups` workgroups of 4 waves, `iters` iterations) and returns the
+ * floating-point operations it performs, so that the caller's event timing
+ * of the launch gives the sustained bf16 MFMA rate of the part (the roofline
+ * peak the attention kernel is compared against).  sink: device buffer of
+ * workgroups * 256 floats that is never written in practice.  Returns -1 on
+ * bad arguments or a failed launch (spark_last_error() says why). */
+double spark_mfma_peak_probe(int32_t workgroups, int32_t iters, float* sink, spark_stream_t stream);
+
 /* ---- routing diagnostics (outside the layer; dense cost) ---------------- */
 
 /* Per query row p of the permuted order (q_p, k_p as written by

@@ -65,10 +65,11 @@ import numpy as np
 
 __all__ = [
     "n_blocks", "block_sizes", "topk_from_ratio", "second_moment", "psd_sqrt",
-    "whiten", "split_group", "split_partition", "reblock_head", "reblock_keys", "gather_pool",
+    "whiten", "argmin_lowest_id", "capacity_partition", "split_group", "split_partition", "reblock_head", "reblock_keys", "gather_pool",
     "block_scores", "select_topk", "anchor_query", "reweight_summaries",
     "mean_summaries", "sparse_attention", "dense_attention", "forward_head",
-    "forward", "attention_mass_recall", "log_mass_error", "HeadResult",
+    "forward", "attention_mass_recall", "attention_mass_recall_rows", "log_mass_error",
+    "log_mass_error_rows", "HeadResult",
     "E4M3_MAX", "e4m3_round", "pow2_scale", "quantize_e4m3_groups",
 ]
 
@@ -128,12 +129,29 @@ def whiten(x: np.ndarray, W: np.ndarray) -> np.ndarray:
     return out
 
 
-def _argmin_lowest_id(vals: np.ndarray, ids: np.ndarray) -> int:
-    """Index (into vals) of the minimum; ties -> lower id; NaN ranks last."""
+def argmin_lowest_id(vals: np.ndarray, ids: np.ndarray) -> int:
+    """Index (into vals) of the minimum; ties -> lower id; NaN ranks last;
+    -0 and +0 are equal values (the ids decide between them)."""
+    vals = np.asarray(vals, dtype=np.float64) + 0.0   # folds -0 onto +0
     isn = np.isnan(vals)
     key = np.where(isn, 0.0, vals)
     order = np.lexsort((ids, key, isn))
     return int(order[0])
+
+
+_argmin_lowest_id = argmin_lowest_id
+
+
+def capacity_partition(s: np.ndarray, ids: np.ndarray, cap_left: int):
+    """Left child = the cap_left members first in (s descending, id
+    ascending) order, NaN scores last and -0 equal to +0; right child = the
+    rest.  Both children are returned with ids ascending."""
+    s = np.asarray(s, dtype=np.float64) + 0.0
+    ids = np.asarray(ids)
+    isn = np.isnan(s)
+    key = np.where(isn, 0.0, -s)
+    order = np.lexsort((ids, key, isn))
+    return np.sort(ids[order[:cap_left]]), np.sort(ids[order[cap_left:]])
 
 
 def split_group(xhat: np.ndarray, ids: np.ndarray, cap_left: int):
@@ -152,17 +170,12 @@ def split_group(xhat: np.ndarray, ids: np.ndarray, cap_left: int):
     """
     X = xhat[ids]
     c = X.sum(axis=0)
-    a = _argmin_lowest_id(X @ c, ids)
+    a = argmin_lowest_id(X @ c, ids)
     xa = X[a]
-    bi = _argmin_lowest_id(X @ xa, ids)
+    bi = argmin_lowest_id(X @ xa, ids)
     xb = X[bi]
     s = X @ xa - X @ xb
-    isn = np.isnan(s)
-    key = np.where(isn, 0.0, -s)
-    order = np.lexsort((ids, key, isn))
-    left = np.sort(ids[order[:cap_left]])
-    right = np.sort(ids[order[cap_left:]])
-    return left, right
+    return capacity_partition(s, ids, cap_left)
 
 
 def split_partition(xhat: np.ndarray, b: int) -> np.ndarray:
@@ -536,14 +549,15 @@ def forward(q, k, v, b: int, topk: int, n_anchor: Optional[int] = None, **kw):
 # Diagnostics ([blog] ablation tables: attention-mass recall, abs log-mass error)
 # ----------------------------------------------------------------------------
 
-def attention_mass_recall(res: HeadResult, b: int) -> float:
-    """Mean over queries of the dense attention probability that falls in
-    the query block's selected key blocks (plain layers only)."""
+def attention_mass_recall_rows(res: HeadResult, b: int) -> np.ndarray:
+    """Per query row p of the permuted order: the dense attention
+    probability (softmax over every key of the head) that falls on the exact
+    keys of row p's query block's selected key blocks (plain layers only)."""
     if res.n_video >= 0:
         raise ValueError("diagnostics are defined for layers without context tokens")
     N, d = res.qp.shape
     nb = n_blocks(N, b)
-    tot = 0.0
+    rec = np.zeros(N)
     for A in range(nb):
         rows = slice(A * b, min(N, (A + 1) * b))
         s = res.qp[rows] @ res.kp.T / math.sqrt(d)
@@ -551,22 +565,35 @@ def attention_mass_recall(res: HeadResult, b: int) -> float:
         p = np.exp(s)
         p /= p.sum(axis=1, keepdims=True)
         ex = np.concatenate([np.arange(B * b, min(N, (B + 1) * b)) for B in res.idx[A]])
-        tot += p[:, ex].sum()
-    return tot / N
+        rec[rows] = p[:, ex].sum(axis=1)
+    return rec
 
 
-def log_mass_error(res: HeadResult, b: int) -> float:
-    """Mean over queries of |log(sum over unselected tokens of exp(logit))
-    - log(sum over unselected blocks of |B| exp(compressed logit))|
-    (plain layers only)."""
+def attention_mass_recall(res: HeadResult, b: int) -> float:
+    """Mean over the head's query rows of attention_mass_recall_rows."""
+    return float(attention_mass_recall_rows(res, b).mean())
+
+
+def log_mass_error_rows(res: HeadResult, b: int) -> np.ndarray:
+    """Per query row p of the permuted order ([blog] Spark-Reweight, the
+    log-mass error of its ablation table and the Jensen-gap figure):
+        | log sum_{B not in S_A} sum_{j in B} exp(q_p . k_j / sqrt(d))
+          - log sum_{B not in S_A} |B| exp(q_p . k~_B / sqrt(d) + beta_B) |
+    where S_A is the selection of row p's query block and |B| the token count
+    of block B (the multiplicity of the summary in the effective keys).  0 for
+    rows whose block selects every key block (plain layers only)."""
     if res.n_video >= 0:
         raise ValueError("diagnostics are defined for layers without context tokens")
     N, d = res.qp.shape
     nb = n_blocks(N, b)
     sizes = block_sizes(N, b).astype(np.float64)
     rs = 1.0 / math.sqrt(d)
-    tot = 0.0
-    cnt = 0
+    err = np.zeros(N)
+
+    def lse(z):
+        m = z.max(axis=1)
+        return m + np.log(np.exp(z - m[:, None]).sum(axis=1))
+
     for A in range(nb):
         rows = slice(A * b, min(N, (A + 1) * b))
         sel = np.zeros(nb, dtype=bool)
@@ -576,9 +603,19 @@ def log_mass_error(res: HeadResult, b: int) -> float:
             continue
         tok = np.concatenate([np.arange(B * b, min(N, (B + 1) * b)) for B in un])
         QA = res.qp[rows]
-        ex = QA @ res.kp[tok].T * rs
-        ap = QA @ res.ksum[un].T * rs + res.bias[un][None, :] + np.log(sizes[un])[None, :]
-        lse = lambda z: z.max(axis=1) + np.log(np.exp(z - z.max(axis=1, keepdims=True)).sum(axis=1))
-        tot += np.abs(lse(ex) - lse(ap)).sum()
-        cnt += QA.shape[0]
-    return tot / max(cnt, 1)
+        exact = QA @ res.kp[tok].T * rs
+        approx = QA @ res.ksum[un].T * rs + res.bias[un][None, :] + np.log(sizes[un])[None, :]
+        err[rows] = np.abs(lse(exact) - lse(approx))
+    return err
+
+
+def log_mass_error(res: HeadResult, b: int) -> float:
+    """Mean of log_mass_error_rows over the rows whose query block leaves at
+    least one key block unselected (0 if none does)."""
+    N = res.qp.shape[0]
+    nb = n_blocks(N, b)
+    has_tail = np.zeros(N, dtype=bool)
+    for A in range(nb):
+        has_tail[A * b:min(N, (A + 1) * b)] = len(set(np.asarray(res.idx[A]).tolist())) < nb
+    rows = log_mass_error_rows(res, b)
+    return float(rows[has_tail].mean()) if has_tail.any() else 0.0

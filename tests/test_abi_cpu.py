@@ -181,3 +181,23 @@ def test_diagnostics_validation(lib):
     assert "k_p is NULL" in L.last_error()
     assert f(ctypes.byref(a), FAKE, FAKE, FAKE, 4, FAKE, FAKE, MISALIGNED, FAKE, None) == -1
     assert f(ctypes.byref(_args(d=96)), FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, None) == -4
+
+
+def test_debug_hooks_validation(lib):
+    p = lib.spark_debug_partition_level
+    nws = lib.spark_debug_partition_ws_bytes(2, 70000, 128)
+    assert nws > 2 * 256 * 4 * 8                      # > 512 blocks: segment counts
+    assert lib.spark_debug_partition_ws_bytes(2, 1000, 64) == 256   # one record block only
+    assert lib.spark_debug_partition_ws_bytes(0, 10, 8) == ctypes.c_size_t(-1).value
+    assert p(0, 10, 8, FAKE, FAKE, FAKE, FAKE, 256, None) == -2
+    assert p(1, 10, 0, FAKE, FAKE, FAKE, FAKE, 256, None) == -2
+    assert p(1, 10, 129, FAKE, FAKE, FAKE, FAKE, 256, None) == -2
+    assert p(1, 10, 8, None, FAKE, FAKE, FAKE, 256, None) == -1
+    assert p(1, 10, 8, FAKE, MISALIGNED, FAKE, FAKE, 256, None) == -1
+    assert p(2, 70000, 128, FAKE, FAKE, FAKE, FAKE, nws - 1, None) == -5
+    assert p(2, 70000, 128, FAKE, FAKE, FAKE, None, nws, None) == -1
+    a = lib.spark_debug_argmin
+    assert a(0, 5, FAKE, FAKE, FAKE, None) == -2
+    assert a(1, 0, FAKE, FAKE, FAKE, None) == -2
+    assert a(1, 5, FAKE, None, FAKE, None) == -1
+    assert a(1, 5, FAKE, FAKE, MISALIGNED, None) == -1

@@ -9,9 +9,9 @@ those comparisons report.
   summaries and the oracle's routing at the fp32 / bf16 bars.
 * IDENTITY layout: permutations are 0..N-1 and the layer equals the oracle's
   fixed-block forward pass.
-* Diagnostics, oracle intermediates injected: the per-query means of the
-  GPU recall and log-mass error equal the oracle's attention_mass_recall and
-  log_mass_error (relative 1e-4; the GPU accumulates in fp32).
+* Diagnostics, oracle intermediates injected: every query row's GPU recall
+  and log-mass error equal the oracle's attention_mass_recall_rows and
+  log_mass_error_rows (absolute 1e-4; the GPU accumulates in fp32).
 * q_reuse_k layout (the key partition groups the queries too): perm_q and
   perm_k both equal, bit for bit, the key permutation of the full Reblock on
   the same inputs, and the layer equals the layer run on that permutation
@@ -156,12 +156,16 @@ def test_diagnostics_match_oracle(name, summary):
     rec, lme = host(rec), host(lme)
     assert np.all((rec >= 0) & (rec <= 1 + 1e-6))
     for h in range(H):
-        want_r = O.attention_mass_recall(res[h], b)
-        want_l = O.log_mass_error(res[h], b)
-        got_r, got_l = rec[h].mean(), lme[h].mean()
-        say(f"[diag] head {h}: recall {got_r:.6f} vs {want_r:.6f}; log-mass {got_l:.6f} vs {want_l:.6f}")
-        assert abs(got_r - want_r) <= 1e-4 * max(abs(want_r), 1e-3)
-        assert abs(got_l - want_l) <= 1e-4 * max(abs(want_l), 1e-3)
+        want_r = O.attention_mass_recall_rows(res[h], b)
+        want_l = O.log_mass_error_rows(res[h], b)
+        er = np.abs(rec[h] - want_r).max()
+        el = np.abs(lme[h] - want_l).max()
+        say(f"[diag] head {h}: recall max |diff| {er:.2e} (mean {rec[h].mean():.6f} vs {want_r.mean():.6f}); "
+            f"log-mass max |diff| {el:.2e} (mean {lme[h].mean():.6f} vs {want_l.mean():.6f})")
+        # row by row; the GPU sums the dense softmax in fp32 (bf16 operands
+        # are exact, the fp32 accumulation over N keys is not)
+        assert er <= 1e-4
+        assert el <= 1e-4 * max(1.0, float(np.abs(want_l).max()))
 
 
 def _layer_diag(q, k, v, b, topk, layout, summary):

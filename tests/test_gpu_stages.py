@@ -236,6 +236,30 @@ def test_topk_row_lengths(nb):
         assert np.array_equal(got[0, A], want), A
 
 
+@pytest.mark.parametrize("nb,d", [(4097, 128), (3999, 64), (5000, 128)])
+def test_topk_from_means_long_rows(nb, d):
+    """Rows of more than 3968 blocks leave room for fewer than 8 query means
+    per workgroup (7 at nb = 4097): the means then start at a 16-byte
+    rounded offset after the score rows.  The scores the kernel computes
+    from the means match the oracle's block scores, and its selection is
+    exactly the oracle's selection on those scores."""
+    rng = np.random.default_rng(nb + d)
+    qbar = rng.standard_normal((1, nb, d)).astype(np.float32)
+    kbar = rng.standard_normal((1, nb, d)).astype(np.float32)
+    topk = max(1, nb // 10)
+    say(f"[select] means nb={nb} d={d} topk={topk}")
+    idx, S = L.spark_select(torch.from_numpy(qbar).to(DEV), torch.from_numpy(kbar).to(DEV), topk, nb, 1,
+                            want_scores=True)
+    torch.cuda.synchronize()
+    S = host(S)[0]
+    rows = sorted(set(range(16)) | set(range(nb - 16, nb)) | set(rng.integers(0, nb, 16).tolist()))
+    want_S = O.block_scores(qbar[0].astype(np.float64)[rows], kbar[0].astype(np.float64))
+    np.testing.assert_allclose(S[rows], want_S, rtol=1e-5, atol=1e-4)
+    got = host(idx)[0]
+    for A in rows:
+        assert np.array_equal(got[A], O.select_topk(S[A:A + 1], topk)[0]), A
+
+
 @pytest.mark.parametrize("name", ["tiny_f32", "draft_bf16"])
 def test_scores_from_means_match_oracle(name, oracle_runs):
     q, k, v, dt, b, topk, res = oracle_runs(name)

@@ -115,6 +115,59 @@ def _check_perm_structure(perm, N, b):
         assert np.all(np.diff(leaf) > 0)                       # ids ascending inside a leaf
 
 
+def _beats(s_a, id_a, s_b, id_b):
+    """Pairwise rule of the capacity split: a larger score wins, -0 equals
+    +0, a NaN loses to every number, equal scores (or two NaNs) go to the
+    lower id."""
+    na, nb_ = math.isnan(s_a), math.isnan(s_b)
+    if na != nb_:
+        return nb_
+    if not na and s_a != s_b:
+        return s_a > s_b
+    return id_a < id_b
+
+
+def _tie_heavy(rng, n):
+    vals = rng.choice([-1.5, -0.0, 0.0, 0.25, 2.0, np.nan, np.inf, -np.inf], size=n)
+    ids = np.sort(rng.choice(10 * n, size=n, replace=False))
+    return vals, ids
+
+
+def test_capacity_partition_pairwise_rule_with_nan_and_signed_zero():
+    """Every member of the left child beats every member of the right child
+    under the pairwise rule (checked pair by pair), the left child has the
+    capacity, both children keep ascending ids."""
+    rng = _rng(53)
+    for trial in range(30):
+        n = int(rng.integers(1, 40))
+        s, ids = _tie_heavy(rng, n)
+        cap = int(rng.integers(0, n + 1))
+        left, right = O.capacity_partition(s, ids, cap)
+        assert len(left) == cap and len(right) == n - cap
+        assert np.all(np.diff(left) > 0) and np.all(np.diff(right) > 0)
+        pos = {int(i): j for j, i in enumerate(ids)}
+        for a in left:
+            for b in right:
+                assert _beats(s[pos[int(a)]], a, s[pos[int(b)]], b), (trial, a, b)
+
+
+def test_argmin_lowest_id_pairwise_rule_with_nan_and_signed_zero():
+    """The winner is not beaten by any member under the mirrored pairwise
+    rule (smaller value wins, -0 = +0, NaN last, ties to the lower id)."""
+    rng = _rng(59)
+    for _ in range(50):
+        n = int(rng.integers(1, 30))
+        v, ids = _tie_heavy(rng, n)
+        w = O.argmin_lowest_id(v, ids)
+        for j in range(n):
+            if j != w:
+                assert _beats(-v[w], ids[w], -v[j], ids[j])
+    # -0 and +0 are one value: the lower id wins whichever sign it carries
+    assert O.argmin_lowest_id(np.array([0.0, -0.0]), np.array([3, 7])) == 0
+    assert O.argmin_lowest_id(np.array([0.0, -0.0]), np.array([7, 3])) == 1
+    assert O.argmin_lowest_id(np.array([np.nan, 5.0]), np.array([0, 1])) == 1
+
+
 @pytest.mark.parametrize("N,b", [(1024, 64), (1025, 64), (1000, 128), (7, 2), (1, 4), (130, 128), (512, 1)])
 def test_split_is_bijection_with_leaves_of_block_size(N, b):
     rng = _rng(N + b)
@@ -389,6 +442,70 @@ def test_recall_and_log_mass_closed_forms():
     assert abs(O.attention_mass_recall(r, b) - 1.0) < 1e-12
     r = O.forward_head(rng.standard_normal((N, d)), k, v, 1, 5)
     assert O.log_mass_error(r, 1) < 1e-12
+
+
+@pytest.mark.parametrize("summary", ["reweight", "mean"])
+def test_log_mass_error_is_zero_for_constant_key_blocks(summary):
+    """Every key block holds one repeated key c_B (b = 64 tokens): the exact
+    mass of block B for query q is 64 e^{q.c_B/sqrt d}, and both estimators
+    give that exactly (k~_B = c_B, beta_B = 0), so every row's log-mass error
+    is 0 -- only if the compressed logit carries the multiplicity log|B|
+    (without it every row would be off by log 64)."""
+    rng = _rng(41)
+    N, d, b = 4 * 64 + 7, 8, 64                   # 5 blocks, the last of 7 tokens
+    nb = O.n_blocks(N, b)
+    cents = rng.standard_normal((nb, d))
+    k = np.repeat(cents, b, axis=0)[:N]
+    q = rng.standard_normal((N, d))
+    v = rng.standard_normal((N, d))
+    r = O.forward_head(q, k, v, b, 2, layout="identity", summary=summary)
+    rows = O.log_mass_error_rows(r, b)
+    assert rows.shape == (N,)
+    assert np.abs(rows).max() < 1e-12
+    assert O.log_mass_error(r, b) < 1e-12
+
+
+def test_log_mass_error_rows_closed_form_for_a_symmetric_pair():
+    """MEAN pooling of an unselected block of the two keys +u and -u: the
+    exact mass e^a + e^-a (a = q.u/sqrt d) against the pooled 2 e^0, so the
+    row's log-mass error is log cosh a (the Jensen gap of the pair), row by
+    row."""
+    rng = _rng(43)
+    d, b = 4, 2
+    u = rng.standard_normal(d)
+    k = np.stack([rng.standard_normal(d), rng.standard_normal(d), u, -u])
+    q = 2.0 * rng.standard_normal((4, d))
+    v = rng.standard_normal((4, d))
+    S = np.array([[1.0, 0.0], [1.0, 0.0]])        # both query blocks keep block 0
+    r = O.forward_head(q, k, v, b, 1, layout="identity", summary="mean", scores_in=S)
+    a = q @ u / math.sqrt(d)
+    np.testing.assert_allclose(O.log_mass_error_rows(r, b), np.log(np.cosh(a)), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(O.log_mass_error(r, b), np.log(np.cosh(a)).mean(), rtol=1e-12)
+
+
+def test_recall_rows_closed_forms():
+    """Per-row recall: a zero query attends uniformly, so its recall is the
+    share of keys in the selected blocks (the short last block counts its
+    real tokens only); a query whose logits are +inf-like on one key of a
+    selected block has recall 1, on an unselected block recall 0."""
+    rng = _rng(47)
+    N, d, b = 100, 4, 32                          # blocks of 32, 32, 32, 4
+    k = rng.standard_normal((N, d))
+    q = np.zeros((N, d))
+    S = np.zeros((4, 4))
+    S[:, 3] = 1.0
+    S[:, 1] = 2.0                                  # every query block keeps blocks 1 and 3
+    r = O.forward_head(q, k, rng.standard_normal((N, d)), b, 2, layout="identity", scores_in=S)
+    np.testing.assert_allclose(O.attention_mass_recall_rows(r, b), np.full(N, 36 / 100), rtol=1e-12)
+    k2 = 1e-3 * k
+    k2[40] = [10.0, 0, 0, 0]                       # block 1 (selected)
+    k2[5] = [0, 10.0, 0, 0]                        # block 0 (unselected)
+    q2 = np.zeros((N, d))
+    q2[0] = [12.0, 0, 0, 0]                        # logit 60 on key 40, ~0 elsewhere
+    q2[1] = [0, 12.0, 0, 0]                        # logit 60 on key 5
+    r = O.forward_head(q2, k2, rng.standard_normal((N, d)), b, 2, layout="identity", scores_in=S)
+    rec = O.attention_mass_recall_rows(r, b)
+    assert rec[0] > 1 - 1e-15 and rec[1] < 1e-20
 
 
 def test_direction_of_the_pages_ablations_on_clustered_data():
