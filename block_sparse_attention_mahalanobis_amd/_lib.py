@@ -33,7 +33,7 @@ EXPORTED = [
     "spark_summarize", "spark_attn", "spark_layer", "spark_moments", "spark_msqrt",
     "spark_whiten", "spark_split", "spark_gather", "spark_diagnostics", "spark_quant_e4m3",
     "spark_debug_partition_ws_bytes", "spark_debug_partition_level", "spark_debug_argmin",
-    "spark_mfma_peak_probe",
+    "spark_mfma_peak_probe", "spark_attn_noalloc", "spark_attn_noalloc_scratch_bytes",
 ]
 
 
@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
         "spark_debug_partition_level": ([_I, _I, _I, _P, _P, _P, _P, _Z, _P], ctypes.c_int),
         "spark_debug_argmin": ([_I, _I, _P, _P, _P, _P], ctypes.c_int),
         "spark_mfma_peak_probe": ([_I, _I, _P, _P], ctypes.c_double),
+        "spark_attn_noalloc": ([_A, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+        "spark_attn_noalloc_scratch_bytes": ([], _Z),
     }
     for name, (argt, rest) in sig.items():
         f = getattr(L, name)
@@ -251,6 +253,21 @@ def spark_attn(q_p, k_p, v_pt, idx, ksum, vsum, bias, N: int, block: int, perm_q
     _check(lib().spark_attn(ctypes.byref(a), _ptr(q_p), _ptr(k_p), _ptr(v_pt), _ptr(idx), topk, _ptr(ksum),
                             _ptr(vsum), _ptr(bias), _ptr(perm_q), _ptr(out), _ptr(ws), nws, _stream()),
            "spark_attn")
+    return out
+
+
+def spark_attn_noalloc(q_p, k_p, v_pt, idx, ksum, vsum, bias, N: int, block: int, perm_q=None, out=None,
+                       n_anchor: Optional[int] = None, context: bool = False, fp8: bool = False):
+    """spark_attn with its scratch in the library's fixed device array (no
+    workspace argument, nothing allocated by the library)."""
+    H, Np, d = q_p.shape
+    topk = idx.shape[2]
+    a = make_args(H, N, d, block, q_p.dtype, n_anchor, context=context, fp8=fp8)
+    if out is None:
+        out = torch.empty((H, N if perm_q is not None else Np, d), dtype=q_p.dtype, device=q_p.device)
+    _check(lib().spark_attn_noalloc(ctypes.byref(a), _ptr(q_p), _ptr(k_p), _ptr(v_pt), _ptr(idx), topk,
+                                    _ptr(ksum), _ptr(vsum), _ptr(bias), _ptr(perm_q), _ptr(out), _stream()),
+           "spark_attn_noalloc")
     return out
 
 

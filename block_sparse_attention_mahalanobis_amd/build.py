@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libspark.so")
 SOURCES = ["spark_api.cpp", "k_attn.hip", "k_gather_summ.hip", "k_select.hip",
-           "k_whiten.hip", "k_split.hip", "k_diag.hip", "k_fp8.hip", "k_probe.hip"]
+           "k_whiten.hip", "k_split.hip", "k_diag.hip", "k_fp8.hip", "k_probe.hip",
+           "k_noalloc.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",

@@ -52,6 +52,11 @@ size_t debug_partition_ws_bytes(int count, int n, int BK);
 int debug_partition_launch(int count, int n, int BK, const float* s, const int32_t* ids_in,
                            int32_t* ids_out, void* ws, hipStream_t st);
 int mfma_peak_launch(int workgroups, int iters, float* sink, hipStream_t st);
+size_t noalloc_scratch_bytes();
+int attn_noalloc_launch(int H, int N, int Nv, int D, int BK, int dtype, const void* qp, const void* kp,
+                        const void* vpt, const int32_t* idx, int topk, const float* ksum,
+                        const float* vsum, const float* bias, const int32_t* perm_q, void* out,
+                        bool fp8, hipStream_t st);
 int diag_launch(int H, int N, int D, int BK, int dtype, const void* qp, const void* kp,
                 const int32_t* idx, int topk, const float* ksum, const float* bias, float* recall,
                 float* logmass, hipStream_t st);
@@ -484,6 +489,35 @@ int spark_attn(const spark_args* a, const void* q_p, const void* k_p, const void
   }
   return attn_launch(a->H, a->N, Nv, a->d, a->block, a->dtype, q_p, k_p, v_pt, idx, topk, ksum, vsum,
                      bias, perm_q, out, ws, fp8_of(a), (hipStream_t)stream);
+}
+
+size_t spark_attn_noalloc_scratch_bytes(void) { return noalloc_scratch_bytes(); }
+
+int spark_attn_noalloc(const spark_args* a, const void* q_p, const void* k_p, const void* v_pt,
+                       const int32_t* idx, int32_t topk, const float* ksum, const float* vsum,
+                       const float* bias, const int32_t* perm_q, void* out, spark_stream_t stream) {
+  const char* fn = "spark_attn_noalloc";
+  CHECK(check_args(a, fn));
+  const int nb = nblocks(a);
+  if (topk < 1 || topk > nb) return spark_set_error(SPARK_E_SHAPE, "%s: topk=%d not in [1, %d]", fn, topk, nb);
+  CHECK(check_ptr(q_p, fn, "q_p"));
+  CHECK(check_ptr(k_p, fn, "k_p"));
+  CHECK(check_ptr(v_pt, fn, "v_pt"));
+  CHECK(check_ptr(idx, fn, "idx"));
+  CHECK(check_ptr(ksum, fn, "ksum"));
+  CHECK(check_ptr(vsum, fn, "vsum"));
+  CHECK(check_ptr(bias, fn, "bias"));
+  CHECK(check_ptr(perm_q, fn, "perm_q", true));
+  CHECK(check_ptr(out, fn, "out"));
+  CHECK(check_fp8(a, fn));
+  const int Nv = geo(a).Nv;
+  const size_t need = attn_ws_bytes(a->H, a->N, Nv, a->d, a->block, a->dtype, fp8_of(a));
+  if (need > noalloc_scratch_bytes())
+    return spark_set_error(SPARK_E_WORKSPACE, "%s: these arguments need %zu bytes of scratch; the "
+                           "allocation-free entry point holds %zu (use spark_attn with a workspace)",
+                           fn, need, noalloc_scratch_bytes());
+  return attn_noalloc_launch(a->H, a->N, Nv, a->d, a->block, a->dtype, q_p, k_p, v_pt, idx, topk, ksum, vsum,
+                             bias, perm_q, out, fp8_of(a), (hipStream_t)stream);
 }
 
 int spark_layer(const spark_args* a, const void* q, const void* k, const void* v, int32_t topk,

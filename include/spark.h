@@ -232,6 +232,26 @@ int spark_attn(const spark_args* args, const void* q_p, const void* k_p, const v
                const float* bias, const int32_t* perm_q, void* out, void* ws, size_t ws_bytes,
                spark_stream_t stream);
 
+/* spark_attn without a workspace argument, for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, results (bit for bit) and
+ * errors as spark_attn; its scratch is a file-scope device array of
+ * spark_attn_noalloc_scratch_bytes() bytes (64 MiB) that each GPU the
+ * library runs on holds until the process ends.  Arguments whose
+ * spark_workspace_bytes(args, SPARK_OP_ATTN, topk) exceeds that size are
+ * rejected with SPARK_E_WORKSPACE before anything is enqueued (the 768p
+ * layer needs about 42 MB; E4M3 logits at that size do not fit).  The first
+ * call made with a device current looks up that device's copy of the array;
+ * no call allocates or frees memory.  All calls on one GPU share its array:
+ * calls that overlap on one GPU (other streams, other host threads) race on
+ * it and must be serialised by the caller. */
+int spark_attn_noalloc(const spark_args* args, const void* q_p, const void* k_p, const void* v_pt,
+                       const int32_t* idx, int32_t topk, const float* ksum, const float* vsum,
+                       const float* bias, const int32_t* perm_q, void* out, spark_stream_t stream);
+
+/* Bytes of the scratch array spark_attn_noalloc works in (per GPU). */
+size_t spark_attn_noalloc_scratch_bytes(void);
+
 /* The whole layer: spark_reblock -> spark_select -> spark_summarize ->
  * spark_attn, with every intermediate in ws
  * (spark_workspace_bytes(args, SPARK_OP_LAYER, topk) bytes). */
