@@ -382,6 +382,15 @@ __device__ __forceinline__ void d128_pipeline() {
     }
 }
 constexpr int D128_LDS_TILES = 2 * 128 * 256;   // K + V^T, 64 KB
+// Workgroup barrier without a memory fence: the waves' own LDS reads are
+// complete (lgkmcnt(0)) and the direct loads are waited for explicitly with
+// vmcnt counts, so loads issued for a later tile stay in flight across it
+// (a fenced barrier would wait for every outstanding direct load, which the
+// compiler counts as an LDS write).  The asm memory clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void d128_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n s_barrier" ::: "memory");
+}
 
 // fp8 logits: issue order of the QK block (16 LDS reads of 16 bytes, 8
 // 32x32x64 MFMAs): the first k step's reads, then each MFMA of that step
@@ -452,7 +461,11 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
   int h, A;
   if (!d128_map(blockIdx.x, nb, nbc, h, A)) return;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  // the wave index as a scalar: every LDS destination of a direct load is
+  // then computed in SGPRs (M0 needs no v_readfirstlane, a VALU op that would
+  // queue behind the other wave's MFMAs)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
   const int nbt = nb + nbc;
   const long Np = (long)nbt * BK;
@@ -596,16 +609,29 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
   {
     const char *kb, *vb;
     tile_base(0, kb, vb);
-    if constexpr (FP8) issue8(kb, sK);
-    else issue(kb, koff, sK);
-    issue(vb, voff, sV);
+    if constexpr (FP8) {
+      issue8(kb, sK);
+      issue(vb, voff, sV);
+    } else {
+      issue(kb, koff, sK);   // V(0) is issued during QK(0)
+    }
   }
+  auto rsrc32k = [&](const char* base) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 128 * 256, 0x00020000);
+  };
+  // load i (0..7) of this wave's share of a 32 KB tile
+  auto load1 = [&](const __amdgpu_buffer_rsrc_t& rs, const uint32_t* off, unsigned char* dst, int i) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (void __attribute__((address_space(3)))*)(dst + (8 * wave + i) * 1024), 16, off[i & 3],
+        (i >> 2) * 4096, 0, 0);
+  };
 
   for (int t = 0; t < ntiles; ++t) {
     const bool exact = t < tp.nex;
-    // K(t) landed (V(t) may still be in flight)
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    __syncthreads();
+    // K(t) landed (bf16: nothing else is in flight; fp8: V(t) may be)
+    if constexpr (FP8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    d128_barrier();
     f32x16 sacc[4];
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
@@ -636,27 +662,40 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
       // below fix the issue order: the reads of steps 0..D128_PF-1 first,
       // then each MFMA of step s followed by one read of step s+D128_PF, so
       // every read has D128_PF steps of MFMAs to land in
+      // V(t) streams in during this product, one direct load per k step
+      const char *kbt, *vbt;
+      tile_base(t, kbt, vbt);
+      const __amdgpu_buffer_rsrc_t rsv = rsrc32k(vbt);
       bf16x8 kop[D / 16][4];
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s)
+      for (int s = 0; s < D128_PF; ++s)
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt)
           kop[s][jt] = *reinterpret_cast<const bf16x8*>(sK + ro[s] + jt * 8192);
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s)
+      for (int s = 0; s < D / 16; ++s) {
+        if (s + D128_PF < D / 16) {
+#pragma unroll
+          for (int jt = 0; jt < 4; ++jt)
+            kop[s + D128_PF][jt] = *reinterpret_cast<const bf16x8*>(sK + ro[s + D128_PF] + jt * 8192);
+        }
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt)
           sacc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[s][jt], qop[s], sacc[jt], 0, 0, 0);
-      d128_pipeline<D / 16>();
+        load1(rsv, voff, sV, s);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     __builtin_amdgcn_s_setprio(0);
-    __syncthreads();  // every wave is done reading sK
+    d128_barrier();  // every wave is done reading sK
     const char *kb1 = nullptr, *vb1 = nullptr;
-    if (t + 1 < ntiles) {
-      tile_base(t + 1, kb1, vb1);
-      if constexpr (FP8) issue8(kb1, sK);
-      else issue(kb1, koff, sK);
+    // bf16: K(t+1) streams in during the softmax; the last tile reloads its
+    // own K (unused) so that every tile issues the same loads
+    tile_base(t + 1 < ntiles ? t + 1 : t, kb1, vb1);
+    if constexpr (FP8) {
+      if (t + 1 < ntiles) issue8(kb1, sK);
     }
+    const __amdgpu_buffer_rsrc_t rsk = rsrc32k(kb1);
 
     // P against the lazy reference m_ref: p = 2^(logit * log2 e - m_ref).
     // Every p of a row half is at most that half's sum, so a sum <= 2^12
@@ -704,7 +743,23 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
         pop[2 * jt + hh][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[jt][8 * hh + e], sc, nm)); \
       psum = rowsum_bf16(pop);                                                          \
     }
-    SPARK_D128_P()
+    if constexpr (FP8) {
+      SPARK_D128_P()
+    } else {
+      const float nm = -m_ref;
+      const float sc = exact ? lsc : 1.f;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            pop[2 * jt + hh][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[jt][8 * hh + e], sc, nm));
+          load1(rsk, koff, sK, 2 * jt + hh);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      psum = rowsum_bf16(pop);
+    }
     if (__builtin_amdgcn_ballot_w64(!(psum <= 4096.f)) != 0) {
       float mx = -INFINITY;
 #pragma unroll
@@ -727,13 +782,13 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
     l_run += psum;
 
     // V(t) landed: only this wave's K(t+1) loads (8 bf16 / 4 fp8) may be outstanding
-    if (t + 1 < ntiles) {
-      if constexpr (FP8) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    if constexpr (FP8) {
+      if (t + 1 < ntiles) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // K(t+1) in flight
     }
-    __syncthreads();
+    d128_barrier();
     __builtin_amdgcn_s_setprio(2);
     {
       bf16x8 vop[BK / 16][4];
@@ -750,9 +805,12 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
       d128_pipeline<BK / 16>();
     }
     __builtin_amdgcn_s_setprio(0);
-    __syncthreads();  // every wave is done reading sV
-    if (t + 1 < ntiles) issue(vb1, voff, sV);
+    d128_barrier();  // every wave is done reading sV
+    if constexpr (FP8) {
+      if (t + 1 < ntiles) issue(vb1, voff, sV);
+    }
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the last tile's K reload
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.f / l_tot;
