@@ -57,6 +57,9 @@ def parse():
     p.add_argument("--context", action="store_true",
                    help="tokens from n_anchor on (the ref2va reference frames) are context tokens: "
                         "exact for every query, outside the video-block top-k")
+    p.add_argument("--one-block", action="store_true",
+                   help="one query block per attention workgroup (SPARK_ATTN_ONE_BLOCK) instead of the "
+                        "paired schedule")
     return p.parse_args()
 
 
@@ -167,9 +170,10 @@ def cpu_baseline(w, topk, sample_blocks, context=False):
                        f"and x{w.H} heads; numpy fp64, BLAS threads = {cores}")}
 
 
-def load_traffic(name, sources, key):
+def load_traffic(name, sources, key, kernel=None):
     """Measured HBM bytes from a committed rocprofv3 --pmc summary under
-    profiles/, if it was taken on the current kernel sources (else None)."""
+    profiles/, if it was taken on the current kernel sources and, where
+    given, for the same kernel (else None)."""
     path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
@@ -181,6 +185,8 @@ def load_traffic(name, sources, key):
     for src in sources:
         h.update(open(src, "rb").read())
     if rec.get("kernel_sha") != h.hexdigest()[:16]:
+        return None
+    if kernel is not None and rec.get("kernel") != kernel:
         return None
     return rec.get(key)
 
@@ -298,7 +304,8 @@ def main():
     vsum = torch.empty((H, nb, d), dtype=torch.float32, device=dev)
     bias = torch.empty((H, nb), dtype=torch.float32, device=dev)
     out = torch.empty_like(q)
-    a = L.make_args(H, N, d, b, dtype, w.n_anchor, args.layout, context=ctx, fp8=args.fp8)
+    a = L.make_args(H, N, d, b, dtype, w.n_anchor, args.layout, context=ctx, fp8=args.fp8,
+                    one_block=args.one_block)
     ws_r = L.workspace_bytes(a, L.OP_REBLOCK)
     ws_a = L.workspace_bytes(a, L.OP_ATTN)
     ws = torch.empty(max(ws_r, ws_a, 256), dtype=torch.uint8, device=dev)
@@ -374,9 +381,12 @@ def main():
     rb_bytes = reblock_bytes(H, N, d, b, es, lev, nb, 1 if args.layout == "q_reuse_k" else 2, Nv)
     rb_ms = st_mean[0] + st_mean[2]
     csrc = os.path.join(ROOT, "block_sparse_attention_mahalanobis_amd", "csrc")
+    paired = (not ctx and not args.fp8 and not args.one_block and d == 128 and b == 128
+              and dtype == torch.bfloat16)
+    attn_kernel = "attn_pair_d128" if paired else "attn_mfma_d128"
     traffic = load_traffic("attn_full768_traffic.txt",
                            [os.path.join(csrc, f) for f in ("common.hpp", "k_attn.hip")],
-                           "bytes_per_launch") if args.config == "full768" else None
+                           "bytes_per_launch", attn_kernel) if args.config == "full768" and args.layout == "reblock" else None
     rb_traffic = load_traffic("reblock_full768_traffic.txt",
                               [os.path.join(csrc, f) for f in ("common.hpp", "k_whiten.hip", "k_split.hip",
                                                                "k_gather_summ.hip")],
@@ -417,7 +427,7 @@ def main():
                                   "achieved_gbs": round(rb_bytes / (rb_ms * 1e-3) / 1e9, 1),
                                   "frac_of_8tbs": round(rb_bytes / (rb_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
                                   "traffic_gb": None if rb_traffic is None else round(rb_traffic / 1e9, 1)},
-        "roofline": {"kernel": "attn_mfma_d128 (spark_attn)", "bound": "mfma",
+        "roofline": {"kernel": attn_kernel + " (spark_attn)", "bound": "mfma",
                      "achieved": round(alg_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(alg_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "measured_peak": round(peak_meas, 1),

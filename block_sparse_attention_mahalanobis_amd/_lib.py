@@ -22,6 +22,7 @@ LAYOUT_REBLOCK, LAYOUT_IDENTITY, LAYOUT_GIVEN, LAYOUT_Q_REUSE_K = 0x0, 0x1, 0x2,
 SUMMARY_REWEIGHT, SUMMARY_MEAN = 0x0, 0x4
 CONTEXT_EXACT = 0x8
 EXACT_FP8 = 0x10
+ATTN_ONE_BLOCK = 0x20
 OP_REBLOCK, OP_SELECT, OP_SUMMARIZE, OP_ATTN, OP_SPLIT, OP_LAYER = range(6)
 _LAYOUTS = {"reblock": LAYOUT_REBLOCK, "identity": LAYOUT_IDENTITY, "given": LAYOUT_GIVEN,
             "q_reuse_k": LAYOUT_Q_REUSE_K}
@@ -131,11 +132,11 @@ def _dtype_code(dt: torch.dtype) -> int:
 
 def make_args(H: int, N: int, d: int, block: int, dtype, n_anchor: Optional[int] = None,
               layout: str = "reblock", summary: str = "reweight", context: bool = False,
-              fp8: bool = False) -> SparkArgs:
+              fp8: bool = False, one_block: bool = False) -> SparkArgs:
     code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
     return SparkArgs(H, N, d, block, code, N if n_anchor is None else n_anchor,
                      _LAYOUTS[layout] | _SUMMARIES[summary] | (CONTEXT_EXACT if context else 0)
-                     | (EXACT_FP8 if fp8 else 0), 0)
+                     | (EXACT_FP8 if fp8 else 0) | (ATTN_ONE_BLOCK if one_block else 0), 0)
 
 
 def n_blocks(N: int, block: int) -> int:
@@ -238,12 +239,14 @@ def spark_summarize(k_p, v_pt, anchor, N: int, block: int, summary: str = "rewei
 
 
 def spark_attn(q_p, k_p, v_pt, idx, ksum, vsum, bias, N: int, block: int, perm_q=None, out=None,
-               ws=None, n_anchor: Optional[int] = None, context: bool = False, fp8: bool = False):
+               ws=None, n_anchor: Optional[int] = None, context: bool = False, fp8: bool = False,
+               one_block: bool = False):
     """Fused two-branch attention; [H, N, d] in original order if perm_q is
-    given, else [H, Np, d] in permuted order.  fp8: E4M3 logits."""
+    given, else [H, Np, d] in permuted order.  fp8: E4M3 logits.  one_block:
+    one query block per workgroup (SPARK_ATTN_ONE_BLOCK)."""
     H, Np, d = q_p.shape
     topk = idx.shape[2]
-    a = make_args(H, N, d, block, q_p.dtype, n_anchor, context=context, fp8=fp8)
+    a = make_args(H, N, d, block, q_p.dtype, n_anchor, context=context, fp8=fp8, one_block=one_block)
     dev = q_p.device
     if out is None:
         out = torch.empty((H, N if perm_q is not None else Np, d), dtype=q_p.dtype, device=dev)
@@ -257,12 +260,13 @@ def spark_attn(q_p, k_p, v_pt, idx, ksum, vsum, bias, N: int, block: int, perm_q
 
 
 def spark_attn_noalloc(q_p, k_p, v_pt, idx, ksum, vsum, bias, N: int, block: int, perm_q=None, out=None,
-                       n_anchor: Optional[int] = None, context: bool = False, fp8: bool = False):
+                       n_anchor: Optional[int] = None, context: bool = False, fp8: bool = False,
+                       one_block: bool = False):
     """spark_attn with its scratch in the library's fixed device array (no
     workspace argument, nothing allocated by the library)."""
     H, Np, d = q_p.shape
     topk = idx.shape[2]
-    a = make_args(H, N, d, block, q_p.dtype, n_anchor, context=context, fp8=fp8)
+    a = make_args(H, N, d, block, q_p.dtype, n_anchor, context=context, fp8=fp8, one_block=one_block)
     if out is None:
         out = torch.empty((H, N if perm_q is not None else Np, d), dtype=q_p.dtype, device=q_p.device)
     _check(lib().spark_attn_noalloc(ctypes.byref(a), _ptr(q_p), _ptr(k_p), _ptr(v_pt), _ptr(idx), topk,
@@ -287,10 +291,10 @@ def spark_diagnostics(q_p, k_p, idx, ksum, bias, N: int, block: int):
 
 def spark_layer(q, k, v, block: int, topk: int, layout: str = "reblock", summary: str = "reweight",
                 n_anchor: Optional[int] = None, out=None, ws=None, context: bool = False,
-                fp8: bool = False):
+                fp8: bool = False, one_block: bool = False):
     """The whole layer in one call; intermediates live in the workspace."""
     H, N, d = q.shape
-    a = make_args(H, N, d, block, q.dtype, n_anchor, layout, summary, context, fp8)
+    a = make_args(H, N, d, block, q.dtype, n_anchor, layout, summary, context, fp8, one_block)
     nws = workspace_bytes(a, OP_LAYER, topk)
     if ws is None:
         ws = _ws(nws, q.device)

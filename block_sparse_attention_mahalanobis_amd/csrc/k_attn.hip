@@ -26,6 +26,7 @@
 // nbc context blocks, followed by the compressed tiles; a context query block
 // attends exactly to all nbt blocks and has no compressed branch.  With
 // nbc = 0 this is the plain layer.
+#include <type_traits>
 #include "common.hpp"
 
 namespace spark {
@@ -838,6 +839,493 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
 }
 
 // ---------------------------------------------------------------------------
+// Paired query blocks (bf16 logits, d = 128, block 128, no context blocks).
+//
+// One workgroup of 8 waves owns two adjacent query blocks of one head (leaf
+// siblings of the split tree, whose top-k selections overlap the most):
+// waves 0-3 (group 0) the even block, waves 4-7 (group 1) the odd one; wave
+// w and wave w + 4 share a SIMD.  Each group visits nct + topk tiles in this
+// order: the compressed tiles, the exact blocks both groups selected, then
+// its own exact blocks.  Up to the end of the shared part one direct load of
+// a tile serves both groups, which removes the L2 -> LDS traffic of the
+// shared blocks' second copy (about a third of all tile bytes on the 768p
+// routing) and the power it costs.
+//
+// The groups run one slot apart.  In a group's matrix slot it streams P V of
+// its previous tile and then S^T of the current one (64 MFMAs); in its next
+// slot it computes that tile's softmax.  So in every slot one wave of each
+// SIMD feeds the matrix core while the other one runs its vector work, and
+// the latter also issues all of the slot's direct loads (issuing them
+// stalls a wave, which the matrix core cannot afford).  One workgroup
+// barrier ends each slot.  Four 32 KB buffers (K and V^T, two each) hold the
+// tiles; the slot in which each tile is loaded is fixed so that no buffer
+// is overwritten while a group still reads it:
+//   shared K(t) at slot 2t - 2 into K[t & 1]; shared V(t) at 2t + 1 into
+//   V[t & 1]; own K(t) of group g at 2t + g - 1 and own V(t) at 2t + g + 1
+//   into K/V[pb ^ g], pb the parity of the shared tile count.
+// Every wave waits for its own loads at the end of the slot, before the
+// barrier, so a tile loaded in slot s is complete in slot s + 1.  The row
+// sums add the fp32 p (not the bf16-rounded P): v_dot2c shares the matrix
+// core's issue and waits behind the other wave's MFMA stream.
+// ---------------------------------------------------------------------------
+constexpr int PAIR_NT = 512;
+// the tiles loaded in a slot (eight 1 KB direct loads each per loading wave)
+struct SlotLoads {
+  __amdgpu_buffer_rsrc_t rsk, rsv;   // the K tile and the V^T tile
+  int dk, dv;                        // their buffers (0/1)
+  bool hk, hv;                       // whether they are loaded
+};
+constexpr int PAIR_TB = 128 * 256;   // bytes of one bf16 K or V^T tile
+
+// LDS bytes of the paired kernel: 4 tiles, two bias rows, two block bitmaps,
+// the shared and the two own block lists, 32 counters, the slot table
+__host__ __device__ inline size_t pair_lds_bytes(int nb, int nbp, int topk) {
+  const int ntiles = ((topk < nb) ? nbp / 128 : 0) + topk;
+  return (size_t)4 * PAIR_TB + (size_t)2 * nbp * 4 + (size_t)2 * ((nb + 31) / 32) * 4 +
+         (size_t)3 * topk * 4 + 33 * 4 + (size_t)2 * (2 * ntiles + 2) * 8;
+}
+
+__global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
+    const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp,
+    const uint16_t* __restrict__ vpt, const int32_t* __restrict__ idx, int topk,
+    const uint16_t* __restrict__ ks16, const uint16_t* __restrict__ vs16t,
+    const float* __restrict__ bias2, const int32_t* __restrict__ perm_q,
+    uint16_t* __restrict__ out, int H, int N, int Nv, int nb, int nbp, float scale_log2) {
+  constexpr int D = 128, BK = 128;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const int nwb = (nb + 31) >> 5;
+  float* sBias0 = reinterpret_cast<float*>(smem + 4 * PAIR_TB);
+  uint32_t* sMap = reinterpret_cast<uint32_t*>(sBias0 + 2 * nbp);
+  int* sS = reinterpret_cast<int*>(sMap + 2 * nwb);
+  int* sP0 = sS + topk;
+  int* sP1 = sP0 + topk;
+  int* sCnt = sP1 + topk;
+  // per slot: the K tile and the V^T tile it loads (8-byte aligned: the
+  // counters end on a multiple of 8 bytes when 3 topk + 32 is even)
+  uint64_t* sSlot = reinterpret_cast<uint64_t*>(sCnt + 32 + ((3 * topk) & 1));
+
+  const int tid = threadIdx.x;
+  const int grp = __builtin_amdgcn_readfirstlane(tid >> 8);
+  const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
+  const int w8 = 4 * grp + wave;
+  const int tg = tid & 255, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+
+  // block pair: head-major, each head's pairs split into 8 contiguous ranges,
+  // one per XCD (consecutive workgroups go to consecutive XCDs)
+  const int npairs = (nb + 1) >> 1, ppx = (npairs + 7) >> 3;
+  const int h = blockIdx.x / (8 * ppx);
+  const int r = blockIdx.x - h * 8 * ppx;
+  const int pr = (r & 7) * ppx + (r >> 3);
+  if (pr >= npairs) return;   // the whole workgroup
+  // group 1 of an odd last pair repeats group 0's block and writes nothing
+  const bool idle = 2 * pr + grp >= nb;
+  const int A = idle ? 2 * pr : 2 * pr + grp;
+  const long Np = (long)nb * BK;
+  const int nct = (topk < nb) ? nbp / BK : 0;
+  const int ntiles = nct + topk;
+  const int32_t* myidx = idx + ((long)h * nb + A) * topk;
+
+  // ---- tile plan: shared blocks (in group 0's order) and each group's own
+  float* sBias = sBias0 + grp * nbp;
+  uint32_t* myMap = sMap + grp * nwb;
+  const uint32_t* otMap = sMap + (1 - grp) * nwb;
+  for (int i = tg; i < nwb; i += 256) myMap[i] = 0u;
+  for (int i = tid; i < 3 * topk; i += PAIR_NT) sS[i] = 0;   // block 0 where a list is short (bad input)
+  if (tid < 3) sCnt[18 + tid] = -1;   // list positions of the last block nb - 1
+  if (nct > 0)
+    for (int i = tg; i < nbp; i += 256) sBias[i] = bias2[(long)h * nbp + i];
+  __syncthreads();
+  for (int i = tg; i < topk; i += 256) {
+    const int B = min(max(myidx[i], 0), nb - 1);
+    atomicOr(&myMap[B >> 5], 1u << (B & 31));
+    if (nct > 0) sBias[B] = -INFINITY;
+  }
+  __syncthreads();
+  int cs = 0, cp = 0;
+  for (int c0 = 0; c0 < topk; c0 += 256) {
+    const int i = c0 + tg;
+    const bool valid = i < topk;
+    int B = 0;
+    bool sh = false;
+    if (valid) {
+      B = min(max(myidx[i], 0), nb - 1);
+      sh = (otMap[B >> 5] >> (B & 31)) & 1u;
+    }
+    const uint64_t bs = __builtin_amdgcn_ballot_w64(valid && sh);
+    const uint64_t bp = __builtin_amdgcn_ballot_w64(valid && !sh);
+    if (lane == 0) {
+      sCnt[grp * 8 + wave] = __builtin_popcountll(bs);
+      sCnt[grp * 8 + 4 + wave] = __builtin_popcountll(bp);
+    }
+    __syncthreads();
+    int os = cs, op = cp, ts = 0, tq = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int a = sCnt[grp * 8 + w], b = sCnt[grp * 8 + 4 + w];
+      if (w < wave) {
+        os += a;
+        op += b;
+      }
+      ts += a;
+      tq += b;
+    }
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int ps_ = os + __builtin_popcountll(bs & lt), pp_ = op + __builtin_popcountll(bp & lt);
+    if (valid && sh && grp == 0) {
+      sS[ps_] = B;
+      if (B == nb - 1) sCnt[18] = ps_;
+    }
+    if (valid && !sh && pp_ < topk) {
+      sS[(1 + grp) * topk + pp_] = B;
+      if (B == nb - 1) sCnt[19 + grp] = pp_;
+    }
+    cs += ts;
+    cp += tq;
+    __syncthreads();
+  }
+  if (tid == 0) sCnt[16] = cs;   // both groups go by group 0's count
+  __syncthreads();
+  const int ns = min(__builtin_amdgcn_readfirstlane(sCnt[16]), topk);
+  const int Tsh = nct + ns;   // shared tiles
+  const int pb = Tsh & 1;
+
+  // step of this group's last block nb - 1 (its padded keys get -inf), or -1
+  const int tlast = __builtin_amdgcn_readfirstlane(
+      (sCnt[18] >= 0) ? nct + sCnt[18] : ((sCnt[19 + grp] >= 0) ? Tsh + sCnt[19 + grp] : -1));
+  // buffer (0/1) of step t of group g; K at smem + buf * TB, V^T at smem + (2 + buf) * TB
+  auto buf_of = [&](int g, int t) -> int { return (t < Tsh) ? (t & 1) : (pb ^ g); };
+
+  // every K, V^T and summary tile is 32 contiguous KB: per-head bases
+  const char* kb_h = reinterpret_cast<const char*>(kp + (long)h * Np * D);
+  const char* vb_h = reinterpret_cast<const char*>(vpt + (long)h * nb * D * BK);
+  const char* ksb_h = reinterpret_cast<const char*>(ks16 + (long)h * nbp * D);
+  const char* vsb_h = reinterpret_cast<const char*>(vs16t + (long)h * nbp * D);
+
+  // ---- slot table: the K tile and the V^T tile each slot loads, as the
+  // tile's address with its buffer (0/1) in bit 48; 0 if none.  Built once,
+  // so the loop needs no tile bookkeeping.
+  const int nslots = 2 * ntiles + 2;
+  {
+    // address of the K (v = 0) or V^T (v = 1) tile of step t of group g
+    auto step_src = [&](int g, int t, int v) -> uint64_t {
+      if (t < nct) return (uint64_t)((v ? vsb_h : ksb_h) + ((long)t << 15));
+      const int o = (t < Tsh) ? t - nct : (g + 1) * topk + t - Tsh;
+      return (uint64_t)((v ? vb_h : kb_h) + ((long)sS[o] << 15));
+    };
+    for (int sl = tid; sl < nslots; sl += PAIR_NT) {
+      uint64_t rk = 0, rv = 0;
+      if ((sl & 1) == 0) {
+        const int ta = (sl >> 1) + 1;   // shared K(ta)
+        const int td = sl >> 1;         // group 1's own K(td)
+        const int tf = (sl >> 1) - 1;   // group 1's own V(tf)
+        if (ta < Tsh && ta < ntiles) rk = ((uint64_t)(ta & 1) << 48) | step_src(0, ta, 0);
+        else if (td >= Tsh && td < ntiles) rk = ((uint64_t)(pb ^ 1) << 48) | step_src(1, td, 0);
+        if (tf >= Tsh && tf >= 0 && tf < ntiles) rv = ((uint64_t)(pb ^ 1) << 48) | step_src(1, tf, 1);
+      } else {
+        const int tb = (sl - 1) >> 1;   // shared V(tb), or group 0's own V(tb)
+        const int tc = (sl + 1) >> 1;   // group 0's own K(tc)
+        if (tb < ntiles) rv = ((uint64_t)buf_of(0, tb) << 48) | step_src(0, tb, 1);
+        if (tc >= Tsh && tc < ntiles) rk = ((uint64_t)pb << 48) | step_src(0, tc, 0);
+      }
+      sSlot[2 * sl] = rk;
+      sSlot[2 * sl + 1] = rv;
+    }
+  }
+  // step 0's K of group 0 (shared, or its own when nothing is shared)
+  const char* k0src = (nct > 0) ? ksb_h : kb_h + ((long)sS[(Tsh > 0) ? 0 : topk] << 15);
+  __syncthreads();
+
+  // In every slot the group that is not in its matrix slot loads the slot's
+  // tiles (a direct load stalls the issuing wave, which the matrix core
+  // cannot afford).  Load j (0..7) of a tile by wave w of that group fills
+  // LDS rows srow = 32 w + 4 j + (lane >> 4) (1 KB), the 16-byte chunk
+  // XOR-swizzled by srow & 15.  V^T rows come in order; K rows in the
+  // permuted order that makes the S^T accumulator the P^T operand, which
+  // swaps bits 2 and 3 of the row: the source row is srow + ((j & 1) -
+  // ((j >> 1) & 1)) * 4.  K and V share the lane offsets of j & 3; the 4096
+  // of j >= 4 and the +-1024 of K go into the scalar offset, with load 2's
+  // lane offset stored 1024 low (it is at least 2048).  (An immediate offset
+  // would also move the LDS destination.)
+  uint32_t loff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r4 = 4 * i + (lane >> 4);
+    const int lc = (lane & 15) ^ r4;
+    loff[i] = (uint32_t)(8192 * wave + r4 * 256 + lc * 16) - (i == 2 ? 1024u : 0u);
+  }
+  auto mk_rsrc = [&](const char* src) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, PAIR_TB, 0x00020000);
+  };
+  // the tiles loaded in slot s, from the slot table
+  auto plan_loads = [&](int s) {
+    const uint64_t rk = sSlot[2 * s], rv = sSlot[2 * s + 1];
+    const uint32_t klo = __builtin_amdgcn_readfirstlane((uint32_t)rk);
+    const uint32_t khi = __builtin_amdgcn_readfirstlane((uint32_t)(rk >> 32));
+    const uint32_t vlo = __builtin_amdgcn_readfirstlane((uint32_t)rv);
+    const uint32_t vhi = __builtin_amdgcn_readfirstlane((uint32_t)(rv >> 32));
+    SlotLoads L;
+    L.hk = (klo | khi) != 0;
+    L.hv = (vlo | vhi) != 0;
+    L.dk = (khi >> 16) & 1;
+    L.dv = (vhi >> 16) & 1;
+    L.rsk = mk_rsrc(reinterpret_cast<const char*>(((uint64_t)(khi & 0xffffu) << 32) | klo));
+    L.rsv = mk_rsrc(reinterpret_cast<const char*>(((uint64_t)(vhi & 0xffffu) << 32) | vlo));
+    return L;
+  };
+  // load l (a constant) of a slot: 0..7 the K tile, 8..15 the V^T tile
+  auto issue_load = [&](const SlotLoads& L, int l) {
+    const int j = l & 7, i = j & 3;
+    if (l < 8) {
+      if (!L.hk) return;
+      auto lp = (void __attribute__((address_space(3)))*)(smem + L.dk * PAIR_TB + (8 * wave + j) * 1024);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(L.rsk, lp, 16, loff[i], 4096 * (j >> 2) + (i == 1 ? 1024 : 0), 0, 0);
+    } else {
+      if (!L.hv) return;
+      auto lp = (void __attribute__((address_space(3)))*)(smem + (2 + L.dv) * PAIR_TB + (8 * wave + j) * 1024);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(L.rsv, lp, 16, loff[i], 4096 * (j >> 2) + (i == 2 ? 1024 : 0), 0, 0);
+    }
+  };
+
+  const long qrow = (long)h * Np + (long)A * BK + wave * 32 + l32;
+  bf16x8 qop[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) qop[s] = *reinterpret_cast<const bf16x8*>(qp + qrow * D + 16 * s + 8 * hf);
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oacc[t][v] = 0.f;
+  float m_ref = -1e30f, l_run = 0.f;
+  int ro[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) ro[s] = sw_off(l32, 2 * s + hf);
+
+  // step 0's K (shared, or group 0's own when nothing is shared)
+  {
+    SlotLoads L0;
+    L0.rsk = L0.rsv = mk_rsrc(k0src);
+    L0.dk = L0.dv = 0;
+    L0.hk = true;
+    L0.hv = false;
+    if (grp == 1) {   // group 1 has no matrix slot before slot 1
+#pragma unroll
+      for (int l = 0; l < 8; ++l) issue_load(L0, l);
+    }
+  }
+  f32x16 sacc[4];
+  bf16x8 pop[8];
+  // every slot starts when all its tiles have landed and every wave is done
+  // with the previous slot's LDS reads
+  auto slot_begin = [&](int s) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    d128_barrier();
+    return plan_loads(s);
+  };
+  auto issue_all = [&](const SlotLoads& L) {
+#pragma unroll
+    for (int l = 0; l < 16; ++l) issue_load(L, l);
+  };
+  // matrix slot of step t: P V of step t - 1 (PV), then S^T of step t (QK)
+  auto matrix_slot = [&](auto pv_tag, auto qk_tag, int t, const SlotLoads&) {
+    constexpr bool PV = decltype(pv_tag)::value, QK = decltype(qk_tag)::value;
+    __builtin_amdgcn_s_setprio(2);
+    if constexpr (PV) {
+      // the K tile loads ride along, one per k step
+      const unsigned char* sV = smem + (2 + buf_of(grp, t - 1)) * PAIR_TB;
+      bf16x8 vop[BK / 16][4];
+#pragma unroll
+      for (int k = 0; k < D128_PF; ++k)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) vop[k][dt] = *reinterpret_cast<const bf16x8*>(sV + ro[k] + dt * 8192);
+#pragma unroll
+      for (int k = 0; k < BK / 16; ++k) {
+        if (k + D128_PF < BK / 16) {
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+            vop[k + D128_PF][dt] = *reinterpret_cast<const bf16x8*>(sV + ro[k + D128_PF] + dt * 8192);
+        }
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[k][dt], pop[k], oacc[dt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if constexpr (QK) {
+      const unsigned char* sK = smem + buf_of(grp, t) * PAIR_TB;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sacc[jt][v] = 0.f;
+      bf16x8 kop[D / 16][4];
+#pragma unroll
+      for (int k = 0; k < D128_PF; ++k)
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) kop[k][jt] = *reinterpret_cast<const bf16x8*>(sK + ro[k] + jt * 8192);
+#pragma unroll
+      for (int k = 0; k < D / 16; ++k) {
+        if (k + D128_PF < D / 16) {
+#pragma unroll
+          for (int jt = 0; jt < 4; ++jt)
+            kop[k + D128_PF][jt] = *reinterpret_cast<const bf16x8*>(sK + ro[k + D128_PF] + jt * 8192);
+        }
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt)
+          sacc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[k][jt], qop[k], sacc[jt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // keys past the end of the last block get -inf logits (in the matrix
+  // slot, where P is dead); the valid row count is opaque to the compiler so
+  // that the compares stay in this rarely taken branch
+  auto mask_tail = [&](int t) {
+    if (t == tlast) {
+      int valid;
+      asm volatile("s_mov_b32 %0, %1" : "=s"(valid) : "s"(Nv - (nb - 1) * BK));
+      const int vb = valid - 8 * hf;   // key j = 8 hf + c, c a constant per element
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int c = 32 * jt + ((v < 8) ? v : 8 + v);
+          if (c >= vb) sacc[jt][v] = -INFINITY;
+        }
+    }
+  };
+  // softmax slot of step t, against the lazy reference m_ref (as in
+  // attn_mfma_d128: no per-tile maximum unless a row half's sum exceeds 2^12).
+  // Exact tiles hold raw logits (the scale goes into the exp argument),
+  // compressed tiles scaled and biased ones.
+  auto softmax_slot = [&](auto exact_tag, int t, const SlotLoads& L) {
+    constexpr bool EXACT = decltype(exact_tag)::value;
+    if constexpr (!EXACT) {
+      // element v of 32-key group jt is key 32 jt + 8 hf + v (v < 8) or
+      // 32 jt + 16 + 8 hf + v - 8: four runs of 8 consecutive biases
+      const float* bb = sBias + t * BK + 8 * hf;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        float4 b4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) b4[u] = *reinterpret_cast<const float4*>(bb + 32 * jt + 16 * (u >> 1) + 4 * (u & 1));
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float4 q4 = b4[v >> 2];
+          const float bv = ((v & 3) == 0) ? q4.x : ((v & 3) == 1) ? q4.y : ((v & 3) == 2) ? q4.z : q4.w;
+          sacc[jt][v] = fmaf(sacc[jt][v], scale_log2, bv);
+        }
+      }
+    }
+    const float sc = EXACT ? scale_log2 : 1.f;
+    // the row sums add the fp32 p with plain adds: v_dot2c shares the matrix
+    // core's issue and stalls behind the other wave's MFMA stream
+    float psum;
+    {
+      const float nm = -m_ref;
+      float ps[2] = {0.f, 0.f};
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[jt][8 * hh + e], sc, nm));
+            pop[2 * jt + hh][e] = (__bf16)pv;
+            ps[e & 1] += pv;
+          }
+          issue_load(L, 2 * (2 * jt + hh));
+          issue_load(L, 2 * (2 * jt + hh) + 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      psum = ps[0] + ps[1];
+    }
+    if (__builtin_amdgcn_ballot_w64(!(psum <= 4096.f)) != 0) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[jt][v]);
+      if (EXACT) mx *= sc;
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
+      const float nm = -m_ref;
+      float ps[2] = {0.f, 0.f};
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[jt][8 * hh + e], sc, nm));
+            pop[2 * jt + hh][e] = (__bf16)pv;
+            ps[e & 1] += pv;
+          }
+      psum = ps[0] + ps[1];
+    }
+    l_run += psum;
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  // group g runs matrix(t) in slot 2t + g and softmax(t) in slot 2t + 1 + g;
+  // group 1 starts with an empty slot 0, group 0 ends with an empty slot
+  // 2 ntiles + 1, so both pass the same 2 ntiles + 2 barriers.  Step 0 and
+  // the last matrix slot are peeled, and the compressed and exact steps run
+  // in loops of their own, so the steady loops carry no step tests.
+  if (grp == 1) issue_all(slot_begin(0));
+  matrix_slot(F_{}, T_{}, 0, slot_begin(grp));
+  if (nct > 0) {
+    softmax_slot(F_{}, 0, slot_begin(1 + grp));
+  } else {
+    mask_tail(0);
+    softmax_slot(T_{}, 0, slot_begin(1 + grp));
+  }
+  for (int t = 1; t < nct; ++t) {
+    matrix_slot(T_{}, T_{}, t, slot_begin(2 * t + grp));
+    softmax_slot(F_{}, t, slot_begin(2 * t + 1 + grp));
+  }
+  for (int t = max(nct, 1); t < ntiles; ++t) {
+    matrix_slot(T_{}, T_{}, t, slot_begin(2 * t + grp));
+    mask_tail(t);
+    softmax_slot(T_{}, t, slot_begin(2 * t + 1 + grp));
+  }
+  matrix_slot(T_{}, F_{}, ntiles, slot_begin(2 * ntiles + grp));
+  if (grp == 0) issue_all(slot_begin(2 * ntiles + 1));
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (idle) return;
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = 1.f / l_tot;
+  const long pos = out_pos(A, wave * 32 + l32, nb, N, Nv, BK);
+  uint16_t* dst;
+  if (perm_q != nullptr) {
+    if (pos < 0) return;
+    dst = out + ((long)h * N + perm_q[(long)h * N + pos]) * D;
+  } else {
+    dst = out + ((long)h * Np + (long)A * BK + wave * 32 + l32) * D;
+  }
+  const bool pad = pos < 0;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      float o[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[c] = pad ? 0.f : oacc[dt][4 * a + c] * inv;
+      uint2 w;
+      w.x = pack_bf2(o[0], o[1]);
+      w.y = pack_bf2(o[2], o[3]);
+      *reinterpret_cast<uint2*>(dst + 32 * dt + 8 * a + 4 * hf) = w;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Generic VALU kernel: one thread per query row of the block.
 // ---------------------------------------------------------------------------
 constexpr int GEN_CH = 32;  // keys per staged chunk
@@ -1031,7 +1519,7 @@ static int launch_mfma(const void* qp, const void* kp, const void* vpt, const in
 static int launch_d128(const void* qp, const void* kp, const void* vpt, const int32_t* idx, int topk,
                      const uint16_t* ks16, const uint16_t* vs16t, const float* bias2,
                      const int32_t* perm_q, void* out, int H, int N, int Nv, int nb, int nbc,
-                     int nbp, bool fp8, const float* kscale, const float* ksscale, hipStream_t st) {
+                     int nbp, bool fp8, bool paired, const float* kscale, const float* ksscale, hipStream_t st) {
   const size_t lds = D128_LDS_TILES + (size_t)nbp * 4;
   static bool attr_set = false;
   if (!attr_set) {
@@ -1042,6 +1530,19 @@ static int launch_d128(const void* qp, const void* kp, const void* vpt, const in
     attr_set = true;
   }
   const float scale_log2 = kLog2e / sqrtf(128.f);
+  if (paired && !fp8 && nbc == 0 && pair_lds_bytes(nb, nbp, topk) <= 160 * 1024) {
+    static bool pair_attr_set = false;
+    if (!pair_attr_set) {
+      hipFuncSetAttribute((const void*)attn_pair_d128, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      pair_attr_set = true;
+    }
+    const long pslots = 8L * (((nb + 1) / 2 + 7) / 8);
+    if ((long)H * pslots > 0x7fffffffL) return spark_set_error(SPARK_E_SHAPE, "spark_attn: grid too large");
+    hipLaunchKernelGGL(attn_pair_d128, dim3((unsigned)(H * pslots)), dim3(PAIR_NT), pair_lds_bytes(nb, nbp, topk), st,
+                       (const uint16_t*)qp, (const uint16_t*)kp, (const uint16_t*)vpt, idx, topk, ks16, vs16t,
+                       bias2, perm_q, (uint16_t*)out, H, N, Nv, nb, nbp, scale_log2);
+    return spark_check_launch("attn_pair_d128");
+  }
   const long slots = 8L * (((nbc + 7) >> 3) + ((nb + 7) >> 3));   // d128_slots
   if ((long)H * slots > 0x7fffffffL) return spark_set_error(SPARK_E_SHAPE, "spark_attn: grid too large");
   const dim3 grid((unsigned)(H * slots)), block(D128_NT);
@@ -1078,11 +1579,12 @@ int quant_e4m3_launch(int H, long in_rows, long out_rows, int D, int G, int dtyp
                       uint8_t* x8, float* scales, hipStream_t st);
 
 // Nv = N: the plain layer; Nv < N: tokens [Nv, N) are context tokens.  fp8:
-// E4M3 logits (the caller has checked attn_fp8_supported).
+// E4M3 logits (the caller has checked attn_fp8_supported).  paired: the bf16
+// d = 128 / block 128 layer may run two query blocks per workgroup.
 int attn_launch(int H, int N, int Nv, int D, int BK, int dtype, const void* qp, const void* kp,
                 const void* vpt, const int32_t* idx, int topk, const float* ksum,
                 const float* vsum, const float* bias, const int32_t* perm_q, void* out, void* ws,
-                bool fp8, hipStream_t st) {
+                bool fp8, bool paired, hipStream_t st) {
   const int nb = cdiv(Nv, BK), nbc = cdiv(N - Nv, BK);
   if (attn_uses_mfma(dtype, BK)) {
     const int nbp = cdiv(nb, BK) * BK;
@@ -1108,12 +1610,12 @@ int attn_launch(int H, int N, int Nv, int D, int BK, int dtype, const void* qp, 
       rc = quant_e4m3_launch(H, nb, nbp, D, BK, SPARK_F32, ksum, ks8, ksscale, st);
       if (rc) return rc;
       return launch_d128(qp, k8, vpt, idx, topk, (const uint16_t*)ks8, vs16t, bias2, perm_q, out, H, N, Nv,
-                         nb, nbc, nbp, true, kscale, ksscale, st);
+                         nb, nbc, nbp, true, false, kscale, ksscale, st);
     }
     if (D == 128) {
       if (BK == 128 && (size_t)D128_LDS_TILES + (size_t)nbp * 4 <= 80 * 1024)
         return launch_d128(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, Nv, nb, nbc, nbp,
-                           false, nullptr, nullptr, st);
+                           false, paired, nullptr, nullptr, st);
       if (BK == 128) return launch_mfma<128, 128>(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, Nv, nb, nbc, nbp, st);
       if (BK == 64) return launch_mfma<128, 64>(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, Nv, nb, nbc, nbp, st);
       return launch_mfma<128, 32>(qp, kp, vpt, idx, topk, ks16, vs16t, bias2, perm_q, out, H, N, Nv, nb, nbc, nbp, st);

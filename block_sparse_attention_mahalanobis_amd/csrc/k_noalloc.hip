@@ -24,7 +24,7 @@ namespace spark {
 int attn_launch(int H, int N, int Nv, int D, int BK, int dtype, const void* qp, const void* kp,
                 const void* vpt, const int32_t* idx, int topk, const float* ksum,
                 const float* vsum, const float* bias, const int32_t* perm_q, void* out, void* ws,
-                bool fp8, hipStream_t st);
+                bool fp8, bool paired, hipStream_t st);
 
 constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(64) << 20;   // 64 MiB per GPU
 constexpr int NOALLOC_MAX_DEVICES = 64;
@@ -63,12 +63,12 @@ static int scratch_address(void** out) {
 int attn_noalloc_launch(int H, int N, int Nv, int D, int BK, int dtype, const void* qp, const void* kp,
                         const void* vpt, const int32_t* idx, int topk, const float* ksum,
                         const float* vsum, const float* bias, const int32_t* perm_q, void* out,
-                        bool fp8, hipStream_t st) {
+                        bool fp8, bool paired, hipStream_t st) {
   void* ws = nullptr;
   const int rc = scratch_address(&ws);
   if (rc) return rc;
   return attn_launch(H, N, Nv, D, BK, dtype, qp, kp, vpt, idx, topk, ksum, vsum, bias, perm_q, out, ws,
-                     fp8, st);
+                     fp8, paired, st);
 }
 
 }  // namespace spark

@@ -15,7 +15,7 @@ namespace spark {
 int attn_launch(int H, int N, int Nv, int D, int BK, int dtype, const void* qp, const void* kp,
                 const void* vpt, const int32_t* idx, int topk, const float* ksum,
                 const float* vsum, const float* bias, const int32_t* perm_q, void* out, void* ws,
-                bool fp8, hipStream_t st);
+                bool fp8, bool paired, hipStream_t st);
 size_t attn_ws_bytes(int H, int N, int Nv, int D, int BK, int dtype, bool fp8);
 bool attn_fp8_supported(int H, int N, int Nv, int D, int BK, int dtype);
 int quant_e4m3_launch(int H, long in_rows, long out_rows, int D, int G, int dtype, const void* x,
@@ -56,7 +56,7 @@ size_t noalloc_scratch_bytes();
 int attn_noalloc_launch(int H, int N, int Nv, int D, int BK, int dtype, const void* qp, const void* kp,
                         const void* vpt, const int32_t* idx, int topk, const float* ksum,
                         const float* vsum, const float* bias, const int32_t* perm_q, void* out,
-                        bool fp8, hipStream_t st);
+                        bool fp8, bool paired, hipStream_t st);
 int diag_launch(int H, int N, int D, int BK, int dtype, const void* qp, const void* kp,
                 const int32_t* idx, int topk, const float* ksum, const float* bias, float* recall,
                 float* logmass, hipStream_t st);
@@ -120,7 +120,8 @@ int check_args(const spark_args* a, const char* fn) {
     return spark_set_error(SPARK_E_SHAPE, "%s: n_anchor=%d not in [1, N=%d]", fn, a->n_anchor, a->N);
   const uint32_t layout = a->flags & SPARK_LAYOUT_MASK;
   if (layout > SPARK_LAYOUT_Q_REUSE_K ||
-      (a->flags & ~(SPARK_LAYOUT_MASK | SPARK_SUMMARY_MEAN | SPARK_CONTEXT_EXACT | SPARK_EXACT_FP8)))
+      (a->flags & ~(SPARK_LAYOUT_MASK | SPARK_SUMMARY_MEAN | SPARK_CONTEXT_EXACT | SPARK_EXACT_FP8 |
+                    SPARK_ATTN_ONE_BLOCK)))
     return spark_set_error(SPARK_E_ARG, "%s: bad flags 0x%x", fn, a->flags);
   const long nb = (a->N + (long)a->block - 1) / a->block;
   if ((long)a->H * nb > 0x7fffffffL || (long)a->N * a->d > 0x7fffffffL)
@@ -488,7 +489,7 @@ int spark_attn(const spark_args* a, const void* q_p, const void* k_p, const void
     if (ws_bytes < need) return spark_set_error(SPARK_E_WORKSPACE, "%s: ws_bytes %zu < %zu", fn, ws_bytes, need);
   }
   return attn_launch(a->H, a->N, Nv, a->d, a->block, a->dtype, q_p, k_p, v_pt, idx, topk, ksum, vsum,
-                     bias, perm_q, out, ws, fp8_of(a), (hipStream_t)stream);
+                     bias, perm_q, out, ws, fp8_of(a), !(a->flags & SPARK_ATTN_ONE_BLOCK), (hipStream_t)stream);
 }
 
 size_t spark_attn_noalloc_scratch_bytes(void) { return noalloc_scratch_bytes(); }
@@ -517,7 +518,8 @@ int spark_attn_noalloc(const spark_args* a, const void* q_p, const void* k_p, co
                            "allocation-free entry point holds %zu (use spark_attn with a workspace)",
                            fn, need, noalloc_scratch_bytes());
   return attn_noalloc_launch(a->H, a->N, Nv, a->d, a->block, a->dtype, q_p, k_p, v_pt, idx, topk, ksum, vsum,
-                             bias, perm_q, out, fp8_of(a), (hipStream_t)stream);
+                             bias, perm_q, out, fp8_of(a), !(a->flags & SPARK_ATTN_ONE_BLOCK),
+                             (hipStream_t)stream);
 }
 
 int spark_layer(const spark_args* a, const void* q, const void* k, const void* v, int32_t topk,

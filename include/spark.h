@@ -110,6 +110,14 @@ typedef enum spark_dtype { SPARK_F32 = 0, SPARK_BF16 = 1 } spark_dtype;
  * spark_attn / spark_layer kernels); SPARK_E_UNSUPPORTED otherwise, and
  * from spark_diagnostics. */
 #define SPARK_EXACT_FP8 0x10u
+/* flags: schedule choice for the bf16, d = 128, block = 128 attention of
+ * spark_attn, spark_attn_noalloc and spark_layer (other entry points ignore
+ * it).  By default, where the layer has no context tokens and the tiles fit
+ * in LDS, one workgroup runs two adjacent query blocks and loads the key
+ * blocks both selected once for both; this flag keeps one query block per
+ * workgroup.  Both compute the same quantity; the outputs differ only in
+ * fp32 rounding order (the tiles are visited in another order). */
+#define SPARK_ATTN_ONE_BLOCK 0x20u
 
 typedef struct spark_args {
   int32_t H;        /* heads                                                  */
@@ -119,7 +127,7 @@ typedef struct spark_args {
   int32_t dtype;    /* spark_dtype of q, k, v                                 */
   int32_t n_anchor; /* the anchor averages query rows [0, n_anchor); 1..N     */
   uint32_t flags;   /* SPARK_LAYOUT_* | SPARK_SUMMARY_* | SPARK_CONTEXT_EXACT |
-                       SPARK_EXACT_FP8 */
+                       SPARK_EXACT_FP8 | SPARK_ATTN_ONE_BLOCK */
   int32_t reserved; /* must be 0                                              */
 } spark_args;
 
