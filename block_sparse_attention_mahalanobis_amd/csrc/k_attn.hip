@@ -1130,7 +1130,6 @@ __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
     constexpr bool PV = decltype(pv_tag)::value, QK = decltype(qk_tag)::value;
     __builtin_amdgcn_s_setprio(2);
     if constexpr (PV) {
-      // the K tile loads ride along, one per k step
       const unsigned char* sV = smem + (2 + buf_of(grp, t - 1)) * PAIR_TB;
       bf16x8 vop[BK / 16][4];
 #pragma unroll
