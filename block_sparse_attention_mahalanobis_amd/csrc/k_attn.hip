@@ -877,12 +877,16 @@ struct SlotLoads {
 };
 constexpr int PAIR_TB = 128 * 256;   // bytes of one bf16 K or V^T tile
 
-// LDS bytes of the paired kernel: 4 tiles, two bias rows, two block bitmaps,
-// the shared and the two own block lists, 32 counters, the slot table
+// LDS bytes of the paired kernel: 4 tiles, two bias rows, the slot table.
+// The plan's scratch (two block bitmaps, the shared and the two own block
+// lists, 32 counters) lives in the second K buffer, which no load touches
+// before the slot table is built; a plan that would not fit there returns
+// a size no workgroup gets.
 __host__ __device__ inline size_t pair_lds_bytes(int nb, int nbp, int topk) {
   const int ntiles = ((topk < nb) ? nbp / 128 : 0) + topk;
-  return (size_t)4 * PAIR_TB + (size_t)2 * nbp * 4 + (size_t)2 * ((nb + 31) / 32) * 4 +
-         (size_t)3 * topk * 4 + 33 * 4 + (size_t)2 * (2 * ntiles + 2) * 8;
+  const size_t plan = (size_t)2 * ((nb + 31) / 32) * 4 + (size_t)3 * topk * 4 + 32 * 4;
+  if (plan > (size_t)PAIR_TB) return ~(size_t)0;
+  return (size_t)4 * PAIR_TB + (size_t)2 * nbp * 4 + (size_t)2 * (2 * ntiles + 2) * 8;
 }
 
 __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
@@ -895,14 +899,14 @@ __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int nwb = (nb + 31) >> 5;
   float* sBias0 = reinterpret_cast<float*>(smem + 4 * PAIR_TB);
-  uint32_t* sMap = reinterpret_cast<uint32_t*>(sBias0 + 2 * nbp);
+  // per slot: the K tile and the V^T tile it loads
+  uint64_t* sSlot = reinterpret_cast<uint64_t*>(sBias0 + 2 * nbp);
+  // plan scratch, in K buffer 1 (first loaded in slot 0, after the plan)
+  uint32_t* sMap = reinterpret_cast<uint32_t*>(smem + PAIR_TB);
   int* sS = reinterpret_cast<int*>(sMap + 2 * nwb);
   int* sP0 = sS + topk;
   int* sP1 = sP0 + topk;
   int* sCnt = sP1 + topk;
-  // per slot: the K tile and the V^T tile it loads (8-byte aligned: the
-  // counters end on a multiple of 8 bytes when 3 topk + 32 is even)
-  uint64_t* sSlot = reinterpret_cast<uint64_t*>(sCnt + 32 + ((3 * topk) & 1));
 
   const int tid = threadIdx.x;
   const int grp = __builtin_amdgcn_readfirstlane(tid >> 8);

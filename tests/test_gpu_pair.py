@@ -117,3 +117,66 @@ def test_pair_full_density_odd_block_count():
     say(f"[pair] full density nb={nb}: {e:.3e}")
     assert e <= 1e-2 and np.abs(outs[False] - want).max() <= 3e-2
     assert rel_l2(outs[False], outs[True]) <= 5e-3
+
+
+@pytest.mark.parametrize("N,topk", [(100, 1), (200, 1), (200, 2), (300, 3)])
+def test_pair_tiny_block_counts(N, topk):
+    """n_b = 1 (a lone block, group 1 idle), 2 and 3, including full density."""
+    want, outs = _run(N, topk, "random", seed=N + topk)
+    assert rel_l2(outs[False], want) <= 1e-2 and np.abs(outs[False] - want).max() <= 3e-2
+    assert rel_l2(outs[False], outs[True]) <= 5e-3
+
+
+def test_large_block_count_falls_back_to_one_block():
+    """n_b = 3,500 at 10%: the paired plan no longer fits in LDS, so the
+    default takes the one-block kernel (bit-identical to SPARK_ATTN_ONE_BLOCK);
+    sampled query blocks against the oracle."""
+    rng = np.random.default_rng(21)
+    N, d = 3500 * B - 17, 128
+    nb = O.n_blocks(N, B)
+    topk = O.topk_from_ratio(0.1, nb)
+    q, k, v = (round_to_bf16(rng.standard_normal((N, d)).astype(np.float32)) for _ in range(3))
+    idx = _routing("random", nb, topk, rng)[None]
+    ks, vs, bias = O.reweight_summaries(k, v, O.anchor_query(q, N), B)
+    t = lambda a, dt=torch.bfloat16: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV).to(dt)
+    g = L.spark_reblock(t(q[None]), t(k[None]), t(v[None]), B, layout="identity")
+    f = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float32)[None]).to(DEV)
+    outs = [L.spark_attn(g["q_p"], g["k_p"], g["v_pt"], torch.from_numpy(idx).to(DEV), f(ks), f(vs), f(bias),
+                         N, B, perm_q=g["perm_q"], one_block=one) for one in (False, True)]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    blocks = [0, 1, nb // 2, nb - 2, nb - 1]
+    want = O.sparse_attention(q, k, v, idx[0], ks, vs, bias, B, qblocks=blocks)
+    got = outs[0][0].float().cpu().numpy().astype(np.float64)
+    rows = np.concatenate([np.arange(A * B, min(N, (A + 1) * B)) for A in blocks])
+    e = rel_l2(got[rows], want[rows])
+    say(f"[pair] fallback nb={nb}: sampled rel-L2 {e:.3e}")
+    assert e <= 1e-2 and np.abs(got[rows] - want[rows]).max() <= 3e-2
+
+
+@pytest.mark.parametrize("ratio", [0.1, 0.2])
+def test_pair_at_the_768p_block_count(ratio):
+    """n_b = 1922 at 10% and 20% (the largest slot tables the paired plan
+    takes at this size): sampled query blocks against the oracle and the
+    whole output against the one-block kernel."""
+    rng = np.random.default_rng(int(ratio * 100))
+    N, d = 245952, 128
+    nb = O.n_blocks(N, B)
+    topk = O.topk_from_ratio(ratio, nb)
+    q, k, v = (round_to_bf16(rng.standard_normal((N, d)).astype(np.float32)) for _ in range(3))
+    idx = _routing("random", nb, topk, rng)[None]
+    ks, vs, bias = O.reweight_summaries(k, v, O.anchor_query(q, N), B)
+    t = lambda a, dt=torch.bfloat16: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV).to(dt)
+    g = L.spark_reblock(t(q[None]), t(k[None]), t(v[None]), B, layout="identity")
+    f = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float32)[None]).to(DEV)
+    outs = [L.spark_attn(g["q_p"], g["k_p"], g["v_pt"], torch.from_numpy(idx).to(DEV), f(ks), f(vs), f(bias),
+                         N, B, perm_q=g["perm_q"], one_block=one) for one in (False, True)]
+    torch.cuda.synchronize()
+    a0, a1 = (o[0].float().cpu().numpy().astype(np.float64) for o in outs)
+    assert rel_l2(a0, a1) <= 5e-3
+    blocks = [0, 1, 2, 3, nb // 2, nb // 2 + 1, nb - 2, nb - 1]
+    want = O.sparse_attention(q, k, v, idx[0], ks, vs, bias, B, qblocks=blocks)
+    rows = np.concatenate([np.arange(A * B, min(N, (A + 1) * B)) for A in blocks])
+    e = rel_l2(a0[rows], want[rows])
+    say(f"[pair] nb={nb} topk={topk}: sampled rel-L2 {e:.3e}, vs one-block {rel_l2(a0, a1):.3e}")
+    assert e <= 1e-2 and np.abs(a0[rows] - want[rows]).max() <= 3e-2
