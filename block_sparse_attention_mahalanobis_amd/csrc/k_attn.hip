@@ -341,8 +341,8 @@ __device__ __forceinline__ int sw_off(int row, int lc) {  // byte offset in a 12
 __device__ __forceinline__ int d128_slots(int nb, int nbc) {  // workgroups per head
   return 8 * (((nbc + 7) >> 3) + ((nb + 7) >> 3));
 }
-__device__ __forceinline__ bool d128_map(int bid, int nb, int nbc, int& h, int& A) {
-  const int cpx = (nbc + 7) >> 3, vpx = (nb + 7) >> 3;
+__device__ __forceinline__ bool d128_map(int bid, int nb, int nbc, int& h, int& A, bool ctx_only = false) {
+  const int cpx = (nbc + 7) >> 3, vpx = ctx_only ? 0 : (nb + 7) >> 3;
   const int R = 8 * (cpx + vpx);
   h = bid / R;
   const int r = bid - h * R;
@@ -451,7 +451,7 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
     const uint16_t* __restrict__ ks16, const uint16_t* __restrict__ vs16t,
     const float* __restrict__ bias2, const int32_t* __restrict__ perm_q,
     uint16_t* __restrict__ out, int H, int N, int Nv, int nb, int nbc, int nbp, float scale_log2,
-    const float* __restrict__ kscale, const float* __restrict__ ksscale) {
+    const float* __restrict__ kscale, const float* __restrict__ ksscale, int ctx_only) {
   constexpr int D = 128, BK = 128;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   unsigned char* sK = smem;
@@ -460,7 +460,7 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
 
   if constexpr (!CTX) nbc = 0;
   int h, A;
-  if (!d128_map(blockIdx.x, nb, nbc, h, A)) return;
+  if (!d128_map(blockIdx.x, nb, nbc, h, A, ctx_only != 0)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // the wave index as a scalar: every LDS destination of a direct load is
@@ -882,8 +882,8 @@ constexpr int PAIR_TB = 128 * 256;   // bytes of one bf16 K or V^T tile
 // lists, 32 counters) lives in the second K buffer, which no load touches
 // before the slot table is built; a plan that would not fit there returns
 // a size no workgroup gets.
-__host__ __device__ inline size_t pair_lds_bytes(int nb, int nbp, int topk) {
-  const int ntiles = ((topk < nb) ? nbp / 128 : 0) + topk;
+__host__ __device__ inline size_t pair_lds_bytes(int nb, int nbc, int nbp, int topk) {
+  const int ntiles = ((topk < nb) ? nbp / 128 : 0) + nbc + topk;
   const size_t plan = (size_t)2 * ((nb + 31) / 32) * 4 + (size_t)3 * topk * 4 + 32 * 4;
   if (plan > (size_t)PAIR_TB) return ~(size_t)0;
   return (size_t)4 * PAIR_TB + (size_t)2 * nbp * 4 + (size_t)2 * (2 * ntiles + 2) * 8;
@@ -894,7 +894,7 @@ __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
     const uint16_t* __restrict__ vpt, const int32_t* __restrict__ idx, int topk,
     const uint16_t* __restrict__ ks16, const uint16_t* __restrict__ vs16t,
     const float* __restrict__ bias2, const int32_t* __restrict__ perm_q,
-    uint16_t* __restrict__ out, int H, int N, int Nv, int nb, int nbp, float scale_log2) {
+    uint16_t* __restrict__ out, int H, int N, int Nv, int nb, int nbc, int nbp, float scale_log2) {
   constexpr int D = 128, BK = 128;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int nwb = (nb + 31) >> 5;
@@ -924,9 +924,11 @@ __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
   // group 1 of an odd last pair repeats group 0's block and writes nothing
   const bool idle = 2 * pr + grp >= nb;
   const int A = idle ? 2 * pr : 2 * pr + grp;
-  const long Np = (long)nb * BK;
+  const int nbt = nb + nbc;   // video blocks, then context blocks
+  const long Np = (long)nbt * BK;
   const int nct = (topk < nb) ? nbp / BK : 0;
-  const int ntiles = nct + topk;
+  const int cbase = nct + nbc;   // first exact video step
+  const int ntiles = cbase + topk;
   const int32_t* myidx = idx + ((long)h * nb + A) * topk;
 
   // ---- tile plan: shared blocks (in group 0's order) and each group's own
@@ -990,18 +992,22 @@ __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
   if (tid == 0) sCnt[16] = cs;   // both groups go by group 0's count
   __syncthreads();
   const int ns = min(__builtin_amdgcn_readfirstlane(sCnt[16]), topk);
-  const int Tsh = nct + ns;   // shared tiles
+  const int Tsh = cbase + ns;   // shared tiles: summaries, context blocks, common video blocks
   const int pb = Tsh & 1;
 
   // step of this group's last block nb - 1 (its padded keys get -inf), or -1
   const int tlast = __builtin_amdgcn_readfirstlane(
-      (sCnt[18] >= 0) ? nct + sCnt[18] : ((sCnt[19 + grp] >= 0) ? Tsh + sCnt[19 + grp] : -1));
+      (sCnt[18] >= 0) ? cbase + sCnt[18] : ((sCnt[19 + grp] >= 0) ? Tsh + sCnt[19 + grp] : -1));
+  // step of the last context block and its valid rows (context tokens are
+  // exact for every video query, outside the top-k budget)
+  const int tctx = (nbc > 0) ? cbase - 1 : -1;
+  const int validc = (N - Nv) - (nbc - 1) * BK;
   // buffer (0/1) of step t of group g; K at smem + buf * TB, V^T at smem + (2 + buf) * TB
   auto buf_of = [&](int g, int t) -> int { return (t < Tsh) ? (t & 1) : (pb ^ g); };
 
   // every K, V^T and summary tile is 32 contiguous KB: per-head bases
   const char* kb_h = reinterpret_cast<const char*>(kp + (long)h * Np * D);
-  const char* vb_h = reinterpret_cast<const char*>(vpt + (long)h * nb * D * BK);
+  const char* vb_h = reinterpret_cast<const char*>(vpt + (long)h * nbt * D * BK);
   const char* ksb_h = reinterpret_cast<const char*>(ks16 + (long)h * nbp * D);
   const char* vsb_h = reinterpret_cast<const char*>(vs16t + (long)h * nbp * D);
 
@@ -1013,7 +1019,8 @@ __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
     // address of the K (v = 0) or V^T (v = 1) tile of step t of group g
     auto step_src = [&](int g, int t, int v) -> uint64_t {
       if (t < nct) return (uint64_t)((v ? vsb_h : ksb_h) + ((long)t << 15));
-      const int o = (t < Tsh) ? t - nct : (g + 1) * topk + t - Tsh;
+      if (t < cbase) return (uint64_t)((v ? vb_h : kb_h) + ((long)(nb + t - nct) << 15));
+      const int o = (t < Tsh) ? t - cbase : (g + 1) * topk + t - Tsh;
       return (uint64_t)((v ? vb_h : kb_h) + ((long)sS[o] << 15));
     };
     for (int sl = tid; sl < nslots; sl += PAIR_NT) {
@@ -1036,7 +1043,8 @@ __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
     }
   }
   // step 0's K of group 0 (shared, or its own when nothing is shared)
-  const char* k0src = (nct > 0) ? ksb_h : kb_h + ((long)sS[(Tsh > 0) ? 0 : topk] << 15);
+  const char* k0src = (nct > 0) ? ksb_h
+                      : kb_h + ((long)((nbc > 0) ? nb : sS[(Tsh > 0) ? 0 : topk]) << 15);
   __syncthreads();
 
   // In every slot the group that is not in its matrix slot loads the slot's
@@ -1183,9 +1191,9 @@ __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
   // slot, where P is dead); the valid row count is opaque to the compiler so
   // that the compares stay in this rarely taken branch
   auto mask_tail = [&](int t) {
-    if (t == tlast) {
+    if (t == tlast || (t == tctx && validc < BK)) {
       int valid;
-      asm volatile("s_mov_b32 %0, %1" : "=s"(valid) : "s"(Nv - (nb - 1) * BK));
+      asm volatile("s_mov_b32 %0, %1" : "=s"(valid) : "s"((t == tlast) ? Nv - (nb - 1) * BK : validc));
       const int vb = valid - 8 * hf;   // key j = 8 hf + c, c a constant per element
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt)
@@ -1533,7 +1541,7 @@ static int launch_d128(const void* qp, const void* kp, const void* vpt, const in
     attr_set = true;
   }
   const float scale_log2 = kLog2e / sqrtf(128.f);
-  if (paired && !fp8 && nbc == 0 && pair_lds_bytes(nb, nbp, topk) <= 160 * 1024) {
+  if (paired && !fp8 && pair_lds_bytes(nb, nbc, nbp, topk) <= 160 * 1024) {
     static bool pair_attr_set = false;
     if (!pair_attr_set) {
       hipFuncSetAttribute((const void*)attn_pair_d128, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
@@ -1541,10 +1549,17 @@ static int launch_d128(const void* qp, const void* kp, const void* vpt, const in
     }
     const long pslots = 8L * (((nb + 1) / 2 + 7) / 8);
     if ((long)H * pslots > 0x7fffffffL) return spark_set_error(SPARK_E_SHAPE, "spark_attn: grid too large");
-    hipLaunchKernelGGL(attn_pair_d128, dim3((unsigned)(H * pslots)), dim3(PAIR_NT), pair_lds_bytes(nb, nbp, topk), st,
+    hipLaunchKernelGGL(attn_pair_d128, dim3((unsigned)(H * pslots)), dim3(PAIR_NT), pair_lds_bytes(nb, nbc, nbp, topk),
+                       st, (const uint16_t*)qp, (const uint16_t*)kp, (const uint16_t*)vpt, idx, topk, ks16, vs16t,
+                       bias2, perm_q, (uint16_t*)out, H, N, Nv, nb, nbc, nbp, scale_log2);
+    int rc = spark_check_launch("attn_pair_d128");
+    if (rc || nbc == 0) return rc;
+    // the context query blocks (dense rows over all n_b + n_c tiles)
+    const long cslots = 8L * ((nbc + 7) >> 3);
+    hipLaunchKernelGGL((attn_mfma_d128<true, false>), dim3((unsigned)(H * cslots)), dim3(D128_NT), lds, st,
                        (const uint16_t*)qp, (const uint16_t*)kp, (const uint16_t*)vpt, idx, topk, ks16, vs16t,
-                       bias2, perm_q, (uint16_t*)out, H, N, Nv, nb, nbp, scale_log2);
-    return spark_check_launch("attn_pair_d128");
+                       bias2, perm_q, (uint16_t*)out, H, N, Nv, nb, nbc, nbp, scale_log2, kscale, ksscale, 1);
+    return spark_check_launch("attn_mfma_d128 (context blocks)");
   }
   const long slots = 8L * (((nbc + 7) >> 3) + ((nb + 7) >> 3));   // d128_slots
   if ((long)H * slots > 0x7fffffffL) return spark_set_error(SPARK_E_SHAPE, "spark_attn: grid too large");
@@ -1552,7 +1567,7 @@ static int launch_d128(const void* qp, const void* kp, const void* vpt, const in
 #define SPARK_D128_LAUNCH(C, F)                                                                    \
   hipLaunchKernelGGL((attn_mfma_d128<C, F>), grid, block, lds, st, (const uint16_t*)qp,             \
                      (const uint16_t*)kp, (const uint16_t*)vpt, idx, topk, ks16, vs16t, bias2, perm_q, \
-                     (uint16_t*)out, H, N, Nv, nb, nbc, nbp, scale_log2, kscale, ksscale)
+                     (uint16_t*)out, H, N, Nv, nb, nbc, nbp, scale_log2, kscale, ksscale, 0)
   if (nbc > 0) {
     if (fp8) SPARK_D128_LAUNCH(true, true);
     else SPARK_D128_LAUNCH(true, false);

@@ -180,3 +180,35 @@ def test_pair_at_the_768p_block_count(ratio):
     e = rel_l2(a0[rows], want[rows])
     say(f"[pair] nb={nb} topk={topk}: sampled rel-L2 {e:.3e}, vs one-block {rel_l2(a0, a1):.3e}")
     assert e <= 1e-2 and np.abs(a0[rows] - want[rows]).max() <= 3e-2
+
+
+@pytest.mark.parametrize("Nv,Nc,topk,kind", [(15900, 1000, 13, "random"), (15872, 2048, 7, "disjoint"),
+                                              (9000, 100, 71, "identical")])
+def test_pair_with_context_tokens(Nv, Nc, topk, kind):
+    """SPARK_CONTEXT_EXACT: video query blocks run paired with every context
+    tile shared by the pair (and the short last context block masked); the
+    context query blocks run one per workgroup.  Video rows against the
+    oracle's sparse attention with the context keys appended exactly,
+    context rows against dense attention, and everything against the
+    one-block kernel."""
+    rng = np.random.default_rng(Nv + Nc + topk)
+    N, d = Nv + Nc, 128
+    q, k, v = (round_to_bf16(rng.standard_normal((N, d)).astype(np.float32) * s) for s in (1.5, 1.5, 1.0))
+    nb = O.n_blocks(Nv, B)
+    idx = _routing(kind, nb, topk, rng)[None]
+    ks, vs, bias = O.reweight_summaries(k[:Nv], v[:Nv], O.anchor_query(q, Nv), B)
+    want = np.concatenate([O.sparse_attention(q[:Nv], k[:Nv], v[:Nv], idx[0], ks, vs, bias, B,
+                                              extra_k=k[Nv:], extra_v=v[Nv:]),
+                           O.dense_attention(q[Nv:], k, v)])
+    t = lambda a, dt=torch.bfloat16: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV).to(dt)
+    g = L.spark_reblock(t(q[None]), t(k[None]), t(v[None]), B, layout="identity", n_anchor=Nv, context=True)
+    f = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float32)[None]).to(DEV)
+    outs = [L.spark_attn(g["q_p"], g["k_p"], g["v_pt"], torch.from_numpy(idx).to(DEV), f(ks), f(vs), f(bias),
+                         N, B, perm_q=g["perm_q"], n_anchor=Nv, context=True, one_block=one) for one in (False, True)]
+    torch.cuda.synchronize()
+    a0, a1 = (o[0].float().cpu().numpy().astype(np.float64) for o in outs)
+    e, ev, ec = rel_l2(a0, want), rel_l2(a0[:Nv], want[:Nv]), rel_l2(a0[Nv:], want[Nv:])
+    say(f"[pair] context Nv={Nv} Nc={Nc} topk={topk} {kind}: {e:.3e} (video {ev:.3e}, context {ec:.3e}), "
+        f"vs one-block {rel_l2(a0, a1):.3e}")
+    assert ev <= 1e-2 and ec <= 1e-2 and np.abs(a0 - want).max() <= 3e-2
+    assert rel_l2(a0, a1) <= 5e-3
