@@ -419,6 +419,40 @@ __device__ __forceinline__ float attn_pow2_scale(float amax) {
 }
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
+// E4M3 query row for the fp8 logits: lane (l32, hf) holds d = 64 s + 32 hf +
+// 0..31 of its row (s = 0, 1), scaled by the row's power-of-two scale
+// (the smallest s with max |q| <= 448 s, taken over the lane pair).
+__device__ __forceinline__ void attn_q8(const uint16_t* __restrict__ qp, long qrow, int hf, i32x8 (&q8)[2],
+                                        float& qscale) {
+  constexpr int D = 128;
+  bf16x8 raw[2][4];
+  float amax = 0.f;
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      raw[s2][u] = *reinterpret_cast<const bf16x8*>(qp + qrow * D + 64 * s2 + 32 * hf + 8 * u);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)raw[s2][u][e]));
+    }
+  amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+  qscale = attn_pow2_scale(amax);
+  const float inv = 1.f / qscale;
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const bf16x8 r = raw[s2][u];
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32((float)r[4 * w] * inv,
+                                                                       (float)r[4 * w + 1] * inv, 0, false) & 0xffffu;
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32((float)r[4 * w + 2] * inv,
+                                                                       (float)r[4 * w + 3] * inv, 0, false) & 0xffffu;
+        q8[s2][2 * u + w] = (int)(lo | (hi << 16));
+      }
+}
+
 // Sum of the 64 bf16 P values a lane holds, two bf16 per dot-product step
 // (against (1, 1)), in two interleaved partial sums: the softmax denominator
 // is summed from the same rounded P that multiplies V.
@@ -556,32 +590,7 @@ __global__ __launch_bounds__(D128_NT, 2) void attn_mfma_d128(
   i32x8 q8[2];       // E4M3 query, lane (l32, hf): d = 64 s + 32 hf + 0..31
   float qscale = 1.f;
   if constexpr (FP8) {
-    bf16x8 raw[2][4];
-    float amax = 0.f;
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        raw[s2][u] = *reinterpret_cast<const bf16x8*>(qp + qrow * D + 64 * s2 + 32 * hf + 8 * u);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)raw[s2][u][e]));
-      }
-    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-    qscale = attn_pow2_scale(amax);
-    const float inv = 1.f / qscale;
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          const bf16x8 r = raw[s2][u];
-          const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32((float)r[4 * w] * inv,
-                                                                         (float)r[4 * w + 1] * inv, 0, false) & 0xffffu;
-          const uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32((float)r[4 * w + 2] * inv,
-                                                                         (float)r[4 * w + 3] * inv, 0, false) & 0xffffu;
-          q8[s2][2 * u + w] = (int)(lo | (hi << 16));
-        }
+    attn_q8(qp, qrow, hf, q8, qscale);
   } else {
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
@@ -877,30 +886,38 @@ struct SlotLoads {
 };
 constexpr int PAIR_TB = 128 * 256;   // bytes of one bf16 K or V^T tile
 
-// LDS bytes of the paired kernel: 4 tiles, two bias rows, the slot table.
+// LDS bytes of the paired kernel: 4 tiles, two bias rows, the slot table
+// (and with fp8 logits the steps' key scales).
 // The plan's scratch (two block bitmaps, the shared and the two own block
 // lists, 32 counters) lives in the second K buffer, which no load touches
 // before the slot table is built; a plan that would not fit there returns
 // a size no workgroup gets.
-__host__ __device__ inline size_t pair_lds_bytes(int nb, int nbc, int nbp, int topk) {
+__host__ __device__ inline size_t pair_lds_bytes(int nb, int nbc, int nbp, int topk, bool fp8) {
   const int ntiles = ((topk < nb) ? nbp / 128 : 0) + nbc + topk;
   const size_t plan = (size_t)2 * ((nb + 31) / 32) * 4 + (size_t)3 * topk * 4 + 32 * 4;
   if (plan > (size_t)PAIR_TB) return ~(size_t)0;
-  return (size_t)4 * PAIR_TB + (size_t)2 * nbp * 4 + (size_t)2 * (2 * ntiles + 2) * 8;
+  return (size_t)4 * PAIR_TB + (size_t)2 * nbp * 4 + (size_t)2 * (2 * ntiles + 2) * 8 +
+         (fp8 ? (size_t)2 * ntiles * 4 : 0);   // fp8: each step's key scale, per group
 }
 
+// FP8: E4M3 logits as in attn_mfma_d128 (kp / ks16 then hold 16 KB E4M3 key
+// tiles with one power-of-two scale per tile in kscale / ksscale).
+template <bool FP8>
 __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
     const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vpt, const int32_t* __restrict__ idx, int topk,
     const uint16_t* __restrict__ ks16, const uint16_t* __restrict__ vs16t,
     const float* __restrict__ bias2, const int32_t* __restrict__ perm_q,
-    uint16_t* __restrict__ out, int H, int N, int Nv, int nb, int nbc, int nbp, float scale_log2) {
+    uint16_t* __restrict__ out, int H, int N, int Nv, int nb, int nbc, int nbp, float scale_log2,
+    const float* __restrict__ kscale, const float* __restrict__ ksscale) {
   constexpr int D = 128, BK = 128;
+  constexpr int KES = FP8 ? 1 : 2;   // bytes per key element
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int nwb = (nb + 31) >> 5;
   float* sBias0 = reinterpret_cast<float*>(smem + 4 * PAIR_TB);
   // per slot: the K tile and the V^T tile it loads
   uint64_t* sSlot = reinterpret_cast<uint64_t*>(sBias0 + 2 * nbp);
+  float* sKsc = nullptr;   // fp8: key scale of step t of group g at [g * ntiles + t] (set below)
   // plan scratch, in K buffer 1 (first loaded in slot 0, after the plan)
   uint32_t* sMap = reinterpret_cast<uint32_t*>(smem + PAIR_TB);
   int* sS = reinterpret_cast<int*>(sMap + 2 * nwb);
@@ -1006,9 +1023,9 @@ __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
   auto buf_of = [&](int g, int t) -> int { return (t < Tsh) ? (t & 1) : (pb ^ g); };
 
   // every K, V^T and summary tile is 32 contiguous KB: per-head bases
-  const char* kb_h = reinterpret_cast<const char*>(kp + (long)h * Np * D);
+  const char* kb_h = reinterpret_cast<const char*>(kp) + (long)h * Np * D * KES;
   const char* vb_h = reinterpret_cast<const char*>(vpt + (long)h * nbt * D * BK);
-  const char* ksb_h = reinterpret_cast<const char*>(ks16 + (long)h * nbp * D);
+  const char* ksb_h = reinterpret_cast<const char*>(ks16) + (long)h * nbp * D * KES;
   const char* vsb_h = reinterpret_cast<const char*>(vs16t + (long)h * nbp * D);
 
   // ---- slot table: the K tile and the V^T tile each slot loads, as the
@@ -1018,10 +1035,11 @@ __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
   {
     // address of the K (v = 0) or V^T (v = 1) tile of step t of group g
     auto step_src = [&](int g, int t, int v) -> uint64_t {
-      if (t < nct) return (uint64_t)((v ? vsb_h : ksb_h) + ((long)t << 15));
-      if (t < cbase) return (uint64_t)((v ? vb_h : kb_h) + ((long)(nb + t - nct) << 15));
+      const int sh = v ? 15 : (FP8 ? 14 : 15);   // log2 of the tile bytes
+      if (t < nct) return (uint64_t)((v ? vsb_h : ksb_h) + ((long)t << sh));
+      if (t < cbase) return (uint64_t)((v ? vb_h : kb_h) + ((long)(nb + t - nct) << sh));
       const int o = (t < Tsh) ? t - cbase : (g + 1) * topk + t - Tsh;
-      return (uint64_t)((v ? vb_h : kb_h) + ((long)sS[o] << 15));
+      return (uint64_t)((v ? vb_h : kb_h) + ((long)sS[o] << sh));
     };
     for (int sl = tid; sl < nslots; sl += PAIR_NT) {
       uint64_t rk = 0, rv = 0;
@@ -1041,10 +1059,24 @@ __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
       sSlot[2 * sl] = rk;
       sSlot[2 * sl + 1] = rv;
     }
+    if constexpr (FP8) {
+      sKsc = reinterpret_cast<float*>(sSlot + 2 * nslots);
+      for (int i = tid; i < 2 * ntiles; i += PAIR_NT) {
+        const int g = i / ntiles, t = i - g * ntiles;
+        float sc;
+        if (t < nct) {
+          sc = ksscale[(long)h * (nbp / BK) + t];
+        } else {
+          const int B = (t < cbase) ? nb + t - nct : sS[(t < Tsh) ? t - cbase : (g + 1) * topk + t - Tsh];
+          sc = kscale[(long)h * nbt + B];
+        }
+        sKsc[i] = sc;
+      }
+    }
   }
   // step 0's K of group 0 (shared, or its own when nothing is shared)
   const char* k0src = (nct > 0) ? ksb_h
-                      : kb_h + ((long)((nbc > 0) ? nb : sS[(Tsh > 0) ? 0 : topk]) << 15);
+                      : kb_h + ((long)((nbc > 0) ? nb : sS[(Tsh > 0) ? 0 : topk]) << (FP8 ? 14 : 15));
   __syncthreads();
 
   // In every slot the group that is not in its matrix slot loads the slot's
@@ -1064,6 +1096,19 @@ __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
     const int r4 = 4 * i + (lane >> 4);
     const int lc = (lane & 15) ^ r4;
     loff[i] = (uint32_t)(8192 * wave + r4 * 256 + lc * 16) - (i == 2 ? 1024u : 0u);
+  }
+  // fp8 K tiles: 128 rows of 128 bytes, in the same permuted row order,
+  // the 16-byte chunk slot XOR-swizzled by (row >> 1) & 7
+  uint32_t koff8[4];
+  if constexpr (FP8) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int srow = 32 * wave + 8 * j + (lane >> 3);
+      const int c = (lane & 7) ^ ((srow >> 1) & 7);
+      const int grow = (srow & ~31) + ((((srow & 31) >> 3) >> 1) << 4) + (((srow >> 2) & 1) << 3) +
+                       ((((srow & 31) >> 3) & 1) << 2) + (srow & 3);
+      koff8[j] = (uint32_t)(grow * 128 + c * 16);
+    }
   }
   auto mk_rsrc = [&](const char* src) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, PAIR_TB, 0x00020000);
@@ -1089,6 +1134,12 @@ __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
     const int j = l & 7, i = j & 3;
     if (l < 8) {
       if (!L.hk) return;
+      if constexpr (FP8) {   // a 16 KB E4M3 tile: loads 0..3 fill rows 32 w + 8 j .. +7
+        if (j >= 4) return;
+        auto lp = (void __attribute__((address_space(3)))*)(smem + L.dk * PAIR_TB + (4 * wave + j) * 1024);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(L.rsk, lp, 16, koff8[j], 0, 0, 0);
+        return;
+      }
       auto lp = (void __attribute__((address_space(3)))*)(smem + L.dk * PAIR_TB + (8 * wave + j) * 1024);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(L.rsk, lp, 16, loff[i], 4096 * (j >> 2) + (i == 1 ? 1024 : 0), 0, 0);
     } else {
@@ -1099,9 +1150,20 @@ __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
   };
 
   const long qrow = (long)h * Np + (long)A * BK + wave * 32 + l32;
-  bf16x8 qop[D / 16];
+  bf16x8 qop[FP8 ? 1 : D / 16];
+  i32x8 q8[2];
+  float qscale = 1.f;
+  if constexpr (FP8) {
+    attn_q8(qp, qrow, hf, q8, qscale);
+  } else {
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) qop[s] = *reinterpret_cast<const bf16x8*>(qp + qrow * D + 16 * s + 8 * hf);
+    for (int s = 0; s < D / 16; ++s) qop[s] = *reinterpret_cast<const bf16x8*>(qp + qrow * D + 16 * s + 8 * hf);
+  }
+  int ro8[2][2];   // fp8 K operand reads: row 32 jt + l32, logical chunks 4 s + 2 hf + u
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) ro8[s2][u] = l32 * 128 + (((4 * s2 + 2 * hf + u) ^ ((l32 >> 1) & 7)) << 4);
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)
@@ -1161,7 +1223,30 @@ __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if constexpr (QK) {
+    if constexpr (QK && FP8) {
+      const unsigned char* sK = smem + buf_of(grp, t) * PAIR_TB;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sacc[jt][v] = 0.f;
+      i32x8 kop8[2][4];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          const uint4 lo = *reinterpret_cast<const uint4*>(sK + ro8[s2][0] + jt * 4096);
+          const uint4 hi = *reinterpret_cast<const uint4*>(sK + ro8[s2][1] + jt * 4096);
+          kop8[s2][jt] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                               (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt)
+          sacc[jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop8[s2][jt], q8[s2], sacc[jt], 0, 0, 0,
+                                                                     0, 0, 0);
+      d128_pipeline_fp8();
+    } else if constexpr (QK) {
       const unsigned char* sK = smem + buf_of(grp, t) * PAIR_TB;
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt)
@@ -1210,6 +1295,9 @@ __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
   // compressed tiles scaled and biased ones.
   auto softmax_slot = [&](auto exact_tag, int t, const SlotLoads& L) {
     constexpr bool EXACT = decltype(exact_tag)::value;
+    // logit -> log2 units (fp8: times the query's and the key tile's scales)
+    float lsc = scale_log2;
+    if constexpr (FP8) lsc = scale_log2 * qscale * sKsc[grp * ntiles + t];
     if constexpr (!EXACT) {
       // element v of 32-key group jt is key 32 jt + 8 hf + v (v < 8) or
       // 32 jt + 16 + 8 hf + v - 8: four runs of 8 consecutive biases
@@ -1223,11 +1311,11 @@ __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
         for (int v = 0; v < 16; ++v) {
           const float4 q4 = b4[v >> 2];
           const float bv = ((v & 3) == 0) ? q4.x : ((v & 3) == 1) ? q4.y : ((v & 3) == 2) ? q4.z : q4.w;
-          sacc[jt][v] = fmaf(sacc[jt][v], scale_log2, bv);
+          sacc[jt][v] = fmaf(sacc[jt][v], lsc, bv);
         }
       }
     }
-    const float sc = EXACT ? scale_log2 : 1.f;
+    const float sc = EXACT ? lsc : 1.f;
     // the row sums add the fp32 p with plain adds: v_dot2c shares the matrix
     // core's issue and stalls behind the other wave's MFMA stream
     float psum;
@@ -1541,24 +1629,36 @@ static int launch_d128(const void* qp, const void* kp, const void* vpt, const in
     attr_set = true;
   }
   const float scale_log2 = kLog2e / sqrtf(128.f);
-  if (paired && !fp8 && pair_lds_bytes(nb, nbc, nbp, topk) <= 160 * 1024) {
+  if (paired && pair_lds_bytes(nb, nbc, nbp, topk, fp8) <= 160 * 1024) {
     static bool pair_attr_set = false;
     if (!pair_attr_set) {
-      hipFuncSetAttribute((const void*)attn_pair_d128, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      hipFuncSetAttribute((const void*)attn_pair_d128<false>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      hipFuncSetAttribute((const void*)attn_pair_d128<true>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
       pair_attr_set = true;
     }
     const long pslots = 8L * (((nb + 1) / 2 + 7) / 8);
     if ((long)H * pslots > 0x7fffffffL) return spark_set_error(SPARK_E_SHAPE, "spark_attn: grid too large");
-    hipLaunchKernelGGL(attn_pair_d128, dim3((unsigned)(H * pslots)), dim3(PAIR_NT), pair_lds_bytes(nb, nbc, nbp, topk),
-                       st, (const uint16_t*)qp, (const uint16_t*)kp, (const uint16_t*)vpt, idx, topk, ks16, vs16t,
-                       bias2, perm_q, (uint16_t*)out, H, N, Nv, nb, nbc, nbp, scale_log2);
+    const size_t plds = pair_lds_bytes(nb, nbc, nbp, topk, fp8);
+    const dim3 pgrid((unsigned)(H * pslots)), pblock(PAIR_NT);
+#define SPARK_PAIR_LAUNCH(F)                                                                       \
+    hipLaunchKernelGGL((attn_pair_d128<F>), pgrid, pblock, plds, st, (const uint16_t*)qp, (const uint16_t*)kp, \
+                       (const uint16_t*)vpt, idx, topk, ks16, vs16t, bias2, perm_q, (uint16_t*)out, H, N, Nv, nb, \
+                       nbc, nbp, scale_log2, kscale, ksscale)
+    if (fp8) SPARK_PAIR_LAUNCH(true);
+    else SPARK_PAIR_LAUNCH(false);
+#undef SPARK_PAIR_LAUNCH
     int rc = spark_check_launch("attn_pair_d128");
     if (rc || nbc == 0) return rc;
     // the context query blocks (dense rows over all n_b + n_c tiles)
     const long cslots = 8L * ((nbc + 7) >> 3);
-    hipLaunchKernelGGL((attn_mfma_d128<true, false>), dim3((unsigned)(H * cslots)), dim3(D128_NT), lds, st,
-                       (const uint16_t*)qp, (const uint16_t*)kp, (const uint16_t*)vpt, idx, topk, ks16, vs16t,
-                       bias2, perm_q, (uint16_t*)out, H, N, Nv, nb, nbc, nbp, scale_log2, kscale, ksscale, 1);
+    if (fp8)
+      hipLaunchKernelGGL((attn_mfma_d128<true, true>), dim3((unsigned)(H * cslots)), dim3(D128_NT), lds, st,
+                         (const uint16_t*)qp, (const uint16_t*)kp, (const uint16_t*)vpt, idx, topk, ks16, vs16t,
+                         bias2, perm_q, (uint16_t*)out, H, N, Nv, nb, nbc, nbp, scale_log2, kscale, ksscale, 1);
+    else
+      hipLaunchKernelGGL((attn_mfma_d128<true, false>), dim3((unsigned)(H * cslots)), dim3(D128_NT), lds, st,
+                         (const uint16_t*)qp, (const uint16_t*)kp, (const uint16_t*)vpt, idx, topk, ks16, vs16t,
+                         bias2, perm_q, (uint16_t*)out, H, N, Nv, nb, nbc, nbp, scale_log2, kscale, ksscale, 1);
     return spark_check_launch("attn_mfma_d128 (context blocks)");
   }
   const long slots = 8L * (((nbc + 7) >> 3) + ((nb + 7) >> 3));   // d128_slots
@@ -1628,7 +1728,7 @@ int attn_launch(int H, int N, int Nv, int D, int BK, int dtype, const void* qp, 
       rc = quant_e4m3_launch(H, nb, nbp, D, BK, SPARK_F32, ksum, ks8, ksscale, st);
       if (rc) return rc;
       return launch_d128(qp, k8, vpt, idx, topk, (const uint16_t*)ks8, vs16t, bias2, perm_q, out, H, N, Nv,
-                         nb, nbc, nbp, true, false, kscale, ksscale, st);
+                         nb, nbc, nbp, true, paired, kscale, ksscale, st);
     }
     if (D == 128) {
       if (BK == 128 && (size_t)D128_LDS_TILES + (size_t)nbp * 4 <= 80 * 1024)

@@ -212,3 +212,28 @@ def test_pair_with_context_tokens(Nv, Nc, topk, kind):
         f"vs one-block {rel_l2(a0, a1):.3e}")
     assert ev <= 1e-2 and ec <= 1e-2 and np.abs(a0 - want).max() <= 3e-2
     assert rel_l2(a0, a1) <= 5e-3
+
+
+@pytest.mark.parametrize("kind", ["random", "disjoint", "identical"])
+def test_pair_fp8_logits(kind):
+    """SPARK_EXACT_FP8 on the paired schedule (E4M3 key tiles of 16 KB, the
+    step's key scale from the plan): against the oracle's fp8 attention and
+    the one-block fp8 kernel."""
+    rng = np.random.default_rng(40 + len(kind))
+    N, d, topk = 15900, 128, 13
+    q, k, v = (round_to_bf16(rng.standard_normal((N, d)).astype(np.float32) * s) for s in (1.5, 1.5, 1.0))
+    nb = O.n_blocks(N, B)
+    idx = _routing(kind, nb, topk, rng)[None]
+    ks, vs, bias = O.reweight_summaries(k, v, O.anchor_query(q, N), B)
+    want = O.sparse_attention(q, k, v, idx[0], ks, vs, bias, B, fp8=True)
+    t = lambda a, dt=torch.bfloat16: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV).to(dt)
+    g = L.spark_reblock(t(q[None]), t(k[None]), t(v[None]), B, layout="identity")
+    f = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float32)[None]).to(DEV)
+    outs = [L.spark_attn(g["q_p"], g["k_p"], g["v_pt"], torch.from_numpy(idx).to(DEV), f(ks), f(vs), f(bias),
+                         N, B, perm_q=g["perm_q"], fp8=True, one_block=one) for one in (False, True)]
+    torch.cuda.synchronize()
+    a0, a1 = (o[0].float().cpu().numpy().astype(np.float64) for o in outs)
+    e = rel_l2(a0, want)
+    say(f"[pair] fp8 {kind}: {e:.3e}, vs one-block {rel_l2(a0, a1):.3e}")
+    assert e <= 1e-2 and np.abs(a0 - want).max() <= 3e-2
+    assert rel_l2(a0, a1) <= 5e-3
