@@ -381,8 +381,7 @@ def main():
     rb_bytes = reblock_bytes(H, N, d, b, es, lev, nb, 1 if args.layout == "q_reuse_k" else 2, Nv)
     rb_ms = st_mean[0] + st_mean[2]
     csrc = os.path.join(ROOT, "block_sparse_attention_mahalanobis_amd", "csrc")
-    paired = (not ctx and not args.fp8 and not args.one_block and d == 128 and b == 128
-              and dtype == torch.bfloat16)
+    paired = not args.one_block and d == 128 and b == 128 and dtype == torch.bfloat16
     attn_kernel = "attn_pair_d128" if paired else "attn_mfma_d128"
     traffic = load_traffic("attn_full768_traffic.txt",
                            [os.path.join(csrc, f) for f in ("common.hpp", "k_attn.hip")],
