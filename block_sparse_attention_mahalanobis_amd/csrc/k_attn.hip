@@ -947,6 +947,106 @@ __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
   const int cbase = nct + nbc;   // first exact video step
   const int ntiles = cbase + topk;
   const int32_t* myidx = idx + ((long)h * nb + A) * topk;
+  // first list entry of this thread, loaded ahead of the query rows and step 0's K
+  const int idx0 = (tg < topk) ? myidx[tg] : 0;
+
+  // every K, V^T and summary tile is 32 contiguous KB: per-head bases
+  const char* kb_h = reinterpret_cast<const char*>(kp) + (long)h * Np * D * KES;
+  const char* vb_h = reinterpret_cast<const char*>(vpt + (long)h * nbt * D * BK);
+  const char* ksb_h = reinterpret_cast<const char*>(ks16) + (long)h * nbp * D * KES;
+  const char* vsb_h = reinterpret_cast<const char*>(vs16t + (long)h * nbp * D);
+
+  // In every slot the group that is not in its matrix slot loads the slot's
+  // tiles (a direct load stalls the issuing wave, which the matrix core
+  // cannot afford).  Load j (0..7) of a tile by wave w of that group fills
+  // LDS rows srow = 32 w + 4 j + (lane >> 4) (1 KB), the 16-byte chunk
+  // XOR-swizzled by srow & 15.  V^T rows come in order; K rows in the
+  // permuted order that makes the S^T accumulator the P^T operand, which
+  // swaps bits 2 and 3 of the row: the source row is srow + ((j & 1) -
+  // ((j >> 1) & 1)) * 4.  K and V share the lane offsets of j & 3; the 4096
+  // of j >= 4 and the +-1024 of K go into the scalar offset, with load 2's
+  // lane offset stored 1024 low (it is at least 2048).  (An immediate offset
+  // would also move the LDS destination.)
+  uint32_t loff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r4 = 4 * i + (lane >> 4);
+    const int lc = (lane & 15) ^ r4;
+    loff[i] = (uint32_t)(8192 * wave + r4 * 256 + lc * 16) - (i == 2 ? 1024u : 0u);
+  }
+  // fp8 K tiles: 128 rows of 128 bytes, in the same permuted row order,
+  // the 16-byte chunk slot XOR-swizzled by (row >> 1) & 7
+  uint32_t koff8[4];
+  if constexpr (FP8) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int srow = 32 * wave + 8 * j + (lane >> 3);
+      const int c = (lane & 7) ^ ((srow >> 1) & 7);
+      const int grow = (srow & ~31) + ((((srow & 31) >> 3) >> 1) << 4) + (((srow >> 2) & 1) << 3) +
+                       ((((srow & 31) >> 3) & 1) << 2) + (srow & 3);
+      koff8[j] = (uint32_t)(grow * 128 + c * 16);
+    }
+  }
+  auto mk_rsrc = [&](const char* src) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, PAIR_TB, 0x00020000);
+  };
+  // load l (a constant) of a slot: 0..7 the K tile, 8..15 the V^T tile
+  auto issue_load = [&](const SlotLoads& L, int l) {
+    const int j = l & 7, i = j & 3;
+    if (l < 8) {
+      if (!L.hk) return;
+      if constexpr (FP8) {   // a 16 KB E4M3 tile: loads 0..3 fill rows 32 w + 8 j .. +7
+        if (j >= 4) return;
+        auto lp = (void __attribute__((address_space(3)))*)(smem + L.dk * PAIR_TB + (4 * wave + j) * 1024);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(L.rsk, lp, 16, koff8[j], 0, 0, 0);
+        return;
+      }
+      auto lp = (void __attribute__((address_space(3)))*)(smem + L.dk * PAIR_TB + (8 * wave + j) * 1024);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(L.rsk, lp, 16, loff[i], 4096 * (j >> 2) + (i == 1 ? 1024 : 0), 0, 0);
+    } else {
+      if (!L.hv) return;
+      auto lp = (void __attribute__((address_space(3)))*)(smem + (2 + L.dv) * PAIR_TB + (8 * wave + j) * 1024);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(L.rsv, lp, 16, loff[i], 4096 * (j >> 2) + (i == 2 ? 1024 : 0), 0, 0);
+    }
+  };
+
+  // step 0's K into buffer 0 (buffer 1 holds the plan's scratch until slot 0)
+  auto issue_k0 = [&](const char* src) {
+    SlotLoads L0;
+    L0.rsk = L0.rsv = mk_rsrc(src);
+    L0.dk = L0.dv = 0;
+    L0.hk = true;
+    L0.hv = false;
+    if (grp == 1) {   // group 1 has no matrix slot before slot 1
+#pragma unroll
+      for (int l = 0; l < 8; ++l) issue_load(L0, l);
+    }
+  };
+  if (nct > 0) issue_k0(ksb_h);   // step 0 is summary tile 0
+  const long qrow = (long)h * Np + (long)A * BK + wave * 32 + l32;
+  bf16x8 qop[FP8 ? 1 : D / 16];
+  i32x8 q8[2];
+  float qscale = 1.f;
+  if constexpr (FP8) {
+    attn_q8(qp, qrow, hf, q8, qscale);
+  } else {
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qop[s] = *reinterpret_cast<const bf16x8*>(qp + qrow * D + 16 * s + 8 * hf);
+  }
+  int ro8[2][2];   // fp8 K operand reads: row 32 jt + l32, logical chunks 4 s + 2 hf + u
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) ro8[s2][u] = l32 * 128 + (((4 * s2 + 2 * hf + u) ^ ((l32 >> 1) & 7)) << 4);
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oacc[t][v] = 0.f;
+  float m_ref = -1e30f, l_run = 0.f;
+  int ro[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) ro[s] = sw_off(l32, 2 * s + hf);
 
   // ---- tile plan: shared blocks (in group 0's order) and each group's own
   float* sBias = sBias0 + grp * nbp;
@@ -959,7 +1059,7 @@ __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
     for (int i = tg; i < nbp; i += 256) sBias[i] = bias2[(long)h * nbp + i];
   __syncthreads();
   for (int i = tg; i < topk; i += 256) {
-    const int B = min(max(myidx[i], 0), nb - 1);
+    const int B = min(max((i == tg) ? idx0 : myidx[i], 0), nb - 1);
     atomicOr(&myMap[B >> 5], 1u << (B & 31));
     if (nct > 0) sBias[B] = -INFINITY;
   }
@@ -971,7 +1071,7 @@ __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
     int B = 0;
     bool sh = false;
     if (valid) {
-      B = min(max(myidx[i], 0), nb - 1);
+      B = min(max((c0 == 0) ? idx0 : myidx[i], 0), nb - 1);
       sh = (otMap[B >> 5] >> (B & 31)) & 1u;
     }
     const uint64_t bs = __builtin_amdgcn_ballot_w64(valid && sh);
@@ -1021,12 +1121,6 @@ __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
   const int validc = (N - Nv) - (nbc - 1) * BK;
   // buffer (0/1) of step t of group g; K at smem + buf * TB, V^T at smem + (2 + buf) * TB
   auto buf_of = [&](int g, int t) -> int { return (t < Tsh) ? (t & 1) : (pb ^ g); };
-
-  // every K, V^T and summary tile is 32 contiguous KB: per-head bases
-  const char* kb_h = reinterpret_cast<const char*>(kp) + (long)h * Np * D * KES;
-  const char* vb_h = reinterpret_cast<const char*>(vpt + (long)h * nbt * D * BK);
-  const char* ksb_h = reinterpret_cast<const char*>(ks16) + (long)h * nbp * D * KES;
-  const char* vsb_h = reinterpret_cast<const char*>(vs16t + (long)h * nbp * D);
 
   // ---- slot table: the K tile and the V^T tile each slot loads, as the
   // tile's address with its buffer (0/1) in bit 48; 0 if none.  Built once,
@@ -1079,40 +1173,6 @@ __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
                       : kb_h + ((long)((nbc > 0) ? nb : sS[(Tsh > 0) ? 0 : topk]) << (FP8 ? 14 : 15));
   __syncthreads();
 
-  // In every slot the group that is not in its matrix slot loads the slot's
-  // tiles (a direct load stalls the issuing wave, which the matrix core
-  // cannot afford).  Load j (0..7) of a tile by wave w of that group fills
-  // LDS rows srow = 32 w + 4 j + (lane >> 4) (1 KB), the 16-byte chunk
-  // XOR-swizzled by srow & 15.  V^T rows come in order; K rows in the
-  // permuted order that makes the S^T accumulator the P^T operand, which
-  // swaps bits 2 and 3 of the row: the source row is srow + ((j & 1) -
-  // ((j >> 1) & 1)) * 4.  K and V share the lane offsets of j & 3; the 4096
-  // of j >= 4 and the +-1024 of K go into the scalar offset, with load 2's
-  // lane offset stored 1024 low (it is at least 2048).  (An immediate offset
-  // would also move the LDS destination.)
-  uint32_t loff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r4 = 4 * i + (lane >> 4);
-    const int lc = (lane & 15) ^ r4;
-    loff[i] = (uint32_t)(8192 * wave + r4 * 256 + lc * 16) - (i == 2 ? 1024u : 0u);
-  }
-  // fp8 K tiles: 128 rows of 128 bytes, in the same permuted row order,
-  // the 16-byte chunk slot XOR-swizzled by (row >> 1) & 7
-  uint32_t koff8[4];
-  if constexpr (FP8) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int srow = 32 * wave + 8 * j + (lane >> 3);
-      const int c = (lane & 7) ^ ((srow >> 1) & 7);
-      const int grow = (srow & ~31) + ((((srow & 31) >> 3) >> 1) << 4) + (((srow >> 2) & 1) << 3) +
-                       ((((srow & 31) >> 3) & 1) << 2) + (srow & 3);
-      koff8[j] = (uint32_t)(grow * 128 + c * 16);
-    }
-  }
-  auto mk_rsrc = [&](const char* src) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, PAIR_TB, 0x00020000);
-  };
   // the tiles loaded in slot s, from the slot table
   auto plan_loads = [&](int s) {
     const uint64_t rk = sSlot[2 * s], rv = sSlot[2 * s + 1];
@@ -1129,63 +1189,7 @@ __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
     L.rsv = mk_rsrc(reinterpret_cast<const char*>(((uint64_t)(vhi & 0xffffu) << 32) | vlo));
     return L;
   };
-  // load l (a constant) of a slot: 0..7 the K tile, 8..15 the V^T tile
-  auto issue_load = [&](const SlotLoads& L, int l) {
-    const int j = l & 7, i = j & 3;
-    if (l < 8) {
-      if (!L.hk) return;
-      if constexpr (FP8) {   // a 16 KB E4M3 tile: loads 0..3 fill rows 32 w + 8 j .. +7
-        if (j >= 4) return;
-        auto lp = (void __attribute__((address_space(3)))*)(smem + L.dk * PAIR_TB + (4 * wave + j) * 1024);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(L.rsk, lp, 16, koff8[j], 0, 0, 0);
-        return;
-      }
-      auto lp = (void __attribute__((address_space(3)))*)(smem + L.dk * PAIR_TB + (8 * wave + j) * 1024);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(L.rsk, lp, 16, loff[i], 4096 * (j >> 2) + (i == 1 ? 1024 : 0), 0, 0);
-    } else {
-      if (!L.hv) return;
-      auto lp = (void __attribute__((address_space(3)))*)(smem + (2 + L.dv) * PAIR_TB + (8 * wave + j) * 1024);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(L.rsv, lp, 16, loff[i], 4096 * (j >> 2) + (i == 2 ? 1024 : 0), 0, 0);
-    }
-  };
-
-  const long qrow = (long)h * Np + (long)A * BK + wave * 32 + l32;
-  bf16x8 qop[FP8 ? 1 : D / 16];
-  i32x8 q8[2];
-  float qscale = 1.f;
-  if constexpr (FP8) {
-    attn_q8(qp, qrow, hf, q8, qscale);
-  } else {
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) qop[s] = *reinterpret_cast<const bf16x8*>(qp + qrow * D + 16 * s + 8 * hf);
-  }
-  int ro8[2][2];   // fp8 K operand reads: row 32 jt + l32, logical chunks 4 s + 2 hf + u
-#pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-    for (int u = 0; u < 2; ++u) ro8[s2][u] = l32 * 128 + (((4 * s2 + 2 * hf + u) ^ ((l32 >> 1) & 7)) << 4);
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) oacc[t][v] = 0.f;
-  float m_ref = -1e30f, l_run = 0.f;
-  int ro[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) ro[s] = sw_off(l32, 2 * s + hf);
-
-  // step 0's K (shared, or group 0's own when nothing is shared)
-  {
-    SlotLoads L0;
-    L0.rsk = L0.rsv = mk_rsrc(k0src);
-    L0.dk = L0.dv = 0;
-    L0.hk = true;
-    L0.hv = false;
-    if (grp == 1) {   // group 1 has no matrix slot before slot 1
-#pragma unroll
-      for (int l = 0; l < 8; ++l) issue_load(L0, l);
-    }
-  }
+  if (nct == 0) issue_k0(k0src);   // step 0 is an exact block: known only now
   f32x16 sacc[4];
   bf16x8 pop[8];
   // every slot starts when all its tiles have landed and every wave is done
