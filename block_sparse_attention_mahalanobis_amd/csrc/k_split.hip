@@ -7,7 +7,7 @@
 // Rule implemented (two-pole capacity bisection), per group g with nb_g >= 2
 // blocks:  left capacity c_L = ceil(nb_g / 2) * block;  centroid c = sum x^_i;
 // pole A = argmin (x^_i . c, id);  pole B = argmin (x^_i . x^_A, id);
-// s_i = x^_i . (x^_A - x^_B);  left child = the c_L members first in
+// s_i = x^_i . x^_A - x^_i . x^_B;  left child = the c_L members first in
 // (s descending, id ascending) order (NaN last), right child = the rest, both
 // keeping ascending ids.  Leaves end up in depth-first left-first order.
 //
@@ -22,10 +22,12 @@
 //                    deterministic); a right child's is parent - left
 //   argmin_partial/argmin_reduce (twice: pole A, pole B; 64-bit (key, id) mins)
 //   score         -> s_i for every position
-//   select_partition (one workgroup per group): exact radix select of the
-//                 c_L-th key, then a stable partition of the ids; groups of
-//                 more than 512 blocks get the key from radix_hist /
-//                 radix_pick_groups rounds over many workgroups first.
+//   capacity select: the exact c_L-th key by radix select, then a stable
+//                 partition of the ids.  Groups of more than 64 blocks:
+//                 radix_hist / radix_pick_groups rounds over many
+//                 workgroups, then seg_count / seg_partition, one workgroup
+//                 per 8192 positions; smaller groups: select_partition, one
+//                 workgroup per group.
 // Once every group fits in LDS (<= FIN_MAX tokens) one workgroup per group
 // loads its rows once and finishes all remaining levels in LDS.
 #include "common.hpp"
@@ -467,10 +469,6 @@ __device__ __forceinline__ void radix_pick(const int* s_hist, uint32_t* s_prefix
   }
 }
 
-// One workgroup per group: radix-select the c_L-th key of the group's scores
-// (streamed from global), then stable-partition the ids.  NT threads: 1024
-// for the top levels (a few groups of up to N tokens, where the loads in
-// flight per group decide the speed), SPL_T below.
 // Capacity select of the large groups by many workgroups, four radix rounds
 // of two launches each, synchronised by the launch boundaries alone (no
 // cross-workgroup fences or atomics, which cost an L2 write-back per
@@ -483,7 +481,7 @@ __device__ __forceinline__ void radix_pick(const int* s_hist, uint32_t* s_prefix
 // level's slot count S, as select_partition reads it).  Per (tree, group)
 // the record rec[RG_REC] holds the prefix and
 // the rank still needed; after the last round it holds the c_L-th key and
-// the number of ties that go left, which select_partition takes as given.
+// the number of ties that go left, which seg_count / seg_partition take.
 constexpr int RG_REC = 2;
 constexpr int RG_SEG = 8192;
 constexpr int RG_T = 256;
@@ -491,9 +489,10 @@ constexpr int RG_T = 256;
 __global__ __launch_bounds__(RG_T) void radix_hist(const float* __restrict__ s, const int* __restrict__ rec,
                                                   int* __restrict__ hpart, int N, int BK, int nb, int level,
                                                   int S, int nseg_max, int shift) {
-  __shared__ int s_whist[RG_T / 64][256];
+  constexpr int NH = 4 * (RG_T / 64);   // four histograms per wave, by lane & 3
+  __shared__ int s_whist[NH][256];
   const int slot = blockIdx.x / nseg_max, seg = blockIdx.x % nseg_max, t = blockIdx.y;
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = threadIdx.x, wave = tid >> 6, hsel = 4 * wave + (tid & 3);
   int start, nbg;
   if (!group_of_slot(slot, level, nb, start, nbg) || nbg < 2) return;
   const long g0 = (long)start * BK;
@@ -502,7 +501,7 @@ __global__ __launch_bounds__(RG_T) void radix_hist(const float* __restrict__ s, 
   if (i0 >= n) return;
   const int i1 = min(n, i0 + RG_SEG);
   const uint32_t pre = (shift == 24) ? 0u : (uint32_t)rec[((long)t * S + slot) * RG_REC];
-  for (int i = tid; i < (RG_T / 64) * 256; i += RG_T) (&s_whist[0][0])[i] = 0;
+  for (int i = tid; i < NH * 256; i += RG_T) (&s_whist[0][0])[i] = 0;
   __syncthreads();
   const uint32_t hmask = (shift == 24) ? 0u : (0xffffffffu << (shift + 8));
   const long base = (long)t * N + g0;
@@ -518,7 +517,7 @@ __global__ __launch_bounds__(RG_T) void radix_hist(const float* __restrict__ s, 
     for (int u = 0; u < U; ++u) {
       const int i = j0 + u * RG_T + tid;
       const uint32_t k = pref_key_desc(v[u]);
-      if (i < i1 && (k & hmask) == pre) atomicAdd(&s_whist[wave][(k >> shift) & 255], 1);
+      if (i < i1 && (k & hmask) == pre) atomicAdd(&s_whist[hsel][(k >> shift) & 255], 1);
     }
   }
   __syncthreads();
@@ -526,7 +525,7 @@ __global__ __launch_bounds__(RG_T) void radix_hist(const float* __restrict__ s, 
   for (int b = tid; b < 256; b += RG_T) {
     int c = 0;
 #pragma unroll
-    for (int w = 0; w < RG_T / 64; ++w) c += s_whist[w][b];
+    for (int w = 0; w < NH; ++w) c += s_whist[w][b];
     hp[b] = c;
   }
 }
@@ -563,11 +562,10 @@ __global__ __launch_bounds__(RG_T) void radix_pick_groups(int* __restrict__ rec,
   }
 }
 
-// The levels whose groups exceed 512 blocks take the threshold from the
-// many-workgroup rounds (at the 768p layer: the top level 408 -> 280 us;
-// below 512 blocks the extra passes over the scores cost more than the
-// one-workgroup select).
-static bool wide_select(int nb, int lev) { return (nb >> lev) > 512; }
+// The levels whose groups exceed WIDE_MIN blocks take the threshold from the
+// many-workgroup rounds and partition one segment per workgroup.
+constexpr int WIDE_MIN = 64;
+static bool wide_select(int nb, int lev) { return (nb >> lev) > WIDE_MIN; }
 
 // Largest radix_hist grid (groups x segments) over the levels that use it.
 static long radix_hist_slots(int N, int BK, int nb, int Lf) {
@@ -580,12 +578,215 @@ static long radix_hist_slots(int N, int BK, int nb, int Lf) {
   return mx;
 }
 
+// Keys (descending-order keys of the scores) and ids of the 8 positions
+// q .. q + 7 of a group's rows [base, base + n); past n: key 0xffffffff, id 0.
+__device__ __forceinline__ void fetch8(const float* __restrict__ s, const int32_t* __restrict__ ids_in,
+                                       long base, int n, int q, bool vec_ok, uint32_t (&kn)[8],
+                                       int32_t (&idn)[8]) {
+  if (vec_ok && q + 8 <= n) {   // two 16-byte loads per array
+    const float4 s0 = *reinterpret_cast<const float4*>(s + base + q);
+    const float4 s1 = *reinterpret_cast<const float4*>(s + base + q + 4);
+    const int4 i0 = *reinterpret_cast<const int4*>(ids_in + base + q);
+    const int4 i1 = *reinterpret_cast<const int4*>(ids_in + base + q + 4);
+    const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    const int32_t iv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kn[e] = pref_key_desc(sv[e]);
+      idn[e] = iv[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int p = q + e;
+      kn[e] = (p < n) ? pref_key_desc(s[base + p]) : 0xffffffffu;
+      idn[e] = (p < n) ? ids_in[base + p] : 0;
+    }
+  }
+}
+
+// One tile of the stable capacity partition: positions p0 .. p0 + 8 NT - 1
+// of a group of n (this thread's keys k and ids idv at p0 + 8 tid ..), the
+// c_L-th key thr and the number of its ties that go left.  Before position
+// p, lt(p) keys are below thr and eq(p) equal to it; a tie goes left iff its
+// rank among ties is < ties_needed, so the lefts before p number lt(p) +
+// min(eq(p), ties_needed): one scan of the packed (lt, eq) counts places
+// every element.  run_lt / run_eq: those counts before the tile, advanced
+// past it.  The tile's lefts land in one run of out, its rights in another:
+// the ids are staged in LDS in output order and both runs written with
+// contiguous stores.  Every thread of the workgroup calls it (three
+// barriers, the stage reusable on return).
+template <int NT>
+__device__ __forceinline__ void partition_tile(const uint32_t (&k)[8], const int32_t (&idv)[8], int p0, int n,
+                                               uint32_t thr, int ties_needed, int cL, int& run_lt,
+                                               int& run_eq, int* s_tmp, int32_t* s_stage,
+                                               int32_t* __restrict__ out) {
+  constexpr int E = 8;
+  const int tid = threadIdx.x;
+  int lt = 0, eq = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool valid = p0 + tid * E + e < n;
+    lt += (valid && k[e] < thr);
+    eq += (valid && k[e] == thr);
+  }
+  int tot;
+  const int packed = wg_exscan<NT>((lt << 16) | eq, s_tmp, tot);   // tile counts < 2^16
+  int lt_c = run_lt + (packed >> 16), eq_c = run_eq + (packed & 0xffff);
+  const int tile_n = min(NT * E, n - p0);
+  const int lb_tile = run_lt + min(run_eq, ties_needed);               // lefts before the tile
+  const int la_tile = run_lt + (tot >> 16) + min(run_eq + (tot & 0xffff), ties_needed);
+  const int nl_tile = la_tile - lb_tile;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int p = p0 + tid * E + e;
+    if (p >= n) continue;
+    const int left_before = lt_c + min(eq_c, ties_needed);
+    bool l;
+    if (k[e] < thr) {
+      l = true;
+      ++lt_c;
+    } else if (k[e] == thr) {
+      l = eq_c < ties_needed;
+      ++eq_c;
+    } else {
+      l = false;
+    }
+    // position in the tile's output: lefts first, then rights, both in order
+    const int j = l ? left_before - lb_tile : nl_tile + (p - left_before) - (p0 - lb_tile);
+    s_stage[j] = idv[e];
+  }
+  __syncthreads();
+  const int rb_tile = p0 - lb_tile;                                     // rights before the tile
+  for (int j = tid; j < tile_n; j += NT) {
+    const int dst = (j < nl_tile) ? lb_tile + j : cL + rb_tile + (j - nl_tile);
+    if (dst < n) out[dst] = s_stage[j];
+  }
+  __syncthreads();   // the stage is rewritten by the next tile
+  run_lt += tot >> 16;
+  run_eq += tot & 0xffff;
+}
+
+// The partition of the large groups, one workgroup per RG_SEG positions of a
+// group, after the many-workgroup radix rounds (thr and the ties that go left
+// in rec).  seg_count stores each segment's keys below and equal to thr,
+// packed (below << 16 | equal); seg_partition takes the counts before its
+// segment as the sums over the earlier segments and places the segment as
+// one tile of the one-workgroup partition: the same positions for every id.
+constexpr int SEG_T = RG_SEG / 8;   // 1024 threads, 8 positions each
+
+__global__ __launch_bounds__(RG_T) void seg_count(const float* __restrict__ s, const int* __restrict__ rec,
+                                                  int* __restrict__ segcnt, int N, int BK, int nb, int level,
+                                                  int S, int nseg_max) {
+  __shared__ int s_red[2][RG_T / 64];
+  const int slot = blockIdx.x / nseg_max, seg = blockIdx.x % nseg_max, t = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int start, nbg;
+  if (!group_of_slot(slot, level, nb, start, nbg) || nbg < 2) return;
+  const long g0 = (long)start * BK;
+  const int n = (int)(min((long)N, (long)(start + nbg) * BK) - g0);
+  const int i0 = seg * RG_SEG;
+  if (i0 >= n) return;
+  const int i1 = min(n, i0 + RG_SEG);
+  const uint32_t thr = (uint32_t)rec[((long)t * S + slot) * RG_REC];
+  const long base = (long)t * N + g0;
+  int lt = 0, eq = 0;
+  constexpr int U = 8;
+  for (int j0 = i0; j0 < i1; j0 += U * RG_T) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = j0 + u * RG_T + tid;
+      v[u] = (i < i1) ? s[base + i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = j0 + u * RG_T + tid;
+      const uint32_t k = pref_key_desc(v[u]);
+      lt += (i < i1 && k < thr);
+      eq += (i < i1 && k == thr);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    lt += __shfl_xor(lt, o, 64);
+    eq += __shfl_xor(eq, o, 64);
+  }
+  if (lane == 0) {
+    s_red[0][wave] = lt;
+    s_red[1][wave] = eq;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int a = 0, b = 0;
+#pragma unroll
+    for (int w = 0; w < RG_T / 64; ++w) {
+      a += s_red[0][w];
+      b += s_red[1][w];
+    }
+    segcnt[((long)t * (1 << level) + slot) * nseg_max + seg] = (a << 16) | b;   // each <= RG_SEG
+  }
+}
+
+__global__ __launch_bounds__(SEG_T) void seg_partition(const float* __restrict__ s,
+                                                      const int32_t* __restrict__ ids_in,
+                                                      int32_t* __restrict__ ids_out, int N, int BK, int nb,
+                                                      int level, const int* __restrict__ rec,
+                                                      const int* __restrict__ segcnt, int S, int nseg_max) {
+  __shared__ int s_tmp[SEG_T / 64];
+  __shared__ int32_t s_stage[RG_SEG];
+  __shared__ int s_before[2];
+  const int slot = blockIdx.x / nseg_max, seg = blockIdx.x % nseg_max, t = blockIdx.y;
+  const int tid = threadIdx.x;
+  int start, nbg;
+  if (!group_of_slot(slot, level, nb, start, nbg)) return;
+  const long g0 = (long)start * BK;
+  const int n = (int)(min((long)N, (long)(start + nbg) * BK) - g0);
+  const int i0 = seg * RG_SEG;
+  if (i0 >= n) return;
+  const long base = (long)t * N + g0;
+  if (nbg < 2) {  // a leaf carried through this level: copy
+    for (int i = i0 + tid; i < min(n, i0 + RG_SEG); i += SEG_T) ids_out[base + i] = ids_in[base + i];
+    return;
+  }
+  const int cL = ((nbg + 1) >> 1) * BK;
+  const int* r = rec + ((long)t * S + slot) * RG_REC;
+  const uint32_t thr = (uint32_t)r[0];
+  const int ties_needed = r[1];
+  if (tid < 64) {   // keys below / equal to thr in the earlier segments
+    const int* sc = segcnt + ((long)t * (1 << level) + slot) * nseg_max;
+    int bl = 0, be = 0;
+    for (int g = tid; g < seg; g += 64) {
+      const int c = sc[g];
+      bl += c >> 16;
+      be += c & 0xffff;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      bl += __shfl_xor(bl, o, 64);
+      be += __shfl_xor(be, o, 64);
+    }
+    if (tid == 0) {
+      s_before[0] = bl;
+      s_before[1] = be;
+    }
+  }
+  uint32_t k[8];
+  int32_t idv[8];
+  fetch8(s, ids_in, base, n, i0 + tid * 8, (base & 3) == 0, k, idv);
+  __syncthreads();
+  int run_lt = s_before[0], run_eq = s_before[1];
+  partition_tile<SEG_T>(k, idv, i0, n, thr, ties_needed, cL, run_lt, run_eq, s_tmp, s_stage, ids_out + base);
+}
+
+// Groups of at most 64 blocks: one workgroup per group radix-selects the
+// c_L-th key of the group's scores (streamed from global; L2-resident at
+// these sizes), then stable-partitions the ids tile by tile.
 template <int NT>
 __global__ __launch_bounds__(NT) void select_partition(const float* __restrict__ s,
                                                        const int32_t* __restrict__ ids_in,
                                                        int32_t* __restrict__ ids_out, int N,
-                                                       int BK, int nb, int level,
-                                                       const int* __restrict__ given, int S) {
+                                                       int BK, int nb, int level) {
   __shared__ int s_hist[256];
   __shared__ int s_whist[NT / 64][256];  // one histogram per wave (less atomic contention)
   __shared__ int s_tmp[NT / 64];
@@ -605,10 +806,10 @@ __global__ __launch_bounds__(NT) void select_partition(const float* __restrict__
   }
   const int cL = ((nbg + 1) >> 1) * BK;
   if (tid == 0) {
-    s_prefix = given ? (uint32_t)given[((long)t * S + slot) * RG_REC] : 0u;
-    s_need = given ? given[((long)t * S + slot) * RG_REC + 1] : cL;
+    s_prefix = 0u;
+    s_need = cL;
   }
-  for (int shift = 24; shift >= 0 && !given; shift -= 8) {
+  for (int shift = 24; shift >= 0; shift -= 8) {
     for (int i = tid; i < (NT / 64) * 256; i += NT) (&s_whist[0][0])[i] = 0;
     __syncthreads();
     const uint32_t pre = s_prefix;
@@ -639,44 +840,16 @@ __global__ __launch_bounds__(NT) void select_partition(const float* __restrict__
     if (tid < 64) radix_pick(s_hist, &s_prefix, &s_need, shift);
     __syncthreads();
   }
-  if (given) __syncthreads();
   const uint32_t thr = s_prefix;
   const int ties_needed = s_need;
-  // stable partition in tiles of NT * E positions, E consecutive per thread.
-  // Before position p, lt(p) keys are below the threshold and eq(p) equal to
-  // it; a tie goes left iff its rank among ties is < ties_needed, so the
-  // lefts before p number lt(p) + min(eq(p), ties_needed): one scan of the
-  // packed (lt, eq) counts per tile places every element.  Each tile's keys
-  // and ids are loaded one tile ahead.
+  // stable partition in tiles of NT * 8 positions, 8 consecutive per
+  // thread; each tile's keys and ids are loaded one tile ahead
   constexpr int E = 8;
   int run_lt = 0, run_eq = 0;  // below / equal before this tile
   uint32_t kn[E];
   int32_t idn[E];
   const bool vec_ok = (base & 3) == 0;   // 16-byte aligned rows of this group
-  auto fetch = [&](int p0) {
-    const int q = p0 + tid * E;
-    if (vec_ok && q + E <= n) {   // two 16-byte loads per array
-      const float4 s0 = *reinterpret_cast<const float4*>(s + base + q);
-      const float4 s1 = *reinterpret_cast<const float4*>(s + base + q + 4);
-      const int4 i0 = *reinterpret_cast<const int4*>(ids_in + base + q);
-      const int4 i1 = *reinterpret_cast<const int4*>(ids_in + base + q + 4);
-      const float sv[E] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-      const int32_t iv[E] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        kn[e] = pref_key_desc(sv[e]);
-        idn[e] = iv[e];
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int p = q + e;
-        kn[e] = (p < n) ? pref_key_desc(s[base + p]) : 0xffffffffu;
-        idn[e] = (p < n) ? ids_in[base + p] : 0;
-      }
-    }
-  };
-  fetch(0);
+  fetch8(s, ids_in, base, n, tid * E, vec_ok, kn, idn);
   for (int p0 = 0; p0 < n; p0 += NT * E) {
     uint32_t k[E];
     int32_t idv[E];
@@ -685,51 +858,8 @@ __global__ __launch_bounds__(NT) void select_partition(const float* __restrict__
       k[e] = kn[e];
       idv[e] = idn[e];
     }
-    if (p0 + NT * E < n) fetch(p0 + NT * E);
-    int lt = 0, eq = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const bool valid = p0 + tid * E + e < n;
-      lt += (valid && k[e] < thr);
-      eq += (valid && k[e] == thr);
-    }
-    int tot;
-    const int packed = wg_exscan<NT>((lt << 16) | eq, s_tmp, tot);   // tile counts < 2^16
-    int lt_c = run_lt + (packed >> 16), eq_c = run_eq + (packed & 0xffff);
-    // the tile's lefts land in one run, its rights in another: stage the ids
-    // in LDS in output order, then write both runs with contiguous stores
-    const int tile_n = min(NT * E, n - p0);
-    const int lb_tile = run_lt + min(run_eq, ties_needed);               // lefts before the tile
-    const int la_tile = run_lt + (tot >> 16) + min(run_eq + (tot & 0xffff), ties_needed);
-    const int nl_tile = la_tile - lb_tile;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int p = p0 + tid * E + e;
-      if (p >= n) continue;
-      const int left_before = lt_c + min(eq_c, ties_needed);
-      bool l;
-      if (k[e] < thr) {
-        l = true;
-        ++lt_c;
-      } else if (k[e] == thr) {
-        l = eq_c < ties_needed;
-        ++eq_c;
-      } else {
-        l = false;
-      }
-      // position in the tile's output: lefts first, then rights, both in order
-      const int j = l ? left_before - lb_tile : nl_tile + (p - left_before) - (p0 - lb_tile);
-      s_stage[j] = idv[e];
-    }
-    __syncthreads();
-    const int rb_tile = p0 - lb_tile;                                     // rights before the tile
-    for (int j = tid; j < tile_n; j += NT) {
-      const int dst = (j < nl_tile) ? lb_tile + j : cL + rb_tile + (j - nl_tile);
-      if (dst < n) ids_out[base + dst] = s_stage[j];
-    }
-    __syncthreads();   // the stage is rewritten by the next tile
-    run_lt += tot >> 16;
-    run_eq += tot & 0xffff;
+    if (p0 + NT * E < n) fetch8(s, ids_in, base, n, p0 + NT * E + tid * E, vec_ok, kn, idn);
+    partition_tile<NT>(k, idv, p0, n, thr, ties_needed, cL, run_lt, run_eq, s_tmp, s_stage, ids_out + base);
   }
 }
 
@@ -837,21 +967,28 @@ __global__ __launch_bounds__(FIN_T) void finisher(const T* __restrict__ xh,
     const int rslot = ttid / CPR, cc = (ttid % CPR) * VE;
     int* hist = s_hist[team];
     float* vecs = s_vec[team];
-    // this lane's 16-byte chunk of the rows at positions a + rslot + k RPT,
-    // their local row numbers and original ids: read from LDS once for the
-    // four row passes below
+    // this lane's 16-byte chunk of the rows at positions a + rslot + k RPT:
+    // read from LDS once for the four row passes below
     uint4 rw[FIN_KR];
-    int rid[FIN_KR], oid[FIN_KR];
+    {
+      int rid[FIN_KR];
 #pragma unroll
-    for (int k = 0; k < FIN_KR; ++k) {
-      const int i = rslot + k * RPT;
-      rid[k] = (i < len) ? (int)s_lid[a + i] : 0;
-    }
+      for (int k = 0; k < FIN_KR; ++k) {
+        const int i = rslot + k * RPT;
+        rid[k] = (i < len) ? (int)s_lid[a + i] : 0;
+      }
 #pragma unroll
-    for (int k = 0; k < FIN_KR; ++k) {
-      rw[k] = *reinterpret_cast<const uint4*>(sX + rid[k] * RS + cc);
-      oid[k] = s_oid[rid[k]];
+      for (int k = 0; k < FIN_KR; ++k) rw[k] = *reinterpret_cast<const uint4*>(sX + rid[k] * RS + cc);
     }
+    // after a row's dot is summed over its CPR lanes every one of them holds
+    // it; lane c of the row's lanes keeps the dot of slot k = c (lanes c >=
+    // FIN_KR keep none), so each row's dot ends on one lane: its local row
+    // number and original id are looked up once per split
+    const int own_k = ttid % CPR;
+    const int own_i = rslot + own_k * RPT;
+    const bool own_ok = own_k < FIN_KR && own_i < len;
+    const int own_rid = own_ok ? (int)s_lid[a + own_i] : 0;
+    const int own_oid = s_oid[own_rid];
     auto widen = [&](const uint4& q, float (&v)[VE]) {
       const uint32_t w[4] = {q.x, q.y, q.z, q.w};
       if constexpr (sizeof(T) == 2) {
@@ -865,41 +1002,57 @@ __global__ __launch_bounds__(FIN_T) void finisher(const T* __restrict__ xh,
         for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(w[i]);
       }
     };
-    // dot of every row of [a, a+len) with vecs; calls f(i, k, dot) on the
-    // lane that owns the row's first chunk (k: the row's cache slot)
-    auto rows_dot = [&](auto&& f) {
-      float vec[VE];
-#pragma unroll
-      for (int e = 0; e < VE; ++e) vec[e] = vecs[cc + e];
+    // dot of every row of [a, a+len) with a vector: chunk_dot(x) is this
+    // lane's partial over its chunk; returns the dot of the row this lane
+    // keeps (garbage where !own_ok)
+    auto rows_dot = [&](auto&& chunk_dot) -> float {
+      float mine = 0.f;
 #pragma unroll
       for (int k = 0; k < FIN_KR; ++k) {
         if (k * RPT < len) {   // uniform
-          float v[VE];
-          widen(rw[k], v);
-          float acc = 0.f;
-#pragma unroll
-          for (int e = 0; e < VE; ++e) acc = fmaf(v[e], vec[e], acc);
-          acc = group_sum<CPR>(acc);
-          const int i = rslot + k * RPT;
-          if (i < len && (ttid % CPR) == 0) f(i, k, acc);
+          const float acc = group_sum<CPR>(chunk_dot(rw[k]));
+          mine = (own_k == k) ? acc : mine;
         }
       }
+      return mine;
     };
-    // argmin over [a, a+len) of (row . vecs, original id) -> local row: the
-    // winning row rides along the reduction, so one barrier suffices
-    auto argmin_range = [&]() -> int {
-      uint64_t best = ~0ull;
-      int brow = 0;
-      rows_dot([&](int, int k, float dv) {
-        const uint64_t key = argmin_key(dv, oid[k]);
-        if (key < best) {
-          best = key;
-          brow = rid[k];
-        }
+    // partial dot with the fp32 vector in vecs (widened chunk, one FMA chain)
+    auto dot_f32 = [&]() -> float {
+      float vec[VE];
+#pragma unroll
+      for (int e = 0; e < VE; ++e) vec[e] = vecs[cc + e];
+      return rows_dot([&](const uint4& x) {
+        // widened afresh (opaque copy): sharing the centroid pass's widened
+        // chunks would keep all of them live between the two passes
+        uint32_t w0 = x.x, w1 = x.y, w2 = x.z, w3 = x.w;
+        asm volatile("" : "+v"(w0), "+v"(w1), "+v"(w2), "+v"(w3));
+        float v[VE];
+        widen(make_uint4(w0, w1, w2, w3), v);
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc = fmaf(v[e], vec[e], acc);
+        return acc;
       });
+    };
+    // bf16 rows against a bf16 row: both operands exact, two products per
+    // v_dot2_f32_bf16, no widening
+    auto dot2_chunk = [](const uint4& x, const uint4& y) -> float {
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      const uint32_t xw[4] = {x.x, x.y, x.z, x.w}, yw[4] = {y.x, y.y, y.z, y.w};
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xw[i]),
+                                              __builtin_bit_cast(bf16x2_t, yw[i]), acc, false);
+      return acc;
+    };
+    // argmin over [a, a+len) of (the kept dot, original id) -> local row: the
+    // winning row rides along the reduction, so one barrier suffices
+    auto argmin_range = [&](float dv) -> int {
+      const uint64_t best = own_ok ? argmin_key(dv, own_oid) : ~0ull;
       const uint64_t wb = group_min_u64<64>(best);
       const uint64_t holders = __builtin_amdgcn_ballot_w64(best == wb);
-      const int wrow = __builtin_amdgcn_readlane(brow, __builtin_ctzll(holders));
+      const int wrow = __builtin_amdgcn_readlane(own_rid, __builtin_ctzll(holders));
       if (lane == 0) {
         s_min[wave] = wb;
         s_minr[wave] = wrow;
@@ -952,14 +1105,27 @@ __global__ __launch_bounds__(FIN_T) void finisher(const T* __restrict__ xh,
       }
       __syncthreads();
     }
-    const int rA = argmin_range();
-    for (int c = ttid; c < D; c += NT) vecs[c] = Elem<T>::load(sX + rA * RS + c);
-    __syncthreads();
-    const int rB = argmin_range();
-    for (int c = ttid; c < D; c += NT)
-      vecs[c] = Elem<T>::load(sX + rA * RS + c) - Elem<T>::load(sX + rB * RS + c);
-    __syncthreads();
-    rows_dot([&](int i, int, float dv) { s_val[a + i] = dv; });
+    // pole A: the row least aligned with the centroid sum (fp32 vector)
+    const int rA = argmin_range(dot_f32());
+    float sv;
+    if constexpr (sizeof(T) == 2) {
+      // pole B and the score against the pole rows themselves (bf16, exact):
+      // s = x . x_A - x . x_B, each lane's two partials differenced before
+      // the lane sum
+      const uint4 xa = *reinterpret_cast<const uint4*>(sX + rA * RS + cc);
+      const int rB = argmin_range(rows_dot([&](const uint4& x) { return dot2_chunk(x, xa); }));
+      const uint4 xb = *reinterpret_cast<const uint4*>(sX + rB * RS + cc);
+      sv = rows_dot([&](const uint4& x) { return dot2_chunk(x, xa) - dot2_chunk(x, xb); });
+    } else {
+      for (int c = ttid; c < D; c += NT) vecs[c] = Elem<T>::load(sX + rA * RS + c);
+      __syncthreads();
+      const int rB = argmin_range(dot_f32());
+      for (int c = ttid; c < D; c += NT)
+        vecs[c] = Elem<T>::load(sX + rA * RS + c) - Elem<T>::load(sX + rB * RS + c);
+      __syncthreads();
+      sv = dot_f32();
+    }
+    if (own_ok) s_val[a + own_i] = sv;
     __syncthreads();
     // the cL-th key: radix select, 8 bits per round, the team's threads
     // counting into its LDS histogram, its first wave picking the digit
@@ -1105,7 +1271,8 @@ size_t split_ws_bytes(int count, int N, int D, int BK, int dtype) {
   b += up256((size_t)count * p.S * D * 4);          // diff
   b += 2 * up256((size_t)count * p.S * 4);          // poleA, poleB
   b += up256((size_t)count * p.S * RG_REC * 4);     // capacity-select records
-  b += up256((size_t)count * radix_hist_slots(N, BK, p.nb, p.Lf) * 256 * 4);   // their segment counts
+  b += up256((size_t)count * radix_hist_slots(N, BK, p.nb, p.Lf) * 256 * 4);   // their segment histograms
+  b += up256((size_t)count * radix_hist_slots(N, BK, p.nb, p.Lf) * 4);         // segment (below, equal) counts
   return b;
 }
 
@@ -1128,7 +1295,8 @@ static int split_t(int count, int N, int BK, const void* xhv, int32_t* perm_lo,
   int32_t* poleA = (int32_t*)w; w += up256((size_t)count * p.S * 4);
   int32_t* poleB = (int32_t*)w; w += up256((size_t)count * p.S * 4);
   int* rec = (int*)w; w += up256((size_t)count * p.S * RG_REC * 4);
-  int* hpart = (int*)w;
+  int* hpart = (int*)w; w += up256((size_t)count * radix_hist_slots(N, BK, p.nb, p.Lf) * 256 * 4);
+  int* segcnt = (int*)w;
   const long total = (long)count * N;
   if (p.nb <= 1) {
     hipLaunchKernelGGL(iota_kernel, dim3((int)std::min<long>((total + 255) / 256, 8192)), dim3(256), 0, st, perm_lo, perm_hi, split_at, N, perm_ld, 0, total);
@@ -1154,8 +1322,8 @@ static int split_t(int count, int N, int BK, const void* xhv, int32_t* perm_lo,
       hipLaunchKernelGGL((argmin_partial<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, cen, poleA, mpart, N, BK, p.nb, lev, p.S, 1);
       hipLaunchKernelGGL((argmin_reduce<T, D>), gs, dim3(64), 0, st, mpart, xh, poleA, poleB, diff, N, p.nb, lev, p.S, 1);
       hipLaunchKernelGGL((score_kernel<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, diff, s, N, BK, p.nb, lev, p.S);
-      // the largest groups: the threshold by many workgroups per group, then
-      // the wide partition; groups of more than 64 blocks: the wide form
+      // groups of more than 64 blocks: the threshold and the partition by
+      // many workgroups per group; smaller ones: one workgroup per group
       if (wide_select(p.nb, lev)) {
         const int gmax = (p.nb + (1 << lev) - 1) >> lev;   // largest group, blocks
         const int nseg_max = (int)(((long)gmax * BK + RG_SEG - 1) / RG_SEG);
@@ -1165,14 +1333,12 @@ static int split_t(int count, int N, int BK, const void* xhv, int32_t* perm_lo,
           hipLaunchKernelGGL(radix_pick_groups, gs, dim3(RG_T), 0, st, rec, hpart, N, BK, p.nb, lev, p.S,
                              nseg_max, shift);
         }
-        hipLaunchKernelGGL(select_partition<1024>, gs, dim3(1024), 0, st, s, cur, nxt, N, BK, p.nb, lev,
-                           (const int*)rec, p.S);
-      } else if ((p.nb >> lev) > 64) {
-        hipLaunchKernelGGL(select_partition<1024>, gs, dim3(1024), 0, st, s, cur, nxt, N, BK, p.nb, lev,
-                           (const int*)nullptr, p.S);
+        hipLaunchKernelGGL(seg_count, dim3(S * nseg_max, count), dim3(RG_T), 0, st, s, rec, segcnt, N, BK, p.nb,
+                           lev, p.S, nseg_max);
+        hipLaunchKernelGGL(seg_partition, dim3(S * nseg_max, count), dim3(SEG_T), 0, st, s, cur, nxt, N, BK,
+                           p.nb, lev, (const int*)rec, (const int*)segcnt, p.S, nseg_max);
       } else {
-        hipLaunchKernelGGL(select_partition<SPL_T>, gs, dim3(SPL_T), 0, st, s, cur, nxt, N, BK, p.nb, lev,
-                           (const int*)nullptr, p.S);
+        hipLaunchKernelGGL(select_partition<SPL_T>, gs, dim3(SPL_T), 0, st, s, cur, nxt, N, BK, p.nb, lev);
       }
       int rc = spark_check_launch("split level");
       if (rc) return rc;
@@ -1257,13 +1423,13 @@ int debug_argmin_launch(int count, int n, const float* vals, const int32_t* ids,
 }
 
 // One capacity partition per row of n scores: the split's level-0 kernels
-// (the many-workgroup threshold above 512 blocks, the 1024-thread select
-// above 64 blocks, the 256-thread one below), with the capacity of a group of
-// ceil(n / BK) blocks.
+// (above 64 blocks the many-workgroup radix rounds and the segmented
+// partition, the one-workgroup select below), with the capacity of a group
+// of ceil(n / BK) blocks.
 size_t debug_partition_ws_bytes(int count, int n, int BK) {
   const int nb = cdiv(n, BK);
   const long nseg = wide_select(nb, 0) ? ((long)nb * BK + RG_SEG - 1) / RG_SEG : 0;
-  return up256((size_t)count * RG_REC * 4) + up256((size_t)count * nseg * 256 * 4);
+  return up256((size_t)count * RG_REC * 4) + up256((size_t)count * nseg * 256 * 4) + up256((size_t)count * nseg * 4);
 }
 
 int debug_partition_launch(int count, int n, int BK, const float* s, const int32_t* ids_in,
@@ -1274,19 +1440,18 @@ int debug_partition_launch(int count, int n, int BK, const float* s, const int32
   const dim3 gs(1, count);
   if (wide_select(nb, 0)) {
     const int nseg_max = (int)(((long)nb * BK + RG_SEG - 1) / RG_SEG);
+    int* segcnt = (int*)((char*)hpart + up256((size_t)count * nseg_max * 256 * 4));
     for (int shift = 24; shift >= 0; shift -= 8) {
       hipLaunchKernelGGL(radix_hist, dim3(nseg_max, count), dim3(RG_T), 0, st, s, rec, hpart, n, BK, nb, 0, 1,
                          nseg_max, shift);
       hipLaunchKernelGGL(radix_pick_groups, gs, dim3(RG_T), 0, st, rec, hpart, n, BK, nb, 0, 1, nseg_max, shift);
     }
-    hipLaunchKernelGGL(select_partition<1024>, gs, dim3(1024), 0, st, s, ids_in, ids_out, n, BK, nb, 0,
-                       (const int*)rec, 1);
-  } else if (nb > 64) {
-    hipLaunchKernelGGL(select_partition<1024>, gs, dim3(1024), 0, st, s, ids_in, ids_out, n, BK, nb, 0,
-                       (const int*)nullptr, 1);
+    hipLaunchKernelGGL(seg_count, dim3(nseg_max, count), dim3(RG_T), 0, st, s, rec, segcnt, n, BK, nb, 0, 1,
+                       nseg_max);
+    hipLaunchKernelGGL(seg_partition, dim3(nseg_max, count), dim3(SEG_T), 0, st, s, ids_in, ids_out, n, BK, nb, 0,
+                       (const int*)rec, (const int*)segcnt, 1, nseg_max);
   } else {
-    hipLaunchKernelGGL(select_partition<SPL_T>, gs, dim3(SPL_T), 0, st, s, ids_in, ids_out, n, BK, nb, 0,
-                       (const int*)nullptr, 1);
+    hipLaunchKernelGGL(select_partition<SPL_T>, gs, dim3(SPL_T), 0, st, s, ids_in, ids_out, n, BK, nb, 0);
   }
   return spark_check_launch("debug partition");
 }
