@@ -326,9 +326,7 @@ def spark_moments(q, k, n_anchor: Optional[int] = None):
 def spark_msqrt(M):
     count, d, _ = M.shape
     W = torch.empty_like(M)
-    nws = count * d * d * 4
-    ws = _ws(nws, M.device)
-    _check(lib().spark_msqrt(count, d, _ptr(M), _ptr(W), _ptr(ws), nws, _stream()), "spark_msqrt")
+    _check(lib().spark_msqrt(count, d, _ptr(M), _ptr(W), None, 0, _stream()), "spark_msqrt")
     return W
 
 

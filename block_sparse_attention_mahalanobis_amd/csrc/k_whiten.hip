@@ -276,14 +276,13 @@ int moments_launch(int H, int N, int D, int dtype, const void* q, const void* k,
 // ridge delta = 1e-6 bounds the smallest eigenvalue the iteration has to
 // reach (and keeps rank-deficient moments from amplifying round-off in their
 // null space); it moves W by at most sqrt(delta * s) in directions of zero
-// energy.  Y and Z live in LDS; T goes through a per-matrix global scratch
-// (L2-resident).  Stops when max|ZY - I| < 3e-5, after at most 40 iterations.
+// energy.  Y, Z and T live in LDS (two D x D slots: see the loop).  Stops
+// when max|ZY - I| < 3e-5, after at most 40 iterations.
 // ---------------------------------------------------------------------------
 constexpr int MSQ_T = 512;
 template <int D>
 __global__ __launch_bounds__(MSQ_T) void msqrt_kernel(const float* __restrict__ M,
-                                                    float* __restrict__ W,
-                                                    float* __restrict__ Tscr) {
+                                                    float* __restrict__ W) {
   // each thread owns an SI x SJ block of every product: 8 x 4 (d = 128) or
   // 4 x 2 (d = 64) with MSQ_T threads, two waves per SIMD
   constexpr int SI = (D == 128) ? 8 : 4, SJ = SI / 2;
@@ -294,7 +293,6 @@ __global__ __launch_bounds__(MSQ_T) void msqrt_kernel(const float* __restrict__ 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const long off = (long)blockIdx.x * D * D;
   const float* m = M + off;
-  float* tg = Tscr + off;
   const int bi = (tid / (D / SJ)) * SI, bj = (tid % (D / SJ)) * SJ;
 
   // Frobenius norm (symmetrised input)
@@ -325,90 +323,117 @@ __global__ __launch_bounds__(MSQ_T) void msqrt_kernel(const float* __restrict__ 
   }
   __syncthreads();
 
+  // Y in sA, Z in sB at the start of every iteration; T never leaves the
+  // workgroup: each thread keeps its own block of Z in registers while T
+  // takes Z's place for Y T, then Z takes Y's place for T Z
+  float* sA = sY;
+  float* sB = sZ;
   for (int it = 0; it < 40; ++it) {
-    // P = Z Y (this thread's block), T = (3I - P)/2 to global
+    // P = Z Y (this thread's block)
     float acc[SI][SJ];
 #pragma unroll
     for (int i = 0; i < SI; ++i)
 #pragma unroll
       for (int j = 0; j < SJ; ++j) acc[i][j] = 0.f;
+#pragma unroll 4
     for (int kx = 0; kx < D; ++kx) {
       float a[SI], b[SJ];
 #pragma unroll
-      for (int i = 0; i < SI; ++i) a[i] = sZ[(bi + i) * D + kx];
+      for (int i = 0; i < SI; ++i) a[i] = sB[(bi + i) * D + kx];
 #pragma unroll
-      for (int j = 0; j < SJ; ++j) b[j] = sY[kx * D + bj + j];
+      for (int j = 0; j < SJ; ++j) b[j] = sA[kx * D + bj + j];
 #pragma unroll
       for (int i = 0; i < SI; ++i)
 #pragma unroll
         for (int j = 0; j < SJ; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
     }
     float dev = 0.f;
+    float zk[SI][SJ];   // this thread's block of Z
 #pragma unroll
     for (int i = 0; i < SI; ++i)
 #pragma unroll
       for (int j = 0; j < SJ; ++j) {
         const float id = (bi + i == bj + j) ? 1.f : 0.f;
         dev = fmaxf(dev, fabsf(acc[i][j] - id));
-        tg[(bi + i) * D + bj + j] = 0.5f * (3.f * id - acc[i][j]);
+        acc[i][j] = 0.5f * (3.f * id - acc[i][j]);   // T
+        zk[i][j] = sB[(bi + i) * D + bj + j];
       }
     dev = wave_max(dev);
     if (lane == 0) s_red[wave] = dev;
-    __syncthreads();  // T visible to the workgroup; s_red ready
+    __syncthreads();  // s_red ready; every read of Z done
     float gdev = s_red[0];
 #pragma unroll
     for (int w = 1; w < NW; ++w) gdev = fmaxf(gdev, s_red[w]);
     if (gdev < 3e-5f) break;
-    // Ynew = Y T, Znew = T Z
-    float ay[SI][SJ], az[SI][SJ];
 #pragma unroll
     for (int i = 0; i < SI; ++i)
 #pragma unroll
-      for (int j = 0; j < SJ; ++j) { ay[i][j] = 0.f; az[i][j] = 0.f; }
+      for (int j = 0; j < SJ; ++j) sB[(bi + i) * D + bj + j] = acc[i][j];
+    __syncthreads();  // T in sB
+    // Ynew = Y T
+    float ay[SI][SJ];
+#pragma unroll
+    for (int i = 0; i < SI; ++i)
+#pragma unroll
+      for (int j = 0; j < SJ; ++j) ay[i][j] = 0.f;
+#pragma unroll 4
     for (int kx = 0; kx < D; ++kx) {
-      float ya[SI], tb[SJ], ta[SI], zb[SJ];
+      float ya[SI], tb[SJ];
 #pragma unroll
-      for (int i = 0; i < SI; ++i) {
-        ya[i] = sY[(bi + i) * D + kx];
-        ta[i] = tg[(bi + i) * D + kx];
-      }
+      for (int i = 0; i < SI; ++i) ya[i] = sA[(bi + i) * D + kx];
 #pragma unroll
-      for (int j = 0; j < SJ; ++j) {
-        tb[j] = tg[kx * D + bj + j];
-        zb[j] = sZ[kx * D + bj + j];
-      }
+      for (int j = 0; j < SJ; ++j) tb[j] = sB[kx * D + bj + j];
 #pragma unroll
       for (int i = 0; i < SI; ++i)
 #pragma unroll
-        for (int j = 0; j < SJ; ++j) {
-          ay[i][j] = fmaf(ya[i], tb[j], ay[i][j]);
-          az[i][j] = fmaf(ta[i], zb[j], az[i][j]);
-        }
+        for (int j = 0; j < SJ; ++j) ay[i][j] = fmaf(ya[i], tb[j], ay[i][j]);
     }
-    __syncthreads();  // everyone done reading old Y, Z and T
+    __syncthreads();  // every read of Y done
+#pragma unroll
+    for (int i = 0; i < SI; ++i)
+#pragma unroll
+      for (int j = 0; j < SJ; ++j) sA[(bi + i) * D + bj + j] = zk[i][j];
+    __syncthreads();  // Z in sA
+    // Znew = T Z
+    float az[SI][SJ];
+#pragma unroll
+    for (int i = 0; i < SI; ++i)
+#pragma unroll
+      for (int j = 0; j < SJ; ++j) az[i][j] = 0.f;
+#pragma unroll 4
+    for (int kx = 0; kx < D; ++kx) {
+      float ta[SI], zb[SJ];
+#pragma unroll
+      for (int i = 0; i < SI; ++i) ta[i] = sB[(bi + i) * D + kx];
+#pragma unroll
+      for (int j = 0; j < SJ; ++j) zb[j] = sA[kx * D + bj + j];
+#pragma unroll
+      for (int i = 0; i < SI; ++i)
+#pragma unroll
+        for (int j = 0; j < SJ; ++j) az[i][j] = fmaf(ta[i], zb[j], az[i][j]);
+    }
+    __syncthreads();  // every read of T and Z done
 #pragma unroll
     for (int i = 0; i < SI; ++i)
 #pragma unroll
       for (int j = 0; j < SJ; ++j) {
-        sY[(bi + i) * D + bj + j] = ay[i][j];
-        sZ[(bi + i) * D + bj + j] = az[i][j];
+        sA[(bi + i) * D + bj + j] = ay[i][j];
+        sB[(bi + i) * D + bj + j] = az[i][j];
       }
     __syncthreads();
   }
   const float sc = sqrtf(fro);
   for (int e = tid; e < D * D; e += MSQ_T) {
     const int r = e / D, c = e % D;
-    W[off + e] = 0.5f * (sY[r * D + c] + sY[c * D + r]) * sc;
+    W[off + e] = 0.5f * (sA[r * D + c] + sA[c * D + r]) * sc;
   }
 }
 
-size_t msqrt_ws_bytes(int count, int D) { return (size_t)count * D * D * 4; }
-
-int msqrt_launch(int count, int D, const float* M, float* W, float* Tscr, hipStream_t st) {
+int msqrt_launch(int count, int D, const float* M, float* W, hipStream_t st) {
   if (D == 128)
-    hipLaunchKernelGGL(msqrt_kernel<128>, dim3(count), dim3(MSQ_T), 0, st, M, W, Tscr);
+    hipLaunchKernelGGL(msqrt_kernel<128>, dim3(count), dim3(MSQ_T), 0, st, M, W);
   else
-    hipLaunchKernelGGL(msqrt_kernel<64>, dim3(count), dim3(MSQ_T), 0, st, M, W, Tscr);
+    hipLaunchKernelGGL(msqrt_kernel<64>, dim3(count), dim3(MSQ_T), 0, st, M, W);
   return spark_check_launch("msqrt");
 }
 

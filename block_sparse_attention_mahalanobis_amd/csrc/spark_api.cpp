@@ -35,8 +35,7 @@ size_t moments_ws_bytes(int H, int N, int D);
 int moments_launch(int H, int N, int D, int dtype, const void* q, const void* k, float* MQ,
                    float* MK, float* anchor, int n_anchor, void* ws, hipStream_t st);
 int copy_perm_launch(long count, const int32_t* src, int32_t* dst, hipStream_t st);
-size_t msqrt_ws_bytes(int count, int D);
-int msqrt_launch(int count, int D, const float* M, float* W, float* Tscr, hipStream_t st);
+int msqrt_launch(int count, int D, const float* M, float* W, hipStream_t st);
 int whiten_launch(int count, int N, int xrows, int D, int dtype, const void* x, const float* W,
                   void* xh, hipStream_t st, float* cpart, int tree_off);
 size_t split_ws_bytes(int count, int N, int D, int BK, int dtype);
@@ -177,7 +176,7 @@ size_t reblock_ws(const spark_args* a) {
   size_t b = 0;
   b += up((size_t)2 * H * D * D * 4);                     // moments [MK | MQ]
   b += up((size_t)2 * H * D * D * 4);                     // roots  [W_Q | W_K]
-  b += up(std::max(moments_ws_bytes(H, N, D), msqrt_ws_bytes(2 * H, D)));
+  b += up(moments_ws_bytes(H, N, D));
   b += up((size_t)2 * H * Nv * D * esize(a->dtype));      // whitened (video) rows
   b += up(split_ws_bytes(2 * H, Nv, D, a->block, a->dtype));
   return b;
@@ -300,10 +299,9 @@ int spark_msqrt(int32_t count, int32_t d, const float* M, float* W, void* ws, si
   if (d != 64 && d != 128) return spark_set_error(SPARK_E_UNSUPPORTED, "%s: d=%d", fn, d);
   CHECK(check_ptr(M, fn, "M"));
   CHECK(check_ptr(W, fn, "W"));
-  CHECK(check_ptr(ws, fn, "ws"));
-  if (ws_bytes < msqrt_ws_bytes(count, d))
-    return spark_set_error(SPARK_E_WORKSPACE, "%s: ws_bytes %zu < %zu", fn, ws_bytes, msqrt_ws_bytes(count, d));
-  return msqrt_launch(count, d, M, W, (float*)ws, (hipStream_t)stream);
+  (void)ws;         // the iteration runs in LDS: no workspace
+  (void)ws_bytes;
+  return msqrt_launch(count, d, M, W, (hipStream_t)stream);
 }
 
 int spark_whiten(const spark_args* a, int32_t count, const void* x, const float* W, void* xhat,
@@ -381,7 +379,7 @@ int spark_reblock(const spark_args* a, const void* q, const void* k, const void*
     char* w = (char*)ws;
     float* Ms = (float*)w;  w += up((size_t)2 * H * D * D * 4);   // [MK | MQ]
     float* Ws = (float*)w;  w += up((size_t)2 * H * D * D * 4);   // [W_Q | W_K]
-    void* scr = w;          w += up(std::max(moments_ws_bytes(H, N, D), msqrt_ws_bytes(2 * H, D)));
+    void* scr = w;          w += up(moments_ws_bytes(H, N, D));
     void* xh = w;           w += up((size_t)2 * H * Nv * D * esize(a->dtype));
     void* sws = w;
     float* MK = Ms;
@@ -389,7 +387,7 @@ int spark_reblock(const spark_args* a, const void* q, const void* k, const void*
     // moments over all N tokens; queries are whitened by M_K^{1/2} (first H
     // roots), keys by M_Q^{1/2}; only the Nv video rows are whitened and split
     CHECK(moments_launch(H, N, D, a->dtype, q, k, MQ, MK, anchor, a->n_anchor, scr, st));
-    CHECK(msqrt_launch(2 * H, D, Ms, Ws, (float*)scr, st));
+    CHECK(msqrt_launch(2 * H, D, Ms, Ws, st));
     // bf16, d = 128, block 128: the whitening pass also stores the split's
     // root partial centroid sums (the split then skips that pass)
     float* cp0 = level0_fusable(a) ? split_level0_partials(sws, 2 * H, Nv, D, BK, a->dtype) : nullptr;
@@ -404,12 +402,12 @@ int spark_reblock(const spark_args* a, const void* q, const void* k, const void*
     char* w = (char*)ws;
     float* Ms = (float*)w;  w += up((size_t)2 * H * D * D * 4);
     float* Ws = (float*)w;  w += up((size_t)2 * H * D * D * 4);
-    void* scr = w;          w += up(std::max(moments_ws_bytes(H, N, D), msqrt_ws_bytes(2 * H, D)));
+    void* scr = w;          w += up(moments_ws_bytes(H, N, D));
     void* xh = w;           w += up((size_t)2 * H * Nv * D * esize(a->dtype));
     void* sws = w;
     float* MQ = Ms;
     CHECK(moments_launch(H, N, D, a->dtype, q, nullptr, MQ, nullptr, anchor, a->n_anchor, scr, st));
-    CHECK(msqrt_launch(H, D, MQ, Ws, (float*)scr, st));
+    CHECK(msqrt_launch(H, D, MQ, Ws, st));
     float* cp0 = level0_fusable(a) ? split_level0_partials(sws, H, Nv, D, BK, a->dtype) : nullptr;
     CHECK(whiten_launch(H, Nv, N, D, a->dtype, k, Ws, xh, st, cp0, 0));
     CHECK(split_launch(H, Nv, D, BK, a->dtype, xh, perm_k, perm_k, H, N, sws, st, cp0 != nullptr));

@@ -278,8 +278,8 @@ int spark_moments(const spark_args* args, const void* q, const void* k, float* M
 /* Symmetric PSD square roots W[i] = M[i]^{1/2} of `count` d x d matrices
  * ([blog] 01 / Method: Spark-Reblock, M_K^{1/2}).  Coupled Newton-Schulz in
  * fp32 after scaling by the Frobenius norm (the input is symmetrised first);
- * an all-zero M gives W = 0, a non-finite M gives NaN.  ws: at least
- * count * d * d * 4 bytes. */
+ * an all-zero M gives W = 0, a non-finite M gives NaN.  ws, ws_bytes:
+ * unused (the iteration runs in on-chip memory); may be NULL and 0. */
 int spark_msqrt(int32_t count, int32_t d, const float* M, float* W, void* ws, size_t ws_bytes,
                 spark_stream_t stream);
 
