@@ -58,11 +58,49 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ x,
     if (ch < BK * C16) {
       if (xp)
         *reinterpret_cast<uint4*>(xp + ((long)h * Np + (long)B * BK + j) * D + cc * (16 / (int)sizeof(T))) = buf[i];
-      *reinterpret_cast<uint4*>(tile + j * RS + cc * (16 / (int)sizeof(T))) = buf[i];
+      if (xpt) *reinterpret_cast<uint4*>(tile + j * RS + cc * (16 / (int)sizeof(T))) = buf[i];
     }
   }
-  __syncthreads();
+  if (xbar && !ctx) {
+    // block means from the loaded chunks: a thread holds chunk column
+    // tid % C16 of rows tid / C16 + (256 / C16) i, summed in i order, then
+    // the lanes of a wave holding the same column (a fixed butterfly), then
+    // the four waves in order
+    __shared__ float s_part[4][D];
+    constexpr int VE = 16 / (int)sizeof(T);
+    float part[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) part[e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      if (src[i] >= 0) {
+        const uint32_t w[4] = {buf[i].x, buf[i].y, buf[i].z, buf[i].w};
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            part[2 * e] += __uint_as_float(w[e] << 16);
+            part[2 * e + 1] += __uint_as_float(w[e] & 0xffff0000u);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) part[e] += __uint_as_float(w[e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int o = C16; o < 64; o <<= 1)
+#pragma unroll
+      for (int e = 0; e < VE; ++e) part[e] += __shfl_xor(part[e], o, 64);
+    const int lane = tid & 63, wave = tid >> 6;
+    if (lane < C16)
+#pragma unroll
+      for (int e = 0; e < VE; ++e) s_part[wave][lane * VE + e] = part[e];
+    __syncthreads();
+    for (int c = tid; c < D; c += blockDim.x)
+      xbar[((long)h * nb + B) * D + c] = (((s_part[0][c] + s_part[1][c]) + s_part[2][c]) + s_part[3][c]) / (float)n_real;
+  }
   if (xpt) {
+    __syncthreads();
     // [D][BK]: a thread packs VE consecutive j of one column c into 16 bytes
     constexpr int VE = 16 / sizeof(T);
     if (BK % VE == 0) {
@@ -92,13 +130,6 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ x,
       }
     }
   }
-  if (xbar && !ctx) {
-    for (int c = tid; c < D; c += blockDim.x) {
-      float s = 0.f;
-      for (int j = 0; j < n_real; ++j) s += Elem<T>::load(tile + j * RS + c);
-      xbar[((long)h * nb + B) * D + c] = s / (float)n_real;
-    }
-  }
 }
 
 template <typename T, int D>
@@ -112,7 +143,7 @@ static int gather_t(int H, int N, int Nv, int BK, const void* x, const int32_t* 
     hipFuncSetAttribute((const void*)gather_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
     attr = true;
   }
-  hipLaunchKernelGGL((gather_kernel<T, D>), dim3(H * nbt), dim3(256), lds, st, (const T*)x, perm,
+  hipLaunchKernelGGL((gather_kernel<T, D>), dim3(H * nbt), dim3(256), xpt ? lds : 0, st, (const T*)x, perm,
                      (T*)xp, (T*)xpt, xbar, N, Nv, BK, nb, nbt, perm == nullptr ? 1 : 0);
   return spark_check_launch("gather");
 }
