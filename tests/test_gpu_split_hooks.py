@@ -7,10 +7,12 @@ test hooks, bit for bit against the oracle's capacity_partition and
 argmin_lowest_id.
 
 * spark_debug_partition_level: rows whose groups take each of the top
-  level's three kernel paths (256-thread select below 65 blocks, 1024-thread
-  select, the many-workgroup threshold above 512 blocks), with values drawn
-  from a tie-heavy set (+-0, +-inf, NaN, repeated numbers) and from a
-  continuous distribution, and ragged last blocks.
+  level's two kernel paths (the one-workgroup select up to 64 blocks, the
+  many-workgroup radix rounds and segmented partition above), on both sides
+  of the boundary (64 and 65 blocks: a second segment of one position) and
+  with unaligned rows, with values drawn from a tie-heavy set (+-0, +-inf,
+  NaN, repeated numbers) and from a continuous distribution, and ragged
+  last blocks.
 * spark_debug_argmin: the pole choice's (value, id) ordering on the same
   kinds of rows, 1 to 5,000 values.
 """
@@ -51,7 +53,8 @@ def _rows(rng, count, n, kind):
     return s.astype(np.float32), ids.astype(np.int32)
 
 
-@pytest.mark.parametrize("n,block", [(37, 8), (1000, 64), (9000, 64), (70000, 128), (70001, 128)])
+@pytest.mark.parametrize("n,block", [(37, 8), (1000, 64), (8192, 128), (8193, 128), (9000, 64), (70000, 128),
+                                     (70001, 128)])
 @pytest.mark.parametrize("kind", ["ties", "few", "normal"])
 def test_capacity_partition_matches_oracle(n, block, kind):
     rng = np.random.default_rng(n * 7 + block + len(kind))
