@@ -1207,6 +1207,99 @@ __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
   auto matrix_slot = [&](auto pv_tag, auto qk_tag, int t, const SlotLoads&) {
     constexpr bool PV = decltype(pv_tag)::value, QK = decltype(qk_tag)::value;
     __builtin_amdgcn_s_setprio(2);
+    if constexpr (PV && QK && !FP8) {
+      // P V(t-1) then S^T(t) as one stream of 16 k-steps with one operand
+      // pipeline: the first K operands are read under the last P V MFMAs
+      const unsigned char* sV = smem + (2 + buf_of(grp, t - 1)) * PAIR_TB;
+      const unsigned char* sK = smem + buf_of(grp, t) * PAIR_TB;
+      auto opnd = [&](int i, int x) {
+        return *reinterpret_cast<const bf16x8*>(((i < 8) ? sV : sK) + ro[i & 7] + x * 8192);
+      };
+      bf16x8 op[16][4];
+#pragma unroll
+      for (int i = 0; i < D128_PF; ++i)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) op[i][x] = opnd(i, x);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i + D128_PF < 16) {
+#pragma unroll
+          for (int x = 0; x < 4; ++x) op[i + D128_PF][x] = opnd(i + D128_PF, x);
+        }
+        if (i < 8) {
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt)
+            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i][dt], pop[i], oacc[dt], 0, 0, 0);
+        } else {
+          if (i == 8) {
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) sacc[jt][v] = 0.f;
+          }
+#pragma unroll
+          for (int jt = 0; jt < 4; ++jt)
+            sacc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i][jt], qop[i - 8], sacc[jt], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      return;
+    }
+    if constexpr (PV && QK && FP8) {
+      // P V(t-1), then S^T(t) on fp8 operands; the first half of the K reads
+      // is issued under the last P V step's MFMAs
+      const unsigned char* sV = smem + (2 + buf_of(grp, t - 1)) * PAIR_TB;
+      const unsigned char* sK = smem + buf_of(grp, t) * PAIR_TB;
+      bf16x8 vop[BK / 16][4];
+      i32x8 kop8[2][4];
+      auto read_k8 = [&](int s2) {
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          const uint4 lo = *reinterpret_cast<const uint4*>(sK + ro8[s2][0] + jt * 4096);
+          const uint4 hi = *reinterpret_cast<const uint4*>(sK + ro8[s2][1] + jt * 4096);
+          kop8[s2][jt] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                               (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+      };
+#pragma unroll
+      for (int k = 0; k < D128_PF; ++k)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) vop[k][dt] = *reinterpret_cast<const bf16x8*>(sV + ro[k] + dt * 8192);
+#pragma unroll
+      for (int k = 0; k < BK / 16; ++k) {
+        if (k + D128_PF < BK / 16) {
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+            vop[k + D128_PF][dt] = *reinterpret_cast<const bf16x8*>(sV + ro[k + D128_PF] + dt * 8192);
+        }
+        if (k == BK / 16 - 1) read_k8(0);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[k][dt], pop[k], oacc[dt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sacc[jt][v] = 0.f;
+      read_k8(1);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt)
+          sacc[jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop8[s2][jt], q8[s2], sacc[jt], 0, 0, 0,
+                                                                     0, 0, 0);
+      // each MFMA of the first half followed by two reads of the second
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_s_setprio(0);
+      return;
+    }
     if constexpr (PV) {
       const unsigned char* sV = smem + (2 + buf_of(grp, t - 1)) * PAIR_TB;
       bf16x8 vop[BK / 16][4];
