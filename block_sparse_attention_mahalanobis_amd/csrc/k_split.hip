@@ -779,6 +779,118 @@ __global__ __launch_bounds__(SEG_T) void seg_partition(const float* __restrict__
   partition_tile<SEG_T>(k, idv, i0, n, thr, ties_needed, cL, run_lt, run_eq, s_tmp, s_stage, ids_out + base);
 }
 
+// Groups of at most 64 blocks, score pass and capacity select fused: one
+// SPL_T workgroup per group gathers the group's rows block by block (ids
+// staged in LDS, the same lane layout and FMA order as score_kernel),
+// keeps every score's order key in LDS, radix-selects the c_L-th key there
+// and stable-partitions the ids: the scores never go to memory (the score
+// pass's small writes cost ~10% of its time) and are never re-read.
+template <typename T, int D>
+__global__ __launch_bounds__(SPL_T) void score_select_small(const T* __restrict__ xh,
+                                                            const int32_t* __restrict__ ids_in,
+                                                            int32_t* __restrict__ ids_out,
+                                                            const float* __restrict__ diff, int N, int BK,
+                                                            int nb, int level, int S) {
+  using CR = ChunkRows<T, D>;
+  constexpr int NT = SPL_T, E = 8, VE = CR::VE, CPR = CR::CPR, RPP = CR::RPP;
+  extern __shared__ uint32_t s_keys[];   // [n] descending-order keys
+  __shared__ int32_t s_ids[128];
+  __shared__ int s_hist[256];
+  __shared__ int s_whist[NT / 64][256];
+  __shared__ int s_tmp[NT / 64];
+  __shared__ int32_t s_stage[NT * E];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_need;
+  const int slot = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+  const int wave = tid >> 6;
+  int start, nbg;
+  if (!group_of_slot(slot, level, nb, start, nbg)) return;
+  const long g0 = (long)start * BK;
+  const int n = (int)(min((long)N, (long)(start + nbg) * BK) - g0);
+  const long base = (long)t * N + g0;
+  if (nbg < 2) {  // a leaf carried through this level: copy
+    for (int i = tid; i < n; i += NT) ids_out[base + i] = ids_in[base + i];
+    return;
+  }
+  const int cL = ((nbg + 1) >> 1) * BK;
+  // scores, one block of the group at a time
+  {
+    const int rg = tid / CPR, c = (tid % CPR) * VE;
+    float vec[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) vec[e] = diff[((long)t * S + slot) * D + c + e];
+    const T* xt = xh + (long)t * N * D;
+    for (int b0 = 0; b0 < n; b0 += BK) {
+      const int n_real = min(BK, n - b0);
+      stage_ids(s_ids, ids_in + base + b0, n_real);
+      CR rows;
+      rows.load(xt, s_ids, n_real, rg, c);
+#pragma unroll
+      for (int it = 0; it < CR::NIT; ++it) {
+        const int j = it * RPP + rg;
+        float v[VE];
+        rows.get(it, v);
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc = fmaf(v[e], vec[e], acc);
+        acc = group_sum<CPR>(acc);
+        if (j < n_real && (tid % CPR) == 0) s_keys[b0 + j] = pref_key_desc(acc);
+      }
+      __syncthreads();   // s_ids is restaged by the next block
+    }
+  }
+  if (tid == 0) {
+    s_prefix = 0u;
+    s_need = cL;
+  }
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < (NT / 64) * 256; i += NT) (&s_whist[0][0])[i] = 0;
+    __syncthreads();
+    const uint32_t pre = s_prefix;
+    const uint32_t hmask = (shift == 24) ? 0u : (0xffffffffu << (shift + 8));
+    for (int i = tid; i < n; i += NT) {
+      const uint32_t k = s_keys[i];
+      if ((k & hmask) == pre) atomicAdd(&s_whist[wave][(k >> shift) & 255], 1);
+    }
+    __syncthreads();
+    for (int i = tid; i < 256; i += NT) {
+      int c = 0;
+#pragma unroll
+      for (int w = 0; w < NT / 64; ++w) c += s_whist[w][i];
+      s_hist[i] = c;
+    }
+    __syncthreads();
+    if (tid < 64) radix_pick(s_hist, &s_prefix, &s_need, shift);
+    __syncthreads();
+  }
+  const uint32_t thr = s_prefix;
+  const int ties_needed = s_need;
+  const bool vec_ok = (base & 3) == 0;
+  int run_lt = 0, run_eq = 0;
+  for (int p0 = 0; p0 < n; p0 += NT * E) {
+    const int q = p0 + tid * E;
+    uint32_t k[E];
+    int32_t idv[E];
+    if (vec_ok && q + E <= n) {
+      const int4 i0 = *reinterpret_cast<const int4*>(ids_in + base + q);
+      const int4 i1 = *reinterpret_cast<const int4*>(ids_in + base + q + 4);
+      const int32_t iv[E] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        k[e] = s_keys[q + e];
+        idv[e] = iv[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        k[e] = (q + e < n) ? s_keys[q + e] : 0xffffffffu;
+        idv[e] = (q + e < n) ? ids_in[base + q + e] : 0;
+      }
+    }
+    partition_tile<NT>(k, idv, p0, n, thr, ties_needed, cL, run_lt, run_eq, s_tmp, s_stage, ids_out + base);
+  }
+}
+
 // Groups of at most 64 blocks: one workgroup per group radix-selects the
 // c_L-th key of the group's scores (streamed from global; L2-resident at
 // these sizes), then stable-partitions the ids tile by tile.
@@ -1321,10 +1433,11 @@ static int split_t(int count, int N, int BK, const void* xhv, int32_t* perm_lo,
       hipLaunchKernelGGL((argmin_reduce<T, D>), gs, dim3(64), 0, st, mpart, xh, poleA, poleB, diff, N, p.nb, lev, p.S, 0);
       hipLaunchKernelGGL((argmin_partial<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, cen, poleA, mpart, N, BK, p.nb, lev, p.S, 1);
       hipLaunchKernelGGL((argmin_reduce<T, D>), gs, dim3(64), 0, st, mpart, xh, poleA, poleB, diff, N, p.nb, lev, p.S, 1);
-      hipLaunchKernelGGL((score_kernel<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, diff, s, N, BK, p.nb, lev, p.S);
-      // groups of more than 64 blocks: the threshold and the partition by
-      // many workgroups per group; smaller ones: one workgroup per group
+      // groups of more than 64 blocks: scores to memory, then the threshold
+      // and the partition by many workgroups per group; smaller ones: one
+      // workgroup per group scores, selects and partitions
       if (wide_select(p.nb, lev)) {
+        hipLaunchKernelGGL((score_kernel<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, diff, s, N, BK, p.nb, lev, p.S);
         const int gmax = (p.nb + (1 << lev) - 1) >> lev;   // largest group, blocks
         const int nseg_max = (int)(((long)gmax * BK + RG_SEG - 1) / RG_SEG);
         for (int shift = 24; shift >= 0; shift -= 8) {
@@ -1338,7 +1451,9 @@ static int split_t(int count, int N, int BK, const void* xhv, int32_t* perm_lo,
         hipLaunchKernelGGL(seg_partition, dim3(S * nseg_max, count), dim3(SEG_T), 0, st, s, cur, nxt, N, BK,
                            p.nb, lev, (const int*)rec, (const int*)segcnt, p.S, nseg_max);
       } else {
-        hipLaunchKernelGGL(select_partition<SPL_T>, gs, dim3(SPL_T), 0, st, s, cur, nxt, N, BK, p.nb, lev);
+        const int gmax = (p.nb + (1 << lev) - 1) >> lev;   // largest group, blocks
+        hipLaunchKernelGGL((score_select_small<T, D>), gs, dim3(SPL_T), (size_t)std::min(N, gmax * BK) * 4, st, xh,
+                           cur, nxt, diff, N, BK, p.nb, lev, p.S);
       }
       int rc = spark_check_launch("split level");
       if (rc) return rc;
