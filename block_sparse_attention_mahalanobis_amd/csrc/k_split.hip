@@ -612,7 +612,9 @@ __device__ __forceinline__ void fetch8(const float* __restrict__ s, const int32_
 // rank among ties is < ties_needed, so the lefts before p number lt(p) +
 // min(eq(p), ties_needed): one scan of the packed (lt, eq) counts places
 // every element.  run_lt / run_eq: those counts before the tile, advanced
-// past it.  The tile's lefts land in one run of out, its rights in another:
+// past it.  lds_left (optional): an LDS copy of the left child's ids at
+// their output positions (each at most its own position, so it may alias
+// keys of this and earlier tiles, already read).  The tile's lefts land in one run of out, its rights in another:
 // the ids are staged in LDS in output order and both runs written with
 // contiguous stores.  Every thread of the workgroup calls it (three
 // barriers, the stage reusable on return).
@@ -620,7 +622,7 @@ template <int NT>
 __device__ __forceinline__ void partition_tile(const uint32_t (&k)[8], const int32_t (&idv)[8], int p0, int n,
                                                uint32_t thr, int ties_needed, int cL, int& run_lt,
                                                int& run_eq, int* s_tmp, int32_t* s_stage,
-                                               int32_t* __restrict__ out) {
+                                               int32_t* __restrict__ out, int32_t* lds_left = nullptr) {
   constexpr int E = 8;
   const int tid = threadIdx.x;
   int lt = 0, eq = 0;
@@ -661,6 +663,7 @@ __device__ __forceinline__ void partition_tile(const uint32_t (&k)[8], const int
   for (int j = tid; j < tile_n; j += NT) {
     const int dst = (j < nl_tile) ? lb_tile + j : cL + rb_tile + (j - nl_tile);
     if (dst < n) out[dst] = s_stage[j];
+    if (lds_left != nullptr && j < nl_tile) lds_left[dst] = s_stage[j];
   }
   __syncthreads();   // the stage is rewritten by the next tile
   run_lt += tot >> 16;
@@ -789,7 +792,9 @@ template <typename T, int D>
 __global__ __launch_bounds__(SPL_T) void score_select_small(const T* __restrict__ xh,
                                                             const int32_t* __restrict__ ids_in,
                                                             int32_t* __restrict__ ids_out,
-                                                            const float* __restrict__ diff, int N, int BK,
+                                                            const float* __restrict__ diff,
+                                                            const double* __restrict__ cen_par,
+                                                            double* __restrict__ cen_next, int N, int BK,
                                                             int nb, int level, int S) {
   using CR = ChunkRows<T, D>;
   constexpr int NT = SPL_T, E = 8, VE = CR::VE, CPR = CR::CPR, RPP = CR::RPP;
@@ -801,6 +806,7 @@ __global__ __launch_bounds__(SPL_T) void score_select_small(const T* __restrict_
   __shared__ int32_t s_stage[NT * E];
   __shared__ uint32_t s_prefix;
   __shared__ int s_need;
+  __shared__ float s_p[NT / 64][D];
   const int slot = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
   const int wave = tid >> 6;
   int start, nbg;
@@ -887,7 +893,70 @@ __global__ __launch_bounds__(SPL_T) void score_select_small(const T* __restrict_
         idv[e] = (q + e < n) ? ids_in[base + q + e] : 0;
       }
     }
-    partition_tile<NT>(k, idv, p0, n, thr, ties_needed, cL, run_lt, run_eq, s_tmp, s_stage, ids_out + base);
+    partition_tile<NT>(k, idv, p0, n, thr, ties_needed, cL, run_lt, run_eq, s_tmp, s_stage, ids_out + base,
+                       cen_next != nullptr ? reinterpret_cast<int32_t*>(s_keys) : nullptr);
+  }
+  if (cen_next == nullptr) return;
+  // the next level's centroid sums of the two children, exactly as the
+  // centroid pass and its reduce would give them: each block of the left
+  // child summed in fp32 in cent_partial's lane order and wave order, the
+  // blocks added in fp64 in cent_reduce's eight chains, the right child's
+  // sum the parent's minus the left's
+  // the left child's ids, in order, are in LDS (over the keys); the last
+  // tile's barrier made them visible
+  const int32_t* left_ids = reinterpret_cast<const int32_t*>(s_keys);
+  using CR = ChunkRows<T, D>;
+  constexpr int RGW = 64 / CPR;
+  const int lane = tid & 63, rl = lane / CPR, cc = (tid % CPR) * VE;
+  const T* xt = xh + (long)t * N * D;
+  const int nL = (nbg + 1) >> 1;   // left child's blocks
+  double a[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) a[u] = 0.0;
+  const int nfull8 = nL & ~7;
+  for (int lb = 0; lb < nL; ++lb) {
+    const int cb = start + lb;
+    const int n_real = min(BK, N - cb * BK);
+    CR rows;
+    rows.load_rows(xt, left_ids + lb * BK, n_real, 32 * wave + rl, RGW, cc);
+    float acc[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int it = 0; it < CR::NIT; ++it) {
+      float v[VE];
+      rows.get(it, v);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc[e] += v[e];
+    }
+#pragma unroll
+    for (int e = 0; e < VE; ++e) acc[e] = group_sum<64, CPR>(acc[e]);
+    if (lane < CPR)
+#pragma unroll
+      for (int e = 0; e < VE; ++e) s_p[wave][cc + e] = acc[e];
+    __syncthreads();
+    for (int c = tid; c < D; c += NT) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < NT / 64; ++w) sum += s_p[w][c];
+      // cent_reduce's chains: blocks in full runs of 8 go to chain lb % 8,
+      // the rest to chain 0 (a thread owns one column: a[] per column)
+      if (c == tid) {
+        const int u = (lb < nfull8) ? (lb & 7) : 0;
+#pragma unroll
+        for (int uu = 0; uu < 8; ++uu)
+          if (uu == u) a[uu] += (double)sum;
+      }
+    }
+    __syncthreads();   // s_p is reused by the next block
+  }
+  if (tid < D) {
+    const double sl = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+    const int lslot = 2 * slot;   // the children's slots at the next level
+    cen_next[((long)t * S + lslot) * D + tid] = sl;
+    int rstart, rnb;
+    if (group_of_slot(lslot + 1, level + 1, nb, rstart, rnb) && rnb >= 2)
+      cen_next[((long)t * S + lslot + 1) * D + tid] = cen_par[((long)t * S + slot) * D + tid] - sl;
   }
 }
 
@@ -1423,12 +1492,16 @@ static int split_t(int count, int N, int BK, const void* xhv, int32_t* perm_lo,
       const int S = 1 << lev;
       dim3 gc(p.nb, count), gs(S, count), gp(lev == 0 ? 1 : S / 2, count);
       double* cen = cen_ab[lev & 1];             // this level's sums; the parents' in the other
-      if (lev > 0 || !level0_given)   // else the whitening pass stored the root's partials
-        hipLaunchKernelGGL((cent_partial<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, cpart, N, BK, p.nb, lev);
-      if ((p.nb >> lev) > 64)
-        hipLaunchKernelGGL((cent_reduce<D, 1024>), gp, dim3(1024), 0, st, cpart, cen_ab[(lev + 1) & 1], cen, p.nb, lev, p.S);
-      else
-        hipLaunchKernelGGL((cent_reduce<D, D>), gp, dim3(D), 0, st, cpart, cen_ab[(lev + 1) & 1], cen, p.nb, lev, p.S);
+      // below a small level its fused kernel has already stored these sums
+      const bool sums_given = lev > 0 && !wide_select(p.nb, lev - 1);
+      if (!sums_given) {
+        if (lev > 0 || !level0_given)   // else the whitening pass stored the root's partials
+          hipLaunchKernelGGL((cent_partial<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, cpart, N, BK, p.nb, lev);
+        if ((p.nb >> lev) > 64)
+          hipLaunchKernelGGL((cent_reduce<D, 1024>), gp, dim3(1024), 0, st, cpart, cen_ab[(lev + 1) & 1], cen, p.nb, lev, p.S);
+        else
+          hipLaunchKernelGGL((cent_reduce<D, D>), gp, dim3(D), 0, st, cpart, cen_ab[(lev + 1) & 1], cen, p.nb, lev, p.S);
+      }
       hipLaunchKernelGGL((argmin_partial<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, cen, poleA, mpart, N, BK, p.nb, lev, p.S, 0);
       hipLaunchKernelGGL((argmin_reduce<T, D>), gs, dim3(64), 0, st, mpart, xh, poleA, poleB, diff, N, p.nb, lev, p.S, 0);
       hipLaunchKernelGGL((argmin_partial<T, D>), gc, dim3(SPL_T), 0, st, xh, cur, cen, poleA, mpart, N, BK, p.nb, lev, p.S, 1);
@@ -1453,7 +1526,8 @@ static int split_t(int count, int N, int BK, const void* xhv, int32_t* perm_lo,
       } else {
         const int gmax = (p.nb + (1 << lev) - 1) >> lev;   // largest group, blocks
         hipLaunchKernelGGL((score_select_small<T, D>), gs, dim3(SPL_T), (size_t)std::min(N, gmax * BK) * 4, st, xh,
-                           cur, nxt, diff, N, BK, p.nb, lev, p.S);
+                           cur, nxt, diff, (const double*)cen, lev + 1 < p.Lf ? cen_ab[(lev + 1) & 1] : nullptr, N,
+                           BK, p.nb, lev, p.S);
       }
       int rc = spark_check_launch("split level");
       if (rc) return rc;
