@@ -21,13 +21,18 @@
 //   cent_reduce   -> per-group centroid sum in fp64 (fixed chunk order:
 //                    deterministic); a right child's is parent - left
 //   argmin_partial/argmin_reduce (twice: pole A, pole B; 64-bit (key, id) mins)
-//   score         -> s_i for every position
-//   capacity select: the exact c_L-th key by radix select, then a stable
-//                 partition of the ids.  Groups of more than 64 blocks:
-//                 radix_hist / radix_pick_groups rounds over many
-//                 workgroups, then seg_count / seg_partition, one workgroup
-//                 per 8192 positions; smaller groups: select_partition, one
-//                 workgroup per group.
+//   groups of more than 64 blocks:
+//     score       -> s_i for every position, to memory
+//     capacity select: the exact c_L-th key by radix_hist /
+//                 radix_pick_groups rounds over many workgroups, then
+//                 seg_count / seg_partition, one workgroup per 8192
+//                 positions (a stable partition of the ids)
+//   groups of at most 64 blocks: score_select_small, one workgroup per
+//     group: scores into LDS, the same radix select and stable partition
+//     there, and the next level's centroid sums (that level then skips
+//     cent_partial / cent_reduce).
+// The capacity select is exact: the c_L-th key and how many of its ties go
+// left, so every form gives the same permutation.
 // Once every group fits in LDS (<= FIN_MAX tokens) one workgroup per group
 // loads its rows once and finishes all remaining levels in LDS.
 #include "common.hpp"
