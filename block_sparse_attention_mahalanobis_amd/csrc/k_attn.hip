@@ -1429,8 +1429,23 @@ __global__ __launch_bounds__(PAIR_NT, 1) void attn_pair_d128(
             pop[2 * jt + hh][e] = (__bf16)pv;
             ps[e & 1] += pv;
           }
-          issue_load(L, 2 * (2 * jt + hh));
-          issue_load(L, 2 * (2 * jt + hh) + 1);
+          if constexpr (EXACT) {
+            // The slot's 16 loads go out 4 per group over the first half of
+            // the exps: late enough that the wave does not stall on a burst
+            // before its first exp, early enough that the last ones land
+            // before the slot ends (2 per group, to the end, is slower).  The
+            // empty asm takes this group's P and sums ahead of its loads;
+            // without it the compiler sinks every exp below the last
+            // (conditional) load block, so all 16 loads go out first.
+            asm volatile("" : "+v"(pop[2 * jt + hh]), "+v"(ps[0]), "+v"(ps[1]));
+            if (2 * jt + hh < 4) {
+#pragma unroll
+              for (int u = 0; u < 4; ++u) issue_load(L, 4 * (2 * jt + hh) + u);
+            }
+          } else {
+            issue_load(L, 2 * (2 * jt + hh));
+            issue_load(L, 2 * (2 * jt + hh) + 1);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       psum = ps[0] + ps[1];
