@@ -28,6 +28,58 @@ __device__ __forceinline__ uint32_t pref_key(float s) {
 // row's keys are first loaded into registers (block B in lane B % 64, slot
 // B / 64; nb <= 64 KPL), so neither the radix rounds nor the emission read
 // LDS per key; KPL = 0: the keys are read from LDS.
+// wave_radix_select with the histogram in SEL_NC copies (lane % SEL_NC
+// picks the copy), so keys that share a digit contend SEL_NC times less
+constexpr int SEL_NC = 2;
+template <typename CountFn>
+__device__ __forceinline__ uint32_t wave_radix_select_nc(int k, int* hist, int* ties_needed,
+                                                         CountFn&& count) {
+  const int lane = threadIdx.x & 63;
+  uint32_t prefix = 0;
+  int need = k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+#pragma unroll
+    for (int j = 0; j < 4 * SEL_NC; ++j) hist[64 * j + lane] = 0;
+    wave_lds_sync();
+    const uint32_t hmask = (shift == 24) ? 0u : (0xffffffffu << (shift + 8));
+    count(prefix, hmask, shift, hist + 256 * (lane % SEL_NC));
+    wave_lds_sync();
+    int c[4], run = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int v = 0;
+#pragma unroll
+      for (int r = 0; r < SEL_NC; ++r) v += hist[256 * r + 4 * lane + j];
+      run += v;
+      c[j] = run;
+    }
+    wave_lds_sync();
+    int incl = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    const int base = incl - run;
+    int found = -1, fb = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int before = base + (j ? c[j - 1] : 0);
+      if (before < need && base + c[j] >= need) {
+        found = 4 * lane + j;
+        fb = before;
+      }
+    }
+    const uint64_t m = __builtin_amdgcn_ballot_w64(found >= 0);
+    const int src = __builtin_ctzll(m);
+    const int digit = __builtin_amdgcn_readlane(found, src);
+    need -= __builtin_amdgcn_readlane(fb, src);
+    prefix |= (uint32_t)digit << shift;
+  }
+  *ties_needed = need;
+  return prefix;
+}
+
 template <int KPL>
 __device__ __forceinline__ void row_topk(const uint32_t* s_key, int nb, int topk, int* hist,
                                          int32_t* __restrict__ out) {
@@ -41,11 +93,11 @@ __device__ __forceinline__ void row_topk(const uint32_t* s_key, int nb, int topk
       const int B = 64 * j + lane;
       kr[j] = (B < nb) ? s_key[B] : 0xffffffffu;
     }
-    thr = wave_radix_select(topk, hist, &ties_needed, [&](uint32_t prefix, uint32_t hmask, int shift) {
+    thr = wave_radix_select_nc(topk, hist, &ties_needed, [&](uint32_t prefix, uint32_t hmask, int shift, int* h) {
 #pragma unroll
       for (int j = 0; j < KPL; ++j) {
         const int B = 64 * j + lane;
-        if (B < nb && (kr[j] & hmask) == prefix) atomicAdd(&hist[(kr[j] >> shift) & 255], 1);
+        if (B < nb && (kr[j] & hmask) == prefix) atomicAdd(&h[(kr[j] >> shift) & 255], 1);
       }
     });
   } else {
@@ -95,7 +147,7 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(const float* __restrict__
                                                        int qb, float rsd) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint32_t* s_keys = reinterpret_cast<uint32_t*>(smem);  // [qb][nb]
-  __shared__ int s_whist[SEL_T / 64][256];                 // one radix histogram per wave
+  __shared__ int s_whist[SEL_T / 64][256 * SEL_NC];        // SEL_NC radix histograms per wave
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nqb = (nb + qb - 1) / qb;
   const int h = blockIdx.x / nqb, A0 = (blockIdx.x % nqb) * qb;
