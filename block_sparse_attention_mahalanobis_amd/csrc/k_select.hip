@@ -14,7 +14,7 @@
 
 namespace spark {
 
-constexpr int SEL_T = 256;
+constexpr int SEL_T = 512;
 
 // Order key for "largest score first, NaN last": ascending key == preference.
 __device__ __forceinline__ uint32_t pref_key(float s) {
@@ -128,8 +128,8 @@ __device__ __forceinline__ void row_topk(const uint32_t* s_key, int nb, int topk
   }
 }
 
-constexpr int SEL_QB = 8;   // query blocks per workgroup (they share each k_bar read)
-constexpr size_t SEL_LDS = 128 * 1024;   // dynamic LDS of a select workgroup
+constexpr int SEL_QB = 16;   // query blocks per workgroup (they share each k_bar read)
+constexpr size_t SEL_LDS = 136 * 1024;   // dynamic LDS of a select workgroup
 
 // Byte offset of the query means after the qb rows of nb keys, rounded up to
 // 16 bytes.
