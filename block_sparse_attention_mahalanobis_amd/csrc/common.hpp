@@ -84,11 +84,13 @@ __device__ __forceinline__ uint32_t float_key_asc(float f) {
 }
 
 // k-th smallest (1-based) of n uint32 keys, found by ONE wave with a private
-// 256-int LDS histogram: 4 radix rounds of 8 bits (count the keys that match
-// the prefix so far, then pick the digit holding rank k).  Returns the key;
-// *ties_needed = k - count(key < result).  count(prefix, hmask, shift)
-// adds, for every key with (key & hmask) == prefix, one to
-// hist[(key >> shift) & 255]; the keys may sit in LDS or in registers.
+// LDS histogram of NC x 256 ints: 4 radix rounds of 8 bits (count the keys
+// that match the prefix so far, then pick the digit holding rank k).
+// Returns the key; *ties_needed = k - count(key < result).
+// count(prefix, hmask, shift, h) adds, for every key with (key & hmask) ==
+// prefix, one to h[(key >> shift) & 255], where h is the lane's copy of the
+// histogram (lane % NC picks it: keys that share a digit then contend NC
+// times less on the same LDS word); the keys may sit in LDS or in registers.
 //
 // The hardware runs one wave's LDS instructions in issue order, but to the
 // compiler the other lanes' atomics race with the plain reads: without an
@@ -97,7 +99,7 @@ __device__ __forceinline__ uint32_t float_key_asc(float f) {
 // the wave's LDS operations and is a compiler memory barrier.
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-template <typename CountFn>
+template <int NC = 1, typename CountFn>
 __device__ __forceinline__ uint32_t wave_radix_select(int k, int* hist, int* ties_needed,
                                                       CountFn&& count) {
   const int lane = threadIdx.x & 63;
@@ -105,15 +107,18 @@ __device__ __forceinline__ uint32_t wave_radix_select(int k, int* hist, int* tie
   int need = k;
   for (int shift = 24; shift >= 0; shift -= 8) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) hist[4 * lane + j] = 0;
+    for (int j = 0; j < 4 * NC; ++j) hist[64 * j + lane] = 0;
     wave_lds_sync();
     const uint32_t hmask = (shift == 24) ? 0u : (0xffffffffu << (shift + 8));
-    count(prefix, hmask, shift);
+    count(prefix, hmask, shift, hist + 256 * (lane % NC));
     wave_lds_sync();
     int c[4], run = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      run += hist[4 * lane + j];
+      int v = 0;
+#pragma unroll
+      for (int r = 0; r < NC; ++r) v += hist[256 * r + 4 * lane + j];
+      run += v;
       c[j] = run;
     }
     wave_lds_sync();  // every lane has read its bins before the next round clears them
@@ -147,10 +152,10 @@ __device__ __forceinline__ uint32_t wave_radix_select(int k, int* hist, int* tie
 __device__ __forceinline__ uint32_t wave_radix_kth(const uint32_t* keys, int n, int k, int* hist,
                                                    int* ties_needed) {
   const int lane = threadIdx.x & 63;
-  return wave_radix_select(k, hist, ties_needed, [&](uint32_t prefix, uint32_t hmask, int shift) {
+  return wave_radix_select(k, hist, ties_needed, [&](uint32_t prefix, uint32_t hmask, int shift, int* h) {
     for (int i = lane; i < n; i += 64) {
       const uint32_t key = keys[i];
-      if ((key & hmask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+      if ((key & hmask) == prefix) atomicAdd(&h[(key >> shift) & 255], 1);
     }
   });
 }

@@ -22,64 +22,14 @@ __device__ __forceinline__ uint32_t pref_key(float s) {
   return ~float_key_asc(s);
 }
 
+constexpr int SEL_NC = 2;   // radix histogram copies per wave
+
 // One row's top-k by one wave: the key of rank topk (radix select), then
 // the blocks below it and the first ties_needed blocks equal to it, in
 // ascending block order, each placed by a ballot prefix sum.  KPL > 0: the
 // row's keys are first loaded into registers (block B in lane B % 64, slot
 // B / 64; nb <= 64 KPL), so neither the radix rounds nor the emission read
 // LDS per key; KPL = 0: the keys are read from LDS.
-// wave_radix_select with the histogram in SEL_NC copies (lane % SEL_NC
-// picks the copy), so keys that share a digit contend SEL_NC times less
-constexpr int SEL_NC = 2;
-template <typename CountFn>
-__device__ __forceinline__ uint32_t wave_radix_select_nc(int k, int* hist, int* ties_needed,
-                                                         CountFn&& count) {
-  const int lane = threadIdx.x & 63;
-  uint32_t prefix = 0;
-  int need = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-#pragma unroll
-    for (int j = 0; j < 4 * SEL_NC; ++j) hist[64 * j + lane] = 0;
-    wave_lds_sync();
-    const uint32_t hmask = (shift == 24) ? 0u : (0xffffffffu << (shift + 8));
-    count(prefix, hmask, shift, hist + 256 * (lane % SEL_NC));
-    wave_lds_sync();
-    int c[4], run = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int v = 0;
-#pragma unroll
-      for (int r = 0; r < SEL_NC; ++r) v += hist[256 * r + 4 * lane + j];
-      run += v;
-      c[j] = run;
-    }
-    wave_lds_sync();
-    int incl = run;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += t;
-    }
-    const int base = incl - run;
-    int found = -1, fb = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int before = base + (j ? c[j - 1] : 0);
-      if (before < need && base + c[j] >= need) {
-        found = 4 * lane + j;
-        fb = before;
-      }
-    }
-    const uint64_t m = __builtin_amdgcn_ballot_w64(found >= 0);
-    const int src = __builtin_ctzll(m);
-    const int digit = __builtin_amdgcn_readlane(found, src);
-    need -= __builtin_amdgcn_readlane(fb, src);
-    prefix |= (uint32_t)digit << shift;
-  }
-  *ties_needed = need;
-  return prefix;
-}
-
 template <int KPL>
 __device__ __forceinline__ void row_topk(const uint32_t* s_key, int nb, int topk, int* hist,
                                          int32_t* __restrict__ out) {
@@ -93,7 +43,7 @@ __device__ __forceinline__ void row_topk(const uint32_t* s_key, int nb, int topk
       const int B = 64 * j + lane;
       kr[j] = (B < nb) ? s_key[B] : 0xffffffffu;
     }
-    thr = wave_radix_select_nc(topk, hist, &ties_needed, [&](uint32_t prefix, uint32_t hmask, int shift, int* h) {
+    thr = wave_radix_select<SEL_NC>(topk, hist, &ties_needed, [&](uint32_t prefix, uint32_t hmask, int shift, int* h) {
 #pragma unroll
       for (int j = 0; j < KPL; ++j) {
         const int B = 64 * j + lane;
